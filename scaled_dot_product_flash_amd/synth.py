@@ -1,0 +1,163 @@
+"""Seeded synthetic inputs for attention problems.
+
+This module holds no attention arithmetic: it only draws inputs.  Both the
+HIP path (through the tests and the benchmark) and the float64 oracle are fed
+from it, so the two sides see identical bits.
+
+Recipe (the same for every workload): numpy PCG64 ``default_rng(seed)``;
+draw order Q, K, V, then key lengths, then the mask; values are i.i.d. N(0, 1)
+in float32, rounded to nearest-even into the storage type (float16 via numpy,
+bfloat16 by bit rounding, kept as uint16 bit patterns).
+"""
+from __future__ import annotations
+
+import dataclasses
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+STORAGE = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}
+
+
+@dataclass(frozen=True)
+class Spec:
+    """Shape and options of one attention problem.
+
+    Layout tags: 'bshd' = [batch, positions, heads, head_dim] (positions
+    first), 'bhsd' = [batch, heads, positions, head_dim] (heads first).
+    ``q_layout`` applies to Q and O, ``kv_layout`` to K and V.
+    """
+    name: str
+    batch: int
+    q_heads: int
+    kv_heads: int
+    q_len: int
+    k_len: int
+    head_dim: int
+    dtype: str
+    seed: int
+    q_layout: str = "bshd"
+    kv_layout: str = "bshd"
+    causal: bool = False
+    causal_offset: Optional[int] = None
+    lse: bool = False
+    decode: bool = False
+    lens: Optional[str] = None        # None, 'uniform' (in [1, k_len]) or 'cross'
+    mask: Optional[str] = None        # None or 'keys' ([B,1,1,Lk], 10% -inf)
+    masked_rows: str = "nan"
+    lens_zero_at: int = 5             # 'cross' lengths: this batch entry has length 0
+    lens_full_at: int = 7             # ... and this one has the full k_len
+    mask_all_at: int = 2              # 'keys' mask: this batch entry is fully -inf
+    mask_p: float = 0.1
+
+    def replace(self, **kw) -> "Spec":
+        return dataclasses.replace(self, **kw)
+
+    @property
+    def flops(self) -> float:
+        """4*B*Hq*Lq*Lk*D, halved under the causal rule."""
+        f = 4.0 * self.batch * self.q_heads * self.q_len * self.k_len * self.head_dim
+        return f / 2 if self.causal and not self.decode else f
+
+
+# The five workloads the measurements and parity tests are built on.
+TINY_F32 = Spec("tiny fp32 MHA B1 H2 L64 D32", 1, 2, 2, 64, 64, 32, "f32", seed=1)
+CAUSAL_GQA_F32 = Spec("fp32 causal GQA prefill B2 H12/4 L512 D64", 2, 12, 4, 512, 512, 64,
+                      "f32", seed=2, causal=True, causal_offset=0, lse=True)
+CAUSAL_GQA_BF16 = Spec("bf16 causal GQA prefill B4 H32/8 L4096 D128", 4, 32, 8, 4096, 4096,
+                       128, "bf16", seed=3, causal=True, causal_offset=0, lse=True)
+DECODE_F16 = Spec("fp16 decode B64 H32/8 cache8192 D128", 64, 32, 8, 1, 8192, 128, "f16",
+                  seed=4, kv_layout="bhsd", causal=True, decode=True, lens="uniform")
+CROSS_MASK_F16 = Spec("fp16 cross-attention B8 H16 Lq1024 Lk2048 D64 mask+lens", 8, 16, 16,
+                      1024, 2048, 64, "f16", seed=5, q_layout="bhsd", kv_layout="bhsd",
+                      lens="cross", mask="keys")
+
+WORKLOADS = {
+    "tiny_f32": TINY_F32,
+    "causal_gqa_f32": CAUSAL_GQA_F32,
+    "causal_gqa_bf16": CAUSAL_GQA_BF16,
+    "decode_f16": DECODE_F16,
+    "cross_mask_f16": CROSS_MASK_F16,
+}
+
+
+def round_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns, round to nearest even (NaN kept NaN)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32)
+    r = ((u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16))
+    r = r.astype(np.uint16)
+    nan = np.isnan(x)
+    if nan.any():
+        r[nan] = ((u[nan] >> np.uint32(16)) | np.uint32(0x40)).astype(np.uint16)
+    return r
+
+
+def to_storage(x: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "f32":
+        return np.ascontiguousarray(x, dtype=np.float32)
+    if dtype == "f16":
+        return x.astype(np.float16)
+    if dtype == "bf16":
+        return round_bf16_bits(x)
+    raise ValueError(dtype)
+
+
+def shape_of(spec: Spec, which: str):
+    """Array shape of 'q'/'o' or 'k'/'v' in the spec's layout."""
+    if which in ("q", "o"):
+        L, H, lay = spec.q_len, spec.q_heads, spec.q_layout
+    else:
+        L, H, lay = spec.k_len, spec.kv_heads, spec.kv_layout
+    if lay == "bshd":
+        return (spec.batch, L, H, spec.head_dim)
+    return (spec.batch, H, L, spec.head_dim)
+
+
+@dataclass
+class Case:
+    spec: Spec
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    key_lens: Optional[np.ndarray]
+    mask: Optional[np.ndarray]
+
+
+def _normal(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=STORAGE[dtype])
+    step = 1 << 26
+    for s in range(0, n, step):          # chunked: keeps the float32 staging small
+        m = min(step, n - s)
+        out[s:s + m] = to_storage(rng.standard_normal(m, dtype=np.float32), dtype)
+    return out.reshape(shape)
+
+
+def generate(spec: Spec) -> Case:
+    rng = np.random.default_rng(spec.seed)
+    q = _normal(rng, shape_of(spec, "q"), spec.dtype)
+    k = _normal(rng, shape_of(spec, "k"), spec.dtype)
+    v = _normal(rng, shape_of(spec, "v"), spec.dtype)
+    lens = None
+    if spec.lens == "uniform":
+        lens = rng.integers(1, spec.k_len + 1, size=spec.batch).astype(np.int32)
+    elif spec.lens == "cross":
+        lens = rng.integers(1, spec.k_len + 1, size=spec.batch).astype(np.int32)
+        if spec.lens_zero_at < spec.batch:
+            lens[spec.lens_zero_at] = 0
+        if spec.lens_full_at < spec.batch:
+            lens[spec.lens_full_at] = spec.k_len
+    elif spec.lens is not None:
+        raise ValueError(spec.lens)
+    mask = None
+    if spec.mask == "keys":
+        hide = rng.random((spec.batch, spec.k_len)) < spec.mask_p
+        mask = np.where(hide, np.float32(-np.inf), np.float32(0.0)).astype(np.float32)
+        if spec.mask_all_at < spec.batch:
+            mask[spec.mask_all_at, :] = -np.inf
+        mask = mask.reshape(spec.batch, 1, 1, spec.k_len)
+    elif spec.mask is not None:
+        raise ValueError(spec.mask)
+    return Case(spec, q, k, v, lens, mask)

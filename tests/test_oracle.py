@@ -1,0 +1,453 @@
+"""Pins for the float64 oracle (CPU only).
+
+Each test checks the oracle against something other than itself: a closed
+form, a value or rule the pages print (tests/golden/), an invariant of the
+definition, or an independent float64 route built on library routines
+(numpy matmul + scipy.special.softmax) on tiny shapes.
+"""
+import math
+import os
+import zlib
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+from scaled_dot_product_flash_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+NEG_INF = np.float32(-np.inf)
+
+
+def _golden(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line.split())
+    return rows
+
+
+def _rand(shape, dtype, seed, scale=1.0):
+    rng = np.random.default_rng(seed)
+    return synth.to_storage(rng.standard_normal(shape).astype(np.float32) * scale, dtype)
+
+
+def _as_f64(a, dtype):
+    """Storage -> float64 through library conversions (numpy / torch)."""
+    if dtype == "bf16":
+        t = torch.from_numpy(a.astype(np.int16)).view(torch.bfloat16)
+        return t.to(torch.float64).numpy()
+    return a.astype(np.float64)
+
+
+def _bhsd(a, layout):
+    return a if layout == "bhsd" else np.transpose(a, (0, 2, 1, 3))
+
+
+def _library_attention(q, k, v, dtype, layout="bshd", causal=False, offset=None, scale=None,
+                       mask=None, key_lens=None, masked_rows="nan"):
+    """Independent float64 route: matmul + scipy softmax over an explicit
+    visibility matrix.  Returns O [B,Hq,Lq,D] and LSE [B,Hq,Lq]."""
+    Q = _bhsd(_as_f64(q, dtype), layout)
+    K = _bhsd(_as_f64(k, dtype), layout)
+    V = _bhsd(_as_f64(v, dtype), layout)
+    B, Hq, Lq, D = Q.shape
+    Hkv, Lk = K.shape[1], K.shape[2]
+    sc = 1.0 / math.sqrt(D) if scale is None else scale
+    off = (Lk - Lq) if offset is None else offset
+    O = np.zeros((B, Hq, Lq, D))
+    LSE = np.zeros((B, Hq, Lq))
+    for b in range(B):
+        kl = Lk if key_lens is None else min(max(int(key_lens[b]), 0), Lk)
+        for h in range(Hq):
+            g = h * Hkv // Hq
+            S = sc * (Q[b, h] @ K[b, g].T)
+            if mask is not None:
+                S = S + np.broadcast_to(mask, (B, Hq, Lq, Lk))[b, h].astype(np.float64)
+            vis = np.zeros((Lq, Lk), dtype=bool)
+            vis[:, :kl] = True
+            if causal:
+                vis &= np.arange(Lk)[None, :] <= np.arange(Lq)[:, None] + off
+            for i in range(Lq):
+                s = S[i][vis[i]]
+                if np.isnan(s).any() or (s == np.inf).any():
+                    O[b, h, i] = np.nan
+                    LSE[b, h, i] = np.nan
+                elif s.size == 0 or (s == -np.inf).all():
+                    O[b, h, i] = 0.0 if masked_rows == "zero" else np.nan
+                    LSE[b, h, i] = -np.inf
+                else:
+                    w = scipy.special.softmax(s)
+                    O[b, h, i] = w @ V[b, g][vis[i]]
+                    LSE[b, h, i] = scipy.special.logsumexp(s)
+    return O, LSE
+
+
+# --------------------------------------------------------------------------
+# Storage decoding and input rounding, against library conversions.
+
+def test_decode_f16_all_patterns():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    want = bits.view(np.float16).astype(np.float64)
+    got = np.array([oracle.decode_f16(int(b)) for b in bits])
+    nan = np.isnan(want)
+    assert (np.isnan(got) == nan).all()
+    assert (got[~nan] == want[~nan]).all()
+    assert np.signbit(got[~nan]).tolist() == np.signbit(want[~nan]).tolist()
+
+
+def test_decode_bf16_all_patterns():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    want = torch.from_numpy(bits.astype(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    got = np.array([oracle.decode_bf16(int(b)) for b in bits])
+    nan = np.isnan(want)
+    assert (np.isnan(got) == nan).all()
+    assert (got[~nan] == want[~nan]).all()
+
+
+def test_synth_bf16_rounding_matches_torch():
+    rng = np.random.default_rng(0)
+    x = np.concatenate([rng.standard_normal(100000).astype(np.float32) * 10,
+                        np.array([0.0, -0.0, np.inf, -np.inf, 1e-40, 3.3895314e38],
+                                 dtype=np.float32)])
+    want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = synth.round_bf16_bits(x)
+    assert (got == want).all()
+    assert np.isnan(_as_f64(synth.round_bf16_bits(np.array([np.nan], np.float32)), "bf16")).all()
+
+
+def test_synth_is_seeded_and_follows_recipe():
+    spec = synth.CROSS_MASK_F16.replace(q_len=16, k_len=40)
+    a, b = synth.generate(spec), synth.generate(spec)
+    for x, y in ((a.q, b.q), (a.k, b.k), (a.v, b.v), (a.mask, b.mask), (a.key_lens, b.key_lens)):
+        assert np.array_equal(x, y)
+    assert a.q.shape == (8, 16, 16, 64) and a.k.shape == (8, 16, 40, 64)
+    assert a.key_lens[5] == 0 and a.key_lens[7] == 40
+    assert (a.mask[2] == -np.inf).all()
+    assert a.mask.shape == (8, 1, 1, 40)
+
+
+# --------------------------------------------------------------------------
+# Closed forms.
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_weights_sum_to_one(dtype):
+    """V = 1 everywhere -> O = 1 on every row that has a visible key."""
+    B, Hq, Hkv, Lq, Lk, D = 2, 4, 2, 13, 29, 8
+    q = _rand((B, Lq, Hq, D), dtype, 1)
+    k = _rand((B, Lk, Hkv, D), dtype, 2)
+    v = synth.to_storage(np.ones((B, Lk, Hkv, D), np.float32), dtype)
+    lens = np.array([29, 11], np.int32)
+    o, lse = oracle.attention(q, k, v, dtype=dtype, causal=True, key_lens=lens)
+    assert np.isfinite(lse).all()
+    assert np.abs(o - 1.0).max() < 1e-13
+
+
+def test_uniform_scores_give_mean_and_log_count():
+    """Q = 0 -> every visible score is 0: O = mean of visible V, LSE = ln|visible|."""
+    B, Hq, Hkv, Lq, Lk, D = 2, 2, 1, 8, 8, 5
+    q = np.zeros((B, Lq, Hq, D), np.float32)
+    k = _rand((B, Lk, Hkv, D), "f32", 3)
+    v = _rand((B, Lk, Hkv, D), "f32", 4)
+    lens = np.array([8, 5], np.int32)
+    o, lse = oracle.attention(q, k, v, dtype="f32", causal=True, causal_offset=0, key_lens=lens)
+    causal_len = {int(r[0]): int(r[1]) for r in _golden("causal_len_s8.txt")}
+    V = v.astype(np.float64)
+    for b in range(B):
+        for h in range(Hq):
+            for i in range(Lq):
+                n = min(causal_len[i], int(lens[b]))
+                want = V[b, :n, 0, :].mean(axis=0)
+                assert np.abs(o[b, h, i] - want).max() < 1e-14
+                assert abs(lse[b, h, i] - math.log(n)) < 1e-14
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_one_hot_is_exact(dtype):
+    """Every key but j0 hidden by -inf -> O = V[j0] exactly, LSE = s_j0."""
+    B, H, Lq, Lk, D = 1, 2, 5, 37, 16
+    q = _rand((B, Lq, H, D), dtype, 5)
+    k = _rand((B, Lk, H, D), dtype, 6)
+    v = _rand((B, Lk, H, D), dtype, 7)
+    j0 = 23
+    mask = np.full((1, 1, 1, Lk), NEG_INF, np.float32)
+    mask[..., j0] = 0.25
+    o, lse = oracle.attention(q, k, v, dtype=dtype, mask=mask)
+    Q, K, V = _as_f64(q, dtype), _as_f64(k, dtype), _as_f64(v, dtype)
+    for h in range(H):
+        for i in range(Lq):
+            assert (o[0, h, i] == V[0, j0, h]).all()
+            s = math.fsum(Q[0, i, h] * K[0, j0, h]) / math.sqrt(D) + 0.25
+            assert abs(lse[0, h, i] - s) < 1e-12
+
+
+def test_two_keys_logistic():
+    """Two visible keys: O = lam*V1 + (1-lam)*V2 with lam = 1/(1+exp(s2-s1))."""
+    D = 4
+    q = _rand((1, 3, 1, D), "f32", 8)
+    k = _rand((1, 2, 1, D), "f32", 9)
+    v = _rand((1, 2, 1, D), "f32", 10)
+    o, lse = oracle.attention(q, k, v, dtype="f32", scale=0.7)
+    Q, K, V = (x.astype(np.float64)[0, :, 0] for x in (q, k, v))
+    for i in range(3):
+        s1 = 0.7 * math.fsum(Q[i] * K[0])
+        s2 = 0.7 * math.fsum(Q[i] * K[1])
+        lam = 1.0 / (1.0 + math.exp(s2 - s1))
+        assert np.abs(o[0, 0, i] - (lam * V[0] + (1 - lam) * V[1])).max() < 1e-14
+        assert abs(lse[0, 0, i] - (s1 + math.log1p(math.exp(s2 - s1)))) < 1e-13
+
+
+def test_default_scale_is_inverse_sqrt_head_dim():
+    q, k, v = (_rand((1, 9, 2, 16), "f32", s) for s in (11, 12, 13))
+    a = oracle.attention(q, k, v, dtype="f32")
+    b = oracle.attention(q, k, v, dtype="f32", scale=0.25)
+    c = oracle.attention(q, k, v, dtype="f32", scale=0.5)
+    assert np.array_equal(a[0], b[0])
+    assert np.abs(a[0] - c[0]).max() > 1e-3
+
+
+def test_gqa_mapping_golden():
+    """V of kv head g is g+1 everywhere -> O of query head h is kv(h)+1."""
+    table = {int(r[0]): int(r[1]) for r in _golden("gqa_map_h12_kv4.txt")}
+    B, Hq, Hkv, L, D = 1, 12, 4, 7, 8
+    q = _rand((B, L, Hq, D), "f32", 14)
+    k = _rand((B, L, Hkv, D), "f32", 15)
+    v = np.empty((B, L, Hkv, D), np.float32)
+    for g in range(Hkv):
+        v[:, :, g, :] = g + 1
+    o, _ = oracle.attention(q, k, v, dtype="f32", causal=True)
+    for h in range(Hq):
+        assert np.abs(o[0, h] - (table[h] + 1)).max() < 1e-13
+
+
+def test_causal_visible_counts_golden():
+    """Offset 0, Lq = Lk: LSE of a zero-score row is ln(number of visible keys)."""
+    table = {int(r[0]): int(r[1]) for r in _golden("causal_len_s8.txt")}
+    q = np.zeros((1, 8, 1, 4), np.float32)
+    k, v = _rand((1, 8, 1, 4), "f32", 16), _rand((1, 8, 1, 4), "f32", 17)
+    _, lse = oracle.attention(q, k, v, dtype="f32", causal=True)   # default offset = 0 here
+    for i, n in table.items():
+        assert abs(lse[0, 0, i] - math.log(n)) < 1e-14
+
+
+def test_default_offset_is_klen_minus_qlen():
+    """Decoder step (Lq = 1 against Lk cached keys): every key visible by default."""
+    q, k, v = _rand((2, 1, 2, 8), "f32", 18), _rand((2, 9, 2, 8), "f32", 19), _rand((2, 9, 2, 8), "f32", 20)
+    a = oracle.attention(q, k, v, dtype="f32", causal=True)
+    b = oracle.attention(q, k, v, dtype="f32", causal=False)
+    c = oracle.attention(q, k, v, dtype="f32", causal=True, causal_offset=8)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[0], c[0])
+
+
+# --------------------------------------------------------------------------
+# Special values (OneGPU "Special values"; tests/golden/special_values.txt).
+
+def _special_case(case):
+    B, H, Lq, Lk, D = 1, 1, 4, 6, 8
+    q = _rand((B, Lq, H, D), "f32", 21)
+    k = _rand((B, Lk, H, D), "f32", 22)
+    v = _rand((B, Lk, H, D), "f32", 23)
+    kw = {}
+    if case == "klen0":
+        k, v = k[:, :0], v[:, :0]
+    elif case == "all_keys_masked":
+        kw["mask"] = np.full((1, 1, 1, Lk), NEG_INF, np.float32)
+    elif case == "nan_score":
+        k = k.copy()
+        k[0, 2, 0, 3] = np.nan
+    elif case == "posinf_score":
+        m = np.zeros((1, 1, 1, Lk), np.float32)
+        m[..., 4] = np.inf
+        kw["mask"] = m
+    return q, k, v, kw
+
+
+@pytest.mark.parametrize("row", _golden("special_values.txt"), ids=lambda r: "-".join(r[:2]))
+def test_special_values_golden(row):
+    case, policy, want_o, want_lse = row
+    q, k, v, kw = _special_case(case)
+    o, lse = oracle.attention(q, k, v, dtype="f32", masked_rows=policy, **kw)
+    if want_o == "nan":
+        assert np.isnan(o).all()
+    else:
+        assert (o == 0.0).all()
+    if want_lse == "nan":
+        assert np.isnan(lse).all()
+    else:
+        assert (lse == -np.inf).all()
+
+
+def test_negative_offset_empties_leading_rows():
+    q, k, v = (_rand((1, 6, 1, 4), "f32", s) for s in (24, 25, 26))
+    o, lse = oracle.attention(q, k, v, dtype="f32", causal=True, causal_offset=-3,
+                              masked_rows="zero")
+    assert (o[0, 0, :3] == 0).all() and (lse[0, 0, :3] == -np.inf).all()
+    assert np.isfinite(lse[0, 0, 3:]).all()
+    o2, _ = oracle.attention(q, k, v, dtype="f32", causal=True, causal_offset=-6)
+    assert np.isnan(o2).all()
+
+
+def test_key_length_zero_and_beyond_capacity():
+    q, k, v = (_rand((3, 2, 1, 4), "f32", s) for s in (27, 28, 29))
+    lens = np.array([0, 99, -5], np.int32)
+    o, lse = oracle.attention(q, k, v, dtype="f32", key_lens=lens, masked_rows="zero")
+    full, _ = oracle.attention(q, k, v, dtype="f32")
+    assert (o[0] == 0).all() and (lse[0] == -np.inf).all()
+    assert np.array_equal(o[1], full[1])          # clamped to Lk
+    assert (o[2] == 0).all()                       # negative -> 0
+
+
+def test_hidden_keys_are_never_read():
+    """Garbage (NaN, huge) beyond the key length or past the causal bound does not leak."""
+    B, H, L, D = 2, 2, 10, 8
+    q, k, v = (_rand((B, L, H, D), "f32", s) for s in (30, 31, 32))
+    lens = np.array([6, 10], np.int32)
+    o, lse = oracle.attention(q, k, v, dtype="f32", causal=True, key_lens=lens)
+    k2, v2 = k.copy(), v.copy()
+    k2[0, 6:] = np.nan
+    v2[0, 6:] = 1e30
+    o2, lse2 = oracle.attention(q, k2, v2, dtype="f32", causal=True, key_lens=lens)
+    assert np.array_equal(o, o2) and np.array_equal(lse, lse2)
+    # Deleting the keys beyond length 6 gives the same rows for batch 0.
+    o3, _ = oracle.attention(q[:1], k[:1, :6], v[:1, :6], dtype="f32", causal=True,
+                             causal_offset=0)
+    assert np.abs(o3[0] - o[0]).max() < 1e-14
+    # Causal-hidden keys: perturbing key j changes no row i < j.
+    k4 = k.copy()
+    k4[1, 7] = np.nan
+    o4, _ = oracle.attention(q, k4, v, dtype="f32", causal=True, key_lens=lens)
+    assert np.array_equal(o4[1, :, :7], o[1, :, :7]) and np.isnan(o4[1, :, 7:]).all()
+
+
+def test_mask_hidden_keys_weigh_zero():
+    """Keys hidden by -inf in the mask contribute nothing: finite garbage there is ignored,
+    and the result equals the attention over the remaining keys."""
+    B, H, Lq, Lk, D = 1, 2, 5, 12, 8
+    q, k, v = _rand((B, Lq, H, D), "f32", 33), _rand((B, Lk, H, D), "f32", 34), _rand((B, Lk, H, D), "f32", 35)
+    hide = np.array([1, 4, 5, 11])
+    mask = np.zeros((1, 1, 1, Lk), np.float32)
+    mask[..., hide] = -np.inf
+    o, lse = oracle.attention(q, k, v, dtype="f32", mask=mask)
+    k2, v2 = k.copy(), v.copy()
+    k2[:, hide] *= 1e3
+    v2[:, hide] = 7e20
+    o2, _ = oracle.attention(q, k2, v2, dtype="f32", mask=mask)
+    assert np.array_equal(o, o2)
+    keep = np.setdiff1d(np.arange(Lk), hide)
+    o3, lse3 = oracle.attention(q, np.ascontiguousarray(k[:, keep]), np.ascontiguousarray(v[:, keep]),
+                                dtype="f32")
+    assert np.abs(o - o3).max() < 1e-14 and np.abs(lse - lse3).max() < 1e-13
+
+
+# --------------------------------------------------------------------------
+# Invariants.
+
+def test_shift_invariance():
+    q, k, v = _rand((1, 7, 3, 8), "f32", 36), _rand((1, 11, 3, 8), "f32", 37), _rand((1, 11, 3, 8), "f32", 38)
+    # Mask values on a 2^-10 grid, so adding 4 is exact in float32.
+    mask = (np.round(_rand((1, 3, 7, 11), "f32", 39) * 1024) / 1024).astype(np.float32)
+    o, lse = oracle.attention(q, k, v, dtype="f32", mask=mask)
+    o2, lse2 = oracle.attention(q, k, v, dtype="f32", mask=(mask + np.float32(4.0)))
+    assert np.abs(o - o2).max() < 1e-12
+    assert np.abs(lse2 - lse - 4.0).max() < 1e-12
+
+
+def test_key_permutation_invariance():
+    q, k, v = _rand((1, 6, 2, 8), "f32", 40), _rand((1, 21, 2, 8), "f32", 41), _rand((1, 21, 2, 8), "f32", 42)
+    mask = _rand((1, 1, 6, 21), "f32", 43)
+    perm = np.random.default_rng(44).permutation(21)
+    o, lse = oracle.attention(q, k, v, dtype="f32", mask=mask)
+    o2, lse2 = oracle.attention(q, np.ascontiguousarray(k[:, perm]), np.ascontiguousarray(v[:, perm]),
+                                dtype="f32", mask=np.ascontiguousarray(mask[..., perm]))
+    assert np.abs(o - o2).max() < 1e-13 and np.abs(lse - lse2).max() < 1e-13
+
+
+def test_layouts_and_broadcast_agree():
+    q, k, v = _rand((2, 9, 4, 8), "f16", 45), _rand((2, 13, 2, 8), "f16", 46), _rand((2, 13, 2, 8), "f16", 47)
+    mask = _rand((2, 1, 1, 13), "f32", 48)
+    o, lse = oracle.attention(q, k, v, dtype="f16", mask=mask, causal=True)
+    qt, kt, vt = (np.ascontiguousarray(np.transpose(x, (0, 2, 1, 3))) for x in (q, k, v))
+    o2, lse2 = oracle.attention(qt, kt, vt, dtype="f16", layout="bhsd", causal=True,
+                                mask=np.ascontiguousarray(np.broadcast_to(mask, (2, 4, 9, 13))))
+    assert np.array_equal(o, o2) and np.array_equal(lse, lse2)
+    # A strided view (every other head of a packed buffer) reads the same values.
+    packed = np.zeros((2, 9, 8, 8), np.float16)
+    packed[:, :, ::2] = q
+    o3, _ = oracle.attention(packed[:, :, ::2], k, v, dtype="f16", mask=mask, causal=True)
+    assert np.array_equal(o, o3)
+    # K and V with different strides: V is a slice of a packed [K|V|pad] buffer.
+    kvbuf = np.zeros((2, 13, 5, 8), np.float16)
+    kvbuf[:, :, 2:4] = v
+    o4, _ = oracle.attention(q, k, kvbuf[:, :, 2:4], dtype="f16", mask=mask, causal=True)
+    assert np.array_equal(o, o4)
+
+
+def test_row_subset_matches_full():
+    q, k, v = _rand((2, 10, 4, 8), "bf16", 49), _rand((2, 10, 2, 8), "bf16", 50), _rand((2, 10, 2, 8), "bf16", 51)
+    o, lse = oracle.attention(q, k, v, dtype="bf16", causal=True)
+    rows = np.array([[1, 3, 9], [0, 0, 0], [1, 2, 4]])
+    o2, lse2 = oracle.attention(q, k, v, dtype="bf16", causal=True, rows=rows)
+    for n, (b, h, i) in enumerate(rows):
+        assert np.array_equal(o2[n], o[b, h, i]) and lse2[n] == lse[b, h, i]
+
+
+# --------------------------------------------------------------------------
+# Brute force against the independent library route, tiny shapes from the
+# OneGPU "Tolerances" test matrix (tile edges, remainders, size 1, odd head
+# dims, grouped heads, Lq != Lk, masks, lengths).
+
+BRUTE = [
+    # B, Hq, Hkv, Lq, Lk, D, dtype, causal, offset, mask, lens
+    (1, 1, 1, 1, 1, 1, "f32", False, None, False, False),
+    (1, 2, 1, 5, 31, 3, "f32", True, None, False, False),
+    (2, 4, 2, 32, 32, 32, "f16", True, 0, False, True),
+    (1, 3, 3, 17, 33, 33, "bf16", False, None, True, False),
+    (2, 2, 1, 40, 63, 64, "f32", True, None, True, True),
+    (1, 4, 1, 64, 64, 128, "bf16", True, 0, False, False),
+    (1, 2, 2, 9, 65, 256, "f16", False, None, True, True),
+    (1, 6, 2, 3, 127, 16, "f32", True, 100, False, True),
+    (2, 1, 1, 129, 128, 8, "f16", True, -2, True, False),
+    (1, 2, 1, 7, 129, 64, "bf16", False, None, False, True),
+]
+
+
+@pytest.mark.parametrize("cfg", BRUTE, ids=lambda c: "x".join(map(str, c)))
+@pytest.mark.parametrize("policy", ["nan", "zero"])
+def test_brute_force_against_library_route(cfg, policy):
+    B, Hq, Hkv, Lq, Lk, D, dtype, causal, offset, use_mask, use_lens = cfg
+    seed = zlib.crc32(repr(cfg).encode()) % 1000
+    q = _rand((B, Lq, Hq, D), dtype, seed)
+    k = _rand((B, Lk, Hkv, D), dtype, seed + 1)
+    v = _rand((B, Lk, Hkv, D), dtype, seed + 2)
+    mask = None
+    if use_mask:
+        rng = np.random.default_rng(seed + 3)
+        mask = rng.standard_normal((B, 1, Lq, Lk)).astype(np.float32)
+        mask[rng.random(mask.shape) < 0.3] = -np.inf
+    lens = None
+    if use_lens:
+        lens = np.random.default_rng(seed + 4).integers(0, Lk + 1, size=B).astype(np.int32)
+    o, lse = oracle.attention(q, k, v, dtype=dtype, causal=causal, causal_offset=offset,
+                              mask=mask, key_lens=lens, masked_rows=policy)
+    o2, lse2 = _library_attention(q, k, v, dtype, causal=causal, offset=offset, mask=mask,
+                                  key_lens=lens, masked_rows=policy)
+    assert (np.isnan(o) == np.isnan(o2)).all()
+    assert (np.isnan(lse) == np.isnan(lse2)).all()
+    fin = ~np.isnan(o)
+    assert np.abs(o[fin] - o2[fin]).max(initial=0) < 1e-12
+    fl = np.isfinite(lse2)
+    assert (lse[~fl & ~np.isnan(lse2)] == lse2[~fl & ~np.isnan(lse2)]).all()
+    assert np.abs(lse[fl] - lse2[fl]).max(initial=0) < 1e-11
+
+
+def test_rejects_bad_problems():
+    q = _rand((1, 4, 3, 8), "f32", 60)
+    k = _rand((1, 4, 2, 8), "f32", 61)
+    with pytest.raises(RuntimeError):
+        oracle.attention(q, k, k, dtype="f32")           # 3 query heads over 2 kv heads
+    with pytest.raises(ValueError):
+        oracle.attention(q, q, q, dtype="f32", rows=np.array([[0, 3, 0]]))

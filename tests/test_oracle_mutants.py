@@ -1,0 +1,91 @@
+"""The oracle pins catch plausible mistakes (CPU only).
+
+Each case plants one mistake in a copy of the oracle's C source (a dropped
+term, a wrong sign, index or bound, a transposed operand), builds it into a
+temporary library, runs the pins of test_oracle.py against it and requires at
+least one pin to fail.  The real oracle is never modified.
+"""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+import oracle
+import test_oracle as pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "sdpa_oracle.c")
+
+MUTANTS = {
+    "gqa_index_modulo": ("const int64_t g = h / group;", "const int64_t g = h % p->kv_heads;"),
+    "causal_strict": ("j <= i + delta", "j < i + delta"),
+    "default_offset_sign": ("p->k_len - p->q_len", "p->q_len - p->k_len"),
+    "mask_dropped": ("sj += (double)mask", "sj -= 0.0 * (double)mask"),
+    "mask_before_scale": ("double sj = scale * dot;", "double sj = dot;"),
+    "default_scale": ("1.0 / sqrt((double)D)", "1.0 / (double)D"),
+    "lse_sign": ("*lse_out = m + log(l);", "*lse_out = m - log(l);"),
+    "policy_swapped": ("p->masked_zero ? 0.0 : NAN", "p->masked_zero ? NAN : 0.0"),
+    "v_uses_k_strides": ("b * p->vs[0] + g * p->vs[1] + j * p->vs[2]",
+                         "b * p->ks[0] + g * p->ks[1] + j * p->ks[2]"),
+    "key_length_off_by_one": ("(j < kv_len)", "(j <= kv_len)"),
+    "f16_exponent_bias": ("e - 25", "e - 24"),
+    "bf16_wrong_half": ("(uint32_t)b << 16", "(uint32_t)b << 15"),
+    "bad_row_ignored": ("            bad = 1;", "            bad = 0;"),
+    "max_not_subtracted": ("l += exp(s[j] - m);", "l += exp(s[j]);"),
+    "weights_not_normalised": ("exp(s[j] - m) / l;", "exp(s[j] - m);"),
+    "q_row_stride_ignored": ("i * p->qs[2];", "0 * p->qs[2];"),
+    "explicit_offset_ignored": ("p->has_offset ? p->causal_offset :", "0 ? p->causal_offset :"),
+    "key_lengths_ignored": ("kv_len = L < 0 ? 0 : (L > p->k_len ? p->k_len : L);",
+                            "kv_len = p->k_len; (void)L;"),
+}
+
+CHECKS = [
+    pins.test_decode_f16_all_patterns,
+    pins.test_decode_bf16_all_patterns,
+    lambda: pins.test_weights_sum_to_one("f16"),
+    pins.test_uniform_scores_give_mean_and_log_count,
+    lambda: pins.test_one_hot_is_exact("bf16"),
+    pins.test_two_keys_logistic,
+    pins.test_default_scale_is_inverse_sqrt_head_dim,
+    pins.test_gqa_mapping_golden,
+    pins.test_causal_visible_counts_golden,
+    pins.test_default_offset_is_klen_minus_qlen,
+    pins.test_negative_offset_empties_leading_rows,
+    pins.test_key_length_zero_and_beyond_capacity,
+    pins.test_hidden_keys_are_never_read,
+    pins.test_mask_hidden_keys_weigh_zero,
+    pins.test_layouts_and_broadcast_agree,
+] + [(lambda r=r: pins.test_special_values_golden(r)) for r in pins._golden("special_values.txt")] \
+  + [(lambda c=c: pins.test_brute_force_against_library_route(c, "nan")) for c in pins.BRUTE]
+
+
+def _any_check_fails():
+    for check in CHECKS:
+        try:
+            check()
+        except (AssertionError, RuntimeError, ValueError):
+            return True
+    return False
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, tmp_path, monkeypatch):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) >= 1, "mutation anchor not found: %r" % old
+    mutated = tmp_path / "mutant.c"
+    mutated.write_text(src.replace(old, new))
+    lib_path = tmp_path / "libmutant.so"
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+                           "-o", str(lib_path), str(mutated), "-lm"])
+    real = oracle._load()
+    lib = ctypes.CDLL(str(lib_path))
+    for fn in ("oracle_attention", "oracle_decode_f16", "oracle_decode_bf16"):
+        getattr(lib, fn).restype = getattr(real, fn).restype
+        getattr(lib, fn).argtypes = getattr(real, fn).argtypes
+    monkeypatch.setattr(oracle, "_lib", lib)
+    assert _any_check_fails(), "no pin caught mutant %s" % name
+
+
+def test_unmutated_oracle_passes_every_check():
+    assert not _any_check_fails()
