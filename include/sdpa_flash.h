@@ -1,0 +1,167 @@
+/*
+ * sdpa_flash.h -- C ABI of the MI355X fused scaled-dot-product attention library.
+ *
+ * Computes, for every batch entry b, query head h and query row i,
+ *
+ *     O[b,h,i,:] = softmax_j( scale * Q[b,h,i,:] . K[b,g,j,:] + Mask[b,h,i,j] ) V[b,g,j,:]
+ *
+ * with g = h / (q_heads / kv_heads), in one pass over the keys with the online
+ * normaliser, so the score matrix is never written to memory.
+ *   - Definition and the running max / running sum / rescaled accumulator:
+ *     OneGPU "Attention" page, introduction; llm.istanbul "05_attention",
+ *     section "Online Softmax Algoritmasi" (also the LSE = m + log l output).
+ *   - Problem description (batch, heads, query and key lengths, head dim, one
+ *     layout per tensor with offset and batch/head/row strides, elements of a
+ *     row contiguous): OneGPU "Attention", code sample and "What it covers".
+ *   - Grouped heads: llm.istanbul "05_attention", section "GQA".
+ *   - Key lengths, causal rule with an offset (default KLen - QLen), additive
+ *     float32 mask broadcast over batch/heads/rows: OneGPU "What it covers".
+ *   - Masked rows (NaN or zero) and NaN/+inf scores: OneGPU "Special values".
+ *   - Key-range split with partials merged in range order, scratch sized by
+ *     the shape: OneGPU "Accuracy at long key lengths", last paragraph.
+ *   - Default scale 1/sqrt(head_dim) when scale is 0: ONNX GroupQueryAttention
+ *     README, "Attributes" table (scale).
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *     keeps no pointer after the call returns and allocates no device memory.
+ *     Buffers must stay valid until the work queued on `stream` completes.
+ *   - Calls are asynchronous: work is enqueued on `stream` (a hipStream_t;
+ *     NULL = the null stream) and the call returns without synchronising.
+ *   - Layout fields are in ELEMENTS.  A row's head_dim elements (or a mask
+ *     row's k_len elements) are contiguous.  Strides must be >= 0; a stride of
+ *     0 broadcasts (used for the mask).
+ *   - Every argument is validated before anything is launched: an error
+ *     status means nothing was enqueued and no output was written.
+ *     attn_last_error() then returns a message (thread-local).
+ *   - Every element of O (and of LSE when requested) is written exactly once,
+ *     masked rows included.  Two identical calls give identical bits (fixed
+ *     summation order, no atomics).
+ *   - Values in device memory are never trapped on: key lengths are clamped
+ *     to [0, k_len]; keys at or beyond a batch entry's length are never read.
+ */
+#ifndef SDPA_FLASH_H
+#define SDPA_FLASH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum attn_status {
+    ATTN_OK = 0,
+    ATTN_ERR_INVALID = 1,      /* malformed problem or pointer                  */
+    ATTN_ERR_UNSUPPORTED = 2,  /* well-formed but not implemented               */
+    ATTN_ERR_WORKSPACE = 3,    /* workspace missing or too small                */
+    ATTN_ERR_HIP = 4           /* the HIP runtime refused a launch              */
+} attn_status;
+
+typedef enum attn_dtype {
+    ATTN_DTYPE_F32 = 0,        /* float32 Q/K/V/O                               */
+    ATTN_DTYPE_F16 = 1,        /* IEEE binary16 Q/K/V/O, float32 accumulation   */
+    ATTN_DTYPE_BF16 = 2        /* bfloat16 Q/K/V/O, float32 accumulation        */
+} attn_dtype;
+
+typedef enum attn_masked_rows {
+    ATTN_MASKED_ROWS_NAN = 0,  /* a row with no visible key is NaN (0/0)        */
+    ATTN_MASKED_ROWS_ZERO = 1  /* ... or all zeros                              */
+} attn_masked_rows;
+
+typedef enum attn_op {
+    ATTN_OP_FORWARD = 0,
+    ATTN_OP_DECODE = 1
+} attn_op;
+
+/* Sentinel for attn_problem.causal_offset: use k_len - q_len. */
+#define ATTN_CAUSAL_OFFSET_DEFAULT INT64_MIN
+
+/* Element (b, h, r, d) of a tensor lives at
+ *   base + offset + b*batch_stride + h*head_stride + r*row_stride + d.
+ * Positions-first [B, L, H, D] contiguous: batch_stride = L*H*D,
+ *   head_stride = D, row_stride = H*D.
+ * Heads-first [B, H, L, D] contiguous: batch_stride = H*L*D,
+ *   head_stride = L*D, row_stride = D.                                        */
+typedef struct attn_layout {
+    int64_t offset;
+    int64_t batch_stride;
+    int64_t head_stride;
+    int64_t row_stride;
+} attn_layout;
+
+typedef struct attn_problem {
+    int32_t batch;       /* >= 0                                                 */
+    int32_t q_heads;     /* >= 1                                                 */
+    int32_t kv_heads;    /* >= 1, divides q_heads                                */
+    int32_t q_len;       /* >= 0 (decode: exactly 1)                             */
+    int32_t k_len;       /* >= 0; for decode, the cache capacity                 */
+    int32_t head_dim;    /* 1..256                                               */
+    int32_t dtype;       /* attn_dtype, shared by Q, K, V and O                  */
+    int32_t causal;      /* 0 or 1: key j visible to row i iff j <= i + offset   */
+    int64_t causal_offset; /* ATTN_CAUSAL_OFFSET_DEFAULT or any value            */
+    float scale;         /* 0 selects 1/sqrt(head_dim)                           */
+    int32_t masked_rows; /* attn_masked_rows                                     */
+    attn_layout q, k, v, o;
+    /* float32 additive mask: element (b, h, i, j) at
+     * mask + offset + b*batch_stride + h*head_stride + i*row_stride + j.
+     * Use stride 0 to broadcast an axis.  Ignored when mask == NULL.          */
+    attn_layout mask;
+    /* float32 LSE: element (b, h, i) at
+     * lse + offset + b*batch_stride + h*head_stride + i*row_stride.
+     * Ignored when lse == NULL.                                               */
+    attn_layout lse;
+} attn_problem;
+
+/*
+ * attn_forward -- fused attention over all query rows (prefill / training
+ * forward / cross-attention).
+ *   p          problem description (host memory, read during the call only).
+ *   q, k, v    device input tensors of p->dtype, laid out per p->q/k/v.
+ *              k and v may be NULL only when k_len == 0.
+ *   o          device output of p->dtype per p->o (may not alias the inputs).
+ *   mask       device float32 additive mask or NULL.  -inf hides a key.
+ *   key_lens   device int32[batch] of real key lengths or NULL (= k_len).
+ *   lse        device float32 log-sum-exp of each row's scores or NULL;
+ *              -inf for a row with no visible key, NaN for a NaN row.
+ *   workspace  device scratch of at least attn_workspace_size(p, FORWARD)
+ *              bytes (NULL allowed when that size is 0).
+ *   stream     hipStream_t to enqueue on.
+ * Returns ATTN_OK, or an error with nothing enqueued.
+ */
+attn_status attn_forward(const attn_problem* p, const void* q, const void* k, const void* v,
+                         void* o, const float* mask, const int32_t* key_lens, float* lse,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_decode -- one query row per (batch, head) against a key/value cache
+ * (llm.istanbul "05_attention", section "attention_decode Farki"; ONNX
+ * GroupQueryAttention README, split-K decode variants and BNSH caches).
+ * Same arguments and semantics as attn_forward, with p->q_len == 1 and
+ * p->k_len the cache capacity; key_lens gives the live length of each batch
+ * entry.  The keys are cut into fixed ranges (a function of the shape only);
+ * each range's partial (max, sum, accumulator) goes to the workspace and a
+ * second kernel merges them in range order.
+ */
+attn_status attn_decode(const attn_problem* p, const void* q, const void* k, const void* v,
+                        void* o, const float* mask, const int32_t* key_lens, float* lse,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_workspace_size -- bytes of device workspace the call `op` needs for
+ * problem p (0 when it needs none).  Host-only: touches no device.
+ * Returns ATTN_ERR_INVALID for a malformed problem.
+ */
+attn_status attn_workspace_size(const attn_problem* p, int32_t op, size_t* bytes);
+
+/* Message for the last error on the calling thread ("" if none). */
+const char* attn_last_error(void);
+
+/* Library version string. */
+const char* attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SDPA_FLASH_H */

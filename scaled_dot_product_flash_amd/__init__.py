@@ -1,1 +1,222 @@
-"""MI355X-native fused scaled-dot-product attention (placeholder during bring-up)."""
+"""MI355X-native fused scaled-dot-product attention.
+
+Thin Python binding over the C ABI in include/sdpa_flash.h (libsdpa_flash.so,
+built in-tree by ``python -m scaled_dot_product_flash_amd.build``).  This
+module only marshals arguments: torch tensors supply device pointers, strides
+and the current HIP stream, and torch allocates the outputs and the
+workspace.  Every step of the computation runs in the library's HIP kernels;
+there is no CPU or PyTorch fallback, and calls fail loudly when the library
+is missing or a tensor is not on the GPU.
+
+    o = forward(q, k, v, causal=True)                       # [B, L, H, D] tensors
+    o, lse = forward(q, k, v, causal=True, return_lse=True)
+    o = decode(q, k_cache, v_cache, key_lens, kv_layout="bhsd")
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["forward", "decode", "workspace_size", "AttnError", "lib_path", "load_library",
+           "Problem", "Layout", "SYMBOLS"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libsdpa_flash.so")
+
+# Every symbol include/sdpa_flash.h declares.
+SYMBOLS = ("attn_forward", "attn_decode", "attn_workspace_size", "attn_last_error",
+           "attn_version")
+
+OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
+DTYPE_F32, DTYPE_F16, DTYPE_BF16 = 0, 1, 2
+MASKED_NAN, MASKED_ZERO = 0, 1
+OP_FORWARD, OP_DECODE = 0, 1
+CAUSAL_OFFSET_DEFAULT = -(1 << 63)
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("attn status %d: %s" % (status, message))
+        self.status = status
+
+
+class Layout(ctypes.Structure):
+    _fields_ = [("offset", ctypes.c_int64), ("batch_stride", ctypes.c_int64),
+                ("head_stride", ctypes.c_int64), ("row_stride", ctypes.c_int64)]
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("q_heads", ctypes.c_int32), ("kv_heads", ctypes.c_int32),
+        ("q_len", ctypes.c_int32), ("k_len", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("dtype", ctypes.c_int32), ("causal", ctypes.c_int32),
+        ("causal_offset", ctypes.c_int64),
+        ("scale", ctypes.c_float), ("masked_rows", ctypes.c_int32),
+        ("q", Layout), ("k", Layout), ("v", Layout), ("o", Layout),
+        ("mask", Layout), ("lse", Layout),
+    ]
+
+
+_lib = None
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libsdpa_flash.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError("libsdpa_flash.so is not built; run "
+                           "`python -m scaled_dot_product_flash_amd.build` first")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp = ctypes.c_void_p
+    call = [ctypes.POINTER(Problem), vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    for name in ("attn_forward", "attn_decode"):
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = call
+    lib.attn_workspace_size.restype = ctypes.c_int
+    lib.attn_workspace_size.argtypes = [ctypes.POINTER(Problem), ctypes.c_int32,
+                                        ctypes.POINTER(ctypes.c_size_t)]
+    lib.attn_last_error.restype = ctypes.c_char_p
+    lib.attn_last_error.argtypes = []
+    lib.attn_version.restype = ctypes.c_char_p
+    lib.attn_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def last_error() -> str:
+    return load_library().attn_last_error().decode()
+
+
+def _check(status: int):
+    if status != OK:
+        raise AttnError(status, last_error())
+
+
+def workspace_size(problem: Problem, op: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().attn_workspace_size(ctypes.byref(problem), op, ctypes.byref(n)))
+    return n.value
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    codes = {torch.float32: DTYPE_F32, torch.float16: DTYPE_F16, torch.bfloat16: DTYPE_BF16}
+    if t.dtype not in codes:
+        raise TypeError("unsupported dtype %s" % t.dtype)
+    return codes[t.dtype]
+
+
+def _layout_of(t, layout: str) -> Layout:
+    if t.dim() != 4:
+        raise ValueError("expected a 4-D tensor, got shape %s" % (tuple(t.shape),))
+    st = t.stride()
+    if t.shape[3] > 1 and st[3] != 1:
+        raise ValueError("the head dimension must be contiguous (stride 1)")
+    if layout == "bshd":
+        return Layout(0, st[0], st[2], st[1])
+    if layout == "bhsd":
+        return Layout(0, st[0], st[1], st[2])
+    raise ValueError("layout must be 'bshd' or 'bhsd'")
+
+
+def _dims(t, layout: str):
+    if layout == "bshd":
+        return t.shape[0], t.shape[2], t.shape[1], t.shape[3]   # B, H, L, D
+    return t.shape[0], t.shape[1], t.shape[2], t.shape[3]
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _run(op: int, q, k, v, *, layout: str, kv_layout: str | None, causal: bool,
+         causal_offset, scale, mask, key_lens, masked_rows: str, return_lse: bool,
+         out=None, stream=None):
+    torch = _torch()
+    kv_layout = kv_layout or layout
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k and v must be GPU tensors (there is no CPU path)")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k and v must share one dtype")
+    B, Hq, Lq, D = _dims(q, layout)
+    Bk, Hkv, Lk, Dk = _dims(k, kv_layout)
+    if _dims(v, kv_layout) != (Bk, Hkv, Lk, Dk) or Bk != B or Dk != D:
+        raise ValueError("inconsistent q/k/v shapes")
+    p = Problem()
+    p.batch, p.q_heads, p.kv_heads, p.q_len, p.k_len, p.head_dim = B, Hq, Hkv, Lq, Lk, D
+    p.dtype = _dtype_code(q)
+    p.causal = 1 if causal else 0
+    p.causal_offset = CAUSAL_OFFSET_DEFAULT if causal_offset is None else int(causal_offset)
+    p.scale = 0.0 if scale is None else float(scale)
+    p.masked_rows = {"nan": MASKED_NAN, "zero": MASKED_ZERO}[masked_rows]
+    p.q = _layout_of(q, layout)
+    p.k = _layout_of(k, kv_layout)
+    p.v = _layout_of(v, kv_layout)
+    if out is None:
+        shape = (B, Lq, Hq, D) if layout == "bshd" else (B, Hq, Lq, D)
+        out = torch.empty(shape, dtype=q.dtype, device=q.device)
+    elif out.dtype != q.dtype or _dims(out, layout) != (B, Hq, Lq, D):
+        raise ValueError("out has the wrong dtype or shape")
+    p.o = _layout_of(out, layout)
+    if mask is not None:
+        if mask.dtype != torch.float32 or mask.dim() != 4 or not mask.is_cuda:
+            raise TypeError("mask must be a float32 GPU tensor [B|1, Hq|1, Lq|1, Lk]")
+        if (mask.shape[3] != Lk or mask.shape[0] not in (1, B) or mask.shape[1] not in (1, Hq)
+                or mask.shape[2] not in (1, Lq)):
+            raise ValueError("mask shape %s does not broadcast to [%d, %d, %d, %d]"
+                             % (tuple(mask.shape), B, Hq, Lq, Lk))
+        if Lk > 1 and mask.stride(3) != 1:
+            mask = mask.contiguous()
+        ms = [s if n > 1 else 0 for s, n in zip(mask.stride(), mask.shape)]
+        p.mask = Layout(0, ms[0], ms[1], ms[2])
+    if key_lens is not None:
+        if key_lens.dtype != torch.int32 or not key_lens.is_cuda or key_lens.shape != (B,):
+            raise TypeError("key_lens must be an int32 GPU tensor of shape [B]")
+        key_lens = key_lens.contiguous()
+    lse = None
+    if return_lse:
+        lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device)
+        p.lse = Layout(0, Hq * Lq, Lq, 1)
+    lib = load_library()
+    ws_bytes = workspace_size(p, op)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
+    with torch.cuda.device(q.device):
+        s = stream if stream is not None else torch.cuda.current_stream(q.device)
+        fn = lib.attn_forward if op == OP_FORWARD else lib.attn_decode
+        _check(fn(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(mask),
+                  _ptr(key_lens), _ptr(lse), _ptr(ws), ws_bytes, ctypes.c_void_p(s.cuda_stream)))
+    return (out, lse) if return_lse else out
+
+
+def forward(q, k, v, *, layout: str = "bshd", kv_layout: str | None = None,
+            causal: bool = False, causal_offset: int | None = None, scale: float | None = None,
+            mask=None, key_lens=None, masked_rows: str = "nan", return_lse: bool = False,
+            out=None, stream=None):
+    """Fused attention.  q: [B, Lq, Hq, D] ('bshd') or [B, Hq, Lq, D] ('bhsd');
+    k, v likewise in ``kv_layout`` (default ``layout``).  Returns O in q's layout
+    (and the float32 LSE [B, Hq, Lq] with ``return_lse``)."""
+    return _run(OP_FORWARD, q, k, v, layout=layout, kv_layout=kv_layout, causal=causal,
+                causal_offset=causal_offset, scale=scale, mask=mask, key_lens=key_lens,
+                masked_rows=masked_rows, return_lse=return_lse, out=out, stream=stream)
+
+
+def decode(q, k_cache, v_cache, key_lens=None, *, layout: str = "bshd", kv_layout: str = "bhsd",
+           scale: float | None = None, mask=None, masked_rows: str = "nan",
+           return_lse: bool = False, out=None, stream=None):
+    """One query row per (batch, head) against a K/V cache of capacity Lk with
+    live lengths ``key_lens`` (int32 [B]); every live key is visible."""
+    return _run(OP_DECODE, q, k_cache, v_cache, layout=layout, kv_layout=kv_layout,
+                causal=True, causal_offset=None, scale=scale, mask=mask, key_lens=key_lens,
+                masked_rows=masked_rows, return_lse=return_lse, out=out, stream=stream)

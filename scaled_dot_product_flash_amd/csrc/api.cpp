@@ -1,0 +1,171 @@
+// api.cpp -- the C ABI declared in include/sdpa_flash.h: argument validation,
+// kernel choice and launch.  Validation runs entirely on the host and before
+// any launch, so an error leaves every output untouched.
+#include "sdpa_flash.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "attn_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+attn_status fail(attn_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+size_t elem_size(int32_t dt) { return dt == ATTN_DTYPE_F32 ? 4 : 2; }
+
+bool nonneg(const attn_layout& l) {
+    return l.offset >= 0 && l.batch_stride >= 0 && l.head_stride >= 0 && l.row_stride >= 0;
+}
+
+// Largest element index a layout touches for (B, H, L, width), +1.
+int64_t extent(const attn_layout& l, int64_t B, int64_t H, int64_t L, int64_t width) {
+    if (B == 0 || H == 0 || L == 0 || width == 0) return 0;
+    return l.offset + (B - 1) * l.batch_stride + (H - 1) * l.head_stride +
+           (L - 1) * l.row_stride + width;
+}
+
+// check_ptrs = false validates the problem alone (for attn_workspace_size).
+attn_status validate(const attn_problem* p, bool check_ptrs, const void* q, const void* k,
+                     const void* v, const void* o, const float* mask, const float* lse) {
+    if (!p) return fail(ATTN_ERR_INVALID, "problem is NULL");
+    if (p->batch < 0 || p->q_len < 0 || p->k_len < 0)
+        return fail(ATTN_ERR_INVALID, "batch, q_len and k_len must be >= 0");
+    if (p->q_heads < 1 || p->kv_heads < 1)
+        return fail(ATTN_ERR_INVALID, "q_heads and kv_heads must be >= 1");
+    if (p->q_heads % p->kv_heads != 0)
+        return fail(ATTN_ERR_INVALID, "q_heads (%d) is not a multiple of kv_heads (%d)",
+                    p->q_heads, p->kv_heads);
+    if (p->q_heads > 65535 || p->batch > 65535)
+        return fail(ATTN_ERR_UNSUPPORTED, "q_heads and batch are limited to 65535");
+    if (p->head_dim < 1 || p->head_dim > 256)
+        return fail(ATTN_ERR_INVALID, "head_dim %d outside 1..256", p->head_dim);
+    if (p->dtype != ATTN_DTYPE_F32 && p->dtype != ATTN_DTYPE_F16 && p->dtype != ATTN_DTYPE_BF16)
+        return fail(ATTN_ERR_INVALID, "unknown dtype %d", p->dtype);
+    if (p->causal != 0 && p->causal != 1) return fail(ATTN_ERR_INVALID, "causal must be 0 or 1");
+    if (p->masked_rows != ATTN_MASKED_ROWS_NAN && p->masked_rows != ATTN_MASKED_ROWS_ZERO)
+        return fail(ATTN_ERR_INVALID, "unknown masked_rows policy %d", p->masked_rows);
+    if (!(std::isfinite(p->scale)) || p->scale < 0.f)
+        return fail(ATTN_ERR_INVALID, "scale must be finite and >= 0");
+    if (!nonneg(p->q) || !nonneg(p->k) || !nonneg(p->v) || !nonneg(p->o))
+        return fail(ATTN_ERR_INVALID, "layout offsets and strides must be >= 0");
+    if (!check_ptrs) {
+        mask = nullptr;
+        lse = nullptr;
+    }
+    if (mask && !nonneg(p->mask)) return fail(ATTN_ERR_INVALID, "mask strides must be >= 0");
+    if (lse && !nonneg(p->lse)) return fail(ATTN_ERR_INVALID, "lse strides must be >= 0");
+    const bool work = check_ptrs && p->batch > 0 && p->q_len > 0;
+    if (work && (!q || !o)) return fail(ATTN_ERR_INVALID, "q and o must be non-NULL");
+    if (work && p->k_len > 0 && (!k || !v))
+        return fail(ATTN_ERR_INVALID, "k and v must be non-NULL when k_len > 0");
+    const int64_t D = p->head_dim;
+    // 64-bit element offsets are used everywhere; reject extents past 2^62.
+    const int64_t lim = int64_t(1) << 62;
+    if (extent(p->q, p->batch, p->q_heads, p->q_len, D) > lim ||
+        extent(p->o, p->batch, p->q_heads, p->q_len, D) > lim ||
+        extent(p->k, p->batch, p->kv_heads, p->k_len, D) > lim ||
+        extent(p->v, p->batch, p->kv_heads, p->k_len, D) > lim)
+        return fail(ATTN_ERR_INVALID, "tensor extent too large");
+    return ATTN_OK;
+}
+
+sdpa::Params make_params(const attn_problem* p, const void* q, const void* k, const void* v,
+                         void* o, const float* mask, const int32_t* key_lens, float* lse) {
+    sdpa::Params r{};
+    const size_t es = elem_size(p->dtype);
+    auto adv = [&](const void* base, int64_t off) -> const void* {
+        return base ? static_cast<const char*>(base) + off * static_cast<int64_t>(es) : nullptr;
+    };
+    r.q = adv(q, p->q.offset);
+    r.k = adv(k, p->k.offset);
+    r.v = adv(v, p->v.offset);
+    r.o = const_cast<void*>(adv(o, p->o.offset));
+    r.mask = mask ? mask + p->mask.offset : nullptr;
+    r.lens = key_lens;
+    r.lse = lse ? lse + p->lse.offset : nullptr;
+    r.qs = {p->q.batch_stride, p->q.head_stride, p->q.row_stride};
+    r.ks = {p->k.batch_stride, p->k.head_stride, p->k.row_stride};
+    r.vs = {p->v.batch_stride, p->v.head_stride, p->v.row_stride};
+    r.os = {p->o.batch_stride, p->o.head_stride, p->o.row_stride};
+    r.ms = {p->mask.batch_stride, p->mask.head_stride, p->mask.row_stride};
+    r.ls = {p->lse.batch_stride, p->lse.head_stride, p->lse.row_stride};
+    r.B = p->batch;
+    r.Hq = p->q_heads;
+    r.Hkv = p->kv_heads;
+    r.Lq = p->q_len;
+    r.Lk = p->k_len;
+    r.D = p->head_dim;
+    r.group = p->q_heads / p->kv_heads;
+    r.causal = p->causal;
+    r.masked_zero = p->masked_rows == ATTN_MASKED_ROWS_ZERO;
+    r.delta = p->causal_offset == ATTN_CAUSAL_OFFSET_DEFAULT
+                  ? static_cast<int64_t>(p->k_len) - p->q_len
+                  : p->causal_offset;
+    const double scale = p->scale != 0.f ? static_cast<double>(p->scale)
+                                         : 1.0 / std::sqrt(static_cast<double>(p->head_dim));
+    r.scale_log2 = static_cast<float>(scale * 1.4426950408889634);
+    return r;
+}
+
+attn_status launched(hipError_t e) {
+    if (e != hipSuccess) return fail(ATTN_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+    g_err[0] = '\0';
+    return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_last_error(void) { return g_err; }
+
+const char* attn_version(void) { return "sdpa_flash 0.1 (gfx950)"; }
+
+attn_status attn_workspace_size(const attn_problem* p, int32_t op, size_t* bytes) {
+    if (!bytes) return fail(ATTN_ERR_INVALID, "bytes is NULL");
+    *bytes = 0;
+    attn_status st = validate(p, false, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
+    if (st != ATTN_OK) return st;
+    if (op != ATTN_OP_FORWARD && op != ATTN_OP_DECODE)
+        return fail(ATTN_ERR_INVALID, "unknown op %d", op);
+    return ATTN_OK;
+}
+
+attn_status attn_forward(const attn_problem* p, const void* q, const void* k, const void* v,
+                         void* o, const float* mask, const int32_t* key_lens, float* lse,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+    (void)workspace;
+    (void)workspace_bytes;
+    attn_status st = validate(p, true, q, k, v, o, mask, lse);
+    if (st != ATTN_OK) return st;
+    if (p->batch == 0 || p->q_len == 0) {
+        g_err[0] = '\0';
+        return ATTN_OK;
+    }
+    const sdpa::Params prm = make_params(p, q, k, v, o, mask, key_lens, lse);
+    const auto dt = static_cast<sdpa::DType>(p->dtype);
+    return launched(sdpa::launch_generic(prm, dt, static_cast<hipStream_t>(stream)));
+}
+
+attn_status attn_decode(const attn_problem* p, const void* q, const void* k, const void* v,
+                        void* o, const float* mask, const int32_t* key_lens, float* lse,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+    if (p && p->q_len != 1) return fail(ATTN_ERR_INVALID, "decode needs q_len == 1");
+    return attn_forward(p, q, k, v, o, mask, key_lens, lse, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,43 @@
+// attn_internal.h -- kernel parameter block and launcher declarations shared by
+// the host dispatch (api.cpp) and the HIP kernels.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sdpa {
+
+// Element strides of one tensor: (b, h, r) -> b*sb + h*sh + r*sr (+ d).
+struct Strides {
+    int64_t sb, sh, sr;
+};
+
+// Everything a kernel needs, passed by value.  Base pointers already include
+// the layout offsets.  All scores are handled in base-2 units:
+// t = s * log2(e), so exp(s - m) = exp2(t - m2).
+struct Params {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    const float* mask;     // nullable
+    const int32_t* lens;   // nullable
+    float* lse;            // nullable
+    void* ws;              // workspace (split partials), nullable
+    Strides qs, ks, vs, os, ms, ls;
+    int32_t B, Hq, Hkv, Lq, Lk, D;
+    int32_t group;         // Hq / Hkv
+    int32_t causal;
+    int32_t masked_zero;
+    int64_t delta;         // causal offset (resolved)
+    float scale_log2;      // scale * log2(e)
+    int32_t n_split;       // key ranges per (b, h) for split kernels
+    int32_t split_len;     // keys per range (multiple of the tile)
+};
+
+enum class DType : int { F32 = 0, F16 = 1, BF16 = 2 };
+
+// Launchers return the hipError_t of the launch.
+hipError_t launch_generic(const Params& p, DType dt, hipStream_t s);
+
+}  // namespace sdpa

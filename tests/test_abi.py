@@ -1,0 +1,140 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared
+symbol, its struct layout matches the binding, and malformed calls are
+rejected on the host before anything is launched."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import scaled_dot_product_flash_amd as sdpa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sdpa_flash.h")
+
+
+def _declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_symbols():
+    assert _declared_symbols() == sorted(sdpa.SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = sdpa.load_library()
+    for name in _declared_symbols():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", sdpa.lib_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\b[TW] (attn_\w+)", out))
+    assert set(_declared_symbols()) <= exported
+
+
+def test_version_string():
+    assert b"gfx950" in sdpa.load_library().attn_version()
+
+
+def test_struct_layout_matches_c(tmp_path):
+    """sizeof/offsetof from the C compiler equal the ctypes layout."""
+    fields = [f[0] for f in sdpa.Problem._fields_]
+    src = tmp_path / "layout.c"
+    body = "".join('printf("%s %%zu\\n", offsetof(attn_problem, %s));' % (f, f) for f in fields)
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "sdpa_flash.h"\n'
+                   'int main(void){printf("size %%zu\\n", sizeof(attn_problem));'
+                   'printf("layout %%zu\\n", sizeof(attn_layout));%s return 0;}\n' % body)
+    exe = tmp_path / "layout"
+    subprocess.check_call(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), str(src),
+                           "-o", str(exe)])
+    got = dict(line.split() for line in subprocess.check_output([str(exe)]).decode().splitlines())
+    assert int(got["size"]) == ctypes.sizeof(sdpa.Problem)
+    assert int(got["layout"]) == ctypes.sizeof(sdpa.Layout)
+    for f in fields:
+        assert int(got[f]) == getattr(sdpa.Problem, f).offset, f
+
+
+def _problem(**kw):
+    p = sdpa.Problem()
+    p.batch, p.q_heads, p.kv_heads, p.q_len, p.k_len, p.head_dim = 1, 4, 2, 8, 8, 64
+    p.dtype = sdpa.DTYPE_BF16
+    p.causal_offset = sdpa.CAUSAL_OFFSET_DEFAULT
+    for lay, H, L in (("q", 4, 8), ("k", 2, 8), ("v", 2, 8), ("o", 4, 8)):
+        setattr(p, lay, sdpa.Layout(0, L * H * 64, 64, H * 64))
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation rejects first
+
+
+@pytest.mark.parametrize("change,status", [
+    (dict(q_heads=3), sdpa.ERR_INVALID),
+    (dict(kv_heads=0), sdpa.ERR_INVALID),
+    (dict(head_dim=0), sdpa.ERR_INVALID),
+    (dict(head_dim=257), sdpa.ERR_INVALID),
+    (dict(dtype=7), sdpa.ERR_INVALID),
+    (dict(causal=2), sdpa.ERR_INVALID),
+    (dict(masked_rows=5), sdpa.ERR_INVALID),
+    (dict(batch=-1), sdpa.ERR_INVALID),
+    (dict(q_len=-3), sdpa.ERR_INVALID),
+    (dict(scale=float("nan")), sdpa.ERR_INVALID),
+    (dict(scale=-1.0), sdpa.ERR_INVALID),
+    (dict(q=sdpa.Layout(0, -1, 64, 256)), sdpa.ERR_INVALID),
+    (dict(batch=70000), sdpa.ERR_UNSUPPORTED),
+])
+def test_invalid_problem_rejected_before_launch(change, status):
+    lib = sdpa.load_library()
+    p = _problem(**change)
+    rc = lib.attn_forward(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, None, None, None, 0, None)
+    assert rc == status
+    assert lib.attn_last_error()
+    n = ctypes.c_size_t(123)
+    assert lib.attn_workspace_size(ctypes.byref(p), sdpa.OP_FORWARD, ctypes.byref(n)) == status
+    assert n.value == 0
+
+
+def test_null_pointers_rejected():
+    lib = sdpa.load_library()
+    p = _problem()
+    assert lib.attn_forward(None, FAKE, FAKE, FAKE, FAKE, None, None, None, None, 0, None) \
+        == sdpa.ERR_INVALID
+    assert lib.attn_forward(ctypes.byref(p), None, FAKE, FAKE, FAKE, None, None, None, None, 0,
+                            None) == sdpa.ERR_INVALID
+    assert lib.attn_forward(ctypes.byref(p), FAKE, None, FAKE, FAKE, None, None, None, None, 0,
+                            None) == sdpa.ERR_INVALID
+    assert lib.attn_workspace_size(ctypes.byref(p), 0, None) == sdpa.ERR_INVALID
+    assert lib.attn_workspace_size(ctypes.byref(p), 9, ctypes.byref(ctypes.c_size_t())) \
+        == sdpa.ERR_INVALID
+
+
+def test_decode_requires_one_query_row():
+    lib = sdpa.load_library()
+    p = _problem(q_len=2)
+    assert lib.attn_decode(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, None, None, None, 0,
+                           None) == sdpa.ERR_INVALID
+    assert b"q_len" in lib.attn_last_error()
+
+
+def test_empty_problem_is_a_no_op():
+    """batch = 0 or q_len = 0 returns OK without touching the device."""
+    lib = sdpa.load_library()
+    for change in (dict(batch=0), dict(q_len=0)):
+        p = _problem(**change)
+        assert lib.attn_forward(ctypes.byref(p), None, None, None, None, None, None, None, None,
+                                0, None) == sdpa.OK
+
+
+def test_workspace_size_is_host_only():
+    n = sdpa.workspace_size(_problem(), sdpa.OP_FORWARD)
+    assert n >= 0
+
+
+def test_python_binding_refuses_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(1, 4, 2, 8)
+    with pytest.raises(ValueError):
+        sdpa.forward(q, q, q)

@@ -1,0 +1,220 @@
+"""GPU parity: the HIP path against the float64 oracle, element by element.
+
+Reduced versions of the five workloads (several tiles and a ragged tail each)
+are compared in full; the full-size workloads are compared on sampled rows
+the oracle computes one by one, plus properties that hold at any size.
+"""
+import numpy as np
+import pytest
+
+from scaled_dot_product_flash_amd import synth
+import parity_util as pu
+
+pytestmark = pytest.mark.gpu
+
+REDUCED = {
+    "tiny_f32": synth.TINY_F32,
+    "causal_gqa_f32": synth.CAUSAL_GQA_F32,
+    "causal_gqa_bf16_L333": synth.CAUSAL_GQA_BF16.replace(batch=1, q_heads=8, kv_heads=2,
+                                                          q_len=333, k_len=333),
+    "decode_f16_cache1000": synth.DECODE_F16.replace(batch=8, k_len=1000),
+    "cross_mask_f16_100x300": synth.CROSS_MASK_F16.replace(q_len=100, k_len=300),
+    "causal_gqa_f16_D64_L200": synth.CAUSAL_GQA_BF16.replace(dtype="f16", batch=2, q_heads=6,
+                                                             kv_heads=3, q_len=200, k_len=200,
+                                                             head_dim=64, seed=11),
+    "cross_bf16_D128_lens": synth.CROSS_MASK_F16.replace(dtype="bf16", head_dim=128, q_len=130,
+                                                         k_len=257, seed=12),
+}
+
+
+@pytest.mark.parametrize("name", sorted(REDUCED))
+@pytest.mark.parametrize("policy", ["nan", "zero"])
+def test_reduced_workload_full_compare(name, policy):
+    spec = REDUCED[name]
+    case = synth.generate(spec)
+    o, lse, _ = pu.run_hip(case, policy, return_lse=True)
+    ro, rl = pu.run_oracle(case, policy)
+    pu.compare(o, ro, lse, rl, spec.dtype, policy, what=name)
+
+
+def _full_case(name):
+    spec = synth.WORKLOADS[name]
+    return spec, synth.generate(spec)
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "causal_gqa_f32"])
+def test_small_workloads_at_full_size(name):
+    spec, case = _full_case(name)
+    o, lse, _ = pu.run_hip(case, "nan", return_lse=True)
+    ro, rl = pu.run_oracle(case, "nan")
+    pu.compare(o, ro, lse, rl, spec.dtype, "nan", what=name)
+
+
+def test_causal_gqa_bf16_full_size_sampled():
+    spec, case = _full_case("causal_gqa_bf16")
+    o, lse, _ = pu.run_hip(case, "nan")
+    assert np.isfinite(o).all() and np.isfinite(lse).all()   # every row sees key 0
+    rows = pu.sample_rows(spec, 96)
+    ro, rl = pu.run_oracle(case, "nan", rows=rows)
+    go = o[rows[:, 0], rows[:, 1], rows[:, 2]]
+    gl = lse[rows[:, 0], rows[:, 1], rows[:, 2]]
+    pu.compare(go, ro, gl, rl, spec.dtype, "nan", what="bf16 causal GQA 4x32x4096x128")
+
+
+def test_decode_f16_full_size_every_row():
+    spec, case = _full_case("decode_f16")
+    o, lse, _ = pu.run_hip(case, "nan", return_lse=True)
+    ro, rl = pu.run_oracle(case, "nan")
+    pu.compare(o, ro, lse, rl, spec.dtype, "nan", what="fp16 decode 64x32 cache 8192")
+
+
+@pytest.mark.parametrize("policy", ["nan", "zero"])
+def test_cross_mask_f16_full_size(policy):
+    spec, case = _full_case("cross_mask_f16")
+    o, lse, _ = pu.run_hip(case, policy, return_lse=True)
+    # Batch entry 2 is fully masked and entry 5 has no keys: whole rows follow the policy.
+    for b in (spec.mask_all_at, spec.lens_zero_at):
+        if policy == "nan":
+            assert np.isnan(o[b]).all()
+        else:
+            assert (o[b] == 0).all()
+        assert (lse[b] == -np.inf).all()
+    rows = pu.sample_rows(spec, 160)
+    rows = np.concatenate([rows, [[2, 3, 7], [5, 0, 1023], [7, 15, 512]]])
+    ro, rl = pu.run_oracle(case, policy, rows=rows)
+    go = o[rows[:, 0], rows[:, 1], rows[:, 2]]
+    gl = lse[rows[:, 0], rows[:, 1], rows[:, 2]]
+    pu.compare(go, ro, gl, rl, spec.dtype, policy, what="fp16 cross 8x16x1024x2048")
+
+
+# ---------------------------------------------------------------------------
+# Edge cases and properties.
+
+EDGE = [
+    # dtype, B, Hq, Hkv, Lq, Lk, D, causal, offset
+    ("f32", 1, 1, 1, 1, 1, 1, False, None),
+    ("f16", 2, 3, 1, 5, 7, 3, True, None),
+    ("bf16", 1, 2, 2, 65, 129, 256, False, None),
+    ("f16", 1, 4, 2, 33, 64, 128, True, 0),
+    ("bf16", 2, 4, 1, 129, 65, 64, True, -5),
+    ("f32", 1, 2, 1, 40, 300, 33, True, 1000),
+    ("f16", 1, 1, 1, 1, 1, 128, False, None),
+    ("bf16", 1, 8, 8, 256, 256, 128, True, 0),
+    ("f16", 3, 2, 2, 64, 64, 64, True, None),
+    ("bf16", 1, 2, 1, 17, 1, 32, False, None),
+]
+
+
+@pytest.mark.parametrize("cfg", EDGE, ids=lambda c: "x".join(map(str, c)))
+def test_edge_shapes(cfg):
+    dtype, B, Hq, Hkv, Lq, Lk, D, causal, offset = cfg
+    spec = synth.Spec("edge", B, Hq, Hkv, Lq, Lk, D, dtype, seed=Lq * 7 + Lk, causal=causal,
+                      causal_offset=offset, lse=True)
+    case = synth.generate(spec)
+    o, lse, _ = pu.run_hip(case, "zero")
+    ro, rl = pu.run_oracle(case, "zero")
+    pu.compare(o, ro, lse, rl, dtype, "zero", what=str(cfg))
+
+
+@pytest.mark.parametrize("policy", ["nan", "zero"])
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_zero_key_length_problem(policy, dtype):
+    spec = synth.Spec("klen0", 2, 4, 2, 9, 0, 64, dtype, seed=3, lse=True)
+    case = synth.generate(spec)
+    o, lse, _ = pu.run_hip(case, policy)
+    assert (np.isnan(o) if policy == "nan" else (o == 0)).all()
+    assert (lse == -np.inf).all()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_special_values(dtype):
+    """NaN in one visible K element -> NaN row; +inf mask entry -> NaN row; NaN in
+    K beyond the key length, and garbage V rows beyond it, never leak."""
+    torch = pu.torch_mod()
+    spec = synth.Spec("special", 2, 2, 1, 70, 150, 64, dtype, seed=9, causal=True, lse=True,
+                      lens="uniform")
+    case = synth.generate(spec)
+    case.key_lens[:] = [120, 150]
+    k = case.k.copy()
+    v = case.v.copy()
+    nanbits = {"f32": np.float32(np.nan), "f16": np.float16(np.nan), "bf16": np.uint16(0x7FC0)}
+    k[0, 120:, :, :] = nanbits[dtype]        # beyond batch 0's length: never read
+    v[0, 120:, :, :] = nanbits[dtype]
+    k[1, 30, 0, 5] = nanbits[dtype]          # visible to batch 1 rows i >= 30 (offset 80)
+    mask = np.zeros((2, 1, 70, 150), np.float32)
+    mask[0, :, 10, 3] = np.inf               # batch 0, row 10 -> NaN row
+    case = synth.Case(spec, case.q, k, v, case.key_lens, mask)
+    for policy in ("nan", "zero"):
+        o, lse, _ = pu.run_hip(case, policy)
+        ro, rl = pu.run_oracle(case, policy)
+        assert np.isnan(ro[0, :, 10]).all() and np.isnan(ro[1, :, 0]).all()
+        pu.compare(o, ro, lse, rl, dtype, policy, what="special %s" % policy)
+    del torch
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "f32"])
+def test_one_hot_is_bit_exact(dtype):
+    """All keys but j0 hidden by -inf: O equals V[j0] bit for bit."""
+    torch = pu.torch_mod()
+    spec = synth.Spec("onehot", 1, 4, 2, 80, 200, 128 if dtype != "f32" else 64, dtype, seed=4)
+    case = synth.generate(spec)
+    mask = np.full((1, 1, 1, 200), -np.inf, np.float32)
+    mask[..., 137] = 0.5
+    case = synth.Case(spec, case.q, case.k, case.v, None, mask)
+    o, _, (ot, _, tens) = pu.run_hip(case, "nan", return_lse=False)
+    vt = tens["v"]
+    for h in range(4):
+        assert torch.equal(ot[0, :, h, :], vt[0, 137, h // 2, :].expand(80, -1))
+
+
+def test_gqa_map_exact():
+    """V of kv head g is g+1 everywhere -> O of query head h is exactly h//(Hq/Hkv)+1."""
+    spec = synth.Spec("gqa", 2, 12, 4, 96, 96, 64, "bf16", seed=5, causal=True)
+    case = synth.generate(spec)
+    v = np.empty_like(case.v)
+    for g in range(4):
+        v[:, :, g, :] = synth.to_storage(np.full(1, g + 1, np.float32), "bf16")[0]
+    case = synth.Case(spec, case.q, case.k, v, None, None)
+    o, _, _ = pu.run_hip(case, "nan", return_lse=False)
+    for h in range(12):
+        assert (o[:, h] == h // 3 + 1).all()
+
+
+def test_strided_packed_qkv_and_broadcast_mask():
+    """Q/K/V as slices of one packed projection [B, L, Hq+2*Hkv, D]; mask [B,1,Lq,Lk]."""
+    torch = pu.torch_mod()
+    B, L, Hq, Hkv, D = 2, 150, 8, 2, 128
+    rng = np.random.default_rng(21)
+    packed = synth.to_storage(rng.standard_normal((B, L, Hq + 2 * Hkv, D)).astype(np.float32), "f16")
+    mask = rng.standard_normal((B, 1, L, L)).astype(np.float32)
+    pt = pu.to_dev(packed, "f16")
+    q, k, v = pt[:, :, :Hq], pt[:, :, Hq:Hq + Hkv], pt[:, :, Hq + Hkv:]
+    mt = torch.from_numpy(mask).cuda()
+    o, lse = __import__("scaled_dot_product_flash_amd").forward(q, k, v, causal=True, mask=mt,
+                                                                return_lse=True)
+    torch.cuda.synchronize()
+    import oracle
+    ro, rl = oracle.attention(packed[:, :, :Hq], packed[:, :, Hq:Hq + Hkv],
+                              packed[:, :, Hq + Hkv:], dtype="f16", causal=True, mask=mask)
+    pu.compare(pu.canon(pu.to_f64(o), "bshd"), ro, lse.cpu().numpy().astype(np.float64), rl,
+               "f16", "nan", what="packed qkv")
+
+
+@pytest.mark.parametrize("name", ["causal_gqa_bf16_L333", "decode_f16_cache1000",
+                                  "cross_mask_f16_100x300", "causal_gqa_f32"])
+def test_two_runs_bit_identical(name):
+    torch = pu.torch_mod()
+    case = synth.generate(REDUCED[name])
+    _, _, (o1, l1, tens) = pu.run_hip(case, "nan", return_lse=True)
+    _, _, (o2, l2, _) = pu.run_hip(case, "nan", return_lse=True, tensors=tens)
+    assert torch.equal(o1.view(torch.int16) if o1.dtype != torch.float32 else o1.view(torch.int32),
+                       o2.view(torch.int16) if o2.dtype != torch.float32 else o2.view(torch.int32))
+    assert torch.equal(l1.view(torch.int32), l2.view(torch.int32))
+
+
+def test_empty_batch_is_a_no_op():
+    torch = pu.torch_mod()
+    import scaled_dot_product_flash_amd as sdpa
+    q = torch.zeros(0, 4, 2, 64, dtype=torch.float16, device="cuda")
+    o = sdpa.forward(q, q, q)
+    assert o.shape == q.shape
