@@ -1,0 +1,210 @@
+"""Throughput of the fused-attention hot path on one MI355X.
+
+A step is one attn_forward call over the bf16 causal GQA prefill workload
+(B=4, Hq=32, Hkv=8, Lq=Lk=4096, D=128, positions-first, fp32 LSE output);
+`value` is its attention TFLOP/s (4*B*Hq*Lq*Lk*D, halved under the causal
+rule).  The fp16 decode workload (B=64, Hq=32, Hkv=8, cache 8192, per-batch
+lengths uniform in [1, 8192]) is timed the same way after it and reported
+under "decode" as KV-read GB/s.  Inputs are synthetic (seeded N(0,1)) and
+resident in HBM before timing starts.  Kernel durations come from HIP events
+recorded around each call on the stream the kernels run on.
+
+Prints one JSON line.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_MFMA_BF16_TFLOPS = 2516.6     # MI355X dense bf16/fp16 matrix peak
+PEAK_HBM_GBS = 8000.0              # MI355X HBM3E
+METRIC = "attention TFLOP/s (prefill) + KV GB/s (decode), % of MI355X roofline"
+
+
+def kernel_source_hash(names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "scaled_dot_product_flash_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(summary: str, src_hash: str):
+    """HBM bytes per launch from a committed rocprofv3 --pmc summary, or None
+    when the summary is missing or was taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", summary)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_hash") != src_hash:
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def time_calls(fn, steps: int, warmup: int):
+    """Per-call HIP event durations (ms) on the current stream, plus wall time."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record()
+        fn()
+        ends[i].record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3
+    durs = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return durs, wall
+
+
+def to_dev(a, dtype):
+    import torch
+    if dtype == "bf16":
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def cpu_baseline_prefill(case, target_s: float = 12.0):
+    """The float64 oracle, as it stands, on a bounded sample of query rows of the
+    same workload, scaled to TFLOP/s with the same causal FLOP count per row."""
+    import oracle
+    s = case.spec
+    rng = np.random.default_rng(7)
+    threads = oracle.max_threads()
+
+    def run(n):
+        rows = np.stack([rng.integers(0, s.batch, n), rng.integers(0, s.q_heads, n),
+                         rng.integers(0, s.q_len, n)], axis=1).astype(np.int64)
+        t0 = time.perf_counter()
+        oracle.attention(case.q, case.k, case.v, dtype=s.dtype, layout=s.q_layout,
+                         kv_layout=s.kv_layout, causal=s.causal, causal_offset=s.causal_offset,
+                         rows=rows)
+        dt = time.perf_counter() - t0
+        flops = float(np.sum(4.0 * s.head_dim * (rows[:, 2] + 1)))   # visible keys of row i: i+1
+        return n, dt, flops
+
+    n, dt = max(threads, 8), 0.0
+    while True:                      # grow the sample until it runs >= 1 s
+        n, dt, _ = run(n)
+        if dt >= 1.0 or n >= 1 << 20:
+            break
+        n *= 4
+    n2 = int(min(1 << 21, n * target_s / max(dt, 1e-3)))
+    n2, dt2, flops2 = run(n2)
+    return {"value": flops2 / dt2 / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "%d random query rows of the bf16 causal prefill workload (float64 "
+                      "three-pass oracle, %.1f s)" % (n2, dt2)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the hot path here is a single-GPU kernel and no "
+              "multi-GPU run is part of this build (got --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import scaled_dot_product_flash_amd as sdpa
+    from scaled_dot_product_flash_amd import synth
+
+    torch.cuda.set_device(0)
+    spec = synth.CAUSAL_GQA_BF16
+    case = synth.generate(spec)
+    q, k, v = (to_dev(x, spec.dtype) for x in (case.q, case.k, case.v))
+    out = torch.empty_like(q)
+
+    def step():
+        sdpa.forward(q, k, v, causal=True, causal_offset=0, return_lse=True, out=out)
+
+    step()
+    kernel = sdpa.last_kernel()
+    durs, wall = time_calls(step, args.steps, args.warmup)
+    ms = float(np.mean(durs))
+    tflops = spec.flops / (ms * 1e-3) / 1e12
+    src_hash = kernel_source_hash(["prefill_mfma.hip"])
+    traffic = read_traffic("prefill_mfma_bf16_causal_B4H32L4096D128_pmc.txt", src_hash)
+    result = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "bf16 causal GQA prefill B=4 Hq=32 Hkv=8 Lq=Lk=4096 D=128, "
+                               "positions-first, fp32 LSE", "batch": 4, "q_heads": 32,
+                   "kv_heads": 8, "seq_len": 4096, "head_dim": 128, "causal": True,
+                   "kernel": kernel, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
+                     "peak": PEAK_MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / PEAK_MFMA_BF16_TFLOPS, 4), "traffic": traffic,
+                     "kernel_ms": round(ms, 4), "kernel_source_hash": src_hash},
+    }
+    del q, k, v, out
+
+    if not args.no_decode:
+        dspec = synth.DECODE_F16
+        dcase = synth.generate(dspec)
+        dq, dk, dv = (to_dev(x, dspec.dtype) for x in (dcase.q, dcase.k, dcase.v))
+        lens = torch.from_numpy(dcase.key_lens).cuda()
+        dout = torch.empty_like(dq)
+
+        def dstep():
+            sdpa.decode(dq, dk, dv, lens, kv_layout="bhsd", out=dout)
+
+        dstep()
+        dkernel = sdpa.last_kernel()
+        ddurs, _ = time_calls(dstep, args.steps, args.warmup)
+        dms = float(np.mean(ddurs))
+        kv_bytes = float(np.sum(dcase.key_lens.astype(np.float64))) * dspec.kv_heads * \
+            dspec.head_dim * 2 * 2
+        gbs = kv_bytes / (dms * 1e-3) / 1e9
+        result["decode"] = {
+            "workload": "fp16 decode B=64 Hq=32 Hkv=8 D=128, head-first cache of 8192, "
+                        "lengths uniform in [1, 8192] (seed 4)",
+            "value": round(gbs, 1), "unit": "GB/s", "ms_per_call": round(dms, 4),
+            "kv_bytes": kv_bytes, "kernel": dkernel,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "traffic": None},
+        }
+        del dq, dk, dv, dout
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_prefill(case)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

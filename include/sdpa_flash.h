@@ -157,6 +157,11 @@ attn_status attn_workspace_size(const attn_problem* p, int32_t op, size_t* bytes
 /* Message for the last error on the calling thread ("" if none). */
 const char* attn_last_error(void);
 
+/* Name of the kernel family the last successful call on this thread launched
+ * ("prefill_mfma", "prefill_f32", "decode_splitk", "generic", or "" when the
+ * call had no work).  For tests and profiling; the string is static.        */
+const char* attn_last_kernel(void);
+
 /* Library version string. */
 const char* attn_version(void);
 

@@ -25,7 +25,7 @@ _LIB_PATH = os.path.join(_PKG, "libsdpa_flash.so")
 
 # Every symbol include/sdpa_flash.h declares.
 SYMBOLS = ("attn_forward", "attn_decode", "attn_workspace_size", "attn_last_error",
-           "attn_version")
+           "attn_last_kernel", "attn_version")
 
 OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 DTYPE_F32, DTYPE_F16, DTYPE_BF16 = 0, 1, 2
@@ -86,12 +86,19 @@ def load_library():
     lib.attn_last_error.argtypes = []
     lib.attn_version.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []
+    lib.attn_last_kernel.restype = ctypes.c_char_p
+    lib.attn_last_kernel.argtypes = []
     _lib = lib
     return lib
 
 
 def last_error() -> str:
     return load_library().attn_last_error().decode()
+
+
+def last_kernel() -> str:
+    """Kernel family the last call on this thread launched."""
+    return load_library().attn_last_kernel().decode()
 
 
 def _check(status: int):

@@ -16,6 +16,14 @@
 namespace {
 
 thread_local char g_err[512] = "";
+thread_local const char* g_kernel = "";
+
+// Test and debugging override: SDPA_FLASH_KERNEL=generic forces the
+// any-shape kernel for every call.
+bool force_generic() {
+    const char* e = std::getenv("SDPA_FLASH_KERNEL");
+    return e && std::strcmp(e, "generic") == 0;
+}
 
 attn_status fail(attn_status st, const char* fmt, ...) {
     va_list ap;
@@ -133,6 +141,8 @@ extern "C" {
 
 const char* attn_last_error(void) { return g_err; }
 
+const char* attn_last_kernel(void) { return g_kernel; }
+
 const char* attn_version(void) { return "sdpa_flash 0.1 (gfx950)"; }
 
 attn_status attn_workspace_size(const attn_problem* p, int32_t op, size_t* bytes) {
@@ -154,11 +164,18 @@ attn_status attn_forward(const attn_problem* p, const void* q, const void* k, co
     if (st != ATTN_OK) return st;
     if (p->batch == 0 || p->q_len == 0) {
         g_err[0] = '\0';
+        g_kernel = "";
         return ATTN_OK;
     }
     const sdpa::Params prm = make_params(p, q, k, v, o, mask, key_lens, lse);
     const auto dt = static_cast<sdpa::DType>(p->dtype);
-    return launched(sdpa::launch_generic(prm, dt, static_cast<hipStream_t>(stream)));
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (!force_generic() && sdpa::prefill_mfma_supported(prm, dt)) {
+        g_kernel = "prefill_mfma";
+        return launched(sdpa::launch_prefill_mfma(prm, dt, s));
+    }
+    g_kernel = "generic";
+    return launched(sdpa::launch_generic(prm, dt, s));
 }
 
 attn_status attn_decode(const attn_problem* p, const void* q, const void* k, const void* v,

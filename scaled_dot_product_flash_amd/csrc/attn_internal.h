@@ -40,4 +40,7 @@ enum class DType : int { F32 = 0, F16 = 1, BF16 = 2 };
 // Launchers return the hipError_t of the launch.
 hipError_t launch_generic(const Params& p, DType dt, hipStream_t s);
 
+bool prefill_mfma_supported(const Params& p, DType dt);
+hipError_t launch_prefill_mfma(const Params& p, DType dt, hipStream_t s);
+
 }  // namespace sdpa

@@ -218,3 +218,21 @@ def test_empty_batch_is_a_no_op():
     q = torch.zeros(0, 4, 2, 64, dtype=torch.float16, device="cuda")
     o = sdpa.forward(q, q, q)
     assert o.shape == q.shape
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f16", 64), ("f16", 128), ("bf16", 64)])
+def test_matrix_core_path_is_used_and_matches_generic(dtype, D, monkeypatch):
+    """The MFMA kernel serves bf16/fp16 at D = 64/128; it agrees with the
+    any-shape kernel (forced through SDPA_FLASH_KERNEL=generic) within tolerance."""
+    import scaled_dot_product_flash_amd as sdpa
+    spec = synth.Spec("mfma", 2, 8, 2, 300, 300, D, dtype, seed=31, causal=True, lse=True,
+                      lens="uniform")
+    case = synth.generate(spec)
+    o1, l1, (_, _, tens) = pu.run_hip(case, "zero")
+    assert sdpa.last_kernel() == "prefill_mfma"
+    monkeypatch.setenv("SDPA_FLASH_KERNEL", "generic")
+    o2, l2, _ = pu.run_hip(case, "zero", tensors=tens)
+    assert sdpa.last_kernel() == "generic"
+    pu.compare(o1, o2, l1, l2, dtype, "zero", what="mfma vs generic")
+    ro, rl = pu.run_oracle(case, "zero")
+    pu.compare(o1, ro, l1, rl, dtype, "zero", what="mfma vs oracle")
