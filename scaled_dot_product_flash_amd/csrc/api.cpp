@@ -145,6 +145,15 @@ const char* attn_last_kernel(void) { return g_kernel; }
 
 const char* attn_version(void) { return "sdpa_flash 0.1 (gfx950)"; }
 
+// Workspace of the split decode path; depends on the shape only.
+size_t decode_ws(const attn_problem* p) {
+    const bool shape_ok = (p->dtype == ATTN_DTYPE_BF16 || p->dtype == ATTN_DTYPE_F16) &&
+                          (p->head_dim == 64 || p->head_dim == 128) && p->q_len == 1 &&
+                          p->k_len > 0;
+    return shape_ok ? sdpa::decode_workspace_bytes(p->batch, p->q_heads, p->k_len, p->head_dim)
+                    : 0;
+}
+
 attn_status attn_workspace_size(const attn_problem* p, int32_t op, size_t* bytes) {
     if (!bytes) return fail(ATTN_ERR_INVALID, "bytes is NULL");
     *bytes = 0;
@@ -152,6 +161,7 @@ attn_status attn_workspace_size(const attn_problem* p, int32_t op, size_t* bytes
     if (st != ATTN_OK) return st;
     if (op != ATTN_OP_FORWARD && op != ATTN_OP_DECODE)
         return fail(ATTN_ERR_INVALID, "unknown op %d", op);
+    if (op == ATTN_OP_DECODE) *bytes = decode_ws(p);
     return ATTN_OK;
 }
 
@@ -181,7 +191,27 @@ attn_status attn_forward(const attn_problem* p, const void* q, const void* k, co
 attn_status attn_decode(const attn_problem* p, const void* q, const void* k, const void* v,
                         void* o, const float* mask, const int32_t* key_lens, float* lse,
                         void* workspace, size_t workspace_bytes, void* stream) {
-    if (p && p->q_len != 1) return fail(ATTN_ERR_INVALID, "decode needs q_len == 1");
+    attn_status st = validate(p, true, q, k, v, o, mask, lse);
+    if (st != ATTN_OK) return st;
+    if (p->q_len != 1) return fail(ATTN_ERR_INVALID, "decode needs q_len == 1");
+    if (p->batch == 0) {
+        g_err[0] = '\0';
+        g_kernel = "";
+        return ATTN_OK;
+    }
+    sdpa::Params prm = make_params(p, q, k, v, o, mask, key_lens, lse);
+    const auto dt = static_cast<sdpa::DType>(p->dtype);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    sdpa::decode_split_plan(p->k_len, &prm.split_len, &prm.n_split);
+    if (!force_generic() && sdpa::decode_split_supported(prm, dt)) {
+        const size_t need = decode_ws(p);
+        if (!workspace || workspace_bytes < need)
+            return fail(ATTN_ERR_WORKSPACE, "decode needs %zu workspace bytes, got %zu", need,
+                        workspace ? workspace_bytes : size_t(0));
+        prm.ws = workspace;
+        g_kernel = "decode_splitk";
+        return launched(sdpa::launch_decode_split(prm, dt, s));
+    }
     return attn_forward(p, q, k, v, o, mask, key_lens, lse, workspace, workspace_bytes, stream);
 }
 

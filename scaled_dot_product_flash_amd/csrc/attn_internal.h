@@ -41,6 +41,10 @@ enum class DType : int { F32 = 0, F16 = 1, BF16 = 2 };
 hipError_t launch_generic(const Params& p, DType dt, hipStream_t s);
 
 bool prefill_mfma_supported(const Params& p, DType dt);
+bool decode_split_supported(const Params& p, DType dt);
+void decode_split_plan(int Lk, int* split_len, int* n_split);
+size_t decode_workspace_bytes(int B, int Hq, int Lk, int D);
+hipError_t launch_decode_split(const Params& p, DType dt, hipStream_t s);
 hipError_t launch_prefill_mfma(const Params& p, DType dt, hipStream_t s);
 
 }  // namespace sdpa

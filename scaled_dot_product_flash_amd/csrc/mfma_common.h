@@ -1,0 +1,105 @@
+// mfma_common.h -- gfx950 matrix-core helpers shared by the prefill and
+// decode kernels: operand vector types, the 32x32x16 bf16/fp16 MFMA, rounding
+// of fp32 pairs to the element type, and the LDS transpose read.
+//
+// Layouts (v_mfma_f32_32x32x16_{bf16,f16}, wave64), with l the lane:
+//   A[i][k]: lane l holds row i = l%32, k = 8*(l/32) + e for e = 0..7
+//   B[k][j]: lane l holds column j = l%32, k = 8*(l/32) + e
+//   C[i][j]: lane l holds column j = l%32, rows i = 8*(r/4) + 4*(l/32) + r%4,
+//            r = 0..15 the accumulator register.
+// (v_mfma_f32_16x16x32_{bf16,f16}):
+//   A[i][k]: lane l holds row i = l%16, k = 8*(l/16) + e
+//   B[k][j]: lane l holds column j = l%16, k = 8*(l/16) + e
+//   C[i][j]: lane l holds column j = l%16, rows i = 4*(l/16) + r, r = 0..3.
+// ds_read_b64_tr_b16: within each group of 16 lanes, source lane L reads 4
+// elements at its own address; lane i of the group receives element (i%4) of
+// source lane 4*e + i/4 as its element e (a 4x16 -> 16x4 transpose).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sdpa {
+namespace mfma {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
+typedef __attribute__((__vector_size__(8 * sizeof(short)))) short i16x8;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(2 * sizeof(_Float16)))) _Float16 f16x2;
+
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+
+template <bool kBf16> struct Mma;
+
+template <> struct Mma<true> {
+    using vec8 = bf16x8;
+    static __device__ __forceinline__ f32x16 mfma(i16x8 a, i16x8 b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ f32x4 mfma16(i16x8 a, i16x8 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    }
+    // Two floats -> two rounded elements packed in 32 bits (low = a), and the
+    // rounded values back as floats.
+    static __device__ __forceinline__ uint32_t pack(float a, float b, float& ra, float& rb) {
+        bf16x2 v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+        const uint32_t u = __builtin_bit_cast(uint32_t, v);
+        ra = __uint_as_float(u << 16);
+        rb = __uint_as_float(u & 0xffff0000u);
+        return u;
+    }
+    static __device__ __forceinline__ uint32_t pack_out(float a, float b) {
+        bf16x2 v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+        return __builtin_bit_cast(uint32_t, v);
+    }
+};
+
+template <> struct Mma<false> {
+    using vec8 = f16x8;
+    static __device__ __forceinline__ f32x16 mfma(i16x8 a, i16x8 b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ f32x4 mfma16(i16x8 a, i16x8 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ uint32_t pack(float a, float b, float& ra, float& rb) {
+        f16x2 v = {static_cast<_Float16>(a), static_cast<_Float16>(b)};
+        ra = static_cast<float>(v[0]);
+        rb = static_cast<float>(v[1]);
+        return __builtin_bit_cast(uint32_t, v);
+    }
+    static __device__ __forceinline__ uint32_t pack_out(float a, float b) {
+        f16x2 v = {static_cast<_Float16>(a), static_cast<_Float16>(b)};
+        return __builtin_bit_cast(uint32_t, v);
+    }
+};
+
+// Word 3 of a raw (unswizzled, untyped) buffer resource on gfx9-family parts.
+constexpr int kBufferWord3 = 0x00020000;
+
+// A raw buffer over [base, base + bytes): loads at or past the end return
+// zeros, so tile edges need no branch and memory past the end is never read.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0,
+                                             static_cast<int>(bytes), kBufferWord3);
+}
+
+__device__ __forceinline__ i16x8 load16(__amdgpu_buffer_rsrc_t r, int byte_off) {
+    return __builtin_bit_cast(i16x8, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+
+__device__ __forceinline__ i16x4 tr_read(const uint16_t* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (i16x4 __attribute__((address_space(3)))*)(
+            (__attribute__((address_space(3))) uint16_t*)(p)));
+}
+
+}  // namespace mfma
+}  // namespace sdpa

@@ -4,10 +4,11 @@
 // Work decomposition.  A workgroup of 4 waves owns one (batch, query head,
 // block of 128 query rows); each wave owns 32 rows.  The keys are visited in
 // increasing order, 64 per tile, staged through LDS (double buffered, one
-// barrier per tile) with coalesced 16-byte global loads; rows past the key
-// length are zero-filled and never read from memory.  (OneGPU "Attention",
-// introduction and "Variants and ordering": a workgroup keeps a block of query
-// rows and walks key/value tiles held in workgroup memory.)
+// barrier per tile) with coalesced 16-byte raw-buffer loads whose range ends
+// at the batch entry's key length, so rows past it read as zeros and are
+// never fetched.  (OneGPU "Attention", introduction and "Variants and
+// ordering": a workgroup keeps a block of query rows and walks key/value tiles
+// held in workgroup memory.)
 //
 // Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16: the
 // output column is the query, so lane l owns query l%32 and holds 16 of its
@@ -16,17 +17,24 @@
 // kernel": scores transposed so one lane keeps one row).
 //
 // Online normaliser (OneGPU "Attention", introduction; llm.istanbul
-// "05_attention", "Online Softmax Algoritmasi") with a lazily raised reference
-// maximum: the reference m only moves when a tile's maximum exceeds it by more
-// than 8 (base 2), so exp2(t - m) <= 2^8 and the accumulator is rescaled
-// rarely (OneGPU "Apple simdgroup kernel", reference maximum).  Raising is a
-// per-row decision taken identically in both lanes of the row, from data only.
+// "05_attention", "Online Softmax Algoritmasi") kept in raw-score units: with
+// c = scale*log2(e), p = exp2(s*c - m*c) is one FMA and one exp2 per score.
+// The reference maximum m is raised lazily, only when a tile's maximum
+// exceeds it by more than 8/c (so p <= 2^8), and the accumulators are
+// rescaled only then (OneGPU "Apple simdgroup kernel", reference maximum).
+// Raising is a per-row decision taken identically in both lanes of the row.
 //
-// P is rounded to the element type before the P V product and the running sum
-// adds the rounded values, so numerator and denominator see the same p
-// (OneGPU "Matrix hardware").  O^T = V^T P^T runs on the same MFMA shape: the
-// rounded scores are already in the B-operand layout, and the V^T operand is
-// read from the row-major V tile with the LDS transpose read ds_read_b64_tr_b16.
+// P is rounded to the element type before the P V product, and the running
+// sum is the sum of the ROUNDED values, so numerator and denominator see the
+// same p (OneGPU "Matrix hardware").  That sum comes from the matrix core:
+// one extra MFMA per 16 keys multiplies P^T by an all-ones operand, which is
+// cheaper here than the vector instructions it replaces.
+// O^T = V^T P^T: the rounded scores are already in the B-operand layout, and
+// the V^T operand is read from the row-major V tile with ds_read_b64_tr_b16.
+//
+// Element-wise work that only some tiles need (the causal diagonal, the tile
+// holding the key length, the additive mask) is done only on those tiles;
+// the mask is a compile-time variant of the kernel.
 //
 // Special values (OneGPU "Special values"): hidden keys get -inf and weigh 0;
 // a row whose reference max is still -inf uses 0 as the exponent base, so
@@ -34,64 +42,18 @@
 // with l == 0 and follows the masked-row policy; NaN / +inf scores make l NaN.
 #include "attn_internal.h"
 #include "device_common.h"
+#include "mfma_common.h"
 
 namespace sdpa {
 
 namespace {
 
-typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
-typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
-typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
-typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
-typedef __attribute__((__vector_size__(8 * sizeof(short)))) short i16x8;
-typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
-typedef __attribute__((__vector_size__(2 * sizeof(_Float16)))) _Float16 f16x2;
+using namespace mfma;
 
 constexpr int kBM = 128;       // query rows per workgroup
 constexpr int kBN = 64;        // keys per tile
 constexpr int kWaves = 4;
 constexpr float kSlack = 8.f;  // lazy-rescale threshold, base-2 units
-
-template <bool kBf16> struct Mma;
-
-template <> struct Mma<true> {
-    using vec8 = bf16x8;
-    static __device__ __forceinline__ f32x16 mfma(i16x8 a, i16x8 b, f32x16 c) {
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-    }
-    // Two floats -> two rounded elements packed in 32 bits (low = a), and the
-    // rounded values back as floats.
-    static __device__ __forceinline__ uint32_t pack(float a, float b, float& ra, float& rb) {
-        bf16x2 v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
-        const uint32_t u = __builtin_bit_cast(uint32_t, v);
-        ra = __uint_as_float(u << 16);
-        rb = __uint_as_float(u & 0xffff0000u);
-        return u;
-    }
-    static __device__ __forceinline__ uint32_t pack_out(float a, float b) {
-        bf16x2 v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
-        return __builtin_bit_cast(uint32_t, v);
-    }
-};
-
-template <> struct Mma<false> {
-    using vec8 = f16x8;
-    static __device__ __forceinline__ f32x16 mfma(i16x8 a, i16x8 b, f32x16 c) {
-        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
-                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-    }
-    static __device__ __forceinline__ uint32_t pack(float a, float b, float& ra, float& rb) {
-        f16x2 v = {static_cast<_Float16>(a), static_cast<_Float16>(b)};
-        ra = static_cast<float>(v[0]);
-        rb = static_cast<float>(v[1]);
-        return __builtin_bit_cast(uint32_t, v);
-    }
-    static __device__ __forceinline__ uint32_t pack_out(float a, float b) {
-        f16x2 v = {static_cast<_Float16>(a), static_cast<_Float16>(b)};
-        return __builtin_bit_cast(uint32_t, v);
-    }
-};
 
 // LDS row strides (elements).  K rows are read 16 lanes x 16 bytes at a time
 // down one column: a stride of 16 mod 256 bytes spreads them over all banks.
@@ -100,18 +62,11 @@ template <> struct Mma<false> {
 template <int D> struct Tile {
     static constexpr int KS = D + 8;
     static constexpr int VS = D + 32;
-    static constexpr int kChunks = kBN * D / 8;              // 16-byte chunks per tile
-    static constexpr int kLoads = kChunks / (64 * kWaves);   // per thread
-    static constexpr int kRowChunks = D / 8;
+    static constexpr int kRowChunks = D / 8;                  // 16-byte chunks per row
+    static constexpr int kLoads = kBN * kRowChunks / (64 * kWaves);   // per thread
 };
 
-__device__ __forceinline__ i16x4 tr_read(const uint16_t* p) {
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (i16x4 __attribute__((address_space(3)))*)(
-            (__attribute__((address_space(3))) uint16_t*)(p)));
-}
-
-template <bool kBf16, int D>
+template <bool kBf16, int D, bool kMask>
 __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(Params p, int n_qblk,
                                                               int xcd_units, int mask_vec4) {
     using M = Mma<kBf16>;
@@ -172,9 +127,11 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(Params p, int n_qb
     if (qw0 >= p.Lq) wave_hi = 0;
     const int n_tiles = static_cast<int>((blk_hi + kBN - 1) / kBN);
 
-    const uint16_t* __restrict__ qg = static_cast<const uint16_t*>(p.q);
-    const uint16_t* __restrict__ kg = static_cast<const uint16_t*>(p.k) + b * p.ks.sb + g * p.ks.sh;
-    const uint16_t* __restrict__ vg = static_cast<const uint16_t*>(p.v) + b * p.vs.sb + g * p.vs.sh;
+    const uint16_t* qg = static_cast<const uint16_t*>(p.q);
+    const uint16_t* kg = static_cast<const uint16_t*>(p.k) + b * p.ks.sb + g * p.ks.sh;
+    const uint16_t* vg = static_cast<const uint16_t*>(p.v) + b * p.vs.sb + g * p.vs.sh;
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(kg, kv_len * p.ks.sr * 2);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vg, kv_len * p.vs.sr * 2);
 
     // ---- Q^T operand, resident in registers -------------------------------
     const int64_t qrow = qw0 + col;
@@ -190,43 +147,41 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(Params p, int n_qb
     }
 
     // ---- staging of one K/V tile: global -> registers -> LDS --------------
+    const int st_row = tid / TL::kRowChunks;                 // + n * kRowsPerPass
+    const int st_col = (tid % TL::kRowChunks) * 8;
+    constexpr int kRowsPerPass = 256 / TL::kRowChunks;
     i16x8 kst[TL::kLoads], vst[TL::kLoads];
     auto fetch = [&](int tile) {
-        const int64_t j0 = static_cast<int64_t>(tile) * kBN;
+        const int key0 = tile * kBN + st_row;
 #pragma unroll
         for (int n = 0; n < TL::kLoads; ++n) {
-            const int c = tid + 256 * n;
-            const int r = c / TL::kRowChunks;
-            const int cc = (c % TL::kRowChunks) * 8;
-            const int64_t key = j0 + r;
-            if (key < kv_len) {
-                kst[n] = *reinterpret_cast<const i16x8*>(kg + key * p.ks.sr + cc);
-                vst[n] = *reinterpret_cast<const i16x8*>(vg + key * p.vs.sr + cc);
-            } else {
-                kst[n] = i16x8{};
-                vst[n] = i16x8{};
-            }
+            const int key = key0 + n * kRowsPerPass;
+            kst[n] = load16(krs, (key * static_cast<int>(p.ks.sr) + st_col) * 2);
+            vst[n] = load16(vrs, (key * static_cast<int>(p.vs.sr) + st_col) * 2);
         }
     };
     auto stash = [&](int buf) {
 #pragma unroll
         for (int n = 0; n < TL::kLoads; ++n) {
-            const int c = tid + 256 * n;
-            const int r = c / TL::kRowChunks;
-            const int cc = (c % TL::kRowChunks) * 8;
-            *reinterpret_cast<i16x8*>(&k_sh[buf][r * KS + cc]) = kst[n];
-            *reinterpret_cast<i16x8*>(&v_sh[buf][r * VS + cc]) = vst[n];
+            const int r = st_row + n * kRowsPerPass;
+            *reinterpret_cast<i16x8*>(&k_sh[buf][r * KS + st_col]) = kst[n];
+            *reinterpret_cast<i16x8*>(&v_sh[buf][r * VS + st_col]) = vst[n];
         }
     };
 
     const float* mrow = nullptr;
-    if (p.mask && qrow < p.Lq) mrow = p.mask + b * p.ms.sb + h * p.ms.sh + qrow * p.ms.sr;
+    if (kMask && qrow < p.Lq) mrow = p.mask + b * p.ms.sb + h * p.ms.sh + qrow * p.ms.sr;
+    const float c = p.scale_log2;          // > 0
+    const float slack = kSlack / c;        // lazy threshold in raw-score units
+    const float inv_scale = kLog2e / c;    // mask (natural units) -> raw-score units
 
-    float m_ref = kNegInf;   // reference maximum of this lane's row (base 2)
-    float l_sum = 0.f;       // this lane's share of the running sum
+    float m_ref = kNegInf;   // reference maximum of this lane's row, raw-score units
     f32x16 acc[ND];
+    f32x16 lacc = f32x16{};  // every row holds this column's sum of rounded p
 #pragma unroll
     for (int d = 0; d < ND; ++d) acc[d] = f32x16{};
+    constexpr short kOne = kBf16 ? 0x3F80 : 0x3C00;   // 1.0 in the element type
+    const i16x8 ones = {kOne, kOne, kOne, kOne, kOne, kOne, kOne, kOne};
 
     if (n_tiles > 0) {
         fetch(0);
@@ -252,62 +207,62 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(Params p, int n_qb
                     s[kb] = M::mfma(a, qop[t], s[kb]);
                 }
             }
-            // -- scores in base-2 units; hide keys past the length / causal bound --
-            const bool partial = (j0 + kBN > kv_len) ||
-                                 (p.causal && j0 + kBN - 1 > qw0 + p.delta);
-            const int64_t qlim = qrow + p.delta;   // causal: key <= qlim
+            // -- additive mask, folded into raw-score units --
+            if (kMask && mrow) {
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
+                for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int kofs = kb * 32 + 8 * u + 4 * hh;   // first of 4 keys
-                    float madd[4] = {0.f, 0.f, 0.f, 0.f};
-                    if (mrow) {
-                        const int64_t key = j0 + kofs;
+                    for (int u = 0; u < 4; ++u) {
+                        const int64_t key = j0 + kb * 32 + 8 * u + 4 * hh;
+                        float mv[4];
                         if (mask_vec4 && key + 3 < kv_len) {
-                            const float4 mv = *reinterpret_cast<const float4*>(mrow + key);
-                            madd[0] = mv.x; madd[1] = mv.y; madd[2] = mv.z; madd[3] = mv.w;
+                            const float4 m4 = *reinterpret_cast<const float4*>(mrow + key);
+                            mv[0] = m4.x; mv[1] = m4.y; mv[2] = m4.z; mv[3] = m4.w;
                         } else {
 #pragma unroll
-                            for (int e = 0; e < 4; ++e)
-                                madd[e] = (key + e < kv_len) ? mrow[key + e] : 0.f;
+                            for (int e = 0; e < 4; ++e) mv[e] = (key + e < kv_len) ? mrow[key + e] : 0.f;
                         }
-                    }
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int r = 4 * u + e;
-                        float t = fmaf(s[kb][r], p.scale_log2, madd[e] * kLog2e);
-                        if (partial) {
-                            const int64_t key = j0 + kofs + e;
-                            const bool hidden = key >= kv_len || (p.causal && key > qlim);
-                            t = hidden ? kNegInf : t;
-                        }
-                        s[kb][r] = t;
+                        for (int e = 0; e < 4; ++e)
+                            s[kb][4 * u + e] = fmaf(mv[e], inv_scale, s[kb][4 * u + e]);
                     }
                 }
+            }
+            // -- hide keys past the length / causal bound (edge tiles only) --
+            const bool partial = (j0 + kBN > kv_len) || (p.causal && j0 + kBN - 1 > qw0 + p.delta);
+            if (partial) {
+                const int64_t qlim = p.causal ? qrow + p.delta : kv_len;
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int64_t key = j0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+                        if (key >= kv_len || key > qlim) s[kb][r] = kNegInf;
+                    }
             }
             // -- row maximum: 32 values in-lane, then the partner lane --
             float mx = kNegInf;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+                for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[kb][r], s[kb][r + 1]));
             mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
             // -- lazy raise of the reference maximum --
-            const bool raise = mx > m_ref + kSlack;
+            const bool raise = mx > m_ref + slack;
             if (__builtin_amdgcn_ballot_w64(raise)) {
                 const float m_new = raise ? mx : m_ref;
                 // 0 when m_ref = -inf; rows that do not raise keep alpha = 1 exactly.
-                const float alpha = raise ? fast_exp2(m_ref - m_new) : 1.f;
-                l_sum *= alpha;
+                const float alpha = raise ? fast_exp2((m_ref - m_new) * c) : 1.f;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) lacc[r] *= alpha;
 #pragma unroll
                 for (int d = 0; d < ND; ++d)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) acc[d][r] *= alpha;
                 m_ref = m_new;
             }
-            const float base = (m_ref == kNegInf) ? 0.f : m_ref;
-            // -- p = exp2(t - base), rounded to the element type; l sums the rounded p --
+            const float neg_mc = (m_ref == kNegInf) ? 0.f : -m_ref * c;
+            // -- p = exp2(s*c - m*c), rounded to the element type --
             i16x8 pop[2][2];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
@@ -317,15 +272,13 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(Params p, int n_qb
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int r = 8 * st + 2 * e;
-                        float ra, rb;
-                        w4[e] = M::pack(fast_exp2(s[kb][r] - base), fast_exp2(s[kb][r + 1] - base),
-                                        ra, rb);
-                        l_sum += ra + rb;
+                        w4[e] = M::pack_out(fast_exp2(fmaf(s[kb][r], c, neg_mc)),
+                                            fast_exp2(fmaf(s[kb][r + 1], c, neg_mc)));
                     }
                     pop[kb][st] = __builtin_bit_cast(i16x8, (uint4){w4[0], w4[1], w4[2], w4[3]});
                 }
             }
-            // -- O^T += V^T P^T; V^T comes from the transpose read of row-major V --
+            // -- O^T += V^T P^T (V^T by transpose read); l += 1^T P^T --
             const int gi = lane & 15;
             const int dsub = 16 * ((lane >> 4) & 1) + 4 * (gi & 3);
 #pragma unroll
@@ -342,6 +295,7 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(Params p, int n_qb
                         const i16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
                         acc[d] = M::mfma(a, pop[kb][st], acc[d]);
                     }
+                    lacc = M::mfma(ones, pop[kb][st], lacc);
                 }
             }
         }
@@ -350,7 +304,7 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(Params p, int n_qb
     }
 
     // ---- epilogue: O = acc / l (or the masked-row policy), LSE = m + log l --
-    const float l_tot = l_sum + __shfl_xor(l_sum, 32, 64);
+    const float l_tot = lacc[0];
     if (qrow < p.Lq) {
         const bool empty = (l_tot == 0.f);
         const float inv = 1.f / l_tot;
@@ -368,7 +322,7 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(Params p, int n_qb
             }
         }
         if (p.lse && hh == 0) {
-            const float lse = empty ? kNegInf : (m_ref + fast_log2(l_tot)) * kLn2;
+            const float lse = empty ? kNegInf : (m_ref * c + fast_log2(l_tot)) * kLn2;
             p.lse[b * p.ls.sb + h * p.ls.sh + qrow * p.ls.sr] = lse;
         }
     }
@@ -382,8 +336,13 @@ hipError_t launch_one(const Params& p, hipStream_t s) {
     const int mask_vec4 = p.mask && (reinterpret_cast<uintptr_t>(p.mask) % 16 == 0) &&
                           p.ms.sb % 4 == 0 && p.ms.sh % 4 == 0 && p.ms.sr % 4 == 0;
     const int64_t blocks = static_cast<int64_t>(n_qblk) * p.B * p.Hq;
-    hipLaunchKernelGGL((prefill_mfma_kernel<kBf16, D>), dim3(static_cast<uint32_t>(blocks)),
-                       dim3(256), 0, s, p, n_qblk, xcd_units, mask_vec4);
+    const dim3 grid(static_cast<uint32_t>(blocks));
+    if (p.mask)
+        hipLaunchKernelGGL((prefill_mfma_kernel<kBf16, D, true>), grid, dim3(256), 0, s, p, n_qblk,
+                           xcd_units, mask_vec4);
+    else
+        hipLaunchKernelGGL((prefill_mfma_kernel<kBf16, D, false>), grid, dim3(256), 0, s, p,
+                           n_qblk, xcd_units, mask_vec4);
     return hipGetLastError();
 }
 
@@ -399,6 +358,12 @@ bool prefill_mfma_supported(const Params& p, DType dt) {
     };
     if (!al(p.q, p.qs, 8) || !al(p.o, p.os, 4)) return false;
     if (p.Lk > 0 && (!al(p.k, p.ks, 8) || !al(p.v, p.vs, 8))) return false;
+    // Buffer offsets within one (b, kv head) slice are 32-bit, including the
+    // up-to-one-tile overrun past the key length.
+    if (p.ks.sr >= (1 << 24) || p.vs.sr >= (1 << 24)) return false;
+    if ((static_cast<int64_t>(p.Lk) + kBN) * p.ks.sr * 2 >= (int64_t(1) << 31) ||
+        (static_cast<int64_t>(p.Lk) + kBN) * p.vs.sr * 2 >= (int64_t(1) << 31))
+        return false;
     const int64_t blocks = static_cast<int64_t>((p.Lq + kBM - 1) / kBM) * p.B * p.Hq;
     return blocks < (int64_t(1) << 31);
 }

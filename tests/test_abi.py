@@ -138,3 +138,19 @@ def test_python_binding_refuses_cpu_tensors():
     q = torch.zeros(1, 4, 2, 8)
     with pytest.raises(ValueError):
         sdpa.forward(q, q, q)
+
+
+def test_decode_workspace_is_checked_before_launch():
+    lib = sdpa.load_library()
+    p = _problem(q_len=1, k_len=4096, dtype=sdpa.DTYPE_F16, head_dim=128)
+    for lay, H, L in (("q", 4, 1), ("k", 2, 4096), ("v", 2, 4096), ("o", 4, 1)):
+        setattr(p, lay, sdpa.Layout(0, L * H * 128, 128, H * 128))
+    need = sdpa.workspace_size(p, sdpa.OP_DECODE)
+    assert need > 0
+    assert sdpa.workspace_size(p, sdpa.OP_FORWARD) == 0
+    rc = lib.attn_decode(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, None, None, None, 0, None)
+    assert rc == sdpa.ERR_WORKSPACE
+    rc = lib.attn_decode(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, None, None, FAKE,
+                         need - 4, None)
+    assert rc == sdpa.ERR_WORKSPACE
+    assert b"workspace" in lib.attn_last_error()

@@ -236,3 +236,56 @@ def test_matrix_core_path_is_used_and_matches_generic(dtype, D, monkeypatch):
     pu.compare(o1, o2, l1, l2, dtype, "zero", what="mfma vs generic")
     ro, rl = pu.run_oracle(case, "zero")
     pu.compare(o1, ro, l1, rl, dtype, "zero", what="mfma vs oracle")
+
+
+DECODE = [
+    # dtype, B, Hq, Hkv, cap, D, lens
+    ("f16", 6, 32, 8, 3000, 128, [1, 3000, 0, 257, 1024, 2999]),
+    ("bf16", 5, 8, 8, 700, 64, [700, 1, 128, 129, 0]),
+    ("f16", 3, 32, 1, 513, 128, [513, 256, 255]),
+    ("bf16", 2, 6, 2, 9000, 128, [9000, 4097]),
+]
+
+
+@pytest.mark.parametrize("cfg", DECODE, ids=lambda c: "x".join(map(str, c[:6])))
+@pytest.mark.parametrize("policy", ["nan", "zero"])
+def test_decode_split_path(cfg, policy, monkeypatch):
+    """Split-K decode + ordered combine against the oracle and the any-shape kernel."""
+    import scaled_dot_product_flash_amd as sdpa
+    dtype, B, Hq, Hkv, cap, D, lens = cfg
+    spec = synth.Spec("decode", B, Hq, Hkv, 1, cap, D, dtype, seed=cap + B, kv_layout="bhsd",
+                      causal=True, decode=True, lens="uniform", lse=True)
+    case = synth.generate(spec)
+    case.key_lens[:] = lens
+    o1, l1, (_, _, tens) = pu.run_hip(case, policy)
+    assert sdpa.last_kernel() == "decode_splitk"
+    ro, rl = pu.run_oracle(case, policy)
+    pu.compare(o1, ro, l1, rl, dtype, policy, what="decode %s" % (cfg,))
+    monkeypatch.setenv("SDPA_FLASH_KERNEL", "generic")
+    o2, l2, _ = pu.run_hip(case, policy, tensors=tens)
+    assert sdpa.last_kernel() == "generic"
+    pu.compare(o1, o2, l1, l2, dtype, policy, what="decode vs generic")
+
+
+def test_decode_with_mask_and_garbage_beyond_length():
+    """Per-head mask rows; NaN cache rows past each length are never read."""
+    torch = pu.torch_mod()
+    spec = synth.Spec("decode-mask", 4, 8, 2, 1, 1500, 128, "f16", seed=77, kv_layout="bhsd",
+                      causal=True, decode=True, lens="uniform", lse=True)
+    case = synth.generate(spec)
+    case.key_lens[:] = [1500, 700, 3, 1]
+    k, v = case.k.copy(), case.v.copy()
+    for b, L in enumerate(case.key_lens):
+        k[b, :, L:] = np.float16(np.nan)
+        v[b, :, L:] = np.float16(np.nan)
+    rng = np.random.default_rng(5)
+    mask = rng.standard_normal((4, 8, 1, 1500)).astype(np.float32)
+    mask[rng.random(mask.shape) < 0.2] = -np.inf
+    mask[3, :, :, 0] = -np.inf                  # batch 3: its only key hidden -> empty rows
+    case = synth.Case(spec, case.q, k, v, case.key_lens, mask)
+    for policy in ("nan", "zero"):
+        o, lse, _ = pu.run_hip(case, policy)
+        ro, rl = pu.run_oracle(case, policy)
+        assert (rl[3] == -np.inf).all()
+        pu.compare(o, ro, lse, rl, "f16", policy, what="decode mask %s" % policy)
+    del torch
