@@ -57,6 +57,11 @@ template <> struct Mma<true> {
         bf16x2 v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
         return __builtin_bit_cast(uint32_t, v);
     }
+    // acc + (both rounded elements of a packed pair), products by 1 are exact.
+    static __device__ __forceinline__ float sum2(uint32_t pair, float acc) {
+        const bf16x2 one = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), one, acc, false);
+    }
 };
 
 template <> struct Mma<false> {
@@ -78,6 +83,10 @@ template <> struct Mma<false> {
     static __device__ __forceinline__ uint32_t pack_out(float a, float b) {
         f16x2 v = {static_cast<_Float16>(a), static_cast<_Float16>(b)};
         return __builtin_bit_cast(uint32_t, v);
+    }
+    static __device__ __forceinline__ float sum2(uint32_t pair, float acc) {
+        const f16x2 one = {static_cast<_Float16>(1.f), static_cast<_Float16>(1.f)};
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pair), one, acc, false);
     }
 };
 

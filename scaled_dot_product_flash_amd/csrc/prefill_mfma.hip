@@ -26,9 +26,8 @@
 //
 // P is rounded to the element type before the P V product, and the running
 // sum is the sum of the ROUNDED values, so numerator and denominator see the
-// same p (OneGPU "Matrix hardware").  That sum comes from the matrix core:
-// one extra MFMA per 16 keys multiplies P^T by an all-ones operand, which is
-// cheaper here than the vector instructions it replaces.
+// same p (OneGPU "Matrix hardware"): one v_dot2 of each packed pair with
+// (1, 1) adds both rounded values exactly.
 // O^T = V^T P^T: the rounded scores are already in the B-operand layout, and
 // the V^T operand is read from the row-major V tile with ds_read_b64_tr_b16.
 //
@@ -146,26 +145,50 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(Params p, int n_qb
         }
     }
 
-    // ---- staging of one K/V tile: global -> registers -> LDS --------------
+    // ---- staging: global -> registers -> LDS.  K runs one tile ahead of V:
+    // while tile t's softmax and P V run, tile t+1's scores are computed, so
+    // LDS holds K(t+1) and V(t) and the registers carry K(t+2) and V(t+1).
     const int st_row = tid / TL::kRowChunks;                 // + n * kRowsPerPass
     const int st_col = (tid % TL::kRowChunks) * 8;
     constexpr int kRowsPerPass = 256 / TL::kRowChunks;
     i16x8 kst[TL::kLoads], vst[TL::kLoads];
-    auto fetch = [&](int tile) {
-        const int key0 = tile * kBN + st_row;
+    auto fetch_k = [&](int tile) {
 #pragma unroll
         for (int n = 0; n < TL::kLoads; ++n) {
-            const int key = key0 + n * kRowsPerPass;
+            const int key = tile * kBN + st_row + n * kRowsPerPass;
             kst[n] = load16(krs, (key * static_cast<int>(p.ks.sr) + st_col) * 2);
+        }
+    };
+    auto fetch_v = [&](int tile) {
+#pragma unroll
+        for (int n = 0; n < TL::kLoads; ++n) {
+            const int key = tile * kBN + st_row + n * kRowsPerPass;
             vst[n] = load16(vrs, (key * static_cast<int>(p.vs.sr) + st_col) * 2);
         }
     };
-    auto stash = [&](int buf) {
+    auto stash_k = [&](int buf) {
 #pragma unroll
-        for (int n = 0; n < TL::kLoads; ++n) {
-            const int r = st_row + n * kRowsPerPass;
-            *reinterpret_cast<i16x8*>(&k_sh[buf][r * KS + st_col]) = kst[n];
-            *reinterpret_cast<i16x8*>(&v_sh[buf][r * VS + st_col]) = vst[n];
+        for (int n = 0; n < TL::kLoads; ++n)
+            *reinterpret_cast<i16x8*>(&k_sh[buf][(st_row + n * kRowsPerPass) * KS + st_col]) = kst[n];
+    };
+    auto stash_v = [&](int buf) {
+#pragma unroll
+        for (int n = 0; n < TL::kLoads; ++n)
+            *reinterpret_cast<i16x8*>(&v_sh[buf][(st_row + n * kRowsPerPass) * VS + st_col]) = vst[n];
+    };
+    // The two 32-key blocks' MFMA chains alternate, so consecutive MFMAs are
+    // independent.
+    auto scores = [&](int buf, f32x16 (&s)[2]) {
+        const uint16_t* krow = &k_sh[buf][col * KS + 8 * hh];
+        s[0] = f32x16{};
+        s[1] = f32x16{};
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const i16x8 a = *reinterpret_cast<const i16x8*>(krow + kb * 32 * KS + 16 * t);
+                s[kb] = M::mfma(a, qop[t], s[kb]);
+            }
         }
     };
 
@@ -176,135 +199,144 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(Params p, int n_qb
     const float inv_scale = kLog2e / c;    // mask (natural units) -> raw-score units
 
     float m_ref = kNegInf;   // reference maximum of this lane's row, raw-score units
+    float l_sum = 0.f;       // this lane's share of the sum of rounded p
     f32x16 acc[ND];
-    f32x16 lacc = f32x16{};  // every row holds this column's sum of rounded p
 #pragma unroll
     for (int d = 0; d < ND; ++d) acc[d] = f32x16{};
-    constexpr short kOne = kBf16 ? 0x3F80 : 0x3C00;   // 1.0 in the element type
-    const i16x8 ones = {kOne, kOne, kOne, kOne, kOne, kOne, kOne, kOne};
 
     if (n_tiles > 0) {
-        fetch(0);
-        stash(0);
+        fetch_k(0);
+        fetch_v(0);
+        if (n_tiles > 1) {
+            stash_k(0);
+            fetch_k(1);
+            stash_k(1);
+        } else {
+            stash_k(0);
+        }
+        stash_v(0);
     }
     __syncthreads();
 
-    for (int tile = 0; tile < n_tiles; ++tile) {
-        const int buf = tile & 1;
-        if (tile + 1 < n_tiles) fetch(tile + 1);
-        const int64_t j0 = static_cast<int64_t>(tile) * kBN;
+    f32x16 s_cur[2];
+    if (n_tiles > 0) scores(0, s_cur);
 
-        if (j0 < wave_hi) {
-            // -- S^T = K Q^T for two 32-key blocks --
-            f32x16 s[2];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                s[kb] = f32x16{};
-                const uint16_t* krow = &k_sh[buf][(kb * 32 + col) * KS + 8 * hh];
-#pragma unroll
-                for (int t = 0; t < NT; ++t) {
-                    const i16x8 a = *reinterpret_cast<const i16x8*>(krow + 16 * t);
-                    s[kb] = M::mfma(a, qop[t], s[kb]);
-                }
-            }
-            // -- additive mask, folded into raw-score units --
-            if (kMask && mrow) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const int64_t key = j0 + kb * 32 + 8 * u + 4 * hh;
-                        float mv[4];
-                        if (mask_vec4 && key + 3 < kv_len) {
-                            const float4 m4 = *reinterpret_cast<const float4*>(mrow + key);
-                            mv[0] = m4.x; mv[1] = m4.y; mv[2] = m4.z; mv[3] = m4.w;
-                        } else {
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) mv[e] = (key + e < kv_len) ? mrow[key + e] : 0.f;
-                        }
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            s[kb][4 * u + e] = fmaf(mv[e], inv_scale, s[kb][4 * u + e]);
-                    }
-                }
-            }
-            // -- hide keys past the length / causal bound (edge tiles only) --
-            const bool partial = (j0 + kBN > kv_len) || (p.causal && j0 + kBN - 1 > qw0 + p.delta);
-            if (partial) {
-                const int64_t qlim = p.causal ? qrow + p.delta : kv_len;
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int64_t key = j0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-                        if (key >= kv_len || key > qlim) s[kb][r] = kNegInf;
-                    }
-            }
-            // -- row maximum: 32 values in-lane, then the partner lane --
-            float mx = kNegInf;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[kb][r], s[kb][r + 1]));
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-            // -- lazy raise of the reference maximum --
-            const bool raise = mx > m_ref + slack;
-            if (__builtin_amdgcn_ballot_w64(raise)) {
-                const float m_new = raise ? mx : m_ref;
-                // 0 when m_ref = -inf; rows that do not raise keep alpha = 1 exactly.
-                const float alpha = raise ? fast_exp2((m_ref - m_new) * c) : 1.f;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) lacc[r] *= alpha;
-#pragma unroll
-                for (int d = 0; d < ND; ++d)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[d][r] *= alpha;
-                m_ref = m_new;
-            }
-            const float neg_mc = (m_ref == kNegInf) ? 0.f : -m_ref * c;
-            // -- p = exp2(s*c - m*c), rounded to the element type --
-            i16x8 pop[2][2];
+    for (int tile = 0; tile < n_tiles; ++tile) {
+        const bool more_k = tile + 2 < n_tiles;
+        const bool more_v = tile + 1 < n_tiles;
+        if (more_k) fetch_k(tile + 2);
+        if (more_v) fetch_v(tile + 1);
+        const int64_t j0 = static_cast<int64_t>(tile) * kBN;
+        const bool sees = j0 < wave_hi;
+
+        // -- additive mask, folded into raw-score units --
+        if (kMask && mrow && sees) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-                for (int st = 0; st < 2; ++st) {
-                    uint32_t w4[4];
+                for (int u = 0; u < 4; ++u) {
+                    const int64_t key = j0 + kb * 32 + 8 * u + 4 * hh;
+                    float mv[4];
+                    if (mask_vec4 && key + 3 < kv_len) {
+                        const float4 m4 = *reinterpret_cast<const float4*>(mrow + key);
+                        mv[0] = m4.x; mv[1] = m4.y; mv[2] = m4.z; mv[3] = m4.w;
+                    } else {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int r = 8 * st + 2 * e;
-                        w4[e] = M::pack_out(fast_exp2(fmaf(s[kb][r], c, neg_mc)),
-                                            fast_exp2(fmaf(s[kb][r + 1], c, neg_mc)));
+                        for (int e = 0; e < 4; ++e) mv[e] = (key + e < kv_len) ? mrow[key + e] : 0.f;
                     }
-                    pop[kb][st] = __builtin_bit_cast(i16x8, (uint4){w4[0], w4[1], w4[2], w4[3]});
-                }
-            }
-            // -- O^T += V^T P^T (V^T by transpose read); l += 1^T P^T --
-            const int gi = lane & 15;
-            const int dsub = 16 * ((lane >> 4) & 1) + 4 * (gi & 3);
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-                for (int st = 0; st < 2; ++st) {
-                    const int row = kb * 32 + 16 * st + 4 * hh + (gi >> 2);
-                    const uint16_t* v0 = &v_sh[buf][row * VS + dsub];
-                    const uint16_t* v1 = v0 + 8 * VS;
-#pragma unroll
-                    for (int d = 0; d < ND; ++d) {
-                        const i16x4 lo = tr_read(v0 + 32 * d);
-                        const i16x4 hi = tr_read(v1 + 32 * d);
-                        const i16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                        acc[d] = M::mfma(a, pop[kb][st], acc[d]);
-                    }
-                    lacc = M::mfma(ones, pop[kb][st], lacc);
+                    for (int e = 0; e < 4; ++e)
+                        s_cur[kb][4 * u + e] = fmaf(mv[e], inv_scale, s_cur[kb][4 * u + e]);
                 }
             }
         }
-        if (tile + 1 < n_tiles) stash(buf ^ 1);
+        // -- hide keys past the length / causal bound (edge tiles only) --
+        const bool partial = (j0 + kBN > kv_len) || (p.causal && j0 + kBN - 1 > qw0 + p.delta);
+        if (partial) {
+            const int64_t qlim = p.causal ? qrow + p.delta : kv_len;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int64_t key = j0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+                    if (key >= kv_len || key > qlim) s_cur[kb][r] = kNegInf;
+                }
+        }
+
+        // -- row maximum: 32 values in-lane, then the partner lane --
+        float mx = kNegInf;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s_cur[kb][r], s_cur[kb][r + 1]));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        // -- lazy raise of the reference maximum --
+        const bool raise = mx > m_ref + slack;
+        if (__builtin_amdgcn_ballot_w64(raise)) {
+            const float m_new = raise ? mx : m_ref;
+            // 0 when m_ref = -inf; rows that do not raise keep alpha = 1 exactly.
+            const float alpha = raise ? fast_exp2((m_ref - m_new) * c) : 1.f;
+            l_sum *= alpha;
+#pragma unroll
+            for (int d = 0; d < ND; ++d)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[d][r] *= alpha;
+            m_ref = m_new;
+        }
+        const float neg_mc = (m_ref == kNegInf) ? 0.f : -m_ref * c;
+        // -- next tile's scores on the matrix core while this tile's softmax
+        // runs (same basic block, so the two interleave).  After the last tile
+        // the buffer holds stale keys and the result is discarded.
+        f32x16 s_next[2];
+        scores((tile + 1) & 1, s_next);
+        // -- p = exp2(s*c - m*c), rounded to the element type --
+        i16x8 pop[2][2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+                uint32_t w4[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 8 * st + 2 * e;
+                    w4[e] = M::pack_out(fast_exp2(fmaf(s_cur[kb][r], c, neg_mc)),
+                                        fast_exp2(fmaf(s_cur[kb][r + 1], c, neg_mc)));
+                    l_sum = M::sum2(w4[e], l_sum);
+                }
+                pop[kb][st] = __builtin_bit_cast(i16x8, (uint4){w4[0], w4[1], w4[2], w4[3]});
+            }
+        }
+        // -- O^T += V^T P^T (V^T by transpose read) --
+        // A wave whose rows cannot see this tile has all p = 0 here (every score
+        // was hidden), so the products add exact zeros.
+        const int gi = lane & 15;
+        const int dsub = 16 * ((lane >> 4) & 1) + 4 * (gi & 3);
+        const int vb = tile & 1;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+                const int row = kb * 32 + 16 * st + 4 * hh + (gi >> 2);
+                const uint16_t* v0 = &v_sh[vb][row * VS + dsub];
+                const uint16_t* v1 = v0 + 8 * VS;
+#pragma unroll
+                for (int d = 0; d < ND; ++d) {
+                    const i16x4 lo = tr_read(v0 + 32 * d);
+                    const i16x4 hi = tr_read(v1 + 32 * d);
+                    const i16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                    acc[d] = M::mfma(a, pop[kb][st], acc[d]);
+                }
+            }
+        }
+        if (more_k) stash_k(tile & 1);
+        if (more_v) stash_v((tile + 1) & 1);
         __syncthreads();
+        s_cur[0] = s_next[0];
+        s_cur[1] = s_next[1];
     }
 
     // ---- epilogue: O = acc / l (or the masked-row policy), LSE = m + log l --
-    const float l_tot = lacc[0];
+    const float l_tot = l_sum + __shfl_xor(l_sum, 32, 64);
     if (qrow < p.Lq) {
         const bool empty = (l_tot == 0.f);
         const float inv = 1.f / l_tot;
