@@ -1,12 +1,15 @@
 // prefill_mfma.hip -- fused attention for bf16 / fp16 inputs with fp32
 // accumulation on the gfx950 matrix cores (head_dim 64 or 128).
 //
-// Work decomposition.  A workgroup of 4 waves owns one (batch, query head,
-// block of 128 query rows); each wave owns 32 rows.  The keys are visited in
-// increasing order, 64 per tile, staged through LDS (double buffered, one
-// barrier per tile) with coalesced 16-byte raw-buffer loads whose range ends
-// at the batch entry's key length, so rows past it read as zeros and are
-// never fetched.  (OneGPU "Attention", introduction and "Variants and
+// Work decomposition.  A workgroup of 8 waves owns one (batch, kv head) and
+// 256 query rows that read it: gw query heads of the group (gw = 8, 4, 2 or 1,
+// the largest that divides Hq/Hkv) times 256/gw consecutive positions.  Each
+// wave owns 32 rows of one head.  One K/V tile load thus serves every query
+// head of the group that shares it (llm.istanbul "05_attention", "GQA").  The
+// keys are visited in increasing order, 64 per tile, staged through LDS
+// (double buffered, one barrier per tile) with coalesced 16-byte raw-buffer
+// loads whose range ends at the batch entry's key length, so rows past it
+// read as zeros and are never fetched.  (OneGPU "Attention", introduction and "Variants and
 // ordering": a workgroup keeps a block of query rows and walks key/value tiles
 // held in workgroup memory.)
 //
@@ -49,9 +52,10 @@ namespace {
 
 using namespace mfma;
 
-constexpr int kBM = 128;       // query rows per workgroup
+constexpr int kRows = 256;     // query rows (all heads) per workgroup
 constexpr int kBN = 64;        // keys per tile
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
 constexpr float kSlack = 8.f;  // lazy-rescale threshold, base-2 units
 
 // LDS row strides (elements).  K rows are read 16 lanes x 16 bytes at a time
@@ -62,12 +66,12 @@ template <int D> struct Tile {
     static constexpr int KS = D + 8;
     static constexpr int VS = D + 32;
     static constexpr int kRowChunks = D / 8;                  // 16-byte chunks per row
-    static constexpr int kLoads = kBN * kRowChunks / (64 * kWaves);   // per thread
+    static constexpr int kLoads = kBN * kRowChunks / kThreads;        // per thread
 };
 
 template <bool kBf16, int D, bool kMask>
-__global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(Params p, int n_qblk,
-                                                              int xcd_units, int mask_vec4) {
+__global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(Params p, int n_qblk, int gw,
+                                                                   int xcd_units, int mask_vec4) {
     using M = Mma<kBf16>;
     using TL = Tile<D>;
     constexpr int KS = TL::KS, VS = TL::VS;
@@ -76,47 +80,52 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(Params p, int n_qb
     __shared__ __attribute__((aligned(16))) uint16_t k_sh[2][kBN * KS];
     __shared__ __attribute__((aligned(16))) uint16_t v_sh[2][kBN * VS];
 
-    // ---- which (b, h, query block) this workgroup owns -------------------
+    // ---- which (b, kv head, head slice, query block) this workgroup owns --
     // Heaviest causal blocks first.  When the (batch, kv-head) units split
     // evenly over the 8 XCDs (consecutive workgroups go to consecutive XCDs),
-    // each XCD keeps whole units so the query heads sharing K/V share its L2.
-    int b, h, qb;
+    // each XCD keeps whole units so the workgroups sharing K/V share its L2.
+    const int n_slice = p.group / gw;           // head slices per kv head
+    int b, g, slice, qb;
     {
         const int L = blockIdx.x;
         if (xcd_units > 0) {
             const int xcd = L & 7, slot = L >> 3;
-            const int per = xcd_units * p.group;
+            const int per = xcd_units * n_slice;
             qb = n_qblk - 1 - slot / per;
             const int rem = slot % per;
-            const int unit = xcd * xcd_units + rem / p.group;
+            const int unit = xcd * xcd_units + rem / n_slice;
             b = unit / p.Hkv;
-            h = (unit % p.Hkv) * p.group + rem % p.group;
+            g = unit % p.Hkv;
+            slice = rem % n_slice;
         } else {
-            const int bh = p.B * p.Hq;
-            qb = n_qblk - 1 - L / bh;
-            const int rem = L % bh;
-            b = rem / p.Hq;
-            h = rem % p.Hq;
+            const int per = p.B * p.Hkv * n_slice;
+            qb = n_qblk - 1 - L / per;
+            const int rem = L % per;
+            b = rem / (p.Hkv * n_slice);
+            g = (rem / n_slice) % p.Hkv;
+            slice = rem % n_slice;
         }
     }
-    const int g = h / p.group;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = tid >> 6;
     const int hh = lane >> 5;          // which half of the wave
     const int col = lane & 31;         // query column owned by this lane
+    const int rows_per_head = kRows / gw;
+    const int waves_per_head = rows_per_head / 32;
+    const int h = g * p.group + slice * gw + w / waves_per_head;
 
     int64_t kv_len = p.Lk;
     if (p.lens) {
         const int64_t L = p.lens[b];
         kv_len = L < 0 ? 0 : (L > p.Lk ? p.Lk : L);
     }
-    const int64_t q0 = static_cast<int64_t>(qb) * kBM;
-    const int64_t qw0 = q0 + 32 * w;
+    const int64_t q0 = static_cast<int64_t>(qb) * rows_per_head;
+    const int64_t qw0 = q0 + 32 * (w % waves_per_head);
     // Keys the block needs: [0, blk_hi); keys this wave can see: [0, wave_hi).
     int64_t blk_hi = kv_len, wave_hi = kv_len;
     if (p.causal) {
-        const int64_t last = (q0 + kBM < p.Lq ? q0 + kBM : p.Lq) - 1;
+        const int64_t last = (q0 + rows_per_head < p.Lq ? q0 + rows_per_head : p.Lq) - 1;
         const int64_t bb = last + p.delta + 1;
         blk_hi = bb < 0 ? 0 : (bb < blk_hi ? bb : blk_hi);
         const int64_t wl = (qw0 + 32 < p.Lq ? qw0 + 32 : p.Lq) - 1;
@@ -150,7 +159,7 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(Params p, int n_qb
     // LDS holds K(t+1) and V(t) and the registers carry K(t+2) and V(t+1).
     const int st_row = tid / TL::kRowChunks;                 // + n * kRowsPerPass
     const int st_col = (tid % TL::kRowChunks) * 8;
-    constexpr int kRowsPerPass = 256 / TL::kRowChunks;
+    constexpr int kRowsPerPass = kThreads / TL::kRowChunks;
     i16x8 kst[TL::kLoads], vst[TL::kLoads];
     auto fetch_k = [&](int tile) {
 #pragma unroll
@@ -360,21 +369,34 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(Params p, int n_qb
     }
 }
 
+// Query heads per workgroup: the largest of 8, 4, 2, 1 that divides the group.
+int heads_per_block(int group) {
+    for (int gw = 8; gw > 1; gw >>= 1)
+        if (group % gw == 0) return gw;
+    return 1;
+}
+
+int64_t block_count(const Params& p) {
+    const int gw = heads_per_block(p.group);
+    const int64_t n_qblk = (p.Lq + kRows / gw - 1) / (kRows / gw);
+    return n_qblk * p.B * p.Hkv * (p.group / gw);
+}
+
 template <bool kBf16, int D>
 hipError_t launch_one(const Params& p, hipStream_t s) {
-    const int n_qblk = (p.Lq + kBM - 1) / kBM;
+    const int gw = heads_per_block(p.group);
+    const int n_qblk = (p.Lq + kRows / gw - 1) / (kRows / gw);
     const int units = p.B * p.Hkv;
     const int xcd_units = (units % 8 == 0) ? units / 8 : 0;
     const int mask_vec4 = p.mask && (reinterpret_cast<uintptr_t>(p.mask) % 16 == 0) &&
                           p.ms.sb % 4 == 0 && p.ms.sh % 4 == 0 && p.ms.sr % 4 == 0;
-    const int64_t blocks = static_cast<int64_t>(n_qblk) * p.B * p.Hq;
-    const dim3 grid(static_cast<uint32_t>(blocks));
+    const dim3 grid(static_cast<uint32_t>(block_count(p)));
     if (p.mask)
-        hipLaunchKernelGGL((prefill_mfma_kernel<kBf16, D, true>), grid, dim3(256), 0, s, p, n_qblk,
-                           xcd_units, mask_vec4);
+        hipLaunchKernelGGL((prefill_mfma_kernel<kBf16, D, true>), grid, dim3(kThreads), 0, s, p,
+                           n_qblk, gw, xcd_units, mask_vec4);
     else
-        hipLaunchKernelGGL((prefill_mfma_kernel<kBf16, D, false>), grid, dim3(256), 0, s, p,
-                           n_qblk, xcd_units, mask_vec4);
+        hipLaunchKernelGGL((prefill_mfma_kernel<kBf16, D, false>), grid, dim3(kThreads), 0, s, p,
+                           n_qblk, gw, xcd_units, mask_vec4);
     return hipGetLastError();
 }
 
@@ -396,8 +418,7 @@ bool prefill_mfma_supported(const Params& p, DType dt) {
     if ((static_cast<int64_t>(p.Lk) + kBN) * p.ks.sr * 2 >= (int64_t(1) << 31) ||
         (static_cast<int64_t>(p.Lk) + kBN) * p.vs.sr * 2 >= (int64_t(1) << 31))
         return false;
-    const int64_t blocks = static_cast<int64_t>((p.Lq + kBM - 1) / kBM) * p.B * p.Hq;
-    return blocks < (int64_t(1) << 31);
+    return block_count(p) < (int64_t(1) << 31);
 }
 
 hipError_t launch_prefill_mfma(const Params& p, DType dt, hipStream_t s) {
