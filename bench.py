@@ -7,7 +7,8 @@ rule).  The fp16 decode workload (B=64, Hq=32, Hkv=8, cache 8192, per-batch
 lengths uniform in [1, 8192]) is timed the same way after it and reported
 under "decode" as KV-read GB/s.  Inputs are synthetic (seeded N(0,1)) and
 resident in HBM before timing starts.  Kernel durations come from HIP events
-recorded around each call on the stream the kernels run on.
+recorded around each call on the stream the kernels run on, after about a
+second of untimed work that brings the GPU clock up (then the W warmup steps).
 
 Prints one JSON line.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -58,9 +59,22 @@ def read_traffic(summary: str, src_hash: str):
         return None
 
 
+def settle(fn, seconds: float = 1.0):
+    """Run fn until the GPU has been busy for `seconds`: the MI355X clock ramps
+    up over the first few hundred milliseconds of load, and kernels timed on a
+    cold part read up to ~20% slow.  Not timed."""
+    import torch
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+
+
 def time_calls(fn, steps: int, warmup: int):
     """Per-call HIP event durations (ms) on the current stream, plus wall time."""
     import torch
+    settle(fn)
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
