@@ -137,6 +137,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 256 MiB device copy (reference for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the hot path here is a single-GPU kernel and no "
@@ -148,6 +150,16 @@ def main():
     from scaled_dot_product_flash_amd import synth
 
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        # A copy of known size: its FETCH_SIZE / WRITE_SIZE readings scale the
+        # counters taken on the attention kernels.
+        src = torch.ones(1 << 27, dtype=torch.float16, device="cuda")   # 256 MiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": 1 << 28, "dispatches": 3}))
+        return
     spec = synth.CAUSAL_GQA_BF16
     case = synth.generate(spec)
     q, k, v = (to_dev(x, spec.dtype) for x in (case.q, case.k, case.v))

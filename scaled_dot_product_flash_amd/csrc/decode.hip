@@ -317,12 +317,17 @@ hipError_t launch_one(const Params& p, hipStream_t s) {
 
 }  // namespace
 
-// Key range length (keys per wave): a multiple of the 32-key step, at least
-// 256 keys, and long enough that no (batch, head) has more than 256 ranges.
-// SDPA_FLASH_DECODE_SPLIT=<keys> overrides it (tuning only).
+// Key range length (keys per wave): about a tenth of the cache capacity, a
+// multiple of the 32-key step, between 256 and 4096 keys, so a long cache
+// is cut into ~10 ranges per (batch, kv head) and a short one into few.
+// (Measured on fp16 B=64 Hkv=8 D=128 with an 8192-key cache: 768-896 keys
+// per range beat 256-640 and 1024-2048.)  SDPA_FLASH_DECODE_SPLIT=<keys>
+// overrides it (tuning only).
 void decode_split_plan(int Lk, int* split_len, int* n_split) {
-    int len = (Lk + 255) / 256;
+    int len = Lk / 10;
+    len = len / 128 * 128;
     if (len < 256) len = 256;
+    if (len > 4096) len = 4096;
     if (const char* e = std::getenv("SDPA_FLASH_DECODE_SPLIT")) {
         const int v = std::atoi(e);
         if (v >= kStep) len = v;
