@@ -154,6 +154,15 @@ size_t decode_ws(const attn_problem* p) {
                     : 0;
 }
 
+// Workspace of the fp32 prefill path (key-range split); shape only.
+size_t forward_ws(const attn_problem* p) {
+    const bool shape_ok = p->dtype == ATTN_DTYPE_F32 &&
+                          (p->head_dim == 32 || p->head_dim == 64 || p->head_dim == 128);
+    return shape_ok ? sdpa::prefill_f32_workspace_bytes(p->batch, p->q_heads, p->q_len, p->k_len,
+                                                        p->head_dim)
+                    : 0;
+}
+
 attn_status attn_workspace_size(const attn_problem* p, int32_t op, size_t* bytes) {
     if (!bytes) return fail(ATTN_ERR_INVALID, "bytes is NULL");
     *bytes = 0;
@@ -161,15 +170,13 @@ attn_status attn_workspace_size(const attn_problem* p, int32_t op, size_t* bytes
     if (st != ATTN_OK) return st;
     if (op != ATTN_OP_FORWARD && op != ATTN_OP_DECODE)
         return fail(ATTN_ERR_INVALID, "unknown op %d", op);
-    if (op == ATTN_OP_DECODE) *bytes = decode_ws(p);
+    *bytes = (op == ATTN_OP_DECODE) ? decode_ws(p) : forward_ws(p);
     return ATTN_OK;
 }
 
 attn_status attn_forward(const attn_problem* p, const void* q, const void* k, const void* v,
                          void* o, const float* mask, const int32_t* key_lens, float* lse,
                          void* workspace, size_t workspace_bytes, void* stream) {
-    (void)workspace;
-    (void)workspace_bytes;
     attn_status st = validate(p, true, q, k, v, o, mask, lse);
     if (st != ATTN_OK) return st;
     if (p->batch == 0 || p->q_len == 0) {
@@ -177,12 +184,24 @@ attn_status attn_forward(const attn_problem* p, const void* q, const void* k, co
         g_kernel = "";
         return ATTN_OK;
     }
-    const sdpa::Params prm = make_params(p, q, k, v, o, mask, key_lens, lse);
+    sdpa::Params prm = make_params(p, q, k, v, o, mask, key_lens, lse);
     const auto dt = static_cast<sdpa::DType>(p->dtype);
     const hipStream_t s = static_cast<hipStream_t>(stream);
     if (!force_generic() && sdpa::prefill_mfma_supported(prm, dt)) {
         g_kernel = "prefill_mfma";
         return launched(sdpa::launch_prefill_mfma(prm, dt, s));
+    }
+    sdpa::prefill_f32_plan(p->batch, p->q_heads, p->q_len, p->k_len, &prm.split_len, &prm.n_split);
+    if (!force_generic() && sdpa::prefill_f32_supported(prm, dt)) {
+        if (prm.n_split > 1) {
+            const size_t need = forward_ws(p);
+            if (!workspace || workspace_bytes < need)
+                return fail(ATTN_ERR_WORKSPACE, "forward needs %zu workspace bytes, got %zu", need,
+                            workspace ? workspace_bytes : size_t(0));
+            prm.ws = workspace;
+        }
+        g_kernel = "prefill_f32";
+        return launched(sdpa::launch_prefill_f32(prm, dt, s));
     }
     g_kernel = "generic";
     return launched(sdpa::launch_generic(prm, dt, s));

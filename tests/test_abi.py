@@ -154,3 +154,17 @@ def test_decode_workspace_is_checked_before_launch():
                          need - 4, None)
     assert rc == sdpa.ERR_WORKSPACE
     assert b"workspace" in lib.attn_last_error()
+
+
+def test_fp32_forward_split_needs_workspace():
+    """The fp32 causal GQA shape (few row blocks) is cut into key ranges and
+    needs a workspace; without it the call fails before launching."""
+    lib = sdpa.load_library()
+    p = _problem(batch=2, q_heads=12, kv_heads=4, q_len=512, k_len=512, head_dim=64,
+                 dtype=sdpa.DTYPE_F32, causal=1)
+    for lay, H, L in (("q", 12, 512), ("k", 4, 512), ("v", 4, 512), ("o", 12, 512)):
+        setattr(p, lay, sdpa.Layout(0, L * H * 64, 64, H * 64))
+    need = sdpa.workspace_size(p, sdpa.OP_FORWARD)
+    assert need > 0
+    rc = lib.attn_forward(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, None, None, None, 0, None)
+    assert rc == sdpa.ERR_WORKSPACE

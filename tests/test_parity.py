@@ -289,3 +289,37 @@ def test_decode_with_mask_and_garbage_beyond_length():
         assert (rl[3] == -np.inf).all()
         pu.compare(o, ro, lse, rl, "f16", policy, what="decode mask %s" % policy)
     del torch
+
+
+F32 = [
+    # B, Hq, Hkv, Lq, Lk, D, causal, offset, lens, mask
+    (1, 2, 2, 64, 64, 32, False, None, False, False),
+    (2, 12, 4, 512, 512, 64, True, 0, False, False),
+    (1, 4, 1, 100, 700, 128, True, None, True, True),
+    (3, 2, 2, 17, 1000, 64, False, None, True, True),
+    (1, 1, 1, 1, 1, 32, True, None, False, False),
+]
+
+
+@pytest.mark.parametrize("cfg", F32, ids=lambda c: "x".join(map(str, c[:6])))
+def test_fp32_vector_path(cfg, monkeypatch):
+    """fp32 runs on the vector-FMA kernel (with the key-range split when the row
+    blocks are few) and matches the oracle and the any-shape kernel."""
+    import scaled_dot_product_flash_amd as sdpa
+    B, Hq, Hkv, Lq, Lk, D, causal, offset, lens, mask = cfg
+    spec = synth.Spec("f32", B, Hq, Hkv, Lq, Lk, D, "f32", seed=Lq + Lk + D, causal=causal,
+                      causal_offset=offset, lse=True, lens="uniform" if lens else None)
+    case = synth.generate(spec)
+    if mask:
+        rng = np.random.default_rng(3)
+        m = rng.standard_normal((B, 1, Lq, Lk)).astype(np.float32)
+        m[rng.random(m.shape) < 0.2] = -np.inf
+        case = synth.Case(spec, case.q, case.k, case.v, case.key_lens, m)
+    for policy in ("nan", "zero"):
+        o1, l1, (_, _, tens) = pu.run_hip(case, policy)
+        assert sdpa.last_kernel() == "prefill_f32"
+        ro, rl = pu.run_oracle(case, policy)
+        pu.compare(o1, ro, l1, rl, "f32", policy, what="f32 %s" % (cfg,))
+    monkeypatch.setenv("SDPA_FLASH_KERNEL", "generic")
+    o2, l2, _ = pu.run_hip(case, "zero", tensors=tens)
+    pu.compare(o1, o2, l1, l2, "f32", "zero", what="f32 vs generic")
