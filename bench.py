@@ -71,10 +71,10 @@ def settle(fn, seconds: float = 1.0):
         torch.cuda.synchronize()
 
 
-def time_calls(fn, steps: int, warmup: int):
+def time_calls(fn, steps: int, warmup: int, settle_s: float = 1.0):
     """Per-call HIP event durations (ms) on the current stream, plus wall time."""
     import torch
-    settle(fn)
+    settle(fn, settle_s)
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -130,6 +130,33 @@ def cpu_baseline_prefill(case, target_s: float = 12.0):
                       "three-pass oracle, %.1f s)" % (n2, dt2)}
 
 
+def other_workloads(sdpa, synth, steps: int, warmup: int):
+    """The three smaller workloads, timed like the headline (report only)."""
+    import torch
+    out = []
+    for name in ("tiny_f32", "causal_gqa_f32", "cross_mask_f16"):
+        spec = synth.WORKLOADS[name]
+        case = synth.generate(spec)
+        q, k, v = (to_dev(x, spec.dtype) for x in (case.q, case.k, case.v))
+        mask = None if case.mask is None else torch.from_numpy(case.mask).cuda()
+        lens = None if case.key_lens is None else torch.from_numpy(case.key_lens).cuda()
+        o = torch.empty_like(q)
+        for policy in (("nan", "zero") if spec.mask else ("nan",)):
+            def f():
+                sdpa.forward(q, k, v, layout=spec.q_layout, kv_layout=spec.kv_layout,
+                             causal=spec.causal, causal_offset=spec.causal_offset, mask=mask,
+                             key_lens=lens, masked_rows=policy, return_lse=spec.lse, out=o)
+            f()
+            kern = sdpa.last_kernel()
+            durs, _ = time_calls(f, steps, warmup, settle_s=0.3)
+            ms = float(np.mean(durs))
+            out.append({"workload": spec.name, "masked_rows": policy, "kernel": kern,
+                        "ms_per_call": round(ms, 5),
+                        "tflops": round(spec.flops / (ms * 1e-3) / 1e12, 3),
+                        "dtype": spec.dtype})
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -137,6 +164,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-others", action="store_true",
+                    help="skip the tiny fp32, fp32 causal GQA and fp16 cross-attention lines")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device copy (reference for HBM counters)")
     args = ap.parse_args()
@@ -226,6 +255,9 @@ def main():
                          "traffic": None},
         }
         del dq, dk, dv, dout
+
+    if not args.no_others:
+        result["other_workloads"] = other_workloads(sdpa, synth, args.steps, args.warmup)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline_prefill(case)

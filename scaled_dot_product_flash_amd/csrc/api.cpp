@@ -150,7 +150,7 @@ size_t decode_ws(const attn_problem* p) {
     const bool shape_ok = (p->dtype == ATTN_DTYPE_BF16 || p->dtype == ATTN_DTYPE_F16) &&
                           (p->head_dim == 64 || p->head_dim == 128) && p->q_len == 1 &&
                           p->k_len > 0;
-    return shape_ok ? sdpa::decode_workspace_bytes(p->batch, p->q_heads, p->k_len, p->head_dim)
+    return shape_ok ? sdpa::decode_workspace_bytes(p->batch, p->q_heads, p->kv_heads, p->head_dim)
                     : 0;
 }
 
@@ -221,7 +221,6 @@ attn_status attn_decode(const attn_problem* p, const void* q, const void* k, con
     sdpa::Params prm = make_params(p, q, k, v, o, mask, key_lens, lse);
     const auto dt = static_cast<sdpa::DType>(p->dtype);
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    sdpa::decode_split_plan(p->k_len, &prm.split_len, &prm.n_split);
     if (!force_generic() && sdpa::decode_split_supported(prm, dt)) {
         const size_t need = decode_ws(p);
         if (!workspace || workspace_bytes < need)

@@ -31,7 +31,7 @@ struct Params {
     int32_t masked_zero;
     int64_t delta;         // causal offset (resolved)
     float scale_log2;      // scale * log2(e)
-    int32_t n_split;       // key ranges per (b, h) for split kernels
+    int32_t n_split;       // key ranges per (b, h) for the fp32 split kernel
     int32_t split_len;     // keys per range (multiple of the tile)
 };
 
@@ -42,8 +42,7 @@ hipError_t launch_generic(const Params& p, DType dt, hipStream_t s);
 
 bool prefill_mfma_supported(const Params& p, DType dt);
 bool decode_split_supported(const Params& p, DType dt);
-void decode_split_plan(int Lk, int* split_len, int* n_split);
-size_t decode_workspace_bytes(int B, int Hq, int Lk, int D);
+size_t decode_workspace_bytes(int B, int Hq, int Hkv, int D);
 hipError_t launch_decode_split(const Params& p, DType dt, hipStream_t s);
 
 void prefill_f32_plan(int B, int Hq, int Lq, int Lk, int* split_len, int* n_split);

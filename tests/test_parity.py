@@ -323,3 +323,17 @@ def test_fp32_vector_path(cfg, monkeypatch):
     monkeypatch.setenv("SDPA_FLASH_KERNEL", "generic")
     o2, l2, _ = pu.run_hip(case, "zero", tensors=tens)
     pu.compare(o1, o2, l1, l2, "f32", "zero", what="f32 vs generic")
+
+
+@pytest.mark.parametrize("lens", [[1, 0, 3, 2], [0, 0, 0, 0], [33, 0, 0, 64]])
+def test_decode_tiny_totals(lens):
+    """Fewer live steps than decode waves: most waves own nothing, and entries
+    with no live key are skipped by the cut."""
+    spec = synth.Spec("decode-tiny", 4, 8, 2, 1, 64, 64, "bf16", seed=8, kv_layout="bhsd",
+                      causal=True, decode=True, lens="uniform", lse=True)
+    case = synth.generate(spec)
+    case.key_lens[:] = lens
+    for policy in ("nan", "zero"):
+        o, lse, _ = pu.run_hip(case, policy)
+        ro, rl = pu.run_oracle(case, policy)
+        pu.compare(o, ro, lse, rl, "bf16", policy, what="decode tiny %s" % lens)
