@@ -104,6 +104,21 @@ __device__ __forceinline__ i16x8 load16(__amdgpu_buffer_rsrc_t r, int byte_off) 
     return __builtin_bit_cast(i16x8, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
 }
 
+// Combine a value with the one in lane l ^ 32 (the other half of the wave)
+// through v_permlane32_swap: with both operands x, the first result holds
+// x[l] in lanes 0..31 and x[l - 32] above, the second x[l + 32] below and
+// x[l] above.  Both lanes of a pair get bit-identical results.
+__device__ __forceinline__ float halves_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ i16x4 tr_read(const uint16_t* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (i16x4 __attribute__((address_space(3)))*)(

@@ -16,7 +16,7 @@
 // Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16: the
 // output column is the query, so lane l owns query l%32 and holds 16 of its
 // keys per 32-key block; lane l^32 holds the other 16.  A row's maximum is an
-// in-lane reduction plus one exchange with lane l^32 (OneGPU "Apple simdgroup
+// in-lane reduction plus one lane swap with lane l^32 (OneGPU "Apple simdgroup
 // kernel": scores transposed so one lane keeps one row).
 //
 // Online normaliser (OneGPU "Attention", introduction; llm.istanbul
@@ -278,7 +278,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(Params p, int
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s_cur[kb][r], s_cur[kb][r + 1]));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        mx = halves_max(mx);
         // -- lazy raise of the reference maximum --
         const bool raise = mx > m_ref + slack;
         if (__builtin_amdgcn_ballot_w64(raise)) {
@@ -345,7 +345,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(Params p, int
     }
 
     // ---- epilogue: O = acc / l (or the masked-row policy), LSE = m + log l --
-    const float l_tot = l_sum + __shfl_xor(l_sum, 32, 64);
+    const float l_tot = halves_sum(l_sum);
     if (qrow < p.Lq) {
         const bool empty = (l_tot == 0.f);
         const float inv = 1.f / l_tot;
