@@ -109,7 +109,7 @@ def _dims(a: np.ndarray, layout: str):
 
 
 def attention(q, k, v, *, dtype: str, layout: str = "bshd", kv_layout: str | None = None,
-              causal: bool = False, causal_offset: int | None = None,
+              causal: bool = False, causal_offset: int | str | None = None,
               scale: float | None = None, mask: np.ndarray | None = None,
               key_lens: np.ndarray | None = None, masked_rows: str = "nan",
               rows: np.ndarray | None = None, threads: int = 0):
@@ -120,6 +120,8 @@ def attention(q, k, v, *, dtype: str, layout: str = "bshd", kv_layout: str | Non
     [B, H, L, D]); ``kv_layout`` defaults to ``layout``.
     mask: float32, 4-D [B|1, Hq|1, Lq|1, Lk] (size-1 axes broadcast).
     key_lens: int32 [B] (real lengths, clamped to [0, Lk]).
+    causal_offset: None (Lk - Lq), an int, or "end": per batch entry the
+    clamped key length minus Lq (the last query row sees the last live key).
     rows: optional int64 [n, 3] of (b, h, i) to compute; default every row.
 
     Returns (O, LSE): O is [B, Hq, Lq, D] (or [n, D] with ``rows``) float64,
@@ -138,8 +140,14 @@ def attention(q, k, v, *, dtype: str, layout: str = "bshd", kv_layout: str | Non
     p.batch, p.q_heads, p.kv_heads, p.q_len, p.k_len, p.head_dim = B, Hq, Hkv, Lq, Lk, D
     p.dtype = DTYPES[dtype]
     p.causal = 1 if causal else 0
-    p.has_offset = 0 if causal_offset is None else 1
-    p.causal_offset = 0 if causal_offset is None else int(causal_offset)
+    if causal_offset is None:
+        p.has_offset, p.causal_offset = 0, 0
+    elif isinstance(causal_offset, str):
+        if causal_offset != "end":
+            raise ValueError("causal_offset must be an int, None or 'end'")
+        p.has_offset, p.causal_offset = 2, 0
+    else:
+        p.has_offset, p.causal_offset = 1, int(causal_offset)
     p.masked_zero = {"nan": 0, "zero": 1}[masked_rows]
     p.scale = 0.0 if scale is None else float(scale)
     p.qs[:] = _bhs_strides(q, layout)

@@ -22,8 +22,14 @@
  * LSE = m + log(l) (llm.istanbul, "Online Softmax Algoritmasi", final step).
  *
  * Readings taken where the pages are silent (listed again in the design doc):
- *   - key lengths are clamped to [0, KLen]; the causal offset is relative to
- *     the problem's KLen, not the per-batch length;
+ *   - key lengths are clamped to [0, KLen]; the default causal offset is
+ *     relative to the problem's KLen, not the per-batch length;
+ *   - the end-aligned offset (mode 2) is, per batch entry, the clamped key
+ *     length minus QLen: the last query row lines up with the entry's last
+ *     live key, as for a chunk of new tokens appended to a cache whose live
+ *     length differs per entry (ONNX GroupQueryAttention README,
+ *     "Implementation variants": causal tiles bounded by each entry's live
+ *     length, right-aligned; "Inputs": per-sample total sequence lengths);
  *   - a row with a NaN or +inf score is NaN under both policies, LSE NaN;
  *     this check comes before the empty-row check;
  *   - an empty row (no visible key, or every visible score -inf) has LSE -inf
@@ -53,9 +59,10 @@ typedef struct oracle_problem {
     int64_t batch, q_heads, kv_heads, q_len, k_len, head_dim;
     int32_t dtype;          /* ORACLE_F32 / ORACLE_F16 / ORACLE_BF16            */
     int32_t causal;         /* 0 or 1                                           */
-    int32_t has_offset;     /* 0: causal offset = k_len - q_len                 */
+    int32_t has_offset;     /* 0: offset k_len - q_len; 1: causal_offset;
+                               2: per batch entry, clamped key length - q_len   */
     int32_t masked_zero;    /* 0: empty rows are NaN, 1: empty rows are zero    */
-    int64_t causal_offset;  /* used when has_offset                             */
+    int64_t causal_offset;  /* used when has_offset == 1                        */
     double scale;           /* 0: 1/sqrt(head_dim)                              */
     int64_t qs[3], ks[3], vs[3]; /* batch, head, row strides                     */
     int64_t ms[3];          /* mask batch, head, row strides (0 = broadcast)    */
@@ -105,13 +112,15 @@ static void one_row(const oracle_problem* p, const void* q, const void* k, const
     const int64_t group = p->q_heads / p->kv_heads;
     const int64_t g = h / group;
     const double scale = p->scale != 0.0 ? p->scale : 1.0 / sqrt((double)D);
-    const int64_t delta = p->has_offset ? p->causal_offset : p->k_len - p->q_len;
 
     int64_t kv_len = p->k_len;
     if (key_lens) {
         int64_t L = key_lens[b];
         kv_len = L < 0 ? 0 : (L > p->k_len ? p->k_len : L);
     }
+    const int64_t delta = p->has_offset == 1   ? p->causal_offset
+                          : p->has_offset == 2 ? kv_len - p->q_len
+                                               : p->k_len - p->q_len;
 
     const int64_t qbase = b * p->qs[0] + h * p->qs[1] + i * p->qs[2];
 

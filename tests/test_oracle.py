@@ -58,11 +58,11 @@ def _library_attention(q, k, v, dtype, layout="bshd", causal=False, offset=None,
     B, Hq, Lq, D = Q.shape
     Hkv, Lk = K.shape[1], K.shape[2]
     sc = 1.0 / math.sqrt(D) if scale is None else scale
-    off = (Lk - Lq) if offset is None else offset
     O = np.zeros((B, Hq, Lq, D))
     LSE = np.zeros((B, Hq, Lq))
     for b in range(B):
         kl = Lk if key_lens is None else min(max(int(key_lens[b]), 0), Lk)
+        off = (Lk - Lq) if offset is None else (kl - Lq if offset == "end" else offset)
         for h in range(Hq):
             g = h * Hkv // Hq
             S = sc * (Q[b, h] @ K[b, g].T)
@@ -291,6 +291,62 @@ def test_negative_offset_empties_leading_rows():
     assert np.isnan(o2).all()
 
 
+def test_end_aligned_visible_counts_golden():
+    """Chunked rows against a cache: visible counts per (entry, row) from the
+    rule the GroupQueryAttention page states (tests/golden/end_aligned_l3.txt).
+    With Q = 0 every visible score is 0, so O is the mean of the visible V
+    rows and LSE = ln(count)."""
+    table = {(int(r[0]), int(r[1])): int(r[2]) for r in _golden("end_aligned_l3.txt")}
+    B, Lq, Lk, D = 2, 3, 5, 1
+    q = np.zeros((B, Lq, 1, D), np.float32)
+    k = _rand((B, Lk, 1, D), "f32", 5)
+    v = np.broadcast_to(np.arange(1, Lk + 1, dtype=np.float32)[None, :, None, None],
+                        (B, Lk, 1, D)).copy()
+    lens = np.array([5, 2], np.int32)
+    for policy in ("nan", "zero"):
+        o, lse = oracle.attention(q, k, v, dtype="f32", causal=True, causal_offset="end",
+                                  key_lens=lens, masked_rows=policy)
+        for (b, i), n in table.items():
+            if n == 0:
+                assert lse[b, 0, i] == -np.inf
+                assert (np.isnan(o[b, 0, i]).all() if policy == "nan"
+                        else (o[b, 0, i] == 0).all())
+            else:
+                assert o[b, 0, i, 0] == pytest.approx((n + 1) / 2, abs=1e-15)
+                assert lse[b, 0, i] == pytest.approx(math.log(n), abs=1e-15)
+
+
+def test_end_aligned_equals_sliced_cache():
+    """Each entry's end-aligned result is the default-offset result on its
+    cache cut to the live length (the rows then end at the cut)."""
+    B, Hq, Hkv, Lq, Lk, D = 4, 4, 2, 6, 20, 8
+    q = _rand((B, Lq, Hq, D), "f16", 11)
+    k = _rand((B, Lk, Hkv, D), "f16", 12)
+    v = _rand((B, Lk, Hkv, D), "f16", 13)
+    lens = np.array([20, 9, 6, 3], np.int32)
+    o, lse = oracle.attention(q, k, v, dtype="f16", causal=True, causal_offset="end",
+                              key_lens=lens)
+    for b in range(B):
+        L = int(lens[b])
+        o1, l1 = oracle.attention(q[b:b + 1], np.ascontiguousarray(k[b:b + 1, :L]),
+                                  np.ascontiguousarray(v[b:b + 1, :L]), dtype="f16",
+                                  causal=True)
+        same = ~np.isnan(o1[0])
+        assert (np.isnan(o[b]) == np.isnan(o1[0])).all()
+        assert (o[b][same] == o1[0][same]).all()
+        assert ((lse[b] == l1[0]) | (np.isnan(lse[b]) & np.isnan(l1[0]))).all()
+
+
+def test_end_aligned_without_lengths_is_the_default():
+    B, Hq, Lq, Lk, D = 2, 2, 7, 11, 4
+    q = _rand((B, Lq, Hq, D), "f32", 21)
+    k = _rand((B, Lk, Hq, D), "f32", 22)
+    v = _rand((B, Lk, Hq, D), "f32", 23)
+    o1, l1 = oracle.attention(q, k, v, dtype="f32", causal=True, causal_offset="end")
+    o2, l2 = oracle.attention(q, k, v, dtype="f32", causal=True)
+    assert (o1 == o2).all() and (l1 == l2).all()
+
+
 def test_key_length_zero_and_beyond_capacity():
     q, k, v = (_rand((3, 2, 1, 4), "f32", s) for s in (27, 28, 29))
     lens = np.array([0, 99, -5], np.int32)
@@ -412,6 +468,9 @@ BRUTE = [
     (1, 6, 2, 3, 127, 16, "f32", True, 100, False, True),
     (2, 1, 1, 129, 128, 8, "f16", True, -2, True, False),
     (1, 2, 1, 7, 129, 64, "bf16", False, None, False, True),
+    (2, 4, 2, 5, 40, 16, "f16", True, "end", False, True),
+    (3, 2, 1, 33, 65, 32, "bf16", True, "end", True, True),
+    (2, 1, 1, 8, 8, 8, "f32", True, "end", False, False),
 ]
 
 

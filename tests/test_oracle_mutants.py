@@ -34,7 +34,11 @@ MUTANTS = {
     "max_not_subtracted": ("l += exp(s[j] - m);", "l += exp(s[j]);"),
     "weights_not_normalised": ("exp(s[j] - m) / l;", "exp(s[j] - m);"),
     "q_row_stride_ignored": ("i * p->qs[2];", "0 * p->qs[2];"),
-    "explicit_offset_ignored": ("p->has_offset ? p->causal_offset :", "0 ? p->causal_offset :"),
+    "explicit_offset_ignored": ("p->has_offset == 1   ? p->causal_offset",
+                                "0 ? p->causal_offset"),
+    "end_offset_uses_capacity": ("p->has_offset == 2 ? kv_len - p->q_len",
+                                 "p->has_offset == 2 ? p->k_len - p->q_len"),
+    "end_offset_ignored": ("p->has_offset == 2 ? kv_len", "0 ? kv_len"),
     "key_lengths_ignored": ("kv_len = L < 0 ? 0 : (L > p->k_len ? p->k_len : L);",
                             "kv_len = p->k_len; (void)L;"),
 }
@@ -51,6 +55,8 @@ CHECKS = [
     pins.test_causal_visible_counts_golden,
     pins.test_default_offset_is_klen_minus_qlen,
     pins.test_negative_offset_empties_leading_rows,
+    pins.test_end_aligned_visible_counts_golden,
+    pins.test_end_aligned_equals_sliced_cache,
     pins.test_key_length_zero_and_beyond_capacity,
     pins.test_hidden_keys_are_never_read,
     pins.test_mask_hidden_keys_weigh_zero,
