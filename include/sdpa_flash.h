@@ -74,8 +74,18 @@ typedef enum attn_op {
     ATTN_OP_DECODE = 1
 } attn_op;
 
-/* Sentinel for attn_problem.causal_offset: use k_len - q_len. */
+/* Sentinel for attn_problem.causal_offset: use k_len - q_len (OneGPU
+ * "Attention", "What it covers": the default offset, the cached-decoder case). */
 #define ATTN_CAUSAL_OFFSET_DEFAULT INT64_MIN
+
+/* Sentinel for attn_problem.causal_offset: per batch entry, that entry's key
+ * length (key_lens[b] clamped to [0, k_len]) minus q_len, so the last query
+ * row lines up with the entry's last live key -- a chunk of q_len new rows
+ * appended to a cache whose live length differs per entry (ONNX
+ * GroupQueryAttention README, "Implementation variants": causal tiles bounded
+ * by each entry's live length, right-aligned).  Without key_lens it equals
+ * the default.                                                               */
+#define ATTN_CAUSAL_OFFSET_KEY_END (INT64_MIN + 1)
 
 /* Element (b, h, r, d) of a tensor lives at
  *   base + offset + b*batch_stride + h*head_stride + r*row_stride + d.
@@ -99,7 +109,7 @@ typedef struct attn_problem {
     int32_t head_dim;    /* 1..256                                               */
     int32_t dtype;       /* attn_dtype, shared by Q, K, V and O                  */
     int32_t causal;      /* 0 or 1: key j visible to row i iff j <= i + offset   */
-    int64_t causal_offset; /* ATTN_CAUSAL_OFFSET_DEFAULT or any value            */
+    int64_t causal_offset; /* a value, ATTN_CAUSAL_OFFSET_DEFAULT or _KEY_END     */
     float scale;         /* 0 selects 1/sqrt(head_dim)                           */
     int32_t masked_rows; /* attn_masked_rows                                     */
     attn_layout q, k, v, o;

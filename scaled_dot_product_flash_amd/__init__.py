@@ -32,6 +32,7 @@ DTYPE_F32, DTYPE_F16, DTYPE_BF16 = 0, 1, 2
 MASKED_NAN, MASKED_ZERO = 0, 1
 OP_FORWARD, OP_DECODE = 0, 1
 CAUSAL_OFFSET_DEFAULT = -(1 << 63)
+CAUSAL_OFFSET_KEY_END = -(1 << 63) + 1
 
 
 class AttnError(RuntimeError):
@@ -165,7 +166,14 @@ def _run(op: int, q, k, v, *, layout: str, kv_layout: str | None, causal: bool,
     p.batch, p.q_heads, p.kv_heads, p.q_len, p.k_len, p.head_dim = B, Hq, Hkv, Lq, Lk, D
     p.dtype = _dtype_code(q)
     p.causal = 1 if causal else 0
-    p.causal_offset = CAUSAL_OFFSET_DEFAULT if causal_offset is None else int(causal_offset)
+    if causal_offset is None:
+        p.causal_offset = CAUSAL_OFFSET_DEFAULT
+    elif isinstance(causal_offset, str):
+        if causal_offset != "end":
+            raise ValueError("causal_offset must be an int, None or 'end'")
+        p.causal_offset = CAUSAL_OFFSET_KEY_END
+    else:
+        p.causal_offset = int(causal_offset)
     p.scale = 0.0 if scale is None else float(scale)
     p.masked_rows = {"nan": MASKED_NAN, "zero": MASKED_ZERO}[masked_rows]
     p.q = _layout_of(q, layout)
@@ -208,12 +216,15 @@ def _run(op: int, q, k, v, *, layout: str, kv_layout: str | None, causal: bool,
 
 
 def forward(q, k, v, *, layout: str = "bshd", kv_layout: str | None = None,
-            causal: bool = False, causal_offset: int | None = None, scale: float | None = None,
-            mask=None, key_lens=None, masked_rows: str = "nan", return_lse: bool = False,
-            out=None, stream=None):
+            causal: bool = False, causal_offset: int | str | None = None,
+            scale: float | None = None, mask=None, key_lens=None, masked_rows: str = "nan",
+            return_lse: bool = False, out=None, stream=None):
     """Fused attention.  q: [B, Lq, Hq, D] ('bshd') or [B, Hq, Lq, D] ('bhsd');
     k, v likewise in ``kv_layout`` (default ``layout``).  Returns O in q's layout
-    (and the float32 LSE [B, Hq, Lq] with ``return_lse``)."""
+    (and the float32 LSE [B, Hq, Lq] with ``return_lse``).
+
+    causal_offset: None (Lk - Lq), an int, or "end": per batch entry its key
+    length minus Lq, for a chunk of Lq new rows at the end of a cache."""
     return _run(OP_FORWARD, q, k, v, layout=layout, kv_layout=kv_layout, causal=causal,
                 causal_offset=causal_offset, scale=scale, mask=mask, key_lens=key_lens,
                 masked_rows=masked_rows, return_lse=return_lse, out=out, stream=stream)

@@ -120,7 +120,8 @@ sdpa::Params make_params(const attn_problem* p, const void* q, const void* k, co
     r.group = p->q_heads / p->kv_heads;
     r.causal = p->causal;
     r.masked_zero = p->masked_rows == ATTN_MASKED_ROWS_ZERO;
-    r.delta = p->causal_offset == ATTN_CAUSAL_OFFSET_DEFAULT
+    r.delta_end = p->causal_offset == ATTN_CAUSAL_OFFSET_KEY_END;
+    r.delta = (p->causal_offset == ATTN_CAUSAL_OFFSET_DEFAULT || r.delta_end)
                   ? static_cast<int64_t>(p->k_len) - p->q_len
                   : p->causal_offset;
     const double scale = p->scale != 0.f ? static_cast<double>(p->scale)

@@ -29,7 +29,8 @@ struct Params {
     int32_t group;         // Hq / Hkv
     int32_t causal;
     int32_t masked_zero;
-    int64_t delta;         // causal offset (resolved)
+    int64_t delta;         // causal offset (resolved), unless delta_end
+    int32_t delta_end;     // 1: offset per batch entry = its clamped key length - Lq
     float scale_log2;      // scale * log2(e)
     int32_t n_split;       // key ranges per (b, h) for the fp32 split kernel
     int32_t split_len;     // keys per range (multiple of the tile)

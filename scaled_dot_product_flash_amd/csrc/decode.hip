@@ -66,7 +66,7 @@ __device__ __forceinline__ int64_t live_keys(const Params& p, int b) {
         kv = L < 0 ? 0 : (L > p.Lk ? p.Lk : L);
     }
     if (p.causal) {                  // the one query row is i = 0
-        const int64_t bb = p.delta + 1;
+        const int64_t bb = causal_delta(p, kv) + 1;
         kv = bb < 0 ? 0 : (bb < kv ? bb : kv);
     }
     return kv;

@@ -5,7 +5,14 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "attn_internal.h"
+
 namespace sdpa {
+
+// The causal offset of batch entry b, given its clamped key length.
+__device__ __forceinline__ int64_t causal_delta(const Params& p, int64_t kv_len) {
+    return p.delta_end ? kv_len - p.Lq : p.delta;
+}
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;

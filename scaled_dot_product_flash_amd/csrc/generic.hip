@@ -34,7 +34,7 @@ __global__ __launch_bounds__(256) void generic_kernel(Params p) {
     }
     int64_t hi = kv_len;
     if (p.causal) {
-        const int64_t bound = i + p.delta + 1;   // keys j <= i + delta
+        const int64_t bound = i + causal_delta(p, kv_len) + 1;   // keys j <= i + delta
         hi = bound < 0 ? 0 : (bound < hi ? bound : hi);
     }
 

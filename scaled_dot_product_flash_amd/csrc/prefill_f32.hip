@@ -70,14 +70,14 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(Params p, int n_rblk) {
     if (p.causal) {
         const int64_t last = (static_cast<int64_t>(rb + 1) * kRowsPerWave < p.Lq
                                   ? static_cast<int64_t>(rb + 1) * kRowsPerWave : p.Lq) - 1;
-        const int64_t bb = last + p.delta + 1;
+        const int64_t bb = last + causal_delta(p, kv_len) + 1;
         blk_hi = bb < 0 ? 0 : (bb < blk_hi ? bb : blk_hi);
     }
     const int64_t j_begin = kSplit ? static_cast<int64_t>(rng) * p.split_len : 0;
     int64_t j_end = blk_hi;
     if (kSplit && j_begin + p.split_len < j_end) j_end = j_begin + p.split_len;
     if (kSplit && j_begin >= blk_hi) return;   // no row of the block sees this range
-    const int64_t row_hi = p.causal ? i + p.delta + 1 : kv_len;   // key < row_hi visible
+    const int64_t row_hi = p.causal ? i + causal_delta(p, kv_len) + 1 : kv_len;   // key < row_hi visible
     const int n_tiles = j_end > j_begin ? static_cast<int>((j_end - j_begin + kTile - 1) / kTile) : 0;
 
     const float* qg = static_cast<const float*>(p.q);
@@ -242,7 +242,7 @@ __global__ __launch_bounds__(256) void prefill_f32_merge_kernel(Params p) {
     }
     int64_t hi = kv_len;
     if (p.causal) {
-        const int64_t bb = i + p.delta + 1;
+        const int64_t bb = i + causal_delta(p, kv_len) + 1;
         hi = bb < 0 ? 0 : (bb < hi ? bb : hi);
     }
     const int n_live = static_cast<int>((hi + p.split_len - 1) / p.split_len);

@@ -120,16 +120,17 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(Params p, int
         const int64_t L = p.lens[b];
         kv_len = L < 0 ? 0 : (L > p.Lk ? p.Lk : L);
     }
+    const int64_t delta = causal_delta(p, kv_len);
     const int64_t q0 = static_cast<int64_t>(qb) * rows_per_head;
     const int64_t qw0 = q0 + 32 * (w % waves_per_head);
     // Keys the block needs: [0, blk_hi); keys this wave can see: [0, wave_hi).
     int64_t blk_hi = kv_len, wave_hi = kv_len;
     if (p.causal) {
         const int64_t last = (q0 + rows_per_head < p.Lq ? q0 + rows_per_head : p.Lq) - 1;
-        const int64_t bb = last + p.delta + 1;
+        const int64_t bb = last + delta + 1;
         blk_hi = bb < 0 ? 0 : (bb < blk_hi ? bb : blk_hi);
         const int64_t wl = (qw0 + 32 < p.Lq ? qw0 + 32 : p.Lq) - 1;
-        const int64_t wb = wl + p.delta + 1;
+        const int64_t wb = wl + delta + 1;
         wave_hi = wb < 0 ? 0 : (wb < wave_hi ? wb : wave_hi);
     }
     if (qw0 >= p.Lq) wave_hi = 0;
@@ -260,9 +261,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(Params p, int
             }
         }
         // -- hide keys past the length / causal bound (edge tiles only) --
-        const bool partial = (j0 + kBN > kv_len) || (p.causal && j0 + kBN - 1 > qw0 + p.delta);
+        const bool partial = (j0 + kBN > kv_len) || (p.causal && j0 + kBN - 1 > qw0 + delta);
         if (partial) {
-            const int64_t qlim = p.causal ? qrow + p.delta : kv_len;
+            const int64_t qlim = p.causal ? qrow + delta : kv_len;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll

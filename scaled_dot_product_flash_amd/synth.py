@@ -13,7 +13,7 @@ from __future__ import annotations
 
 import dataclasses
 from dataclasses import dataclass
-from typing import Optional
+from typing import Optional, Union
 
 import numpy as np
 
@@ -40,10 +40,11 @@ class Spec:
     q_layout: str = "bshd"
     kv_layout: str = "bshd"
     causal: bool = False
-    causal_offset: Optional[int] = None
+    causal_offset: Optional[Union[int, str]] = None   # None, an int or 'end'
     lse: bool = False
     decode: bool = False
-    lens: Optional[str] = None        # None, 'uniform' (in [1, k_len]) or 'cross'
+    lens: Optional[str] = None        # None, 'uniform' (in [1, k_len]), 'cross' or
+                                      # 'chunk' (in [q_len, k_len]: the chunk fits)
     mask: Optional[str] = None        # None or 'keys' ([B,1,1,Lk], 10% -inf)
     masked_rows: str = "nan"
     lens_zero_at: int = 5             # 'cross' lengths: this batch entry has length 0
@@ -69,6 +70,11 @@ CAUSAL_GQA_BF16 = Spec("bf16 causal GQA prefill B4 H32/8 L4096 D128", 4, 32, 8, 
                        128, "bf16", seed=3, causal=True, causal_offset=0, lse=True)
 DECODE_F16 = Spec("fp16 decode B64 H32/8 cache8192 D128", 64, 32, 8, 1, 8192, 128, "f16",
                   seed=4, kv_layout="bhsd", causal=True, decode=True, lens="uniform")
+# A chunk of 128 new query rows per entry at the end of a cache whose live
+# length differs per entry (end-aligned causal rule).
+CHUNK_F16 = Spec("fp16 chunked prefill B16 H32/8 Lq128 cache8192 D128", 16, 32, 8, 128, 8192,
+                 128, "f16", seed=6, kv_layout="bhsd", causal=True, causal_offset="end",
+                 lse=True, lens="chunk")
 CROSS_MASK_F16 = Spec("fp16 cross-attention B8 H16 Lq1024 Lk2048 D64 mask+lens", 8, 16, 16,
                       1024, 2048, 64, "f16", seed=5, q_layout="bhsd", kv_layout="bhsd",
                       lens="cross", mask="keys")
@@ -79,6 +85,11 @@ WORKLOADS = {
     "causal_gqa_bf16": CAUSAL_GQA_BF16,
     "decode_f16": DECODE_F16,
     "cross_mask_f16": CROSS_MASK_F16,
+}
+
+# Workloads of the extensions beyond the five (measured and tested the same way).
+EXTRA_WORKLOADS = {
+    "chunk_f16": CHUNK_F16,
 }
 
 
@@ -149,6 +160,9 @@ def generate(spec: Spec) -> Case:
             lens[spec.lens_zero_at] = 0
         if spec.lens_full_at < spec.batch:
             lens[spec.lens_full_at] = spec.k_len
+    elif spec.lens == "chunk":
+        lens = rng.integers(min(spec.q_len, spec.k_len), spec.k_len + 1,
+                            size=spec.batch).astype(np.int32)
     elif spec.lens is not None:
         raise ValueError(spec.lens)
     mask = None

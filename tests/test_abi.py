@@ -168,3 +168,16 @@ def test_fp32_forward_split_needs_workspace():
     assert need > 0
     rc = lib.attn_forward(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, None, None, None, 0, None)
     assert rc == sdpa.ERR_WORKSPACE
+
+
+def test_offset_sentinels_match_c(tmp_path):
+    src = tmp_path / "sentinels.c"
+    src.write_text('#include <stdio.h>\n#include <inttypes.h>\n#include "sdpa_flash.h"\n'
+                   'int main(void){printf("%" PRId64 " %" PRId64 "\\n",'
+                   '(int64_t)ATTN_CAUSAL_OFFSET_DEFAULT,(int64_t)ATTN_CAUSAL_OFFSET_KEY_END);'
+                   'return 0;}\n')
+    exe = tmp_path / "sentinels"
+    subprocess.check_call(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), str(src),
+                           "-o", str(exe)])
+    d, e = map(int, subprocess.check_output([str(exe)]).split())
+    assert (d, e) == (sdpa.CAUSAL_OFFSET_DEFAULT, sdpa.CAUSAL_OFFSET_KEY_END)

@@ -24,6 +24,16 @@ REDUCED = {
                                                              head_dim=64, seed=11),
     "cross_bf16_D128_lens": synth.CROSS_MASK_F16.replace(dtype="bf16", head_dim=128, q_len=130,
                                                          k_len=257, seed=12),
+    # End-aligned chunks: lengths include 0, the capacity, and values below
+    # q_len (leading rows with no visible key).
+    "chunk_f16_70x300": synth.CHUNK_F16.replace(batch=8, q_heads=8, kv_heads=2, q_len=70,
+                                                k_len=300, lens="cross"),
+    "chunk_bf16_D64": synth.CHUNK_F16.replace(dtype="bf16", batch=4, q_heads=6, kv_heads=3,
+                                              q_len=100, k_len=257, head_dim=64, lens="cross",
+                                              lens_zero_at=1, lens_full_at=2, seed=13),
+    "chunk_f32": synth.CHUNK_F16.replace(dtype="f32", batch=3, q_heads=4, kv_heads=2, q_len=40,
+                                         k_len=130, head_dim=64, lens="cross", lens_zero_at=0,
+                                         lens_full_at=1, seed=14),
 }
 
 
@@ -59,6 +69,20 @@ def test_causal_gqa_bf16_full_size_sampled():
     go = o[rows[:, 0], rows[:, 1], rows[:, 2]]
     gl = lse[rows[:, 0], rows[:, 1], rows[:, 2]]
     pu.compare(go, ro, gl, rl, spec.dtype, "nan", what="bf16 causal GQA 4x32x4096x128")
+
+
+def test_chunk_f16_full_size_sampled():
+    """128 new rows per entry at the end of an 8192-key cache, lengths in
+    [128, 8192]: every row sees at least one key."""
+    spec = synth.EXTRA_WORKLOADS["chunk_f16"]
+    case = synth.generate(spec)
+    o, lse, _ = pu.run_hip(case, "nan")
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    rows = pu.sample_rows(spec, 96, seed=6)
+    ro, rl = pu.run_oracle(case, "nan", rows=rows)
+    go = o[rows[:, 0], rows[:, 1], rows[:, 2]]
+    gl = lse[rows[:, 0], rows[:, 1], rows[:, 2]]
+    pu.compare(go, ro, gl, rl, spec.dtype, "nan", what="fp16 chunk 16x32x128 cache 8192")
 
 
 def test_decode_f16_full_size_every_row():
