@@ -44,6 +44,9 @@ class _Problem(ctypes.Structure):
         ("ks", ctypes.c_int64 * 3),
         ("vs", ctypes.c_int64 * 3),
         ("ms", ctypes.c_int64 * 3),
+        ("window", ctypes.c_int32),
+        ("sink", ctypes.c_int32),
+        ("softcap", ctypes.c_double),
     ]
 
 
@@ -67,8 +70,8 @@ def _load():
         lib.oracle_attention.restype = ctypes.c_int
         lib.oracle_attention.argtypes = [
             ctypes.POINTER(_Problem), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
-            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
-            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
         lib.oracle_decode_f16.restype = ctypes.c_double
         lib.oracle_decode_f16.argtypes = [ctypes.c_uint16]
         lib.oracle_decode_bf16.restype = ctypes.c_double
@@ -112,6 +115,8 @@ def attention(q, k, v, *, dtype: str, layout: str = "bshd", kv_layout: str | Non
               causal: bool = False, causal_offset: int | str | None = None,
               scale: float | None = None, mask: np.ndarray | None = None,
               key_lens: np.ndarray | None = None, masked_rows: str = "nan",
+              window: int = -1, softcap: float = 0.0, sink: bool = False,
+              head_sink: np.ndarray | None = None,
               rows: np.ndarray | None = None, threads: int = 0):
     """Reference attention in float64.
 
@@ -122,6 +127,10 @@ def attention(q, k, v, *, dtype: str, layout: str = "bshd", kv_layout: str | Non
     key_lens: int32 [B] (real lengths, clamped to [0, Lk]).
     causal_offset: None (Lk - Lq), an int, or "end": per batch entry the
     clamped key length minus Lq (the last query row sees the last live key).
+    window: -1, or W >= 0 keys left of each causal row's position.
+    softcap: 0, or c > 0 (score -> c*tanh(score/c) before the mask).
+    sink: add exp(head_sink[h]) (0 without head_sink) to each denominator;
+    head_sink: float32 [Hq] or None.
     rows: optional int64 [n, 3] of (b, h, i) to compute; default every row.
 
     Returns (O, LSE): O is [B, Hq, Lq, D] (or [n, D] with ``rows``) float64,
@@ -150,6 +159,9 @@ def attention(q, k, v, *, dtype: str, layout: str = "bshd", kv_layout: str | Non
         p.has_offset, p.causal_offset = 1, int(causal_offset)
     p.masked_zero = {"nan": 0, "zero": 1}[masked_rows]
     p.scale = 0.0 if scale is None else float(scale)
+    p.window = int(window)
+    p.softcap = float(softcap)
+    p.sink = 1 if sink else 0
     p.qs[:] = _bhs_strides(q, layout)
     p.ks[:] = _bhs_strides(k, kv_layout)
     p.vs[:] = _bhs_strides(v, kv_layout)
@@ -174,6 +186,13 @@ def attention(q, k, v, *, dtype: str, layout: str = "bshd", kv_layout: str | Non
             raise ValueError("key_lens must be int32 [B]")
         keep.append(key_lens)
         lens_ptr = key_lens.ctypes.data
+    sink_ptr = None
+    if head_sink is not None:
+        head_sink = np.ascontiguousarray(head_sink, dtype=np.float32)
+        if head_sink.shape != (Hq,):
+            raise ValueError("head_sink must be float32 [Hq]")
+        keep.append(head_sink)
+        sink_ptr = head_sink.ctypes.data
     if rows is None:
         n = B * Hq * Lq
         rows_ptr = None
@@ -188,7 +207,7 @@ def attention(q, k, v, *, dtype: str, layout: str = "bshd", kv_layout: str | Non
     o = np.empty((n, D), dtype=np.float64)
     lse = np.empty((n,), dtype=np.float64)
     rc = _load().oracle_attention(ctypes.byref(p), q.ctypes.data, k.ctypes.data, v.ctypes.data,
-                                  mask_ptr, lens_ptr, rows_ptr, n, o.ctypes.data,
+                                  mask_ptr, lens_ptr, sink_ptr, rows_ptr, n, o.ctypes.data,
                                   lse.ctypes.data, int(threads))
     if rc != 0:
         raise RuntimeError("oracle rejected the problem")

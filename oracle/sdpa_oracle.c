@@ -37,6 +37,19 @@
  *   - the mask is added after scaling; keys hidden by length or by the causal
  *     rule are never evaluated (so garbage there cannot leak in).
  *
+ * Score-rule variants (ONNX GroupQueryAttention README, "Attributes" and
+ * "Inputs"; readings, listed again in the design doc):
+ *   - local window W >= 0 (causal only): the row at position p = i + offset
+ *     also needs j >= p - W, i.e. W keys to its left and itself ("left window
+ *     size for causal local attention"); -1 disables it;
+ *   - softcap c > 0: the scaled score becomes c * tanh(score / c), before the
+ *     additive mask is added (so a -inf mask entry still hides its key);
+ *   - sink: one more term exp(sink_h) in each row's softmax denominator, a
+ *     key of score sink_h with no value ("per-head smooth factor added to the
+ *     softmax denominator"; smooth softmax without per-head values uses 0).
+ *     A row then always has weight somewhere: with no visible key O = 0 and
+ *     LSE = sink_h under both policies; a NaN / +inf score still gives NaN.
+ *
  * Inputs are read in their storage type and decoded exactly to double
  * (float32 widened; float16 and bfloat16 bit patterns decoded from their IEEE
  * definitions), as the OneGPU "Tolerances" section describes its reference
@@ -66,6 +79,9 @@ typedef struct oracle_problem {
     double scale;           /* 0: 1/sqrt(head_dim)                              */
     int64_t qs[3], ks[3], vs[3]; /* batch, head, row strides                     */
     int64_t ms[3];          /* mask batch, head, row strides (0 = broadcast)    */
+    int32_t window;         /* -1: none; W >= 0: causal rows need j >= i+delta-W */
+    int32_t sink;           /* 0: none; 1: exp(sink_h) joins the denominator     */
+    double softcap;         /* 0: none; c > 0: score -> c * tanh(score / c)      */
 } oracle_problem;
 
 /* float16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. */
@@ -104,7 +120,7 @@ static double load_elem(const void* base, int32_t dtype, int64_t idx)
 
 /* One query row (b, h, i).  s is scratch of k_len doubles. */
 static void one_row(const oracle_problem* p, const void* q, const void* k, const void* v,
-                    const float* mask, const int32_t* key_lens,
+                    const float* mask, const int32_t* key_lens, const float* head_sink,
                     int64_t b, int64_t h, int64_t i, double* s, unsigned char* vis,
                     double* o_row, double* lse_out)
 {
@@ -126,7 +142,8 @@ static void one_row(const oracle_problem* p, const void* q, const void* k, const
 
     /* Scores of the visible keys. */
     for (int64_t j = 0; j < p->k_len; ++j) {
-        vis[j] = (j < kv_len) && (!p->causal || j <= i + delta);
+        vis[j] = (j < kv_len) &&
+                 (!p->causal || (j <= i + delta && (p->window < 0 || j >= i + delta - p->window)));
         if (!vis[j])
             continue;
         const int64_t kbase = b * p->ks[0] + g * p->ks[1] + j * p->ks[2];
@@ -134,6 +151,8 @@ static void one_row(const oracle_problem* p, const void* q, const void* k, const
         for (int64_t d = 0; d < D; ++d)
             dot += load_elem(q, p->dtype, qbase + d) * load_elem(k, p->dtype, kbase + d);
         double sj = scale * dot;
+        if (p->softcap > 0.0)
+            sj = p->softcap * tanh(sj / p->softcap);
         if (mask)
             sj += (double)mask[b * p->ms[0] + h * p->ms[1] + i * p->ms[2] + j];
         s[j] = sj;
@@ -156,6 +175,10 @@ static void one_row(const oracle_problem* p, const void* q, const void* k, const
         *lse_out = NAN;
         return;
     }
+    /* The sink is one more softmax term with no value vector. */
+    const double sink = p->sink ? (head_sink ? (double)head_sink[h] : 0.0) : -INFINITY;
+    if (sink > m)
+        m = sink;
     if (m == -INFINITY) {
         /* No visible key with a finite score: the masked-row policy. */
         for (int64_t d = 0; d < D; ++d)
@@ -165,7 +188,7 @@ static void one_row(const oracle_problem* p, const void* q, const void* k, const
     }
 
     /* Pass 2: normaliser. */
-    double l = 0.0;
+    double l = p->sink ? exp(sink - m) : 0.0;
     for (int64_t j = 0; j < p->k_len; ++j)
         if (vis[j])
             l += exp(s[j] - m);
@@ -191,7 +214,7 @@ static void one_row(const oracle_problem* p, const void* q, const void* k, const
  * Returns 0, or -1 on a malformed problem.
  */
 int oracle_attention(const oracle_problem* p, const void* q, const void* k, const void* v,
-                     const float* mask, const int32_t* key_lens,
+                     const float* mask, const int32_t* key_lens, const float* head_sink,
                      const int64_t* rows, int64_t n_rows, double* o, double* lse,
                      int n_threads)
 {
@@ -231,7 +254,8 @@ int oracle_attention(const oracle_problem* p, const void* q, const void* k, cons
                 i = r % p->q_len;
             }
             double lse_r;
-            one_row(p, q, k, v, mask, key_lens, b, h, i, s, vis, o + r * p->head_dim, &lse_r);
+            one_row(p, q, k, v, mask, key_lens, head_sink, b, h, i, s, vis, o + r * p->head_dim,
+                    &lse_r);
             if (lse)
                 lse[r] = lse_r;
         }

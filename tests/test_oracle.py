@@ -49,7 +49,8 @@ def _bhsd(a, layout):
 
 
 def _library_attention(q, k, v, dtype, layout="bshd", causal=False, offset=None, scale=None,
-                       mask=None, key_lens=None, masked_rows="nan"):
+                       mask=None, key_lens=None, masked_rows="nan", window=-1, softcap=0.0,
+                       head_sink=None):
     """Independent float64 route: matmul + scipy softmax over an explicit
     visibility matrix.  Returns O [B,Hq,Lq,D] and LSE [B,Hq,Lq]."""
     Q = _bhsd(_as_f64(q, dtype), layout)
@@ -66,14 +67,23 @@ def _library_attention(q, k, v, dtype, layout="bshd", causal=False, offset=None,
         for h in range(Hq):
             g = h * Hkv // Hq
             S = sc * (Q[b, h] @ K[b, g].T)
+            if softcap > 0:
+                S = softcap * np.tanh(S / softcap)
             if mask is not None:
                 S = S + np.broadcast_to(mask, (B, Hq, Lq, Lk))[b, h].astype(np.float64)
             vis = np.zeros((Lq, Lk), dtype=bool)
             vis[:, :kl] = True
             if causal:
-                vis &= np.arange(Lk)[None, :] <= np.arange(Lq)[:, None] + off
+                pos = np.arange(Lq)[:, None] + off
+                vis &= np.arange(Lk)[None, :] <= pos
+                if window >= 0:
+                    vis &= np.arange(Lk)[None, :] >= pos - window
             for i in range(Lq):
                 s = S[i][vis[i]]
+                vals = V[b, g][vis[i]]
+                if head_sink is not None:       # one more term, with a zero value row
+                    s = np.append(s, float(head_sink[h]))
+                    vals = np.vstack([vals, np.zeros((1, D))])
                 if np.isnan(s).any() or (s == np.inf).any():
                     O[b, h, i] = np.nan
                     LSE[b, h, i] = np.nan
@@ -82,7 +92,7 @@ def _library_attention(q, k, v, dtype, layout="bshd", causal=False, offset=None,
                     LSE[b, h, i] = -np.inf
                 else:
                     w = scipy.special.softmax(s)
-                    O[b, h, i] = w @ V[b, g][vis[i]]
+                    O[b, h, i] = w @ vals
                     LSE[b, h, i] = scipy.special.logsumexp(s)
     return O, LSE
 
@@ -501,6 +511,132 @@ def test_brute_force_against_library_route(cfg, policy):
     fl = np.isfinite(lse2)
     assert (lse[~fl & ~np.isnan(lse2)] == lse2[~fl & ~np.isnan(lse2)]).all()
     assert np.abs(lse[fl] - lse2[fl]).max(initial=0) < 1e-11
+
+
+# --------------------------------------------------------------------------
+# Score-rule variants (GroupQueryAttention README: local window, softcap,
+# head sink / smooth softmax).
+
+BRUTE_VARIANTS = [
+    # B, Hq, Hkv, Lq, Lk, D, dtype, offset, lens, window, softcap, sink
+    (1, 2, 1, 20, 20, 16, "f32", None, False, 3, 0.0, False),
+    (2, 4, 2, 33, 65, 32, "f16", "end", True, 10, 0.0, False),
+    (1, 2, 2, 17, 40, 8, "bf16", None, False, -1, 0.5, False),
+    (2, 2, 1, 9, 30, 16, "f32", 5, True, 0, 2.0, True),
+    (1, 3, 1, 12, 12, 4, "f16", None, False, -1, 0.0, True),
+    (2, 4, 1, 40, 70, 64, "bf16", "end", True, 25, 30.0, True),
+]
+
+
+@pytest.mark.parametrize("cfg", BRUTE_VARIANTS, ids=lambda c: "x".join(map(str, c)))
+@pytest.mark.parametrize("policy", ["nan", "zero"])
+def test_variants_against_library_route(cfg, policy):
+    B, Hq, Hkv, Lq, Lk, D, dtype, offset, use_lens, window, softcap, sink = cfg
+    seed = zlib.crc32(repr(cfg).encode()) % 1000
+    q = _rand((B, Lq, Hq, D), dtype, seed, scale=2.0)
+    k = _rand((B, Lk, Hkv, D), dtype, seed + 1, scale=2.0)
+    v = _rand((B, Lk, Hkv, D), dtype, seed + 2)
+    lens = None
+    if use_lens:
+        lens = np.random.default_rng(seed + 4).integers(0, Lk + 1, size=B).astype(np.int32)
+    hs = (np.random.default_rng(seed + 5).standard_normal(Hq).astype(np.float32) * 3
+          if sink else None)
+    o, lse = oracle.attention(q, k, v, dtype=dtype, causal=True, causal_offset=offset,
+                              key_lens=lens, masked_rows=policy, window=window,
+                              softcap=softcap, sink=sink, head_sink=hs)
+    o2, lse2 = _library_attention(q, k, v, dtype, causal=True, offset=offset, key_lens=lens,
+                                  masked_rows=policy, window=window, softcap=softcap,
+                                  head_sink=hs)
+    assert (np.isnan(o) == np.isnan(o2)).all()
+    fin = ~np.isnan(o)
+    assert np.abs(o[fin] - o2[fin]).max(initial=0) < 1e-12
+    with np.errstate(invalid="ignore"):
+        close = np.abs(lse - lse2) < 1e-11
+    assert ((lse == lse2) | close | (np.isnan(lse) & np.isnan(lse2))).all()
+
+
+def test_window_visible_counts_golden():
+    """tests/golden/window_l8_w2.txt: with Q = 0 each row is the mean of its
+    visible V rows; V[j] = j + 1 makes count and first key recoverable."""
+    table = [(int(r[0]), int(r[1]), int(r[2])) for r in _golden("window_l8_w2.txt")]
+    L, D = 8, 1
+    q = np.zeros((1, L, 1, D), np.float32)
+    k = _rand((1, L, 1, D), "f32", 3)
+    v = np.arange(1, L + 1, dtype=np.float32).reshape(1, L, 1, 1)
+    o, lse = oracle.attention(q, k, v, dtype="f32", causal=True, causal_offset=0, window=2)
+    for i, n, first in table:
+        assert lse[0, 0, i] == pytest.approx(math.log(n), abs=1e-15)
+        assert o[0, 0, i, 0] == pytest.approx(first + (n + 1) / 2, abs=1e-14)
+
+
+def test_window_wider_than_keys_is_plain_causal():
+    q = _rand((2, 9, 2, 8), "f16", 31)
+    k = _rand((2, 14, 2, 8), "f16", 32)
+    v = _rand((2, 14, 2, 8), "f16", 33)
+    a = oracle.attention(q, k, v, dtype="f16", causal=True, window=14)
+    b = oracle.attention(q, k, v, dtype="f16", causal=True)
+    assert (a[0] == b[0]).all() and (a[1] == b[1]).all()
+
+
+def test_sink_closed_form_uniform_scores():
+    """Q = 0: n visible keys of score 0 and a sink of score t share weight
+    1 / (n + e^t) each (the sink's share carries no value); LSE = ln(n + e^t)."""
+    Lq, Lk, D = 4, 6, 3
+    q = np.zeros((1, Lq, 2, D), np.float32)
+    k = _rand((1, Lk, 2, D), "f32", 41)
+    v = _rand((1, Lk, 2, D), "f32", 42)
+    hs = np.array([0.7, -1.5], np.float32)
+    o, lse = oracle.attention(q, k, v, dtype="f32", causal=True, causal_offset=0, sink=True,
+                              head_sink=hs)
+    for h in range(2):
+        t = float(hs[h])
+        for i in range(Lq):
+            n = i + 1
+            ref = v[0, :n, h].astype(np.float64).sum(axis=0) / (n + math.exp(t))
+            assert np.abs(o[0, h, i] - ref).max() < 1e-14
+            assert lse[0, h, i] == pytest.approx(math.log(n + math.exp(t)), abs=1e-14)
+
+
+def test_sink_row_without_keys_is_zero_under_both_policies():
+    """All weight goes to the sink: O = 0 exactly, LSE = the sink's score (0
+    for smooth softmax without per-head values)."""
+    q = _rand((1, 3, 1, 4), "f32", 51)
+    k = _rand((1, 5, 1, 4), "f32", 52)
+    v = _rand((1, 5, 1, 4), "f32", 53)
+    for hs, t in ((np.array([2.5], np.float32), 2.5), (None, 0.0)):
+        for policy in ("nan", "zero"):
+            o, lse = oracle.attention(q, k, v, dtype="f32", causal=True, causal_offset=-3,
+                                      sink=True, head_sink=hs, masked_rows=policy)
+            assert (o == 0).all() and (lse == t).all()
+
+
+def test_softcap_two_keys_logistic():
+    """Two keys with scaled scores s1, s2 and cap c: weights are logistic in
+    c*tanh(s1/c) - c*tanh(s2/c)."""
+    D = 1
+    q = np.array([[[[1.0]]]], np.float32)
+    k = np.array([[[[3.0]], [[-1.0]]]], np.float32)
+    v = np.array([[[[10.0]], [[-4.0]]]], np.float32)
+    c = 1.5
+    o, lse = oracle.attention(q, k, v, dtype="f32", softcap=c)
+    t1, t2 = c * math.tanh(3.0 / c), c * math.tanh(-1.0 / c)
+    lam = 1.0 / (1.0 + math.exp(t2 - t1))
+    assert o[0, 0, 0, 0] == pytest.approx(lam * 10.0 + (1 - lam) * -4.0, abs=1e-13)
+    assert lse[0, 0, 0] == pytest.approx(math.log(math.exp(t1) + math.exp(t2)), abs=1e-13)
+
+
+def test_softcap_comes_before_the_mask():
+    """A -inf mask entry still hides its key under a softcap, and a finite mask
+    entry shifts the capped score (it is not capped itself)."""
+    q = np.array([[[[1.0]]]], np.float32)
+    k = np.array([[[[2.0]], [[0.5]], [[1.0]]]], np.float32)
+    v = np.array([[[[1.0]], [[2.0]], [[3.0]]]], np.float32)
+    mask = np.array([0.0, 5.0, -np.inf], np.float32).reshape(1, 1, 1, 3)
+    c = 1.0
+    o, _ = oracle.attention(q, k, v, dtype="f32", softcap=c, mask=mask)
+    t = np.array([c * math.tanh(2.0 / c), c * math.tanh(0.5 / c) + 5.0])
+    w = np.exp(t - t.max()) / np.exp(t - t.max()).sum()
+    assert o[0, 0, 0, 0] == pytest.approx(w[0] * 1.0 + w[1] * 2.0, abs=1e-13)
 
 
 def test_rejects_bad_problems():

@@ -39,6 +39,17 @@ MUTANTS = {
     "end_offset_uses_capacity": ("p->has_offset == 2 ? kv_len - p->q_len",
                                  "p->has_offset == 2 ? p->k_len - p->q_len"),
     "end_offset_ignored": ("p->has_offset == 2 ? kv_len", "0 ? kv_len"),
+    "window_strict": ("j >= i + delta - p->window", "j > i + delta - p->window"),
+    "window_ignored": ("(p->window < 0 ||", "(1 ||"),
+    "softcap_ignored": ("            sj = p->softcap * tanh(sj / p->softcap);\n",
+                        "            sj = sj;\n"),
+    "softcap_after_mask": (
+        "        if (p->softcap > 0.0)\n            sj = p->softcap * tanh(sj / p->softcap);\n"
+        "        if (mask)\n            sj += (double)mask[b * p->ms[0] + h * p->ms[1] + i * p->ms[2] + j];\n",
+        "        if (mask)\n            sj += (double)mask[b * p->ms[0] + h * p->ms[1] + i * p->ms[2] + j];\n"
+        "        if (p->softcap > 0.0)\n            sj = p->softcap * tanh(sj / p->softcap);\n"),
+    "sink_not_in_denominator": ("double l = p->sink ? exp(sink - m) : 0.0;", "double l = 0.0;"),
+    "sink_ignores_head": ("(double)head_sink[h]", "(double)head_sink[0]"),
     "key_lengths_ignored": ("kv_len = L < 0 ? 0 : (L > p->k_len ? p->k_len : L);",
                             "kv_len = p->k_len; (void)L;"),
 }
@@ -57,12 +68,19 @@ CHECKS = [
     pins.test_negative_offset_empties_leading_rows,
     pins.test_end_aligned_visible_counts_golden,
     pins.test_end_aligned_equals_sliced_cache,
+    pins.test_window_visible_counts_golden,
+    pins.test_sink_closed_form_uniform_scores,
+    pins.test_sink_row_without_keys_is_zero_under_both_policies,
+    pins.test_softcap_two_keys_logistic,
+    pins.test_softcap_comes_before_the_mask,
     pins.test_key_length_zero_and_beyond_capacity,
     pins.test_hidden_keys_are_never_read,
     pins.test_mask_hidden_keys_weigh_zero,
     pins.test_layouts_and_broadcast_agree,
 ] + [(lambda r=r: pins.test_special_values_golden(r)) for r in pins._golden("special_values.txt")] \
-  + [(lambda c=c: pins.test_brute_force_against_library_route(c, "nan")) for c in pins.BRUTE]
+  + [(lambda c=c: pins.test_brute_force_against_library_route(c, "nan")) for c in pins.BRUTE] \
+  + [(lambda c=c: pins.test_variants_against_library_route(c, "nan"))
+     for c in pins.BRUTE_VARIANTS]
 
 
 def _any_check_fails():
