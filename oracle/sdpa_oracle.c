@@ -48,7 +48,8 @@
  *     key of score sink_h with no value ("per-head smooth factor added to the
  *     softmax denominator"; smooth softmax without per-head values uses 0).
  *     A row then always has weight somewhere: with no visible key O = 0 and
- *     LSE = sink_h under both policies; a NaN / +inf score still gives NaN.
+ *     LSE = sink_h under both policies; a NaN / +inf score, the sink's own
+ *     included, still gives NaN.
  *
  * Inputs are read in their storage type and decoded exactly to double
  * (float32 widened; float16 and bfloat16 bit patterns decoded from their IEEE
@@ -158,9 +159,12 @@ static void one_row(const oracle_problem* p, const void* q, const void* k, const
         s[j] = sj;
     }
 
+    /* The sink is one more softmax term with no value vector. */
+    const double sink = p->sink ? (head_sink ? (double)head_sink[h] : 0.0) : -INFINITY;
+
     /* Pass 1: maximum, and whether any score is NaN or +inf. */
     double m = -INFINITY;
-    int bad = 0;
+    int bad = isnan(sink) || sink == INFINITY;
     for (int64_t j = 0; j < p->k_len; ++j) {
         if (!vis[j])
             continue;
@@ -175,8 +179,6 @@ static void one_row(const oracle_problem* p, const void* q, const void* k, const
         *lse_out = NAN;
         return;
     }
-    /* The sink is one more softmax term with no value vector. */
-    const double sink = p->sink ? (head_sink ? (double)head_sink[h] : 0.0) : -INFINITY;
     if (sink > m)
         m = sink;
     if (m == -INFINITY) {

@@ -646,3 +646,20 @@ def test_rejects_bad_problems():
         oracle.attention(q, k, k, dtype="f32")           # 3 query heads over 2 kv heads
     with pytest.raises(ValueError):
         oracle.attention(q, q, q, dtype="f32", rows=np.array([[0, 3, 0]]))
+
+
+def test_nan_or_infinite_sink_makes_the_row_nan():
+    q = _rand((1, 2, 2, 4), "f32", 61)
+    k = _rand((1, 3, 1, 4), "f32", 62)
+    v = _rand((1, 3, 1, 4), "f32", 63)
+    hs = np.array([np.nan, np.inf], np.float32)
+    for off in (0, -5):                      # rows with and without visible keys
+        for policy in ("nan", "zero"):
+            o, lse = oracle.attention(q, k, v, dtype="f32", causal=True, causal_offset=off,
+                                      sink=True, head_sink=hs, masked_rows=policy)
+            assert np.isnan(o).all() and np.isnan(lse).all()
+    # A -inf sink is no term at all.
+    hs = np.array([-np.inf, -np.inf], np.float32)
+    a = oracle.attention(q, k, v, dtype="f32", causal=True, sink=True, head_sink=hs)
+    b = oracle.attention(q, k, v, dtype="f32", causal=True)
+    assert (a[0] == b[0]).all() and (a[1] == b[1]).all()
