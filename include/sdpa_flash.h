@@ -121,6 +121,23 @@ typedef struct attn_problem {
      * lse + offset + b*batch_stride + h*head_stride + i*row_stride.
      * Ignored when lse == NULL.                                               */
     attn_layout lse;
+    /* Score-rule variants (ONNX GroupQueryAttention README, "Attributes" and
+     * "Inputs").  A zero-filled tail selects none of them.                    */
+    /* Local window: 0 = none; W >= 1 (causal only) = a row sees at most the W
+     * keys ending at its own position i + offset, i.e. keys j with
+     * i + offset - W < j <= i + offset.  The README's local_window_size L
+     * (keys to the left of the position) is W = L + 1.                        */
+    int32_t window;
+    /* Softcap: 0 = none; c > 0 = the scaled score s becomes c * tanh(s / c)
+     * before the additive mask is added (a -inf mask entry still hides).      */
+    float softcap;
+    /* Sink: 0 = none; 1 = each row's softmax denominator gets one more term
+     * exp(sink_h), a key of score sink_h with no value: sink_h = head_sink[h]
+     * (device float32[q_heads]) or 0 when head_sink is NULL (smooth softmax).
+     * A row with no visible key then gives O = 0 and LSE = sink_h under both
+     * masked-row policies; a NaN or +inf sink_h gives a NaN row.              */
+    int32_t sink;
+    const float* head_sink;
 } attn_problem;
 
 /*

@@ -55,6 +55,8 @@ class Problem(ctypes.Structure):
         ("scale", ctypes.c_float), ("masked_rows", ctypes.c_int32),
         ("q", Layout), ("k", Layout), ("v", Layout), ("o", Layout),
         ("mask", Layout), ("lse", Layout),
+        ("window", ctypes.c_int32), ("softcap", ctypes.c_float),
+        ("sink", ctypes.c_int32), ("head_sink", ctypes.c_void_p),
     ]
 
 
@@ -151,6 +153,7 @@ def _ptr(t):
 
 def _run(op: int, q, k, v, *, layout: str, kv_layout: str | None, causal: bool,
          causal_offset, scale, mask, key_lens, masked_rows: str, return_lse: bool,
+         local_window: int = -1, softcap: float = 0.0, sink: bool = False, head_sink=None,
          out=None, stream=None):
     torch = _torch()
     kv_layout = kv_layout or layout
@@ -176,6 +179,18 @@ def _run(op: int, q, k, v, *, layout: str, kv_layout: str | None, causal: bool,
         p.causal_offset = int(causal_offset)
     p.scale = 0.0 if scale is None else float(scale)
     p.masked_rows = {"nan": MASKED_NAN, "zero": MASKED_ZERO}[masked_rows]
+    if local_window is None or local_window < 0:
+        p.window = 0
+    else:
+        p.window = int(local_window) + 1      # keys ending at the row's own position
+    p.softcap = float(softcap)
+    p.sink = 1 if sink else 0
+    if head_sink is not None:
+        if (head_sink.dtype != torch.float32 or not head_sink.is_cuda
+                or head_sink.shape != (Hq,)):
+            raise TypeError("head_sink must be a float32 GPU tensor of shape [Hq]")
+        head_sink = head_sink.contiguous()
+        p.head_sink = head_sink.data_ptr()
     p.q = _layout_of(q, layout)
     p.k = _layout_of(k, kv_layout)
     p.v = _layout_of(v, kv_layout)
@@ -218,23 +233,33 @@ def _run(op: int, q, k, v, *, layout: str, kv_layout: str | None, causal: bool,
 def forward(q, k, v, *, layout: str = "bshd", kv_layout: str | None = None,
             causal: bool = False, causal_offset: int | str | None = None,
             scale: float | None = None, mask=None, key_lens=None, masked_rows: str = "nan",
-            return_lse: bool = False, out=None, stream=None):
+            return_lse: bool = False, local_window: int = -1, softcap: float = 0.0,
+            sink: bool = False, head_sink=None, out=None, stream=None):
     """Fused attention.  q: [B, Lq, Hq, D] ('bshd') or [B, Hq, Lq, D] ('bhsd');
     k, v likewise in ``kv_layout`` (default ``layout``).  Returns O in q's layout
     (and the float32 LSE [B, Hq, Lq] with ``return_lse``).
 
     causal_offset: None (Lk - Lq), an int, or "end": per batch entry its key
-    length minus Lq, for a chunk of Lq new rows at the end of a cache."""
+    length minus Lq, for a chunk of Lq new rows at the end of a cache.
+    local_window: -1, or L >= 0 keys left of each causal row's position.
+    softcap: 0, or c > 0 (scaled score -> c*tanh(score/c) before the mask).
+    sink: add exp(head_sink[h]) (float32 GPU [Hq]; 0 when None) to each
+    row's softmax denominator."""
     return _run(OP_FORWARD, q, k, v, layout=layout, kv_layout=kv_layout, causal=causal,
                 causal_offset=causal_offset, scale=scale, mask=mask, key_lens=key_lens,
-                masked_rows=masked_rows, return_lse=return_lse, out=out, stream=stream)
+                masked_rows=masked_rows, return_lse=return_lse, local_window=local_window,
+                softcap=softcap, sink=sink, head_sink=head_sink, out=out, stream=stream)
 
 
 def decode(q, k_cache, v_cache, key_lens=None, *, layout: str = "bshd", kv_layout: str = "bhsd",
            scale: float | None = None, mask=None, masked_rows: str = "nan",
-           return_lse: bool = False, out=None, stream=None):
+           return_lse: bool = False, local_window: int = -1, softcap: float = 0.0,
+           sink: bool = False, head_sink=None, out=None, stream=None):
     """One query row per (batch, head) against a K/V cache of capacity Lk with
-    live lengths ``key_lens`` (int32 [B]); every live key is visible."""
+    live lengths ``key_lens`` (int32 [B]).  The row is the newest position of
+    its entry (end-aligned causal offset), so every live key is visible and a
+    local window counts back from the entry's last live key."""
     return _run(OP_DECODE, q, k_cache, v_cache, layout=layout, kv_layout=kv_layout,
-                causal=True, causal_offset=None, scale=scale, mask=mask, key_lens=key_lens,
-                masked_rows=masked_rows, return_lse=return_lse, out=out, stream=stream)
+                causal=True, causal_offset="end", scale=scale, mask=mask, key_lens=key_lens,
+                masked_rows=masked_rows, return_lse=return_lse, local_window=local_window,
+                softcap=softcap, sink=sink, head_sink=head_sink, out=out, stream=stream)

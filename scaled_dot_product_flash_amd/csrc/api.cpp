@@ -68,6 +68,14 @@ attn_status validate(const attn_problem* p, bool check_ptrs, const void* q, cons
         return fail(ATTN_ERR_INVALID, "unknown masked_rows policy %d", p->masked_rows);
     if (!(std::isfinite(p->scale)) || p->scale < 0.f)
         return fail(ATTN_ERR_INVALID, "scale must be finite and >= 0");
+    if (p->window < 0) return fail(ATTN_ERR_INVALID, "window must be >= 0");
+    if (p->window > 0 && !p->causal)
+        return fail(ATTN_ERR_INVALID, "a local window needs the causal rule");
+    if (!(std::isfinite(p->softcap)) || p->softcap < 0.f)
+        return fail(ATTN_ERR_INVALID, "softcap must be finite and >= 0");
+    if (p->sink != 0 && p->sink != 1) return fail(ATTN_ERR_INVALID, "sink must be 0 or 1");
+    if (p->head_sink && !p->sink)
+        return fail(ATTN_ERR_INVALID, "head_sink given without sink = 1");
     if (!nonneg(p->q) || !nonneg(p->k) || !nonneg(p->v) || !nonneg(p->o))
         return fail(ATTN_ERR_INVALID, "layout offsets and strides must be >= 0");
     if (!check_ptrs) {
@@ -127,6 +135,11 @@ sdpa::Params make_params(const attn_problem* p, const void* q, const void* k, co
     const double scale = p->scale != 0.f ? static_cast<double>(p->scale)
                                          : 1.0 / std::sqrt(static_cast<double>(p->head_dim));
     r.scale_log2 = static_cast<float>(scale * 1.4426950408889634);
+    r.scale = static_cast<float>(scale);
+    r.window = p->window;
+    r.softcap = p->softcap;
+    r.sink = p->sink;
+    r.head_sink = p->head_sink;
     return r;
 }
 

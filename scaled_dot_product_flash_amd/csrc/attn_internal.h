@@ -32,6 +32,11 @@ struct Params {
     int64_t delta;         // causal offset (resolved), unless delta_end
     int32_t delta_end;     // 1: offset per batch entry = its clamped key length - Lq
     float scale_log2;      // scale * log2(e)
+    float scale;           // scale (natural units)
+    int32_t window;        // 0, or W: keys i + delta - W < j <= i + delta (causal)
+    float softcap;         // 0, or c: s -> c * tanh(s / c) on scaled scores
+    int32_t sink;          // 1: a sink term joins each denominator
+    const float* head_sink;   // per query head sink scores (nullable: 0)
     int32_t n_split;       // key ranges per (b, h) for the fp32 split kernel
     int32_t split_len;     // keys per range (multiple of the tile)
 };

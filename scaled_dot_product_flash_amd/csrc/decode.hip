@@ -30,6 +30,11 @@
 // S^T = K Q^T and O^T += V^T P^T on 16x16x32 MFMAs with the query heads as the
 // columns.  Online normaliser with a lazily raised reference maximum; P is
 // rounded to the element type and the sum adds the rounded values.
+//
+// Score-rule variants (ONNX GroupQueryAttention README, "Attributes",
+// "Inputs"): a local window moves the start of the live range up (the range
+// is [lo, hi) and steps count from lo); the softcap maps raw scores before
+// the mask; the sink joins the denominator in the merge.
 #include "attn_internal.h"
 #include "device_common.h"
 #include "mfma_common.h"
@@ -59,21 +64,28 @@ template <int D> struct DLay {
 // Partial record of one (slot, head): [m, l, -, -, acc[0..D)], floats.
 __host__ __device__ constexpr int rec_stride(int D) { return D + 4; }
 
-__device__ __forceinline__ int64_t live_keys(const Params& p, int b) {
+// Live keys of batch entry b: [lo, lo + n).  The one query row is i = 0.
+struct LiveRange {
+    int64_t lo, n;
+};
+__device__ __forceinline__ LiveRange live_range(const Params& p, int b) {
     int64_t kv = p.Lk;
     if (p.lens) {
         const int64_t L = p.lens[b];
         kv = L < 0 ? 0 : (L > p.Lk ? p.Lk : L);
     }
-    if (p.causal) {                  // the one query row is i = 0
-        const int64_t bb = causal_delta(p, kv) + 1;
-        kv = bb < 0 ? 0 : (bb < kv ? bb : kv);
+    int64_t hi = kv, lo = 0;
+    if (p.causal) {
+        const int64_t delta = causal_delta(p, kv);
+        const int64_t bb = delta + 1;
+        hi = bb < 0 ? 0 : (bb < kv ? bb : kv);
+        lo = window_lo(p, 0, delta);
     }
-    return kv;
+    return {lo < hi ? lo : hi, lo < hi ? hi - lo : 0};
 }
 
 __device__ __forceinline__ int64_t steps_of(const Params& p, int b) {
-    return (live_keys(p, b) + kStep - 1) / kStep;
+    return (live_range(p, b).n + kStep - 1) / kStep;
 }
 
 // Steps before batch entry b (all kv heads and slices of entries < b), summed
@@ -97,7 +109,7 @@ __device__ __forceinline__ int owner_wave(int64_t x, int64_t S) {
     return static_cast<int>(((x + 1) * kWavesTotal - 1) / S);
 }
 
-template <bool kBf16, int D>
+template <bool kBf16, int D, bool kCap>
 __global__ __launch_bounds__(64) void decode_split_kernel(Params p, int n_hgrp, int slot_heads) {
     using M = Mma<kBf16>;
     using LY = DLay<D>;
@@ -133,11 +145,13 @@ __global__ __launch_bounds__(64) void decode_split_kernel(Params p, int n_hgrp, 
     const float c = p.scale_log2;
     const float slack = kSlack / c;
     const float inv_scale = kLog2e / c;
+    const float cap_k2 = kCap ? 2.f * kLog2e * p.scale / p.softcap : 0.f;
+    const float cap_back = kCap ? p.softcap / p.scale : 0.f;
 
-    // Per-unit state (wave-uniform: b, uu, kv length; per-lane: the head).
+    // Per-unit state (wave-uniform: b, uu, live range; per-lane: the head).
     int h = 0;
     bool live_col = false;
-    int64_t kv_hi = 0;
+    int64_t kv_lo = 0, kv_hi = 0;   // kv_hi: live keys counted from kv_lo
     i16x8 qop[NT];
     const float* mrow = nullptr;
     float m_ref = kNegInf, l_sum = 0.f;
@@ -148,14 +162,16 @@ __global__ __launch_bounds__(64) void decode_split_kernel(Params p, int n_hgrp, 
         const int hbase = (uu % n_hgrp) * 16;
         live_col = hbase + col < p.group;
         h = g * p.group + (live_col ? hbase + col : 0);
-        kv_hi = live_keys(p, b);
+        const LiveRange lr = live_range(p, b);
+        kv_lo = lr.lo;
+        kv_hi = lr.n;
         const uint16_t* src = static_cast<const uint16_t*>(p.q) + b * p.qs.sb + h * p.qs.sh + 8 * q4;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             const i16x8 v = *reinterpret_cast<const i16x8*>(src + 32 * t);
             qop[t] = live_col ? v : i16x8{};
         }
-        mrow = (p.mask && live_col) ? p.mask + b * p.ms.sb + h * p.ms.sh : nullptr;
+        mrow = (p.mask && live_col) ? p.mask + b * p.ms.sb + h * p.ms.sh + kv_lo : nullptr;
         m_ref = kNegInf;
         l_sum = 0.f;
 #pragma unroll
@@ -182,11 +198,13 @@ __global__ __launch_bounds__(64) void decode_split_kernel(Params p, int n_hgrp, 
     i16x8 kst[LY::kLoads], vst[LY::kLoads];
     auto fetch = [&](int fb, int fuu, int64_t fls) {
         const int fg = fuu / n_hgrp;
-        const int64_t kv = live_keys(p, fb);
-        const uint16_t* kg = static_cast<const uint16_t*>(p.k) + fb * p.ks.sb + fg * p.ks.sh;
-        const uint16_t* vg = static_cast<const uint16_t*>(p.v) + fb * p.vs.sb + fg * p.vs.sh;
-        const __amdgpu_buffer_rsrc_t krs = make_rsrc(kg, kv * p.ks.sr * 2);
-        const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vg, kv * p.vs.sr * 2);
+        const LiveRange lr = live_range(p, fb);
+        const uint16_t* kg =
+            static_cast<const uint16_t*>(p.k) + fb * p.ks.sb + fg * p.ks.sh + lr.lo * p.ks.sr;
+        const uint16_t* vg =
+            static_cast<const uint16_t*>(p.v) + fb * p.vs.sb + fg * p.vs.sh + lr.lo * p.vs.sr;
+        const __amdgpu_buffer_rsrc_t krs = make_rsrc(kg, lr.n * p.ks.sr * 2);
+        const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vg, lr.n * p.vs.sr * 2);
         const int j0 = static_cast<int>(fls) * kStep + ld_row;
 #pragma unroll
         for (int n = 0; n < LY::kLoads; ++n) {
@@ -231,6 +249,12 @@ __global__ __launch_bounds__(64) void decode_split_kernel(Params p, int n_hgrp, 
 #pragma unroll
             for (int t = 0; t < NT; ++t)
                 s[kb] = M::mfma16(*reinterpret_cast<const i16x8*>(krow + 32 * t), qop[t], s[kb]);
+        }
+        if (kCap) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) s[kb][r] = softcap_raw(s[kb][r], cap_k2, cap_back);
         }
         if (mrow) {
 #pragma unroll
@@ -343,8 +367,10 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(Params p, int n_hgr
             }
         }
     }
+    float m2 = M * p.scale_log2;                 // base-2 reference (-inf stays -inf)
+    const float fs = fold_sink(p, h, m2, L);
     const bool empty = (L == 0.f);
-    const float inv = 1.f / L;
+    const float inv = fs / L;
     const int64_t orow = b * p.os.sb + h * p.os.sh;
 #pragma unroll
     for (int cc = 0; cc < NPL; ++cc) {
@@ -356,7 +382,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(Params p, int n_hgr
     }
     if (p.lse && lane == 0)
         p.lse[b * p.ls.sb + h * p.ls.sh] =
-            empty ? kNegInf : (M * p.scale_log2 + fast_log2(L)) * kLn2;
+            empty ? kNegInf : (m2 + fast_log2(L)) * kLn2;
 }
 
 int slice_count(int group) { return (group + 15) / 16; }
@@ -365,8 +391,12 @@ int heads_per_slot(int group) { return group < 16 ? group : 16; }
 template <bool kBf16, int D>
 hipError_t launch_one(const Params& p, hipStream_t s) {
     const int n_hgrp = slice_count(p.group), hs = heads_per_slot(p.group);
-    hipLaunchKernelGGL((decode_split_kernel<kBf16, D>), dim3(kWavesTotal), dim3(64), 0, s, p,
-                       n_hgrp, hs);
+    if (p.softcap > 0.f)
+        hipLaunchKernelGGL((decode_split_kernel<kBf16, D, true>), dim3(kWavesTotal), dim3(64), 0, s,
+                           p, n_hgrp, hs);
+    else
+        hipLaunchKernelGGL((decode_split_kernel<kBf16, D, false>), dim3(kWavesTotal), dim3(64), 0,
+                           s, p, n_hgrp, hs);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t rows = static_cast<int64_t>(p.B) * p.Hq;

@@ -57,6 +57,40 @@ template <> struct Elem<bf16_t> {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
+// First key a causal row i may see under a local window of W keys (ONNX
+// GroupQueryAttention README, "Attributes"): j > i + delta - W; 0 without one.
+__device__ __forceinline__ int64_t window_lo(const Params& p, int64_t i, int64_t delta) {
+    if (!p.causal || p.window <= 0) return 0;
+    const int64_t lo = i + delta - p.window + 1;
+    return lo < 0 ? 0 : lo;
+}
+
+// Softcap on a raw score s = q.k (before scaling): the scaled score becomes
+// c * tanh(scale * s / c), i.e. in raw units back * tanh(s * k2 / 2) with
+// k2 = 2 * log2(e) * scale / c and back = c / scale, through
+// tanh(x) = 1 - 2 / (2^(2 x log2 e) + 1): exact +-1 at +-inf, NaN stays NaN.
+__device__ __forceinline__ float softcap_raw(float s, float k2, float back) {
+    const float e = __builtin_amdgcn_exp2f(s * k2);
+    return back * (1.f - 2.f * __builtin_amdgcn_rcpf(e + 1.f));
+}
+
+// Folds the sink term of query head h into a row's final state: m2 is the
+// base-2 reference of the accumulated terms (-inf when none) and l their sum.
+// Returns the factor for the accumulator; m2 and l become those of the full
+// denominator (GroupQueryAttention README, "Inputs": a per-head smooth factor
+// added to the softmax denominator).  A -inf sink is no term; a NaN or +inf
+// sink makes l NaN.
+__device__ __forceinline__ float fold_sink(const Params& p, int h, float& m2, float& l) {
+    if (!p.sink) return 1.f;
+    const float s2 = (p.head_sink ? p.head_sink[h] : 0.f) * kLog2e;
+    if (s2 == kNegInf) return 1.f;
+    const float M = fmaxf(m2, s2);
+    const float f = (m2 == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m2 - M);
+    l = l * f + __builtin_amdgcn_exp2f(s2 - M);
+    m2 = M;
+    return f;
+}
+
 // IEEE maxNum: a NaN operand is ignored (NaN reaches the output through exp2).
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll

@@ -33,10 +33,12 @@ __global__ __launch_bounds__(256) void generic_kernel(Params p) {
         kv_len = L < 0 ? 0 : (L > p.Lk ? p.Lk : L);
     }
     int64_t hi = kv_len;
+    const int64_t delta = causal_delta(p, kv_len);
     if (p.causal) {
-        const int64_t bound = i + causal_delta(p, kv_len) + 1;   // keys j <= i + delta
+        const int64_t bound = i + delta + 1;   // keys j <= i + delta
         hi = bound < 0 ? 0 : (bound < hi ? bound : hi);
     }
+    const int64_t lo = window_lo(p, i, delta);   // and j >= lo under a local window
 
     const int64_t qrow = b * p.qs.sb + h * p.qs.sh + i * p.qs.sr;
     for (int d = lane; d < D; d += 64) q_sh[w][d] = Elem<T>::load(p.q, qrow + d);
@@ -53,7 +55,7 @@ __global__ __launch_bounds__(256) void generic_kernel(Params p) {
 #pragma unroll
     for (int c = 0; c < kMaxD / 64; ++c) acc[c] = 0.f;
 
-    for (int64_t j0 = 0; j0 < hi; j0 += 64) {
+    for (int64_t j0 = lo; j0 < hi; j0 += 64) {
         const int64_t j = j0 + lane;
         float t = kNegInf;
         if (j < hi) {
@@ -61,7 +63,10 @@ __global__ __launch_bounds__(256) void generic_kernel(Params p) {
             float dot = 0.f;
             for (int d = 0; d < D; ++d) dot = fmaf(q_sh[w][d], Elem<T>::load(p.k, kr + d), dot);
             const float madd = mrow ? mrow[j] * kLog2e : 0.f;
-            t = fmaf(dot, p.scale_log2, madd);
+            if (p.softcap > 0.f)   // softcap on the scaled score, then the mask
+                t = fmaf(p.softcap * tanhf(dot * p.scale / p.softcap), kLog2e, madd);
+            else
+                t = fmaf(dot, p.scale_log2, madd);
         }
         const float m_new = fmaxf(m, wave_max(t));
         const float base = (m_new == kNegInf) ? 0.f : m_new;   // all hidden so far: exp2(-inf) = 0
@@ -85,8 +90,9 @@ __global__ __launch_bounds__(256) void generic_kernel(Params p) {
     }
 
     const int64_t orow = b * p.os.sb + h * p.os.sh + i * p.os.sr;
+    const float fs = fold_sink(p, h, m, l);
     const bool empty = (l == 0.f);
-    const float inv = 1.f / l;
+    const float inv = fs / l;
 #pragma unroll
     for (int c = 0; c < kMaxD / 64; ++c) {
         const int d = lane + 64 * c;

@@ -35,8 +35,12 @@
 // the V^T operand is read from the row-major V tile with ds_read_b64_tr_b16.
 //
 // Element-wise work that only some tiles need (the causal diagonal, the tile
-// holding the key length, the additive mask) is done only on those tiles;
-// the mask is a compile-time variant of the kernel.
+// holding the key length, the lower edge of a local window, the additive
+// mask) is done only on those tiles; the mask and the softcap are
+// compile-time variants of the kernel.  Score-rule variants follow the ONNX
+// GroupQueryAttention README ("Attributes", "Inputs"): a local window starts
+// the key loop at the block's first visible tile; the softcap maps each raw
+// score before the mask is added; the sink joins the denominator at the end.
 //
 // Special values (OneGPU "Special values"): hidden keys get -inf and weigh 0;
 // a row whose reference max is still -inf uses 0 as the exponent base, so
@@ -69,7 +73,7 @@ template <int D> struct Tile {
     static constexpr int kLoads = kBN * kRowChunks / kThreads;        // per thread
 };
 
-template <bool kBf16, int D, bool kMask>
+template <bool kBf16, int D, bool kMask, bool kCap>
 __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(Params p, int n_qblk, int gw,
                                                                    int xcd_units, int mask_vec4) {
     using M = Mma<kBf16>;
@@ -135,6 +139,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(Params p, int
     }
     if (qw0 >= p.Lq) wave_hi = 0;
     const int n_tiles = static_cast<int>((blk_hi + kBN - 1) / kBN);
+    // Under a local window the block's first row sees the lowest keys, and a
+    // tile below the wave's last row's window edge needs the element test.
+    const int t_first = static_cast<int>(window_lo(p, q0, delta) / kBN);
+    const int64_t wave_lo =
+        window_lo(p, (qw0 + 31 < p.Lq ? qw0 + 31 : p.Lq - 1), delta);
 
     const uint16_t* qg = static_cast<const uint16_t*>(p.q);
     const uint16_t* kg = static_cast<const uint16_t*>(p.k) + b * p.ks.sb + g * p.ks.sh;
@@ -214,24 +223,26 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(Params p, int
 #pragma unroll
     for (int d = 0; d < ND; ++d) acc[d] = f32x16{};
 
-    if (n_tiles > 0) {
-        fetch_k(0);
-        fetch_v(0);
-        if (n_tiles > 1) {
-            stash_k(0);
-            fetch_k(1);
-            stash_k(1);
-        } else {
-            stash_k(0);
+    // LDS buffers go by the parity of the absolute tile index.
+    if (t_first < n_tiles) {
+        fetch_k(t_first);
+        fetch_v(t_first);
+        stash_k(t_first & 1);
+        if (t_first + 1 < n_tiles) {
+            fetch_k(t_first + 1);
+            stash_k((t_first + 1) & 1);
         }
-        stash_v(0);
+        stash_v(t_first & 1);
     }
     __syncthreads();
 
     f32x16 s_cur[2];
-    if (n_tiles > 0) scores(0, s_cur);
+    if (t_first < n_tiles) scores(t_first & 1, s_cur);
+    const int64_t row_lo = window_lo(p, qrow, delta);
+    const float cap_k2 = kCap ? 2.f * kLog2e * p.scale / p.softcap : 0.f;
+    const float cap_back = kCap ? p.softcap / p.scale : 0.f;
 
-    for (int tile = 0; tile < n_tiles; ++tile) {
+    for (int tile = t_first; tile < n_tiles; ++tile) {
         const bool more_k = tile + 2 < n_tiles;
         const bool more_v = tile + 1 < n_tiles;
         if (more_k) fetch_k(tile + 2);
@@ -239,6 +250,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(Params p, int
         const int64_t j0 = static_cast<int64_t>(tile) * kBN;
         const bool sees = j0 < wave_hi;
 
+        // -- softcap on the raw scores, before the mask --
+        if (kCap) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) s_cur[kb][r] = softcap_raw(s_cur[kb][r], cap_k2, cap_back);
+        }
         // -- additive mask, folded into raw-score units --
         if (kMask && mrow && sees) {
 #pragma unroll
@@ -260,8 +278,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(Params p, int
                 }
             }
         }
-        // -- hide keys past the length / causal bound (edge tiles only) --
-        const bool partial = (j0 + kBN > kv_len) || (p.causal && j0 + kBN - 1 > qw0 + delta);
+        // -- hide keys past the length / causal bound / below the window
+        // (edge tiles only) --
+        const bool partial = (j0 + kBN > kv_len) || (p.causal && j0 + kBN - 1 > qw0 + delta) ||
+                             (j0 < wave_lo);
         if (partial) {
             const int64_t qlim = p.causal ? qrow + delta : kv_len;
 #pragma unroll
@@ -269,7 +289,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(Params p, int
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int64_t key = j0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-                    if (key >= kv_len || key > qlim) s_cur[kb][r] = kNegInf;
+                    if (key >= kv_len || key > qlim || key < row_lo) s_cur[kb][r] = kNegInf;
                 }
         }
 
@@ -346,10 +366,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(Params p, int
     }
 
     // ---- epilogue: O = acc / l (or the masked-row policy), LSE = m + log l --
-    const float l_tot = halves_sum(l_sum);
+    float l_tot = halves_sum(l_sum);
+    float m2 = m_ref * c;                       // base-2 reference (-inf stays -inf)
+    const float fs = fold_sink(p, h, m2, l_tot);
     if (qrow < p.Lq) {
         const bool empty = (l_tot == 0.f);
-        const float inv = 1.f / l_tot;
+        const float inv = fs / l_tot;
         const float fill = p.masked_zero ? 0.f : __builtin_nanf("");
         uint16_t* og = static_cast<uint16_t*>(p.o) + b * p.os.sb + h * p.os.sh + qrow * p.os.sr;
 #pragma unroll
@@ -364,7 +386,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(Params p, int
             }
         }
         if (p.lse && hh == 0) {
-            const float lse = empty ? kNegInf : (m_ref * c + fast_log2(l_tot)) * kLn2;
+            const float lse = empty ? kNegInf : (m2 + fast_log2(l_tot)) * kLn2;
             p.lse[b * p.ls.sb + h * p.ls.sh + qrow * p.ls.sr] = lse;
         }
     }
@@ -392,12 +414,19 @@ hipError_t launch_one(const Params& p, hipStream_t s) {
     const int mask_vec4 = p.mask && (reinterpret_cast<uintptr_t>(p.mask) % 16 == 0) &&
                           p.ms.sb % 4 == 0 && p.ms.sh % 4 == 0 && p.ms.sr % 4 == 0;
     const dim3 grid(static_cast<uint32_t>(block_count(p)));
-    if (p.mask)
-        hipLaunchKernelGGL((prefill_mfma_kernel<kBf16, D, true>), grid, dim3(kThreads), 0, s, p,
-                           n_qblk, gw, xcd_units, mask_vec4);
+    const bool cap = p.softcap > 0.f;
+    if (p.mask && cap)
+        hipLaunchKernelGGL((prefill_mfma_kernel<kBf16, D, true, true>), grid, dim3(kThreads), 0, s,
+                           p, n_qblk, gw, xcd_units, mask_vec4);
+    else if (p.mask)
+        hipLaunchKernelGGL((prefill_mfma_kernel<kBf16, D, true, false>), grid, dim3(kThreads), 0,
+                           s, p, n_qblk, gw, xcd_units, mask_vec4);
+    else if (cap)
+        hipLaunchKernelGGL((prefill_mfma_kernel<kBf16, D, false, true>), grid, dim3(kThreads), 0,
+                           s, p, n_qblk, gw, xcd_units, mask_vec4);
     else
-        hipLaunchKernelGGL((prefill_mfma_kernel<kBf16, D, false>), grid, dim3(kThreads), 0, s, p,
-                           n_qblk, gw, xcd_units, mask_vec4);
+        hipLaunchKernelGGL((prefill_mfma_kernel<kBf16, D, false, false>), grid, dim3(kThreads), 0,
+                           s, p, n_qblk, gw, xcd_units, mask_vec4);
     return hipGetLastError();
 }
 

@@ -5,9 +5,10 @@ HIP path (through the tests and the benchmark) and the float64 oracle are fed
 from it, so the two sides see identical bits.
 
 Recipe (the same for every workload): numpy PCG64 ``default_rng(seed)``;
-draw order Q, K, V, then key lengths, then the mask; values are i.i.d. N(0, 1)
-in float32, rounded to nearest-even into the storage type (float16 via numpy,
-bfloat16 by bit rounding, kept as uint16 bit patterns).
+draw order Q, K, V, then key lengths, then the mask, then per-head sink
+scores; values are i.i.d. N(0, 1) in float32 (sink scores 2 * N(0, 1)),
+rounded to nearest-even into the storage type (float16 via numpy, bfloat16
+by bit rounding, kept as uint16 bit patterns).
 """
 from __future__ import annotations
 
@@ -51,6 +52,9 @@ class Spec:
     lens_full_at: int = 7             # ... and this one has the full k_len
     mask_all_at: int = 2              # 'keys' mask: this batch entry is fully -inf
     mask_p: float = 0.1
+    local_window: int = -1            # -1, or keys left of each causal row's position
+    softcap: float = 0.0              # 0, or c > 0
+    sink: Optional[str] = None        # None, 'zero' (smooth softmax) or 'heads' (drawn)
 
     def replace(self, **kw) -> "Spec":
         return dataclasses.replace(self, **kw)
@@ -87,9 +91,24 @@ WORKLOADS = {
     "cross_mask_f16": CROSS_MASK_F16,
 }
 
+# Score-rule variants on the prefill and decode shapes: a 1024-key causal
+# local window; softcap 30 with per-head sinks.
+WINDOW_BF16 = CAUSAL_GQA_BF16.replace(
+    name="bf16 causal GQA prefill B4 H32/8 L4096 D128, local window 1023", local_window=1023,
+    seed=7)
+SOFTCAP_SINK_BF16 = CAUSAL_GQA_BF16.replace(
+    name="bf16 causal GQA prefill B4 H32/8 L4096 D128, softcap 30, head sinks", softcap=30.0,
+    sink="heads", seed=8)
+DECODE_WINDOW_F16 = DECODE_F16.replace(
+    name="fp16 decode B64 H32/8 cache8192 D128, local window 2047, head sinks",
+    local_window=2047, sink="heads", seed=9)
+
 # Workloads of the extensions beyond the five (measured and tested the same way).
 EXTRA_WORKLOADS = {
     "chunk_f16": CHUNK_F16,
+    "window_bf16": WINDOW_BF16,
+    "softcap_sink_bf16": SOFTCAP_SINK_BF16,
+    "decode_window_f16": DECODE_WINDOW_F16,
 }
 
 
@@ -134,6 +153,7 @@ class Case:
     v: np.ndarray
     key_lens: Optional[np.ndarray]
     mask: Optional[np.ndarray]
+    head_sink: Optional[np.ndarray] = None
 
 
 def _normal(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
@@ -174,4 +194,9 @@ def generate(spec: Spec) -> Case:
         mask = mask.reshape(spec.batch, 1, 1, spec.k_len)
     elif spec.mask is not None:
         raise ValueError(spec.mask)
-    return Case(spec, q, k, v, lens, mask)
+    head_sink = None
+    if spec.sink == "heads":
+        head_sink = (2.0 * rng.standard_normal(spec.q_heads, dtype=np.float32)).astype(np.float32)
+    elif spec.sink not in (None, "zero"):
+        raise ValueError(spec.sink)
+    return Case(spec, q, k, v, lens, mask, head_sink)

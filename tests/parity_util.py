@@ -51,17 +51,20 @@ def run_hip(case: synth.Case, policy: str = "nan", *, return_lse=None, tensors=N
         tensors = dict(q=to_dev(case.q, s.dtype), k=to_dev(case.k, s.dtype),
                        v=to_dev(case.v, s.dtype),
                        mask=None if case.mask is None else torch.from_numpy(case.mask).cuda(),
-                       lens=None if case.key_lens is None else torch.from_numpy(case.key_lens).cuda())
+                       lens=None if case.key_lens is None else torch.from_numpy(case.key_lens).cuda(),
+                       sink=None if case.head_sink is None else torch.from_numpy(case.head_sink).cuda())
+    var = dict(local_window=s.local_window, softcap=s.softcap, sink=s.sink is not None,
+               head_sink=tensors.get("sink"))
     want_lse = s.lse if return_lse is None else return_lse
     if s.decode:
         r = sdpa.decode(tensors["q"], tensors["k"], tensors["v"], tensors["lens"],
                         layout=s.q_layout, kv_layout=s.kv_layout, mask=tensors["mask"],
-                        masked_rows=policy, return_lse=want_lse)
+                        masked_rows=policy, return_lse=want_lse, **var)
     else:
         r = sdpa.forward(tensors["q"], tensors["k"], tensors["v"], layout=s.q_layout,
                          kv_layout=s.kv_layout, causal=s.causal, causal_offset=s.causal_offset,
                          mask=tensors["mask"], key_lens=tensors["lens"], masked_rows=policy,
-                         return_lse=want_lse)
+                         return_lse=want_lse, **var)
     torch.cuda.synchronize()
     o, lse = (r if want_lse else (r, None))
     O = canon(to_f64(o), s.q_layout)
@@ -71,10 +74,13 @@ def run_hip(case: synth.Case, policy: str = "nan", *, return_lse=None, tensors=N
 
 def run_oracle(case: synth.Case, policy: str = "nan", rows=None):
     s = case.spec
+    # Decode rows are the newest position of their entry (end-aligned offset).
+    off = "end" if s.decode else s.causal_offset
     return oracle.attention(case.q, case.k, case.v, dtype=s.dtype, layout=s.q_layout,
-                            kv_layout=s.kv_layout, causal=s.causal,
-                            causal_offset=s.causal_offset, mask=case.mask,
-                            key_lens=case.key_lens, masked_rows=policy, rows=rows)
+                            kv_layout=s.kv_layout, causal=s.causal, causal_offset=off,
+                            mask=case.mask, key_lens=case.key_lens, masked_rows=policy,
+                            window=s.local_window, softcap=s.softcap, sink=s.sink is not None,
+                            head_sink=case.head_sink, rows=rows)
 
 
 def compare(gpu_o, ref_o, gpu_lse, ref_lse, dtype: str, policy: str, what: str = ""):

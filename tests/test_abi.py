@@ -85,6 +85,12 @@ FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation rejects first
     (dict(scale=-1.0), sdpa.ERR_INVALID),
     (dict(q=sdpa.Layout(0, -1, 64, 256)), sdpa.ERR_INVALID),
     (dict(batch=70000), sdpa.ERR_UNSUPPORTED),
+    (dict(window=-1), sdpa.ERR_INVALID),
+    (dict(window=4), sdpa.ERR_INVALID),              # a window needs the causal rule
+    (dict(softcap=-1.0), sdpa.ERR_INVALID),
+    (dict(softcap=float("nan")), sdpa.ERR_INVALID),
+    (dict(sink=2), sdpa.ERR_INVALID),
+    (dict(head_sink=0x1000), sdpa.ERR_INVALID),      # values without sink = 1
 ])
 def test_invalid_problem_rejected_before_launch(change, status):
     lib = sdpa.load_library()

@@ -7,6 +7,7 @@ the oracle computes one by one, plus properties that hold at any size.
 import numpy as np
 import pytest
 
+import scaled_dot_product_flash_amd as sdpa
 from scaled_dot_product_flash_amd import synth
 import parity_util as pu
 
@@ -361,3 +362,83 @@ def test_decode_tiny_totals(lens):
         o, lse, _ = pu.run_hip(case, policy)
         ro, rl = pu.run_oracle(case, policy)
         pu.compare(o, ro, lse, rl, "bf16", policy, what="decode tiny %s" % lens)
+
+
+# --------------------------------------------------------------------------
+# Score-rule variants: local window, softcap, sink (GroupQueryAttention
+# README attributes), on every kernel that runs them.
+
+VARIANTS = {
+    "window50_bf16_L333": (synth.CAUSAL_GQA_BF16.replace(
+        batch=1, q_heads=8, kv_heads=2, q_len=333, k_len=333, local_window=50, seed=21),
+        "prefill_mfma"),
+    "window0_f16_D64": (synth.CAUSAL_GQA_BF16.replace(
+        dtype="f16", batch=2, q_heads=6, kv_heads=3, q_len=200, k_len=260, head_dim=64,
+        local_window=0, seed=22), "prefill_mfma"),
+    "softcap5_bf16_mask_lens": (synth.CROSS_MASK_F16.replace(
+        dtype="bf16", head_dim=128, q_len=130, k_len=257, softcap=5.0, seed=23), "prefill_mfma"),
+    "sink_heads_f16_chunk": (synth.CHUNK_F16.replace(
+        batch=8, q_heads=8, kv_heads=2, q_len=70, k_len=300, lens="cross", sink="heads",
+        seed=24), "prefill_mfma"),
+    "window_cap_smooth_bf16": (synth.CAUSAL_GQA_BF16.replace(
+        batch=2, q_heads=8, kv_heads=4, q_len=300, k_len=300, local_window=77, softcap=20.0,
+        sink="zero", seed=25), "prefill_mfma"),
+    "window_cap_sink_f32": (synth.CAUSAL_GQA_F32.replace(
+        batch=1, q_heads=4, kv_heads=2, q_len=100, k_len=100, local_window=10, softcap=3.0,
+        sink="heads", seed=26), "generic"),
+    "decode_window_cap_sink": (synth.DECODE_F16.replace(
+        batch=8, k_len=1000, local_window=100, softcap=30.0, sink="heads", seed=27),
+        "decode_splitk"),
+    "decode_window0_bf16": (synth.DECODE_F16.replace(
+        dtype="bf16", batch=8, k_len=700, head_dim=64, local_window=0, seed=28), "decode_splitk"),
+    "decode_sink_zero_lens0": (synth.DECODE_F16.replace(
+        batch=8, k_len=500, lens="cross", lens_zero_at=3, lens_full_at=4, sink="zero",
+        local_window=3000, seed=29), "decode_splitk"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(VARIANTS))
+@pytest.mark.parametrize("policy", ["nan", "zero"])
+def test_score_variants_full_compare(name, policy):
+    spec, kernel = VARIANTS[name]
+    case = synth.generate(spec)
+    o, lse, _ = pu.run_hip(case, policy, return_lse=True)
+    assert sdpa.last_kernel() == kernel
+    ro, rl = pu.run_oracle(case, policy)
+    pu.compare(o, ro, lse, rl, spec.dtype, policy, what=name)
+
+
+def test_sink_rows_without_keys_are_zero():
+    """Rows that see no key put all weight on the sink: O = 0, LSE = sink."""
+    spec = synth.CHUNK_F16.replace(batch=4, q_heads=8, kv_heads=2, q_len=64, k_len=128,
+                                   lens="cross", lens_zero_at=0, lens_full_at=1, sink="heads",
+                                   seed=30)
+    case = synth.generate(spec)
+    for policy in ("nan", "zero"):
+        o, lse, _ = pu.run_hip(case, policy, return_lse=True)
+        assert (o[0] == 0).all()
+        # LSE = sink, up to the fp32 round trip through base 2.
+        want = np.broadcast_to(case.head_sink.astype(np.float64)[:, None], lse[0].shape)
+        assert np.abs(lse[0] - want).max() < 1e-6
+
+
+@pytest.mark.parametrize("name", ["window_bf16", "softcap_sink_bf16"])
+def test_variant_prefill_full_size_sampled(name):
+    spec = synth.EXTRA_WORKLOADS[name]
+    case = synth.generate(spec)
+    o, lse, _ = pu.run_hip(case, "nan")
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    rows = pu.sample_rows(spec, 96, seed=7)
+    ro, rl = pu.run_oracle(case, "nan", rows=rows)
+    go = o[rows[:, 0], rows[:, 1], rows[:, 2]]
+    gl = lse[rows[:, 0], rows[:, 1], rows[:, 2]]
+    pu.compare(go, ro, gl, rl, spec.dtype, "nan", what=spec.name)
+
+
+def test_variant_decode_full_size_every_row():
+    spec = synth.EXTRA_WORKLOADS["decode_window_f16"]
+    case = synth.generate(spec)
+    o, lse, _ = pu.run_hip(case, "nan", return_lse=True)
+    assert sdpa.last_kernel() == "decode_splitk"
+    ro, rl = pu.run_oracle(case, "nan")
+    pu.compare(o, ro, lse, rl, spec.dtype, "nan", what=spec.name)
