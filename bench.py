@@ -132,8 +132,9 @@ def cpu_baseline_prefill(case, target_s: float = 12.0):
 
 def visible_flops(case) -> float:
     """4*D flop per visible (query row, key) pair, summed over all rows and
-    heads: key lengths, the causal rule and its offset applied (keys a mask
-    hides are still counted; the kernels compute their scores)."""
+    heads: key lengths, the causal rule, its offset and a local window
+    applied (keys a mask hides are still counted; the kernels compute their
+    scores)."""
     s = case.spec
     Lq, Lk = s.q_len, s.k_len
     lens = (np.full(s.batch, Lk) if case.key_lens is None
@@ -145,7 +146,10 @@ def visible_flops(case) -> float:
         if s.causal:
             d = (L - Lq if s.causal_offset == "end"
                  else (Lk - Lq if s.causal_offset is None else int(s.causal_offset)))
-            pairs += int(np.clip(i + d + 1, 0, L).sum())
+            hi = np.clip(i + d + 1, 0, L)
+            lo = (np.clip(i + d - s.local_window, 0, None) if s.local_window >= 0
+                  else np.zeros_like(i))
+            pairs += int(np.clip(hi - lo, 0, None).sum())
         else:
             pairs += L * Lq
     return 4.0 * s.head_dim * s.q_heads * pairs
@@ -157,18 +161,21 @@ def other_workloads(sdpa, synth, steps: int, warmup: int):
     import torch
     out = []
     specs = [synth.WORKLOADS[n] for n in ("tiny_f32", "causal_gqa_f32", "cross_mask_f16")]
-    specs += [synth.EXTRA_WORKLOADS["chunk_f16"]]
+    specs += [synth.EXTRA_WORKLOADS[n] for n in ("chunk_f16", "window_bf16", "softcap_sink_bf16")]
     for spec in specs:
         case = synth.generate(spec)
         q, k, v = (to_dev(x, spec.dtype) for x in (case.q, case.k, case.v))
         mask = None if case.mask is None else torch.from_numpy(case.mask).cuda()
         lens = None if case.key_lens is None else torch.from_numpy(case.key_lens).cuda()
+        sink = None if case.head_sink is None else torch.from_numpy(case.head_sink).cuda()
         o = torch.empty_like(q)
         for policy in (("nan", "zero") if spec.mask else ("nan",)):
             def f():
                 sdpa.forward(q, k, v, layout=spec.q_layout, kv_layout=spec.kv_layout,
                              causal=spec.causal, causal_offset=spec.causal_offset, mask=mask,
-                             key_lens=lens, masked_rows=policy, return_lse=spec.lse, out=o)
+                             key_lens=lens, masked_rows=policy, return_lse=spec.lse,
+                             local_window=spec.local_window, softcap=spec.softcap,
+                             sink=spec.sink is not None, head_sink=sink, out=o)
             f()
             kern = sdpa.last_kernel()
             durs, _ = time_calls(f, steps, warmup, settle_s=0.3)
@@ -177,6 +184,25 @@ def other_workloads(sdpa, synth, steps: int, warmup: int):
                         "ms_per_call": round(ms, 5),
                         "tflops": round(visible_flops(case) / (ms * 1e-3) / 1e12, 3),
                         "dtype": spec.dtype})
+    # Decode with a local window and head sinks: KV GB/s over the live ranges.
+    spec = synth.EXTRA_WORKLOADS["decode_window_f16"]
+    case = synth.generate(spec)
+    q, k, v = (to_dev(x, spec.dtype) for x in (case.q, case.k, case.v))
+    lens = torch.from_numpy(case.key_lens).cuda()
+    sink = torch.from_numpy(case.head_sink).cuda()
+    o = torch.empty_like(q)
+
+    def g():
+        sdpa.decode(q, k, v, lens, kv_layout=spec.kv_layout, local_window=spec.local_window,
+                    softcap=spec.softcap, sink=True, head_sink=sink, out=o)
+    g()
+    kern = sdpa.last_kernel()
+    durs, _ = time_calls(g, steps, warmup, settle_s=0.3)
+    ms = float(np.mean(durs))
+    live = np.minimum(case.key_lens.astype(np.float64), spec.local_window + 1)
+    kv_bytes = float(live.sum()) * spec.kv_heads * spec.head_dim * 2 * 2
+    out.append({"workload": spec.name, "kernel": kern, "ms_per_call": round(ms, 5),
+                "gbs": round(kv_bytes / (ms * 1e-3) / 1e9, 1), "dtype": spec.dtype})
     return out
 
 
