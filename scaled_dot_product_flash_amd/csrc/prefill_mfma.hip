@@ -36,8 +36,8 @@
 //
 // Element-wise work that only some tiles need (the causal diagonal, the tile
 // holding the key length, the lower edge of a local window, the additive
-// mask) is done only on those tiles; the mask and the softcap are
-// compile-time variants of the kernel.  Score-rule variants follow the ONNX
+// mask) is done only on those tiles; the mask and the window/softcap rules
+// are compile-time variants of the kernel.  Score-rule variants follow the ONNX
 // GroupQueryAttention README ("Attributes", "Inputs"): a local window starts
 // the key loop at the block's first visible tile; the softcap maps each raw
 // score before the mask is added; the sink joins the denominator at the end.
@@ -73,7 +73,7 @@ template <int D> struct Tile {
     static constexpr int kLoads = kBN * kRowChunks / kThreads;        // per thread
 };
 
-template <bool kBf16, int D, bool kMask, bool kCap>
+template <bool kBf16, int D, bool kMask, bool kVar>
 __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(Params p, int n_qblk, int gw,
                                                                    int xcd_units, int mask_vec4) {
     using M = Mma<kBf16>;
@@ -141,9 +141,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(Params p, int
     const int n_tiles = static_cast<int>((blk_hi + kBN - 1) / kBN);
     // Under a local window the block's first row sees the lowest keys, and a
     // tile below the wave's last row's window edge needs the element test.
-    const int t_first = static_cast<int>(window_lo(p, q0, delta) / kBN);
+    const int t_first = kVar ? static_cast<int>(window_lo(p, q0, delta) / kBN) : 0;
     const int64_t wave_lo =
-        window_lo(p, (qw0 + 31 < p.Lq ? qw0 + 31 : p.Lq - 1), delta);
+        kVar ? window_lo(p, (qw0 + 31 < p.Lq ? qw0 + 31 : p.Lq - 1), delta) : 0;
 
     const uint16_t* qg = static_cast<const uint16_t*>(p.q);
     const uint16_t* kg = static_cast<const uint16_t*>(p.k) + b * p.ks.sb + g * p.ks.sh;
@@ -238,9 +238,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(Params p, int
 
     f32x16 s_cur[2];
     if (t_first < n_tiles) scores(t_first & 1, s_cur);
-    const int64_t row_lo = window_lo(p, qrow, delta);
-    const float cap_k2 = kCap ? 2.f * kLog2e * p.scale / p.softcap : 0.f;
-    const float cap_back = kCap ? p.softcap / p.scale : 0.f;
+    const int64_t row_lo = kVar ? window_lo(p, qrow, delta) : 0;
+    const bool cap = kVar && p.softcap > 0.f;
+    const float cap_k2 = cap ? 2.f * kLog2e * p.scale / p.softcap : 0.f;
+    const float cap_back = cap ? p.softcap / p.scale : 0.f;
 
     for (int tile = t_first; tile < n_tiles; ++tile) {
         const bool more_k = tile + 2 < n_tiles;
@@ -251,7 +252,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(Params p, int
         const bool sees = j0 < wave_hi;
 
         // -- softcap on the raw scores, before the mask --
-        if (kCap) {
+        if (cap) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -281,7 +282,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(Params p, int
         // -- hide keys past the length / causal bound / below the window
         // (edge tiles only) --
         const bool partial = (j0 + kBN > kv_len) || (p.causal && j0 + kBN - 1 > qw0 + delta) ||
-                             (j0 < wave_lo);
+                             (kVar && j0 < wave_lo);
         if (partial) {
             const int64_t qlim = p.causal ? qrow + delta : kv_len;
 #pragma unroll
@@ -289,7 +290,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(Params p, int
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int64_t key = j0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-                    if (key >= kv_len || key > qlim || key < row_lo) s_cur[kb][r] = kNegInf;
+                    if (key >= kv_len || key > qlim || (kVar && key < row_lo))
+                        s_cur[kb][r] = kNegInf;
                 }
         }
 
@@ -414,14 +416,14 @@ hipError_t launch_one(const Params& p, hipStream_t s) {
     const int mask_vec4 = p.mask && (reinterpret_cast<uintptr_t>(p.mask) % 16 == 0) &&
                           p.ms.sb % 4 == 0 && p.ms.sh % 4 == 0 && p.ms.sr % 4 == 0;
     const dim3 grid(static_cast<uint32_t>(block_count(p)));
-    const bool cap = p.softcap > 0.f;
-    if (p.mask && cap)
+    const bool var = p.softcap > 0.f || (p.causal && p.window > 0);
+    if (p.mask && var)
         hipLaunchKernelGGL((prefill_mfma_kernel<kBf16, D, true, true>), grid, dim3(kThreads), 0, s,
                            p, n_qblk, gw, xcd_units, mask_vec4);
     else if (p.mask)
         hipLaunchKernelGGL((prefill_mfma_kernel<kBf16, D, true, false>), grid, dim3(kThreads), 0,
                            s, p, n_qblk, gw, xcd_units, mask_vec4);
-    else if (cap)
+    else if (var)
         hipLaunchKernelGGL((prefill_mfma_kernel<kBf16, D, false, true>), grid, dim3(kThreads), 0,
                            s, p, n_qblk, gw, xcd_units, mask_vec4);
     else
