@@ -47,6 +47,9 @@ class _Problem(ctypes.Structure):
         ("window", ctypes.c_int32),
         ("sink", ctypes.c_int32),
         ("softcap", ctypes.c_double),
+        ("kv_int8", ctypes.c_int32),
+        ("k_quant", ctypes.c_int32),
+        ("v_quant", ctypes.c_int32),
     ]
 
 
@@ -71,6 +74,7 @@ def _load():
         lib.oracle_attention.argtypes = [
             ctypes.POINTER(_Problem), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_void_p,
             ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
         lib.oracle_decode_f16.restype = ctypes.c_double
         lib.oracle_decode_f16.argtypes = [ctypes.c_uint16]
@@ -117,6 +121,7 @@ def attention(q, k, v, *, dtype: str, layout: str = "bshd", kv_layout: str | Non
               key_lens: np.ndarray | None = None, masked_rows: str = "nan",
               window: int = -1, softcap: float = 0.0, sink: bool = False,
               head_sink: np.ndarray | None = None,
+              k_scale: np.ndarray | None = None, v_scale: np.ndarray | None = None,
               rows: np.ndarray | None = None, threads: int = 0):
     """Reference attention in float64.
 
@@ -131,6 +136,9 @@ def attention(q, k, v, *, dtype: str, layout: str = "bshd", kv_layout: str | Non
     softcap: 0, or c > 0 (score -> c*tanh(score/c) before the mask).
     sink: add exp(head_sink[h]) (0 without head_sink) to each denominator;
     head_sink: float32 [Hq] or None.
+    k, v may be int8 (a quantized cache); then k_scale / v_scale are float32
+    of size 1 (per tensor) or Hkv * D (per channel, index g * D + d) and an
+    element's value is the integer times its scale.
     rows: optional int64 [n, 3] of (b, h, i) to compute; default every row.
 
     Returns (O, LSE): O is [B, Hq, Lq, D] (or [n, D] with ``rows``) float64,
@@ -138,9 +146,12 @@ def attention(q, k, v, *, dtype: str, layout: str = "bshd", kv_layout: str | Non
     """
     kv_layout = kv_layout or layout
     st = STORAGE[dtype]
+    kv_int8 = k.dtype == np.int8
+    keep_scales = []
     for name, a in (("q", q), ("k", k), ("v", v)):
-        if a.dtype != st or a.ndim != 4:
-            raise TypeError("%s must be a 4-D %s array" % (name, np.dtype(st)))
+        want = np.int8 if (kv_int8 and name != "q") else st
+        if a.dtype != want or a.ndim != 4:
+            raise TypeError("%s must be a 4-D %s array" % (name, np.dtype(want)))
     B, Hq, Lq, D = _dims(q, layout)
     Bk, Hkv, Lk, Dk = _dims(k, kv_layout)
     if _dims(v, kv_layout) != (Bk, Hkv, Lk, Dk) or Bk != B or Dk != D:
@@ -162,6 +173,23 @@ def attention(q, k, v, *, dtype: str, layout: str = "bshd", kv_layout: str | Non
     p.window = int(window)
     p.softcap = float(softcap)
     p.sink = 1 if sink else 0
+    scale_ptrs = [None, None]
+    if kv_int8:
+        p.kv_int8 = 1
+        modes = []
+        for j, sc in enumerate((k_scale, v_scale)):
+            if sc is None:
+                raise ValueError("an int8 cache needs k_scale and v_scale")
+            sc = np.ascontiguousarray(sc, dtype=np.float32).reshape(-1)
+            if sc.size == 1:
+                modes.append(1)
+            elif sc.size == Hkv * D:
+                modes.append(2)
+            else:
+                raise ValueError("a scale has 1 or Hkv*D entries")
+            keep_scales.append(sc)
+            scale_ptrs[j] = sc.ctypes.data
+        p.k_quant, p.v_quant = modes
     p.qs[:] = _bhs_strides(q, layout)
     p.ks[:] = _bhs_strides(k, kv_layout)
     p.vs[:] = _bhs_strides(v, kv_layout)
@@ -207,7 +235,8 @@ def attention(q, k, v, *, dtype: str, layout: str = "bshd", kv_layout: str | Non
     o = np.empty((n, D), dtype=np.float64)
     lse = np.empty((n,), dtype=np.float64)
     rc = _load().oracle_attention(ctypes.byref(p), q.ctypes.data, k.ctypes.data, v.ctypes.data,
-                                  mask_ptr, lens_ptr, sink_ptr, rows_ptr, n, o.ctypes.data,
+                                  mask_ptr, lens_ptr, sink_ptr, scale_ptrs[0], scale_ptrs[1],
+                                  rows_ptr, n, o.ctypes.data,
                                   lse.ctypes.data, int(threads))
     if rc != 0:
         raise RuntimeError("oracle rejected the problem")

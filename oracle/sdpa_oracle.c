@@ -51,6 +51,14 @@
  *     LSE = sink_h under both policies; a NaN / +inf score, the sink's own
  *     included, still gives NaN.
  *
+ * Quantized key/value cache (ONNX GroupQueryAttention README, "Inputs":
+ * k_scale / v_scale; "Attributes": k_quant_type / v_quant_type, cache bit
+ * width 8): a cache element is a signed 8-bit integer and its value is that
+ * integer times a float32 scale -- one scale for the whole tensor (per
+ * tensor), or one per (kv head, head-dim index), stored at g * D + d (per
+ * channel).  Reading: symmetric, no zero point; Q and the output keep the
+ * problem's element type.
+ *
  * Inputs are read in their storage type and decoded exactly to double
  * (float32 widened; float16 and bfloat16 bit patterns decoded from their IEEE
  * definitions), as the OneGPU "Tolerances" section describes its reference
@@ -83,6 +91,9 @@ typedef struct oracle_problem {
     int32_t window;         /* -1: none; W >= 0: causal rows need j >= i+delta-W */
     int32_t sink;           /* 0: none; 1: exp(sink_h) joins the denominator     */
     double softcap;         /* 0: none; c > 0: score -> c * tanh(score / c)      */
+    int32_t kv_int8;        /* 0: K/V in dtype; 1: int8 cache with scales        */
+    int32_t k_quant;        /* with kv_int8: 1 per tensor, 2 per channel         */
+    int32_t v_quant;        /* likewise for V                                    */
 } oracle_problem;
 
 /* float16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. */
@@ -119,9 +130,21 @@ static double load_elem(const void* base, int32_t dtype, int64_t idx)
     return oracle_decode_bf16(((const uint16_t*)base)[idx]);
 }
 
+/* Element d of a K or V row: the stored value, or for an int8 cache the
+ * integer times its scale (per tensor: scale[0]; per channel: scale[g*D+d]). */
+static double load_kv(const oracle_problem* p, const void* base, const float* scale, int32_t quant,
+                      int64_t g, int64_t idx, int64_t d)
+{
+    if (!p->kv_int8)
+        return load_elem(base, p->dtype, idx);
+    const double x = (double)((const int8_t*)base)[idx];
+    return x * (double)(quant == 1 ? scale[0] : scale[g * p->head_dim + d]);
+}
+
 /* One query row (b, h, i).  s is scratch of k_len doubles. */
 static void one_row(const oracle_problem* p, const void* q, const void* k, const void* v,
                     const float* mask, const int32_t* key_lens, const float* head_sink,
+                    const float* k_scale, const float* v_scale,
                     int64_t b, int64_t h, int64_t i, double* s, unsigned char* vis,
                     double* o_row, double* lse_out)
 {
@@ -150,7 +173,8 @@ static void one_row(const oracle_problem* p, const void* q, const void* k, const
         const int64_t kbase = b * p->ks[0] + g * p->ks[1] + j * p->ks[2];
         double dot = 0.0;
         for (int64_t d = 0; d < D; ++d)
-            dot += load_elem(q, p->dtype, qbase + d) * load_elem(k, p->dtype, kbase + d);
+            dot += load_elem(q, p->dtype, qbase + d) *
+                   load_kv(p, k, k_scale, p->k_quant, g, kbase + d, d);
         double sj = scale * dot;
         if (p->softcap > 0.0)
             sj = p->softcap * tanh(sj / p->softcap);
@@ -204,7 +228,7 @@ static void one_row(const oracle_problem* p, const void* q, const void* k, const
         const double w = exp(s[j] - m) / l;
         const int64_t vbase = b * p->vs[0] + g * p->vs[1] + j * p->vs[2];
         for (int64_t d = 0; d < D; ++d)
-            o_row[d] += w * load_elem(v, p->dtype, vbase + d);
+            o_row[d] += w * load_kv(p, v, v_scale, p->v_quant, g, vbase + d, d);
     }
     *lse_out = m + log(l);
 }
@@ -217,6 +241,7 @@ static void one_row(const oracle_problem* p, const void* q, const void* k, const
  */
 int oracle_attention(const oracle_problem* p, const void* q, const void* k, const void* v,
                      const float* mask, const int32_t* key_lens, const float* head_sink,
+                     const float* k_scale, const float* v_scale,
                      const int64_t* rows, int64_t n_rows, double* o, double* lse,
                      int n_threads)
 {
@@ -224,6 +249,9 @@ int oracle_attention(const oracle_problem* p, const void* q, const void* k, cons
         p->head_dim <= 0 || p->batch < 0 || p->q_len < 0 || p->k_len < 0)
         return -1;
     if (!rows && n_rows != p->batch * p->q_heads * p->q_len)
+        return -1;
+    if (p->kv_int8 && (!k_scale || !v_scale || p->k_quant < 1 || p->k_quant > 2 ||
+                       p->v_quant < 1 || p->v_quant > 2))
         return -1;
 #ifdef _OPENMP
     if (n_threads > 0)
@@ -256,8 +284,8 @@ int oracle_attention(const oracle_problem* p, const void* q, const void* k, cons
                 i = r % p->q_len;
             }
             double lse_r;
-            one_row(p, q, k, v, mask, key_lens, head_sink, b, h, i, s, vis, o + r * p->head_dim,
-                    &lse_r);
+            one_row(p, q, k, v, mask, key_lens, head_sink, k_scale, v_scale, b, h, i, s, vis,
+                    o + r * p->head_dim, &lse_r);
             if (lse)
                 lse[r] = lse_r;
         }

@@ -37,7 +37,10 @@ def _rand(shape, dtype, seed, scale=1.0):
 
 
 def _as_f64(a, dtype):
-    """Storage -> float64 through library conversions (numpy / torch)."""
+    """Storage -> float64 through library conversions (numpy / torch); float64
+    arrays (already decoded) pass through."""
+    if a.dtype == np.float64:
+        return a
     if dtype == "bf16":
         t = torch.from_numpy(a.astype(np.int16)).view(torch.bfloat16)
         return t.to(torch.float64).numpy()
@@ -637,6 +640,76 @@ def test_softcap_comes_before_the_mask():
     t = np.array([c * math.tanh(2.0 / c), c * math.tanh(0.5 / c) + 5.0])
     w = np.exp(t - t.max()) / np.exp(t - t.max()).sum()
     assert o[0, 0, 0, 0] == pytest.approx(w[0] * 1.0 + w[1] * 2.0, abs=1e-13)
+
+
+# --------------------------------------------------------------------------
+# Quantized (int8) key/value cache with float32 scales (GroupQueryAttention
+# README: k_scale / v_scale, per tensor or per (kv head, head-dim) channel).
+
+def _int8(shape, seed):
+    return np.random.default_rng(seed).integers(-127, 128, size=shape).astype(np.int8)
+
+
+def _dequant(x8, scale, layout="bshd"):
+    """int8 [B, L, Hkv, D] (or bhsd) times its scale, in float64."""
+    x = x8.astype(np.float64)
+    sc = np.asarray(scale, np.float64).reshape(-1)
+    if sc.size == 1:
+        return x * sc[0]
+    Hkv, D = (x.shape[2], x.shape[3]) if layout == "bshd" else (x.shape[1], x.shape[3])
+    sc = sc.reshape(Hkv, D)
+    return x * (sc[None, None] if layout == "bshd" else sc[None, :, None, :])
+
+
+@pytest.mark.parametrize("per_channel", [False, True])
+def test_int8_cache_equals_exact_float_cache(per_channel):
+    """Power-of-two scales make every int8 * scale exact in float32, so the
+    int8 path must reproduce the float32 path on the dequantized cache."""
+    B, Hq, Hkv, Lq, Lk, D = 2, 4, 2, 3, 17, 8
+    q = _rand((B, Lq, Hq, D), "f32", 71)
+    k8, v8 = _int8((B, Lk, Hkv, D), 72), _int8((B, Lk, Hkv, D), 73)
+    rng = np.random.default_rng(74)
+    shape = (Hkv * D,) if per_channel else (1,)
+    ks = (2.0 ** rng.integers(-9, -4, size=shape)).astype(np.float32)
+    vs = (2.0 ** rng.integers(-9, -4, size=shape)).astype(np.float32)
+    kf = _dequant(k8, ks).astype(np.float32)
+    vf = _dequant(v8, vs).astype(np.float32)
+    a = oracle.attention(q, k8, v8, dtype="f32", causal=True, k_scale=ks, v_scale=vs)
+    b = oracle.attention(q, kf, vf, dtype="f32", causal=True)
+    assert (a[0] == b[0]).all() and (a[1] == b[1]).all()
+
+
+INT8_CASES = [
+    # B, Hq, Hkv, Lk, D, dtype, k per channel, v per channel, lens
+    (2, 8, 2, 40, 16, "f16", False, False, True),
+    (3, 4, 4, 33, 32, "bf16", True, True, False),
+    (2, 6, 3, 65, 64, "f16", True, False, True),
+    (1, 2, 1, 7, 8, "f32", False, True, False),
+]
+
+
+@pytest.mark.parametrize("cfg", INT8_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_int8_cache_against_library_route(cfg):
+    B, Hq, Hkv, Lk, D, dtype, kc, vc, use_lens = cfg
+    seed = zlib.crc32(repr(cfg).encode()) % 1000
+    q = _rand((B, 1, Hq, D), dtype, seed)
+    k8 = _int8((B, Hkv, Lk, D), seed + 1)
+    v8 = _int8((B, Hkv, Lk, D), seed + 2)
+    rng = np.random.default_rng(seed + 3)
+    ks = (rng.random(Hkv * D if kc else 1) * 0.05 + 0.005).astype(np.float32)
+    vs = (rng.random(Hkv * D if vc else 1) * 0.05 + 0.005).astype(np.float32)
+    lens = rng.integers(0, Lk + 1, size=B).astype(np.int32) if use_lens else None
+    o, lse = oracle.attention(q, k8, v8, dtype=dtype, kv_layout="bhsd", causal=True,
+                              causal_offset="end", key_lens=lens, k_scale=ks, v_scale=vs)
+    kd = np.transpose(_dequant(k8, ks, "bhsd"), (0, 2, 1, 3))
+    vd = np.transpose(_dequant(v8, vs, "bhsd"), (0, 2, 1, 3))
+    o2, lse2 = _library_attention(q, kd, vd, dtype, causal=True, offset="end", key_lens=lens)
+    assert (np.isnan(o) == np.isnan(o2)).all()
+    fin = ~np.isnan(o)
+    assert np.abs(o[fin] - o2[fin]).max(initial=0) < 1e-12
+    with np.errstate(invalid="ignore"):
+        close = np.abs(lse - lse2) < 1e-11
+    assert ((lse == lse2) | close | (np.isnan(lse) & np.isnan(lse2))).all()
 
 
 def test_rejects_bad_problems():

@@ -50,6 +50,10 @@ MUTANTS = {
         "        if (p->softcap > 0.0)\n            sj = p->softcap * tanh(sj / p->softcap);\n"),
     "sink_not_in_denominator": ("double l = p->sink ? exp(sink - m) : 0.0;", "double l = 0.0;"),
     "sink_ignores_head": ("(double)head_sink[h]", "(double)head_sink[0]"),
+    "channel_scale_ignores_head": ("scale[g * p->head_dim + d]", "scale[d]"),
+    "channel_scale_transposed": ("scale[g * p->head_dim + d]", "scale[d * p->kv_heads + g]"),
+    "v_uses_k_scale": ("load_kv(p, v, v_scale, p->v_quant", "load_kv(p, v, k_scale, p->k_quant"),
+    "int8_unscaled": ("return x * (double)(quant == 1", "return x * 1.0 + 0.0 * (double)(quant == 1"),
     "key_lengths_ignored": ("kv_len = L < 0 ? 0 : (L > p->k_len ? p->k_len : L);",
                             "kv_len = p->k_len; (void)L;"),
 }
@@ -80,7 +84,10 @@ CHECKS = [
 ] + [(lambda r=r: pins.test_special_values_golden(r)) for r in pins._golden("special_values.txt")] \
   + [(lambda c=c: pins.test_brute_force_against_library_route(c, "nan")) for c in pins.BRUTE] \
   + [(lambda c=c: pins.test_variants_against_library_route(c, "nan"))
-     for c in pins.BRUTE_VARIANTS]
+     for c in pins.BRUTE_VARIANTS] \
+  + [lambda: pins.test_int8_cache_equals_exact_float_cache(True),
+     lambda: pins.test_int8_cache_equals_exact_float_cache(False)] \
+  + [(lambda c=c: pins.test_int8_cache_against_library_route(c)) for c in pins.INT8_CASES]
 
 
 def _any_check_fails():
