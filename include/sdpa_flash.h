@@ -69,6 +69,12 @@ typedef enum attn_masked_rows {
     ATTN_MASKED_ROWS_ZERO = 1  /* ... or all zeros                              */
 } attn_masked_rows;
 
+typedef enum attn_quant {
+    ATTN_QUANT_NONE = 0,
+    ATTN_QUANT_PER_TENSOR = 1,
+    ATTN_QUANT_PER_CHANNEL = 2
+} attn_quant;
+
 typedef enum attn_op {
     ATTN_OP_FORWARD = 0,
     ATTN_OP_DECODE = 1
@@ -138,6 +144,21 @@ typedef struct attn_problem {
      * masked-row policies; a NaN or +inf sink_h gives a NaN row.              */
     int32_t sink;
     const float* head_sink;
+    /* Quantized key/value cache (GroupQueryAttention README, "Inputs":
+     * k_scale / v_scale; "Attributes": k_quant_type / v_quant_type, cache bit
+     * width 8).  kv_int8 = 0: K and V are in dtype.  kv_int8 = 1: K and V are
+     * signed 8-bit integers (layout strides count elements, i.e. bytes) whose
+     * value is the integer times a float32 scale: k_quant / v_quant =
+     * ATTN_QUANT_PER_TENSOR uses scale[0], ATTN_QUANT_PER_CHANNEL uses
+     * scale[g * head_dim + d] for kv head g.  k_scale / v_scale are device
+     * pointers.  Only attn_decode runs int8 caches (fp16 or bf16 Q/O,
+     * head_dim 64 or 128; K/V rows and strides 16-byte aligned); other
+     * problems return ATTN_ERR_UNSUPPORTED.                                   */
+    int32_t kv_int8;
+    int32_t k_quant;
+    int32_t v_quant;
+    const float* k_scale;
+    const float* v_scale;
 } attn_problem;
 
 /*

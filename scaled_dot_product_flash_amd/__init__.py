@@ -30,6 +30,7 @@ SYMBOLS = ("attn_forward", "attn_decode", "attn_workspace_size", "attn_last_erro
 OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 DTYPE_F32, DTYPE_F16, DTYPE_BF16 = 0, 1, 2
 MASKED_NAN, MASKED_ZERO = 0, 1
+QUANT_PER_TENSOR, QUANT_PER_CHANNEL = 1, 2
 OP_FORWARD, OP_DECODE = 0, 1
 CAUSAL_OFFSET_DEFAULT = -(1 << 63)
 CAUSAL_OFFSET_KEY_END = -(1 << 63) + 1
@@ -57,6 +58,8 @@ class Problem(ctypes.Structure):
         ("mask", Layout), ("lse", Layout),
         ("window", ctypes.c_int32), ("softcap", ctypes.c_float),
         ("sink", ctypes.c_int32), ("head_sink", ctypes.c_void_p),
+        ("kv_int8", ctypes.c_int32), ("k_quant", ctypes.c_int32), ("v_quant", ctypes.c_int32),
+        ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
     ]
 
 
@@ -154,12 +157,16 @@ def _ptr(t):
 def _run(op: int, q, k, v, *, layout: str, kv_layout: str | None, causal: bool,
          causal_offset, scale, mask, key_lens, masked_rows: str, return_lse: bool,
          local_window: int = -1, softcap: float = 0.0, sink: bool = False, head_sink=None,
-         out=None, stream=None):
+         k_scale=None, v_scale=None, out=None, stream=None):
     torch = _torch()
     kv_layout = kv_layout or layout
     if not (q.is_cuda and k.is_cuda and v.is_cuda):
         raise ValueError("q, k and v must be GPU tensors (there is no CPU path)")
-    if not (q.dtype == k.dtype == v.dtype):
+    kv_int8 = k.dtype == torch.int8
+    if kv_int8:
+        if v.dtype != torch.int8 or k_scale is None or v_scale is None:
+            raise TypeError("an int8 cache needs int8 k and v and both k_scale and v_scale")
+    elif not (q.dtype == k.dtype == v.dtype):
         raise TypeError("q, k and v must share one dtype")
     B, Hq, Lq, D = _dims(q, layout)
     Bk, Hkv, Lk, Dk = _dims(k, kv_layout)
@@ -191,6 +198,16 @@ def _run(op: int, q, k, v, *, layout: str, kv_layout: str | None, causal: bool,
             raise TypeError("head_sink must be a float32 GPU tensor of shape [Hq]")
         head_sink = head_sink.contiguous()
         p.head_sink = head_sink.data_ptr()
+    if kv_int8:
+        p.kv_int8 = 1
+        modes = []
+        for name, sc in (("k_scale", k_scale), ("v_scale", v_scale)):
+            if sc.dtype != torch.float32 or not sc.is_cuda or sc.numel() not in (1, Hkv * D):
+                raise TypeError("%s must be a float32 GPU tensor of 1 or Hkv*D values" % name)
+            modes.append(QUANT_PER_TENSOR if sc.numel() == 1 else QUANT_PER_CHANNEL)
+        k_scale, v_scale = k_scale.contiguous(), v_scale.contiguous()
+        p.k_quant, p.v_quant = modes
+        p.k_scale, p.v_scale = k_scale.data_ptr(), v_scale.data_ptr()
     p.q = _layout_of(q, layout)
     p.k = _layout_of(k, kv_layout)
     p.v = _layout_of(v, kv_layout)
@@ -254,12 +271,16 @@ def forward(q, k, v, *, layout: str = "bshd", kv_layout: str | None = None,
 def decode(q, k_cache, v_cache, key_lens=None, *, layout: str = "bshd", kv_layout: str = "bhsd",
            scale: float | None = None, mask=None, masked_rows: str = "nan",
            return_lse: bool = False, local_window: int = -1, softcap: float = 0.0,
-           sink: bool = False, head_sink=None, out=None, stream=None):
+           sink: bool = False, head_sink=None, k_scale=None, v_scale=None, out=None,
+           stream=None):
     """One query row per (batch, head) against a K/V cache of capacity Lk with
     live lengths ``key_lens`` (int32 [B]).  The row is the newest position of
     its entry (end-aligned causal offset), so every live key is visible and a
-    local window counts back from the entry's last live key."""
+    local window counts back from the entry's last live key.  An int8 cache
+    (k_cache / v_cache int8) takes float32 k_scale / v_scale of 1 value (per
+    tensor) or Hkv*D values (per channel, index g*D + d)."""
     return _run(OP_DECODE, q, k_cache, v_cache, layout=layout, kv_layout=kv_layout,
                 causal=True, causal_offset="end", scale=scale, mask=mask, key_lens=key_lens,
                 masked_rows=masked_rows, return_lse=return_lse, local_window=local_window,
-                softcap=softcap, sink=sink, head_sink=head_sink, out=out, stream=stream)
+                softcap=softcap, sink=sink, head_sink=head_sink, k_scale=k_scale,
+                v_scale=v_scale, out=out, stream=stream)

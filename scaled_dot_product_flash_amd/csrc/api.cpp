@@ -76,6 +76,19 @@ attn_status validate(const attn_problem* p, bool check_ptrs, const void* q, cons
     if (p->sink != 0 && p->sink != 1) return fail(ATTN_ERR_INVALID, "sink must be 0 or 1");
     if (p->head_sink && !p->sink)
         return fail(ATTN_ERR_INVALID, "head_sink given without sink = 1");
+    if (p->kv_int8 != 0 && p->kv_int8 != 1) return fail(ATTN_ERR_INVALID, "kv_int8 must be 0 or 1");
+    if (p->kv_int8) {
+        auto qok = [](int32_t m) {
+            return m == ATTN_QUANT_PER_TENSOR || m == ATTN_QUANT_PER_CHANNEL;
+        };
+        if (!qok(p->k_quant) || !qok(p->v_quant))
+            return fail(ATTN_ERR_INVALID, "an int8 cache needs k_quant and v_quant per tensor or "
+                                          "per channel");
+        if (check_ptrs && (!p->k_scale || !p->v_scale))
+            return fail(ATTN_ERR_INVALID, "an int8 cache needs k_scale and v_scale");
+    } else if (p->k_quant || p->v_quant || p->k_scale || p->v_scale) {
+        return fail(ATTN_ERR_INVALID, "quantization fields set without kv_int8 = 1");
+    }
     if (!nonneg(p->q) || !nonneg(p->k) || !nonneg(p->v) || !nonneg(p->o))
         return fail(ATTN_ERR_INVALID, "layout offsets and strides must be >= 0");
     if (!check_ptrs) {
@@ -106,9 +119,13 @@ sdpa::Params make_params(const attn_problem* p, const void* q, const void* k, co
     auto adv = [&](const void* base, int64_t off) -> const void* {
         return base ? static_cast<const char*>(base) + off * static_cast<int64_t>(es) : nullptr;
     };
+    const size_t kes = p->kv_int8 ? 1 : es;       // K/V element size
+    auto adv_kv = [&](const void* base, int64_t off) -> const void* {
+        return base ? static_cast<const char*>(base) + off * static_cast<int64_t>(kes) : nullptr;
+    };
     r.q = adv(q, p->q.offset);
-    r.k = adv(k, p->k.offset);
-    r.v = adv(v, p->v.offset);
+    r.k = adv_kv(k, p->k.offset);
+    r.v = adv_kv(v, p->v.offset);
     r.o = const_cast<void*>(adv(o, p->o.offset));
     r.mask = mask ? mask + p->mask.offset : nullptr;
     r.lens = key_lens;
@@ -140,6 +157,11 @@ sdpa::Params make_params(const attn_problem* p, const void* q, const void* k, co
     r.softcap = p->softcap;
     r.sink = p->sink;
     r.head_sink = p->head_sink;
+    r.kv_int8 = p->kv_int8;
+    r.k_quant = p->k_quant;
+    r.v_quant = p->v_quant;
+    r.k_scale = p->k_scale;
+    r.v_scale = p->v_scale;
     return r;
 }
 
@@ -198,6 +220,8 @@ attn_status attn_forward(const attn_problem* p, const void* q, const void* k, co
         g_kernel = "";
         return ATTN_OK;
     }
+    if (p->kv_int8)
+        return fail(ATTN_ERR_UNSUPPORTED, "an int8 key/value cache runs through attn_decode only");
     sdpa::Params prm = make_params(p, q, k, v, o, mask, key_lens, lse);
     const auto dt = static_cast<sdpa::DType>(p->dtype);
     const hipStream_t s = static_cast<hipStream_t>(stream);
@@ -241,9 +265,12 @@ attn_status attn_decode(const attn_problem* p, const void* q, const void* k, con
             return fail(ATTN_ERR_WORKSPACE, "decode needs %zu workspace bytes, got %zu", need,
                         workspace ? workspace_bytes : size_t(0));
         prm.ws = workspace;
-        g_kernel = "decode_splitk";
+        g_kernel = p->kv_int8 ? "decode_splitk_int8" : "decode_splitk";
         return launched(sdpa::launch_decode_split(prm, dt, s));
     }
+    if (p->kv_int8)
+        return fail(ATTN_ERR_UNSUPPORTED, "int8 cache decode needs fp16/bf16, head_dim 64 or "
+                                          "128 and 16-byte aligned K/V rows");
     return attn_forward(p, q, k, v, o, mask, key_lens, lse, workspace, workspace_bytes, stream);
 }
 

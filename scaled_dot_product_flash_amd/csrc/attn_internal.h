@@ -37,6 +37,10 @@ struct Params {
     float softcap;         // 0, or c: s -> c * tanh(s / c) on scaled scores
     int32_t sink;          // 1: a sink term joins each denominator
     const float* head_sink;   // per query head sink scores (nullable: 0)
+    int32_t kv_int8;       // 1: K/V are int8 with scales
+    int32_t k_quant, v_quant;   // 1 per tensor, 2 per channel (g * D + d)
+    const float* k_scale;
+    const float* v_scale;
     int32_t n_split;       // key ranges per (b, h) for the fp32 split kernel
     int32_t split_len;     // keys per range (multiple of the tile)
 };

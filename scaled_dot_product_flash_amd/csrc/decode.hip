@@ -35,6 +35,14 @@
 // "Inputs"): a local window moves the start of the live range up (the range
 // is [lo, hi) and steps count from lo); the softcap maps raw scores before
 // the mask; the sink joins the denominator in the merge.
+//
+// Int8 cache (GroupQueryAttention README, "Inputs": k_scale / v_scale): rows
+// are read as 16-byte loads of 16 int8 values -- half the bytes of fp16 --
+// and widened to the element type on their way into LDS (exact: |x| <= 128).
+// A per-tensor K scale multiplies the exponent constant (exact); a
+// per-channel K scale is folded into the query row, rounded to the element
+// type.  V scales apply per output element in the merge, where they factor
+// out of the sum over keys.
 #include "attn_internal.h"
 #include "device_common.h"
 #include "mfma_common.h"
@@ -60,6 +68,45 @@ template <int D> struct DLay {
     static constexpr int kLoads = kStep / kRowsPerLoad;      // loads per lane per tensor
     static constexpr int kWaveBytes = kStep * (KS + VS) * 2;
 };
+
+// Int8 rows: 16 values per 16-byte load.
+template <int D> struct I8Lay {
+    static constexpr int kRowChunks = D / 16;
+    static constexpr int kRowsPerLoad = 64 / kRowChunks;
+    static constexpr int kLoads = kStep / kRowsPerLoad;
+};
+
+// 16 signed bytes -> 16 elements of the MFMA type, exactly.
+template <bool kBf16>
+__device__ __forceinline__ void widen_i8(uint4 raw, i16x8& lo, i16x8& hi) {
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+    uint32_t out[8];
+    if (kBf16) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float f0 = static_cast<float>(static_cast<int8_t>(w[i] & 0xffu));
+            const float f1 = static_cast<float>(static_cast<int8_t>((w[i] >> 8) & 0xffu));
+            const float f2 = static_cast<float>(static_cast<int8_t>((w[i] >> 16) & 0xffu));
+            const float f3 = static_cast<float>(static_cast<int8_t>(w[i] >> 24));
+            out[2 * i] = Mma<true>::pack_out(f0, f1);
+            out[2 * i + 1] = Mma<true>::pack_out(f2, f3);
+        }
+    } else {
+        // fp16 0x6400 | u is 1024 + u for a byte u; u = x + 128 (x ^ 0x80),
+        // then one packed subtract of 1152 gives x.
+        const f16x2 bias = {static_cast<_Float16>(1152.f), static_cast<_Float16>(1152.f)};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t u = w[i] ^ 0x80808080u;
+            const uint32_t a = 0x64006400u | (u & 0x000000ffu) | ((u & 0x0000ff00u) << 8);
+            const uint32_t b = 0x64006400u | ((u >> 16) & 0x000000ffu) | ((u >> 8) & 0x00ff0000u);
+            out[2 * i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, a) - bias);
+            out[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, b) - bias);
+        }
+    }
+    lo = __builtin_bit_cast(i16x8, (uint4){out[0], out[1], out[2], out[3]});
+    hi = __builtin_bit_cast(i16x8, (uint4){out[4], out[5], out[6], out[7]});
+}
 
 // Partial record of one (slot, head): [m, l, -, -, acc[0..D)], floats.
 __host__ __device__ constexpr int rec_stride(int D) { return D + 4; }
@@ -109,7 +156,7 @@ __device__ __forceinline__ int owner_wave(int64_t x, int64_t S) {
     return static_cast<int>(((x + 1) * kWavesTotal - 1) / S);
 }
 
-template <bool kBf16, int D, bool kCap>
+template <bool kBf16, int D, bool kCap, bool kI8>
 __global__ __launch_bounds__(64) void decode_split_kernel(Params p, int n_hgrp, int slot_heads) {
     using M = Mma<kBf16>;
     using LY = DLay<D>;
@@ -140,13 +187,17 @@ __global__ __launch_bounds__(64) void decode_split_kernel(Params p, int n_hgrp, 
     int64_t ls = (a - base_b) % sb;                 // step within the unit
 
     const int col = lane & 15, q4 = lane >> 4;
-    const int ld_row = lane / LY::kRowChunks;
-    const int ld_col = (lane % LY::kRowChunks) * 8;
-    const float c = p.scale_log2;
+    using L8 = I8Lay<D>;
+    const int ld_row = kI8 ? lane / L8::kRowChunks : lane / LY::kRowChunks;
+    const int ld_col = kI8 ? (lane % L8::kRowChunks) * 16 : (lane % LY::kRowChunks) * 8;
+    // Raw scores are q.k with the K integers; a per-tensor K scale joins c.
+    const float kscale = (kI8 && p.k_quant == 1) ? p.k_scale[0] : 1.f;
+    const bool k_chan = kI8 && p.k_quant == 2;
+    const float c = p.scale_log2 * kscale;
     const float slack = kSlack / c;
     const float inv_scale = kLog2e / c;
-    const float cap_k2 = kCap ? 2.f * kLog2e * p.scale / p.softcap : 0.f;
-    const float cap_back = kCap ? p.softcap / p.scale : 0.f;
+    const float cap_k2 = kCap ? 2.f * kLog2e * p.scale * kscale / p.softcap : 0.f;
+    const float cap_back = kCap ? p.softcap / (p.scale * kscale) : 0.f;
 
     // Per-unit state (wave-uniform: b, uu, live range; per-lane: the head).
     int h = 0;
@@ -168,7 +219,29 @@ __global__ __launch_bounds__(64) void decode_split_kernel(Params p, int n_hgrp, 
         const uint16_t* src = static_cast<const uint16_t*>(p.q) + b * p.qs.sb + h * p.qs.sh + 8 * q4;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            const i16x8 v = *reinterpret_cast<const i16x8*>(src + 32 * t);
+            i16x8 v = *reinterpret_cast<const i16x8*>(src + 32 * t);
+            if (k_chan) {   // q_d * k_scale[g, d], rounded to the element type
+                const float* ks = p.k_scale + g * D + 32 * t + 8 * q4;
+                const uint4 u = __builtin_bit_cast(uint4, v);
+                const uint32_t in[4] = {u.x, u.y, u.z, u.w};
+                uint32_t w[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    // Elements 2e (low half) and 2e + 1 (high half) of the word.
+                    const uint16_t b0 = static_cast<uint16_t>(in[e] & 0xffffu);
+                    const uint16_t b1 = static_cast<uint16_t>(in[e] >> 16);
+                    float x0, x1;
+                    if (kBf16) {
+                        x0 = __uint_as_float(static_cast<uint32_t>(b0) << 16);
+                        x1 = __uint_as_float(static_cast<uint32_t>(b1) << 16);
+                    } else {
+                        x0 = static_cast<float>(__builtin_bit_cast(_Float16, b0));
+                        x1 = static_cast<float>(__builtin_bit_cast(_Float16, b1));
+                    }
+                    w[e] = M::pack_out(x0 * ks[2 * e], x1 * ks[2 * e + 1]);
+                }
+                v = __builtin_bit_cast(i16x8, (uint4){w[0], w[1], w[2], w[3]});
+            }
             qop[t] = live_col ? v : i16x8{};
         }
         mrow = (p.mask && live_col) ? p.mask + b * p.ms.sb + h * p.ms.sh + kv_lo : nullptr;
@@ -195,22 +268,25 @@ __global__ __launch_bounds__(64) void decode_split_kernel(Params p, int n_hgrp, 
     };
 
     // Prefetch of one step, given the (entry, unit, step-in-unit) of that step.
-    i16x8 kst[LY::kLoads], vst[LY::kLoads];
+    constexpr int kEs = kI8 ? 1 : 2;                          // cache bytes per element
+    constexpr int kLd = kI8 ? L8::kLoads : LY::kLoads;
+    constexpr int kRpl = kI8 ? L8::kRowsPerLoad : LY::kRowsPerLoad;
+    i16x8 kst[kLd], vst[kLd];
     auto fetch = [&](int fb, int fuu, int64_t fls) {
         const int fg = fuu / n_hgrp;
         const LiveRange lr = live_range(p, fb);
-        const uint16_t* kg =
-            static_cast<const uint16_t*>(p.k) + fb * p.ks.sb + fg * p.ks.sh + lr.lo * p.ks.sr;
-        const uint16_t* vg =
-            static_cast<const uint16_t*>(p.v) + fb * p.vs.sb + fg * p.vs.sh + lr.lo * p.vs.sr;
-        const __amdgpu_buffer_rsrc_t krs = make_rsrc(kg, lr.n * p.ks.sr * 2);
-        const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vg, lr.n * p.vs.sr * 2);
+        const uint8_t* kg = static_cast<const uint8_t*>(p.k) +
+                            (fb * p.ks.sb + fg * p.ks.sh + lr.lo * p.ks.sr) * kEs;
+        const uint8_t* vg = static_cast<const uint8_t*>(p.v) +
+                            (fb * p.vs.sb + fg * p.vs.sh + lr.lo * p.vs.sr) * kEs;
+        const __amdgpu_buffer_rsrc_t krs = make_rsrc(kg, lr.n * p.ks.sr * kEs);
+        const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vg, lr.n * p.vs.sr * kEs);
         const int j0 = static_cast<int>(fls) * kStep + ld_row;
 #pragma unroll
-        for (int n = 0; n < LY::kLoads; ++n) {
-            const int key = j0 + n * LY::kRowsPerLoad;
-            kst[n] = load16(krs, (key * static_cast<int>(p.ks.sr) + ld_col) * 2);
-            vst[n] = load16(vrs, (key * static_cast<int>(p.vs.sr) + ld_col) * 2);
+        for (int n = 0; n < kLd; ++n) {
+            const int key = j0 + n * kRpl;
+            kst[n] = load16(krs, (key * static_cast<int>(p.ks.sr) + ld_col) * kEs);
+            vst[n] = load16(vrs, (key * static_cast<int>(p.vs.sr) + ld_col) * kEs);
         }
     };
 
@@ -232,10 +308,20 @@ __global__ __launch_bounds__(64) void decode_split_kernel(Params p, int n_hgrp, 
         // The previous step's LDS reads precede these writes in this wave's
         // in-order LDS queue, so one buffer suffices.
 #pragma unroll
-        for (int n = 0; n < LY::kLoads; ++n) {
-            const int row = n * LY::kRowsPerLoad + ld_row;
-            *reinterpret_cast<i16x8*>(&k_sh[row * KS + ld_col]) = kst[n];
-            *reinterpret_cast<i16x8*>(&v_sh[row * VS + ld_col]) = vst[n];
+        for (int n = 0; n < kLd; ++n) {
+            const int row = n * kRpl + ld_row;
+            if (kI8) {
+                i16x8 a0, a1, b0, b1;
+                widen_i8<kBf16>(__builtin_bit_cast(uint4, kst[n]), a0, a1);
+                widen_i8<kBf16>(__builtin_bit_cast(uint4, vst[n]), b0, b1);
+                *reinterpret_cast<i16x8*>(&k_sh[row * KS + ld_col]) = a0;
+                *reinterpret_cast<i16x8*>(&k_sh[row * KS + ld_col + 8]) = a1;
+                *reinterpret_cast<i16x8*>(&v_sh[row * VS + ld_col]) = b0;
+                *reinterpret_cast<i16x8*>(&v_sh[row * VS + ld_col + 8]) = b1;
+            } else {
+                *reinterpret_cast<i16x8*>(&k_sh[row * KS + ld_col]) = kst[n];
+                *reinterpret_cast<i16x8*>(&v_sh[row * VS + ld_col]) = vst[n];
+            }
         }
         if (x + 1 < e) fetch(nb, nuu, nls);
         const int64_t j0 = ls * kStep;
@@ -342,6 +428,9 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(Params p, int n_hgr
     const int64_t unit = static_cast<int64_t>(b) * per_b + uu;
     const int64_t first = steps_before(p, b, per_b) + uu * sb;   // first step of the unit
     constexpr int NPL = (D + 63) / 64;
+    // Records are in raw-score units: with a per-tensor int8 K scale, c
+    // carries it (as in the split kernel).
+    const float c = p.scale_log2 * ((p.kv_int8 && p.k_quant == 1) ? p.k_scale[0] : 1.f);
     float M = kNegInf, L = 0.f, A[NPL];
 #pragma unroll
     for (int cc = 0; cc < NPL; ++cc) A[cc] = 0.f;
@@ -358,7 +447,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(Params p, int n_hgr
         for (int w = w_lo; w <= w_hi; ++w) {
             if (empty_share(w)) continue;
             const float* r = base + ((unit + w) * slot_heads + col) * rs;
-            const float f = (r[0] == kNegInf) ? 0.f : fast_exp2((r[0] - M) * p.scale_log2);
+            const float f = (r[0] == kNegInf) ? 0.f : fast_exp2((r[0] - M) * c);
             L = fmaf(r[1], f, L);
 #pragma unroll
             for (int cc = 0; cc < NPL; ++cc) {
@@ -367,7 +456,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(Params p, int n_hgr
             }
         }
     }
-    float m2 = M * p.scale_log2;                 // base-2 reference (-inf stays -inf)
+    float m2 = M * c;                            // base-2 reference (-inf stays -inf)
     const float fs = fold_sink(p, h, m2, L);
     const bool empty = (L == 0.f);
     const float inv = fs / L;
@@ -376,7 +465,9 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(Params p, int n_hgr
     for (int cc = 0; cc < NPL; ++cc) {
         const int d = lane + 64 * cc;
         if (d < D) {
-            const float o = empty ? (p.masked_zero ? 0.f : __builtin_nanf("")) : A[cc] * inv;
+            // An int8 V scale factors out of the sum over keys.
+            const float vsc = !p.kv_int8 ? 1.f : (p.v_quant == 1 ? p.v_scale[0] : p.v_scale[g * D + d]);
+            const float o = empty ? (p.masked_zero ? 0.f : __builtin_nanf("")) : A[cc] * vsc * inv;
             Elem<T>::store(p.o, orow + d, o);
         }
     }
@@ -391,12 +482,16 @@ int heads_per_slot(int group) { return group < 16 ? group : 16; }
 template <bool kBf16, int D>
 hipError_t launch_one(const Params& p, hipStream_t s) {
     const int n_hgrp = slice_count(p.group), hs = heads_per_slot(p.group);
-    if (p.softcap > 0.f)
-        hipLaunchKernelGGL((decode_split_kernel<kBf16, D, true>), dim3(kWavesTotal), dim3(64), 0, s,
-                           p, n_hgrp, hs);
+    const dim3 g(kWavesTotal), blk(64);
+    const bool cap = p.softcap > 0.f;
+    if (p.kv_int8 && cap)
+        hipLaunchKernelGGL((decode_split_kernel<kBf16, D, true, true>), g, blk, 0, s, p, n_hgrp, hs);
+    else if (p.kv_int8)
+        hipLaunchKernelGGL((decode_split_kernel<kBf16, D, false, true>), g, blk, 0, s, p, n_hgrp, hs);
+    else if (cap)
+        hipLaunchKernelGGL((decode_split_kernel<kBf16, D, true, false>), g, blk, 0, s, p, n_hgrp, hs);
     else
-        hipLaunchKernelGGL((decode_split_kernel<kBf16, D, false>), dim3(kWavesTotal), dim3(64), 0,
-                           s, p, n_hgrp, hs);
+        hipLaunchKernelGGL((decode_split_kernel<kBf16, D, false, false>), g, blk, 0, s, p, n_hgrp, hs);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t rows = static_cast<int64_t>(p.B) * p.Hq;
@@ -432,6 +527,13 @@ bool decode_split_supported(const Params& p, DType dt) {
         return reinterpret_cast<uintptr_t>(ptr) % (2 * a) == 0 && st.sb % a == 0 &&
                st.sh % a == 0 && st.sr % a == 0;
     };
+    if (p.kv_int8) {   // 16-byte loads of 16 int8 values
+        auto al8 = [](const void* ptr, const Strides& st) {
+            return reinterpret_cast<uintptr_t>(ptr) % 16 == 0 && st.sb % 16 == 0 &&
+                   st.sh % 16 == 0 && st.sr % 16 == 0;
+        };
+        return al(p.q, p.qs, 8) && al8(p.k, p.ks) && al8(p.v, p.vs);
+    }
     return al(p.q, p.qs, 8) && al(p.k, p.ks, 8) && al(p.v, p.vs, 8);
 }
 

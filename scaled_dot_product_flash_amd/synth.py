@@ -6,9 +6,12 @@ from it, so the two sides see identical bits.
 
 Recipe (the same for every workload): numpy PCG64 ``default_rng(seed)``;
 draw order Q, K, V, then key lengths, then the mask, then per-head sink
-scores; values are i.i.d. N(0, 1) in float32 (sink scores 2 * N(0, 1)),
-rounded to nearest-even into the storage type (float16 via numpy, bfloat16
-by bit rounding, kept as uint16 bit patterns).
+scores, then int8-cache scales; values are i.i.d. N(0, 1) in float32 (sink
+scores 2 * N(0, 1)), rounded to nearest-even into the storage type (float16
+via numpy, bfloat16 by bit rounding, kept as uint16 bit patterns).  An int8
+cache keeps K and V as float32 draws and quantizes them at the end: scale
+4/127 per tensor, or (0.5 + U[0, 1)) * 4/127 per (kv head, head-dim)
+channel; value = clip(round_half_even(x / scale), -127, 127).
 """
 from __future__ import annotations
 
@@ -55,6 +58,8 @@ class Spec:
     local_window: int = -1            # -1, or keys left of each causal row's position
     softcap: float = 0.0              # 0, or c > 0
     sink: Optional[str] = None        # None, 'zero' (smooth softmax) or 'heads' (drawn)
+    kv_quant: Optional[str] = None    # int8 cache: None, 'tensor', 'channel' or 'mixed'
+                                      # ('mixed': K per tensor, V per channel)
 
     def replace(self, **kw) -> "Spec":
         return dataclasses.replace(self, **kw)
@@ -103,12 +108,18 @@ DECODE_WINDOW_F16 = DECODE_F16.replace(
     name="fp16 decode B64 H32/8 cache8192 D128, local window 2047, head sinks",
     local_window=2047, sink="heads", seed=9)
 
+# The decode workload with an int8 cache and per-channel scales.
+DECODE_INT8_F16 = DECODE_F16.replace(
+    name="fp16 decode B64 H32/8 cache8192 D128, int8 cache, per-channel scales",
+    kv_quant="channel", seed=10)
+
 # Workloads of the extensions beyond the five (measured and tested the same way).
 EXTRA_WORKLOADS = {
     "chunk_f16": CHUNK_F16,
     "window_bf16": WINDOW_BF16,
     "softcap_sink_bf16": SOFTCAP_SINK_BF16,
     "decode_window_f16": DECODE_WINDOW_F16,
+    "decode_int8_f16": DECODE_INT8_F16,
 }
 
 
@@ -154,6 +165,8 @@ class Case:
     key_lens: Optional[np.ndarray]
     mask: Optional[np.ndarray]
     head_sink: Optional[np.ndarray] = None
+    k_scale: Optional[np.ndarray] = None
+    v_scale: Optional[np.ndarray] = None
 
 
 def _normal(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
@@ -169,8 +182,9 @@ def _normal(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
 def generate(spec: Spec) -> Case:
     rng = np.random.default_rng(spec.seed)
     q = _normal(rng, shape_of(spec, "q"), spec.dtype)
-    k = _normal(rng, shape_of(spec, "k"), spec.dtype)
-    v = _normal(rng, shape_of(spec, "v"), spec.dtype)
+    kv_dtype = "f32" if spec.kv_quant else spec.dtype
+    k = _normal(rng, shape_of(spec, "k"), kv_dtype)
+    v = _normal(rng, shape_of(spec, "v"), kv_dtype)
     lens = None
     if spec.lens == "uniform":
         lens = rng.integers(1, spec.k_len + 1, size=spec.batch).astype(np.int32)
@@ -199,4 +213,26 @@ def generate(spec: Spec) -> Case:
         head_sink = (2.0 * rng.standard_normal(spec.q_heads, dtype=np.float32)).astype(np.float32)
     elif spec.sink not in (None, "zero"):
         raise ValueError(spec.sink)
-    return Case(spec, q, k, v, lens, mask, head_sink)
+    k_scale = v_scale = None
+    if spec.kv_quant:
+        if spec.kv_quant not in ("tensor", "channel", "mixed"):
+            raise ValueError(spec.kv_quant)
+        base = np.float32(4.0 / 127.0)
+        n_ch = spec.kv_heads * spec.head_dim
+        chan = ((0.5 + rng.random(2 * n_ch, dtype=np.float32)) * base).astype(np.float32)
+        k_scale = (np.array([base], np.float32) if spec.kv_quant in ("tensor", "mixed")
+                   else chan[:n_ch])
+        v_scale = np.array([base], np.float32) if spec.kv_quant == "tensor" else chan[n_ch:]
+        k = _quantize(k, k_scale, spec)
+        v = _quantize(v, v_scale, spec)
+    return Case(spec, q, k, v, lens, mask, head_sink, k_scale, v_scale)
+
+
+def _quantize(x: np.ndarray, scale: np.ndarray, spec: Spec) -> np.ndarray:
+    """float32 cache -> int8 codes with a per-tensor or per-channel scale."""
+    if scale.size == 1:
+        s = scale[0]
+    else:
+        s = scale.reshape(spec.kv_heads, spec.head_dim)
+        s = s[None, None] if spec.kv_layout == "bshd" else s[None, :, None, :]
+    return np.clip(np.rint(x / s), -127, 127).astype(np.int8)

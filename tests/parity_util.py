@@ -27,6 +27,8 @@ def torch_mod():
 
 def to_dev(a: np.ndarray, dtype: str):
     torch = torch_mod()
+    if a.dtype == np.int8:
+        return torch.from_numpy(a).to("cuda")
     if dtype == "bf16":
         t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)
     else:
@@ -55,11 +57,15 @@ def run_hip(case: synth.Case, policy: str = "nan", *, return_lse=None, tensors=N
                        sink=None if case.head_sink is None else torch.from_numpy(case.head_sink).cuda())
     var = dict(local_window=s.local_window, softcap=s.softcap, sink=s.sink is not None,
                head_sink=tensors.get("sink"))
+    dvar = {}
+    if case.k_scale is not None:
+        dvar = dict(k_scale=torch.from_numpy(case.k_scale).cuda(),
+                    v_scale=torch.from_numpy(case.v_scale).cuda())
     want_lse = s.lse if return_lse is None else return_lse
     if s.decode:
         r = sdpa.decode(tensors["q"], tensors["k"], tensors["v"], tensors["lens"],
                         layout=s.q_layout, kv_layout=s.kv_layout, mask=tensors["mask"],
-                        masked_rows=policy, return_lse=want_lse, **var)
+                        masked_rows=policy, return_lse=want_lse, **var, **dvar)
     else:
         r = sdpa.forward(tensors["q"], tensors["k"], tensors["v"], layout=s.q_layout,
                          kv_layout=s.kv_layout, causal=s.causal, causal_offset=s.causal_offset,
@@ -80,7 +86,8 @@ def run_oracle(case: synth.Case, policy: str = "nan", rows=None):
                             kv_layout=s.kv_layout, causal=s.causal, causal_offset=off,
                             mask=case.mask, key_lens=case.key_lens, masked_rows=policy,
                             window=s.local_window, softcap=s.softcap, sink=s.sink is not None,
-                            head_sink=case.head_sink, rows=rows)
+                            head_sink=case.head_sink, k_scale=case.k_scale,
+                            v_scale=case.v_scale, rows=rows)
 
 
 def compare(gpu_o, ref_o, gpu_lse, ref_lse, dtype: str, policy: str, what: str = ""):

@@ -187,3 +187,17 @@ def test_offset_sentinels_match_c(tmp_path):
                            "-o", str(exe)])
     d, e = map(int, subprocess.check_output([str(exe)]).split())
     assert (d, e) == (sdpa.CAUSAL_OFFSET_DEFAULT, sdpa.CAUSAL_OFFSET_KEY_END)
+
+
+def test_int8_cache_is_decode_only_and_checked():
+    lib = sdpa.load_library()
+    p = _problem(kv_int8=1, k_quant=1, v_quant=2, k_scale=0x1000, v_scale=0x1000)
+    assert lib.attn_forward(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, None, None, None, 0,
+                            None) == sdpa.ERR_UNSUPPORTED
+    for bad in (dict(kv_int8=1, k_quant=0, v_quant=1, k_scale=0x1000, v_scale=0x1000),
+                dict(kv_int8=1, k_quant=1, v_quant=1, k_scale=0x1000, v_scale=None),
+                dict(kv_int8=0, k_quant=1),
+                dict(kv_int8=2)):
+        p = _problem(**bad)
+        assert lib.attn_forward(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, None, None, None,
+                                0, None) == sdpa.ERR_INVALID

@@ -442,3 +442,38 @@ def test_variant_decode_full_size_every_row():
     assert sdpa.last_kernel() == "decode_splitk"
     ro, rl = pu.run_oracle(case, "nan")
     pu.compare(o, ro, lse, rl, spec.dtype, "nan", what=spec.name)
+
+
+# --------------------------------------------------------------------------
+# int8 key/value cache with float32 scales (decode).
+
+INT8 = {
+    "i8_tensor_f16": synth.DECODE_F16.replace(batch=8, k_len=1000, kv_quant="tensor", seed=31),
+    "i8_channel_bf16_D64": synth.DECODE_F16.replace(dtype="bf16", batch=8, k_len=777,
+                                                    head_dim=64, kv_quant="channel", seed=32),
+    "i8_mixed_window_cap_sink": synth.DECODE_F16.replace(
+        batch=8, k_len=900, kv_quant="mixed", local_window=300, softcap=20.0, sink="heads",
+        seed=33),
+    "i8_channel_lens0_mask": synth.DECODE_F16.replace(
+        batch=8, k_len=600, kv_quant="channel", lens="cross", lens_zero_at=2, lens_full_at=3,
+        mask="keys", mask_all_at=5, seed=34),
+}
+
+
+@pytest.mark.parametrize("name", sorted(INT8))
+@pytest.mark.parametrize("policy", ["nan", "zero"])
+def test_int8_cache_decode(name, policy):
+    spec = INT8[name]
+    case = synth.generate(spec)
+    o, lse, _ = pu.run_hip(case, policy, return_lse=True)
+    assert sdpa.last_kernel() == "decode_splitk_int8"
+    ro, rl = pu.run_oracle(case, policy)
+    pu.compare(o, ro, lse, rl, spec.dtype, policy, what=name)
+
+
+def test_int8_cache_decode_full_size_every_row():
+    spec = synth.EXTRA_WORKLOADS["decode_int8_f16"]
+    case = synth.generate(spec)
+    o, lse, _ = pu.run_hip(case, "nan", return_lse=True)
+    ro, rl = pu.run_oracle(case, "nan")
+    pu.compare(o, ro, lse, rl, spec.dtype, "nan", what=spec.name)
