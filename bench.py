@@ -203,6 +203,27 @@ def other_workloads(sdpa, synth, steps: int, warmup: int):
     kv_bytes = float(live.sum()) * spec.kv_heads * spec.head_dim * 2 * 2
     out.append({"workload": spec.name, "kernel": kern, "ms_per_call": round(ms, 5),
                 "gbs": round(kv_bytes / (ms * 1e-3) / 1e9, 1), "dtype": spec.dtype})
+    # Decode against an int8 cache: GB/s of int8 K/V bytes read (1 byte each).
+    spec = synth.EXTRA_WORKLOADS["decode_int8_f16"]
+    case = synth.generate(spec)
+    q = to_dev(case.q, spec.dtype)
+    k = torch.from_numpy(case.k).cuda()
+    v = torch.from_numpy(case.v).cuda()
+    lens = torch.from_numpy(case.key_lens).cuda()
+    ks = torch.from_numpy(case.k_scale).cuda()
+    vs = torch.from_numpy(case.v_scale).cuda()
+    o = torch.empty_like(q)
+
+    def h():
+        sdpa.decode(q, k, v, lens, kv_layout=spec.kv_layout, k_scale=ks, v_scale=vs, out=o)
+    h()
+    kern = sdpa.last_kernel()
+    durs, _ = time_calls(h, steps, warmup, settle_s=0.3)
+    ms = float(np.mean(durs))
+    kv_bytes = float(case.key_lens.astype(np.float64).sum()) * spec.kv_heads * spec.head_dim * 2
+    out.append({"workload": spec.name, "kernel": kern, "ms_per_call": round(ms, 5),
+                "gbs": round(kv_bytes / (ms * 1e-3) / 1e9, 1),
+                "fp16_equiv_gbs": round(2 * kv_bytes / (ms * 1e-3) / 1e9, 1), "dtype": "f16/i8"})
     return out
 
 
