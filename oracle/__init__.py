@@ -74,7 +74,7 @@ def _load():
         lib.oracle_attention.argtypes = [
             ctypes.POINTER(_Problem), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
-            ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
             ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
         lib.oracle_decode_f16.restype = ctypes.c_double
         lib.oracle_decode_f16.argtypes = [ctypes.c_uint16]
@@ -122,6 +122,7 @@ def attention(q, k, v, *, dtype: str, layout: str = "bshd", kv_layout: str | Non
               window: int = -1, softcap: float = 0.0, sink: bool = False,
               head_sink: np.ndarray | None = None,
               k_scale: np.ndarray | None = None, v_scale: np.ndarray | None = None,
+              doc_start: np.ndarray | None = None,
               rows: np.ndarray | None = None, threads: int = 0):
     """Reference attention in float64.
 
@@ -139,6 +140,8 @@ def attention(q, k, v, *, dtype: str, layout: str = "bshd", kv_layout: str | Non
     k, v may be int8 (a quantized cache); then k_scale / v_scale are float32
     of size 1 (per tensor) or Hkv * D (per channel, index g * D + d) and an
     element's value is the integer times its scale.
+    doc_start: int32 [B, Lq] or None: row i of entry b sees only keys
+    j >= doc_start[b, i] (its document's first key).
     rows: optional int64 [n, 3] of (b, h, i) to compute; default every row.
 
     Returns (O, LSE): O is [B, Hq, Lq, D] (or [n, D] with ``rows``) float64,
@@ -221,6 +224,13 @@ def attention(q, k, v, *, dtype: str, layout: str = "bshd", kv_layout: str | Non
             raise ValueError("head_sink must be float32 [Hq]")
         keep.append(head_sink)
         sink_ptr = head_sink.ctypes.data
+    doc_ptr = None
+    if doc_start is not None:
+        doc_start = np.ascontiguousarray(doc_start, dtype=np.int32)
+        if doc_start.shape != (B, Lq):
+            raise ValueError("doc_start must be int32 [B, Lq]")
+        keep.append(doc_start)
+        doc_ptr = doc_start.ctypes.data
     if rows is None:
         n = B * Hq * Lq
         rows_ptr = None
@@ -236,7 +246,7 @@ def attention(q, k, v, *, dtype: str, layout: str = "bshd", kv_layout: str | Non
     lse = np.empty((n,), dtype=np.float64)
     rc = _load().oracle_attention(ctypes.byref(p), q.ctypes.data, k.ctypes.data, v.ctypes.data,
                                   mask_ptr, lens_ptr, sink_ptr, scale_ptrs[0], scale_ptrs[1],
-                                  rows_ptr, n, o.ctypes.data,
+                                  doc_ptr, rows_ptr, n, o.ctypes.data,
                                   lse.ctypes.data, int(threads))
     if rc != 0:
         raise RuntimeError("oracle rejected the problem")

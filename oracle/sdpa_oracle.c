@@ -51,6 +51,11 @@
  *     LSE = sink_h under both policies; a NaN / +inf score, the sink's own
  *     included, still gives NaN.
  *
+ * Document masks (llm.istanbul "05_attention", line-by-line steps "Phase 0"
+ * and "K-block iteration"): packed documents give each query row the index
+ * of its document's first key, doc_start[b * Lq + i]; keys before it are
+ * hidden (row i sees j >= doc_start, together with the other rules).
+ *
  * Quantized key/value cache (ONNX GroupQueryAttention README, "Inputs":
  * k_scale / v_scale; "Attributes": k_quant_type / v_quant_type, cache bit
  * width 8): a cache element is a signed 8-bit integer and its value is that
@@ -144,7 +149,7 @@ static double load_kv(const oracle_problem* p, const void* base, const float* sc
 /* One query row (b, h, i).  s is scratch of k_len doubles. */
 static void one_row(const oracle_problem* p, const void* q, const void* k, const void* v,
                     const float* mask, const int32_t* key_lens, const float* head_sink,
-                    const float* k_scale, const float* v_scale,
+                    const float* k_scale, const float* v_scale, const int32_t* doc_start,
                     int64_t b, int64_t h, int64_t i, double* s, unsigned char* vis,
                     double* o_row, double* lse_out)
 {
@@ -163,10 +168,11 @@ static void one_row(const oracle_problem* p, const void* q, const void* k, const
                                                : p->k_len - p->q_len;
 
     const int64_t qbase = b * p->qs[0] + h * p->qs[1] + i * p->qs[2];
+    const int64_t first_key = doc_start ? (int64_t)doc_start[b * p->q_len + i] : 0;
 
     /* Scores of the visible keys. */
     for (int64_t j = 0; j < p->k_len; ++j) {
-        vis[j] = (j < kv_len) &&
+        vis[j] = (j < kv_len) && j >= first_key &&
                  (!p->causal || (j <= i + delta && (p->window < 0 || j >= i + delta - p->window)));
         if (!vis[j])
             continue;
@@ -241,7 +247,7 @@ static void one_row(const oracle_problem* p, const void* q, const void* k, const
  */
 int oracle_attention(const oracle_problem* p, const void* q, const void* k, const void* v,
                      const float* mask, const int32_t* key_lens, const float* head_sink,
-                     const float* k_scale, const float* v_scale,
+                     const float* k_scale, const float* v_scale, const int32_t* doc_start,
                      const int64_t* rows, int64_t n_rows, double* o, double* lse,
                      int n_threads)
 {
@@ -284,8 +290,8 @@ int oracle_attention(const oracle_problem* p, const void* q, const void* k, cons
                 i = r % p->q_len;
             }
             double lse_r;
-            one_row(p, q, k, v, mask, key_lens, head_sink, k_scale, v_scale, b, h, i, s, vis,
-                    o + r * p->head_dim, &lse_r);
+            one_row(p, q, k, v, mask, key_lens, head_sink, k_scale, v_scale, doc_start, b, h, i,
+                    s, vis, o + r * p->head_dim, &lse_r);
             if (lse)
                 lse[r] = lse_r;
         }

@@ -53,7 +53,7 @@ def _bhsd(a, layout):
 
 def _library_attention(q, k, v, dtype, layout="bshd", causal=False, offset=None, scale=None,
                        mask=None, key_lens=None, masked_rows="nan", window=-1, softcap=0.0,
-                       head_sink=None):
+                       head_sink=None, doc_start=None):
     """Independent float64 route: matmul + scipy softmax over an explicit
     visibility matrix.  Returns O [B,Hq,Lq,D] and LSE [B,Hq,Lq]."""
     Q = _bhsd(_as_f64(q, dtype), layout)
@@ -81,6 +81,8 @@ def _library_attention(q, k, v, dtype, layout="bshd", causal=False, offset=None,
                 vis &= np.arange(Lk)[None, :] <= pos
                 if window >= 0:
                     vis &= np.arange(Lk)[None, :] >= pos - window
+            if doc_start is not None:
+                vis &= np.arange(Lk)[None, :] >= np.asarray(doc_start)[b][:, None]
             for i in range(Lq):
                 s = S[i][vis[i]]
                 vals = V[b, g][vis[i]]
@@ -704,6 +706,80 @@ def test_int8_cache_against_library_route(cfg):
     kd = np.transpose(_dequant(k8, ks, "bhsd"), (0, 2, 1, 3))
     vd = np.transpose(_dequant(v8, vs, "bhsd"), (0, 2, 1, 3))
     o2, lse2 = _library_attention(q, kd, vd, dtype, causal=True, offset="end", key_lens=lens)
+    assert (np.isnan(o) == np.isnan(o2)).all()
+    fin = ~np.isnan(o)
+    assert np.abs(o[fin] - o2[fin]).max(initial=0) < 1e-12
+    with np.errstate(invalid="ignore"):
+        close = np.abs(lse - lse2) < 1e-11
+    assert ((lse == lse2) | close | (np.isnan(lse) & np.isnan(lse2))).all()
+
+
+# --------------------------------------------------------------------------
+# Document masks over packed documents (llm.istanbul "05_attention").
+
+def _packed_doc_start(doc_lens):
+    """doc_start per position of documents packed back to back."""
+    out = []
+    for start, n in zip(np.cumsum([0] + list(doc_lens[:-1])), doc_lens):
+        out += [int(start)] * int(n)
+    return np.array(out, np.int32)
+
+
+def test_doc_mask_visible_counts_golden():
+    table = [(int(r[0]), int(r[1]), int(r[2])) for r in _golden("doc_packed_l8.txt")]
+    seg = np.array([r[1] for r in table], np.int32)
+    assert (seg == _packed_doc_start([3, 2, 3])).all()
+    L, D = 8, 1
+    q = np.zeros((1, L, 1, D), np.float32)
+    k = _rand((1, L, 1, D), "f32", 81)
+    v = np.arange(1, L + 1, dtype=np.float32).reshape(1, L, 1, 1)
+    o, lse = oracle.attention(q, k, v, dtype="f32", causal=True, doc_start=seg[None])
+    for i, start, n in table:
+        assert lse[0, 0, i] == pytest.approx(math.log(n), abs=1e-15)
+        assert o[0, 0, i, 0] == pytest.approx(start + (n + 1) / 2, abs=1e-14)
+
+
+def test_doc_mask_equals_separate_documents():
+    """Packed documents with their starts give, row for row, the result of
+    attending within each document on its own."""
+    docs = [5, 1, 9, 3]
+    L, Hq, Hkv, D = sum(docs), 4, 2, 16
+    q = _rand((1, L, Hq, D), "bf16", 82)
+    k = _rand((1, L, Hkv, D), "bf16", 83)
+    v = _rand((1, L, Hkv, D), "bf16", 84)
+    seg = _packed_doc_start(docs)[None]
+    o, lse = oracle.attention(q, k, v, dtype="bf16", causal=True, doc_start=seg)
+    start = 0
+    for n in docs:
+        sl = slice(start, start + n)
+        o1, l1 = oracle.attention(*(np.ascontiguousarray(x[:, sl]) for x in (q, k, v)),
+                                  dtype="bf16", causal=True)
+        assert (o[:, :, sl] == o1).all() and (lse[:, :, sl] == l1).all()
+        start += n
+
+
+DOC_CASES = [
+    # B, Hq, Hkv, L, D, dtype, window, lens
+    (2, 4, 2, 40, 16, "f16", -1, False),
+    (1, 2, 1, 64, 32, "bf16", 7, False),
+    (3, 3, 3, 25, 8, "f32", -1, True),
+]
+
+
+@pytest.mark.parametrize("cfg", DOC_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_doc_mask_against_library_route(cfg):
+    B, Hq, Hkv, L, D, dtype, window, use_lens = cfg
+    seed = zlib.crc32(repr(cfg).encode()) % 1000
+    rng = np.random.default_rng(seed)
+    q = _rand((B, L, Hq, D), dtype, seed)
+    k = _rand((B, L, Hkv, D), dtype, seed + 1)
+    v = _rand((B, L, Hkv, D), dtype, seed + 2)
+    seg = np.stack([_packed_doc_start(rng.multinomial(L, [0.25] * 4)) for _ in range(B)])
+    lens = rng.integers(0, L + 1, size=B).astype(np.int32) if use_lens else None
+    o, lse = oracle.attention(q, k, v, dtype=dtype, causal=True, doc_start=seg, key_lens=lens,
+                              window=window)
+    o2, lse2 = _library_attention(q, k, v, dtype, causal=True, doc_start=seg, key_lens=lens,
+                                  window=window)
     assert (np.isnan(o) == np.isnan(o2)).all()
     fin = ~np.isnan(o)
     assert np.abs(o[fin] - o2[fin]).max(initial=0) < 1e-12

@@ -54,6 +54,10 @@ MUTANTS = {
     "channel_scale_transposed": ("scale[g * p->head_dim + d]", "scale[d * p->kv_heads + g]"),
     "v_uses_k_scale": ("load_kv(p, v, v_scale, p->v_quant", "load_kv(p, v, k_scale, p->k_quant"),
     "int8_unscaled": ("return x * (double)(quant == 1", "return x * 1.0 + 0.0 * (double)(quant == 1"),
+    "doc_start_strict": ("j >= first_key", "j > first_key"),
+    "doc_start_ignored": ("doc_start ? (int64_t)doc_start[b * p->q_len + i] : 0",
+                          "doc_start ? 0 * (int64_t)doc_start[0] : 0"),
+    "doc_start_wrong_row": ("doc_start[b * p->q_len + i]", "doc_start[b * p->q_len]"),
     "key_lengths_ignored": ("kv_len = L < 0 ? 0 : (L > p->k_len ? p->k_len : L);",
                             "kv_len = p->k_len; (void)L;"),
 }
@@ -87,7 +91,9 @@ CHECKS = [
      for c in pins.BRUTE_VARIANTS] \
   + [lambda: pins.test_int8_cache_equals_exact_float_cache(True),
      lambda: pins.test_int8_cache_equals_exact_float_cache(False)] \
-  + [(lambda c=c: pins.test_int8_cache_against_library_route(c)) for c in pins.INT8_CASES]
+  + [(lambda c=c: pins.test_int8_cache_against_library_route(c)) for c in pins.INT8_CASES] \
+  + [pins.test_doc_mask_visible_counts_golden, pins.test_doc_mask_equals_separate_documents] \
+  + [(lambda c=c: pins.test_doc_mask_against_library_route(c)) for c in pins.DOC_CASES]
 
 
 def _any_check_fails():
