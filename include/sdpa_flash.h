@@ -159,6 +159,12 @@ typedef struct attn_problem {
     int32_t v_quant;
     const float* k_scale;
     const float* v_scale;
+    /* Document mask (llm.istanbul "05_attention", line-by-line steps "Phase
+     * 0" and "K-block iteration"): NULL, or device int32[batch * q_len] whose
+     * element b * q_len + i is the first key of the document holding query
+     * row i; keys before it are hidden for that row (with every other rule).
+     * Blocks of keys below a block's first document start are skipped.       */
+    const int32_t* doc_start;
 } attn_problem;
 
 /*

@@ -60,6 +60,7 @@ class Problem(ctypes.Structure):
         ("sink", ctypes.c_int32), ("head_sink", ctypes.c_void_p),
         ("kv_int8", ctypes.c_int32), ("k_quant", ctypes.c_int32), ("v_quant", ctypes.c_int32),
         ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+        ("doc_start", ctypes.c_void_p),
     ]
 
 
@@ -157,7 +158,7 @@ def _ptr(t):
 def _run(op: int, q, k, v, *, layout: str, kv_layout: str | None, causal: bool,
          causal_offset, scale, mask, key_lens, masked_rows: str, return_lse: bool,
          local_window: int = -1, softcap: float = 0.0, sink: bool = False, head_sink=None,
-         k_scale=None, v_scale=None, out=None, stream=None):
+         k_scale=None, v_scale=None, doc_start=None, out=None, stream=None):
     torch = _torch()
     kv_layout = kv_layout or layout
     if not (q.is_cuda and k.is_cuda and v.is_cuda):
@@ -198,6 +199,12 @@ def _run(op: int, q, k, v, *, layout: str, kv_layout: str | None, causal: bool,
             raise TypeError("head_sink must be a float32 GPU tensor of shape [Hq]")
         head_sink = head_sink.contiguous()
         p.head_sink = head_sink.data_ptr()
+    if doc_start is not None:
+        if (doc_start.dtype != torch.int32 or not doc_start.is_cuda
+                or doc_start.numel() != B * Lq):
+            raise TypeError("doc_start must be an int32 GPU tensor of B*Lq values")
+        doc_start = doc_start.contiguous()
+        p.doc_start = doc_start.data_ptr()
     if kv_int8:
         p.kv_int8 = 1
         modes = []
@@ -251,7 +258,7 @@ def forward(q, k, v, *, layout: str = "bshd", kv_layout: str | None = None,
             causal: bool = False, causal_offset: int | str | None = None,
             scale: float | None = None, mask=None, key_lens=None, masked_rows: str = "nan",
             return_lse: bool = False, local_window: int = -1, softcap: float = 0.0,
-            sink: bool = False, head_sink=None, out=None, stream=None):
+            sink: bool = False, head_sink=None, doc_start=None, out=None, stream=None):
     """Fused attention.  q: [B, Lq, Hq, D] ('bshd') or [B, Hq, Lq, D] ('bhsd');
     k, v likewise in ``kv_layout`` (default ``layout``).  Returns O in q's layout
     (and the float32 LSE [B, Hq, Lq] with ``return_lse``).
@@ -261,18 +268,21 @@ def forward(q, k, v, *, layout: str = "bshd", kv_layout: str | None = None,
     local_window: -1, or L >= 0 keys left of each causal row's position.
     softcap: 0, or c > 0 (scaled score -> c*tanh(score/c) before the mask).
     sink: add exp(head_sink[h]) (float32 GPU [Hq]; 0 when None) to each
-    row's softmax denominator."""
+    row's softmax denominator.
+    doc_start: int32 GPU [B, Lq]: row i of entry b sees only keys
+    j >= doc_start[b, i] (packed documents)."""
     return _run(OP_FORWARD, q, k, v, layout=layout, kv_layout=kv_layout, causal=causal,
                 causal_offset=causal_offset, scale=scale, mask=mask, key_lens=key_lens,
                 masked_rows=masked_rows, return_lse=return_lse, local_window=local_window,
-                softcap=softcap, sink=sink, head_sink=head_sink, out=out, stream=stream)
+                softcap=softcap, sink=sink, head_sink=head_sink, doc_start=doc_start, out=out,
+                stream=stream)
 
 
 def decode(q, k_cache, v_cache, key_lens=None, *, layout: str = "bshd", kv_layout: str = "bhsd",
            scale: float | None = None, mask=None, masked_rows: str = "nan",
            return_lse: bool = False, local_window: int = -1, softcap: float = 0.0,
-           sink: bool = False, head_sink=None, k_scale=None, v_scale=None, out=None,
-           stream=None):
+           sink: bool = False, head_sink=None, k_scale=None, v_scale=None, doc_start=None,
+           out=None, stream=None):
     """One query row per (batch, head) against a K/V cache of capacity Lk with
     live lengths ``key_lens`` (int32 [B]).  The row is the newest position of
     its entry (end-aligned causal offset), so every live key is visible and a
@@ -283,4 +293,4 @@ def decode(q, k_cache, v_cache, key_lens=None, *, layout: str = "bshd", kv_layou
                 causal=True, causal_offset="end", scale=scale, mask=mask, key_lens=key_lens,
                 masked_rows=masked_rows, return_lse=return_lse, local_window=local_window,
                 softcap=softcap, sink=sink, head_sink=head_sink, k_scale=k_scale,
-                v_scale=v_scale, out=out, stream=stream)
+                v_scale=v_scale, doc_start=doc_start, out=out, stream=stream)

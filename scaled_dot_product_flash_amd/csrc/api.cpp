@@ -162,6 +162,7 @@ sdpa::Params make_params(const attn_problem* p, const void* q, const void* k, co
     r.v_quant = p->v_quant;
     r.k_scale = p->k_scale;
     r.v_scale = p->v_scale;
+    r.doc_start = p->doc_start;
     return r;
 }
 

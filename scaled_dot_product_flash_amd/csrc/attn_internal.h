@@ -41,6 +41,7 @@ struct Params {
     int32_t k_quant, v_quant;   // 1 per tensor, 2 per channel (g * D + d)
     const float* k_scale;
     const float* v_scale;
+    const int32_t* doc_start;   // nullable: per (b, i) first visible key
     int32_t n_split;       // key ranges per (b, h) for the fp32 split kernel
     int32_t split_len;     // keys per range (multiple of the tile)
 };

@@ -128,6 +128,10 @@ __device__ __forceinline__ LiveRange live_range(const Params& p, int b) {
         hi = bb < 0 ? 0 : (bb < kv ? bb : kv);
         lo = window_lo(p, 0, delta);
     }
+    if (p.doc_start) {               // the row's document start (q_len == 1)
+        const int64_t d = p.doc_start[b];
+        lo = d > lo ? d : lo;
+    }
     return {lo < hi ? lo : hi, lo < hi ? hi - lo : 0};
 }
 

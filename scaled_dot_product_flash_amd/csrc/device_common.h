@@ -65,6 +65,18 @@ __device__ __forceinline__ int64_t window_lo(const Params& p, int64_t i, int64_t
     return lo < 0 ? 0 : lo;
 }
 
+// First key row i of entry b may see under the window and the document
+// mask (llm.istanbul "05_attention": keys before the document start are
+// hidden); 0 without either.
+__device__ __forceinline__ int64_t first_key(const Params& p, int b, int64_t i, int64_t delta) {
+    int64_t lo = window_lo(p, i, delta);
+    if (p.doc_start) {
+        const int64_t d = p.doc_start[static_cast<int64_t>(b) * p.Lq + i];
+        lo = d > lo ? d : lo;
+    }
+    return lo;
+}
+
 // Softcap on a raw score s = q.k (before scaling): the scaled score becomes
 // c * tanh(scale * s / c), i.e. in raw units back * tanh(s * k2 / 2) with
 // k2 = 2 * log2(e) * scale / c and back = c / scale, through

@@ -38,7 +38,7 @@ __global__ __launch_bounds__(256) void generic_kernel(Params p) {
         const int64_t bound = i + delta + 1;   // keys j <= i + delta
         hi = bound < 0 ? 0 : (bound < hi ? bound : hi);
     }
-    const int64_t lo = window_lo(p, i, delta);   // and j >= lo under a local window
+    const int64_t lo = first_key(p, b, i, delta);   // and j >= lo (window, document)
 
     const int64_t qrow = b * p.qs.sb + h * p.qs.sh + i * p.qs.sr;
     for (int d = lane; d < D; d += 64) q_sh[w][d] = Elem<T>::load(p.q, qrow + d);

@@ -317,7 +317,7 @@ bool prefill_f32_supported(const Params& p, DType dt) {
     if (dt != DType::F32) return false;
     if (p.D != 32 && p.D != 64 && p.D != 128) return false;
     // Local window, softcap and sink run on the any-shape kernel for fp32.
-    if (p.window > 0 || p.softcap > 0.f || p.sink) return false;
+    if (p.window > 0 || p.softcap > 0.f || p.sink || p.doc_start) return false;
     auto al = [](const void* ptr, const Strides& st) {
         return reinterpret_cast<uintptr_t>(ptr) % 16 == 0 && st.sb % 4 == 0 && st.sh % 4 == 0 &&
                st.sr % 4 == 0;

@@ -141,9 +141,33 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(Params p, int
     const int n_tiles = static_cast<int>((blk_hi + kBN - 1) / kBN);
     // Under a local window the block's first row sees the lowest keys, and a
     // tile below the wave's last row's window edge needs the element test.
-    const int t_first = kVar ? static_cast<int>(window_lo(p, q0, delta) / kBN) : 0;
-    const int64_t wave_lo =
-        kVar ? window_lo(p, (qw0 + 31 < p.Lq ? qw0 + 31 : p.Lq - 1), delta) : 0;
+    // Lower key bounds (local window, document starts; variant kernel only):
+    // row_lo for this lane's row, wave_lo the largest in the wave (tiles below
+    // it need the element test) and the block's smallest, which sets the first
+    // tile -- blocks of keys before every row's bound are skipped (llm.istanbul
+    // "05_attention", "K-block iteration").
+    const int64_t qrow = qw0 + col;
+    int64_t row_lo = 0, wave_lo = 0;
+    int t_first = 0;
+    if (kVar) {
+        __shared__ int blk_min[kWaves];
+        const bool ok = qrow < p.Lq;
+        row_lo = ok ? first_key(p, b, qrow, delta) : 0;
+        int mn = ok ? static_cast<int>(row_lo < kv_len ? row_lo : kv_len) : INT32_MAX;
+        int mx = static_cast<int>(row_lo < kv_len ? row_lo : kv_len);
+#pragma unroll
+        for (int off = 16; off > 0; off >>= 1) {
+            mn = min(mn, __shfl_xor(mn, off, 64));
+            mx = max(mx, __shfl_xor(mx, off, 64));
+        }
+        wave_lo = mx;
+        if (lane == 0) blk_min[w] = mn;
+        __syncthreads();
+        int bm = INT32_MAX;
+#pragma unroll
+        for (int i = 0; i < kWaves; ++i) bm = min(bm, blk_min[i]);
+        t_first = bm == INT32_MAX ? n_tiles : bm / kBN;
+    }
 
     const uint16_t* qg = static_cast<const uint16_t*>(p.q);
     const uint16_t* kg = static_cast<const uint16_t*>(p.k) + b * p.ks.sb + g * p.ks.sh;
@@ -152,7 +176,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(Params p, int
     const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vg, kv_len * p.vs.sr * 2);
 
     // ---- Q^T operand, resident in registers -------------------------------
-    const int64_t qrow = qw0 + col;
     i16x8 qop[NT];
     {
         const bool ok = qrow < p.Lq;
@@ -238,7 +261,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(Params p, int
 
     f32x16 s_cur[2];
     if (t_first < n_tiles) scores(t_first & 1, s_cur);
-    const int64_t row_lo = kVar ? window_lo(p, qrow, delta) : 0;
     const bool cap = kVar && p.softcap > 0.f;
     const float cap_k2 = cap ? 2.f * kLog2e * p.scale / p.softcap : 0.f;
     const float cap_back = cap ? p.softcap / p.scale : 0.f;
@@ -416,7 +438,7 @@ hipError_t launch_one(const Params& p, hipStream_t s) {
     const int mask_vec4 = p.mask && (reinterpret_cast<uintptr_t>(p.mask) % 16 == 0) &&
                           p.ms.sb % 4 == 0 && p.ms.sh % 4 == 0 && p.ms.sr % 4 == 0;
     const dim3 grid(static_cast<uint32_t>(block_count(p)));
-    const bool var = p.softcap > 0.f || (p.causal && p.window > 0);
+    const bool var = p.softcap > 0.f || (p.causal && p.window > 0) || p.doc_start;
     if (p.mask && var)
         hipLaunchKernelGGL((prefill_mfma_kernel<kBf16, D, true, true>), grid, dim3(kThreads), 0, s,
                            p, n_qblk, gw, xcd_units, mask_vec4);

@@ -6,12 +6,16 @@ from it, so the two sides see identical bits.
 
 Recipe (the same for every workload): numpy PCG64 ``default_rng(seed)``;
 draw order Q, K, V, then key lengths, then the mask, then per-head sink
-scores, then int8-cache scales; values are i.i.d. N(0, 1) in float32 (sink
+scores, then int8-cache scales, then document starts; values are i.i.d.
+N(0, 1) in float32 (sink
 scores 2 * N(0, 1)), rounded to nearest-even into the storage type (float16
 via numpy, bfloat16 by bit rounding, kept as uint16 bit patterns).  An int8
 cache keeps K and V as float32 draws and quantizes them at the end: scale
 4/127 per tensor, or (0.5 + U[0, 1)) * 4/127 per (kv head, head-dim)
-channel; value = clip(round_half_even(x / scale), -127, 127).
+channel; value = clip(round_half_even(x / scale), -127, 127).  Packed
+documents: lengths uniform in [1, 2 * doc_mean) placed back to back until
+the entry's q_len positions are filled (doc_start = each position's
+document's first index); 'random' starts are uniform in [0, k_len].
 """
 from __future__ import annotations
 
@@ -58,6 +62,8 @@ class Spec:
     local_window: int = -1            # -1, or keys left of each causal row's position
     softcap: float = 0.0              # 0, or c > 0
     sink: Optional[str] = None        # None, 'zero' (smooth softmax) or 'heads' (drawn)
+    docs: Optional[str] = None        # None, 'packed' or 'random' (doc_start per row)
+    doc_mean: int = 512
     kv_quant: Optional[str] = None    # int8 cache: None, 'tensor', 'channel' or 'mixed'
                                       # ('mixed': K per tensor, V per channel)
 
@@ -113,6 +119,11 @@ DECODE_INT8_F16 = DECODE_F16.replace(
     name="fp16 decode B64 H32/8 cache8192 D128, int8 cache, per-channel scales",
     kv_quant="channel", seed=10)
 
+# Packed documents (mean length 512) on the bf16 causal prefill shape.
+DOCS_BF16 = CAUSAL_GQA_BF16.replace(
+    name="bf16 causal GQA prefill B4 H32/8 L4096 D128, packed documents (mean 512)",
+    docs="packed", doc_mean=512, seed=11)
+
 # Workloads of the extensions beyond the five (measured and tested the same way).
 EXTRA_WORKLOADS = {
     "chunk_f16": CHUNK_F16,
@@ -120,6 +131,7 @@ EXTRA_WORKLOADS = {
     "softcap_sink_bf16": SOFTCAP_SINK_BF16,
     "decode_window_f16": DECODE_WINDOW_F16,
     "decode_int8_f16": DECODE_INT8_F16,
+    "docs_bf16": DOCS_BF16,
 }
 
 
@@ -167,6 +179,7 @@ class Case:
     head_sink: Optional[np.ndarray] = None
     k_scale: Optional[np.ndarray] = None
     v_scale: Optional[np.ndarray] = None
+    doc_start: Optional[np.ndarray] = None
 
 
 def _normal(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
@@ -225,7 +238,20 @@ def generate(spec: Spec) -> Case:
         v_scale = np.array([base], np.float32) if spec.kv_quant == "tensor" else chan[n_ch:]
         k = _quantize(k, k_scale, spec)
         v = _quantize(v, v_scale, spec)
-    return Case(spec, q, k, v, lens, mask, head_sink, k_scale, v_scale)
+    doc_start = None
+    if spec.docs == "packed":
+        doc_start = np.empty((spec.batch, spec.q_len), np.int32)
+        for b in range(spec.batch):
+            pos = 0
+            while pos < spec.q_len:
+                n = int(rng.integers(1, 2 * spec.doc_mean))
+                doc_start[b, pos:pos + n] = pos
+                pos += n
+    elif spec.docs == "random":
+        doc_start = rng.integers(0, spec.k_len + 1, size=(spec.batch, spec.q_len)).astype(np.int32)
+    elif spec.docs is not None:
+        raise ValueError(spec.docs)
+    return Case(spec, q, k, v, lens, mask, head_sink, k_scale, v_scale, doc_start)
 
 
 def _quantize(x: np.ndarray, scale: np.ndarray, spec: Spec) -> np.ndarray:

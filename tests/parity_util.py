@@ -54,9 +54,10 @@ def run_hip(case: synth.Case, policy: str = "nan", *, return_lse=None, tensors=N
                        v=to_dev(case.v, s.dtype),
                        mask=None if case.mask is None else torch.from_numpy(case.mask).cuda(),
                        lens=None if case.key_lens is None else torch.from_numpy(case.key_lens).cuda(),
-                       sink=None if case.head_sink is None else torch.from_numpy(case.head_sink).cuda())
+                       sink=None if case.head_sink is None else torch.from_numpy(case.head_sink).cuda(),
+                       docs=None if case.doc_start is None else torch.from_numpy(case.doc_start).cuda())
     var = dict(local_window=s.local_window, softcap=s.softcap, sink=s.sink is not None,
-               head_sink=tensors.get("sink"))
+               head_sink=tensors.get("sink"), doc_start=tensors.get("docs"))
     dvar = {}
     if case.k_scale is not None:
         dvar = dict(k_scale=torch.from_numpy(case.k_scale).cuda(),
@@ -87,7 +88,7 @@ def run_oracle(case: synth.Case, policy: str = "nan", rows=None):
                             mask=case.mask, key_lens=case.key_lens, masked_rows=policy,
                             window=s.local_window, softcap=s.softcap, sink=s.sink is not None,
                             head_sink=case.head_sink, k_scale=case.k_scale,
-                            v_scale=case.v_scale, rows=rows)
+                            v_scale=case.v_scale, doc_start=case.doc_start, rows=rows)
 
 
 def compare(gpu_o, ref_o, gpu_lse, ref_lse, dtype: str, policy: str, what: str = ""):

@@ -477,3 +477,49 @@ def test_int8_cache_decode_full_size_every_row():
     o, lse, _ = pu.run_hip(case, "nan", return_lse=True)
     ro, rl = pu.run_oracle(case, "nan")
     pu.compare(o, ro, lse, rl, spec.dtype, "nan", what=spec.name)
+
+
+# --------------------------------------------------------------------------
+# Document masks (packed documents; arbitrary per-row starts too).
+
+DOCS = {
+    "docs_bf16_L333": (synth.CAUSAL_GQA_BF16.replace(
+        batch=2, q_heads=8, kv_heads=2, q_len=333, k_len=333, docs="packed", doc_mean=40,
+        seed=41), "prefill_mfma"),
+    "docs_random_f16_D64_lens": (synth.CAUSAL_GQA_BF16.replace(
+        dtype="f16", batch=3, q_heads=6, kv_heads=3, q_len=200, k_len=260, head_dim=64,
+        docs="random", lens="cross", lens_zero_at=1, lens_full_at=2, seed=42), "prefill_mfma"),
+    "docs_window_sink_bf16": (synth.CAUSAL_GQA_BF16.replace(
+        batch=1, q_heads=8, kv_heads=4, q_len=300, k_len=300, docs="packed", doc_mean=70,
+        local_window=50, sink="heads", seed=43), "prefill_mfma"),
+    "docs_noncausal_f16_mask": (synth.CROSS_MASK_F16.replace(
+        q_len=100, k_len=300, docs="random", seed=44), "prefill_mfma"),
+    "docs_f32_generic": (synth.CAUSAL_GQA_F32.replace(
+        batch=2, q_heads=4, kv_heads=2, q_len=90, k_len=90, docs="packed", doc_mean=12,
+        seed=45), "generic"),
+    "docs_decode": (synth.DECODE_F16.replace(
+        batch=8, k_len=700, docs="random", seed=46), "decode_splitk"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(DOCS))
+@pytest.mark.parametrize("policy", ["nan", "zero"])
+def test_doc_masks_full_compare(name, policy):
+    spec, kernel = DOCS[name]
+    case = synth.generate(spec)
+    o, lse, _ = pu.run_hip(case, policy, return_lse=True)
+    assert sdpa.last_kernel() == kernel
+    ro, rl = pu.run_oracle(case, policy)
+    pu.compare(o, ro, lse, rl, spec.dtype, policy, what=name)
+
+
+def test_docs_bf16_full_size_sampled():
+    spec = synth.EXTRA_WORKLOADS["docs_bf16"]
+    case = synth.generate(spec)
+    o, lse, _ = pu.run_hip(case, "nan")
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    rows = pu.sample_rows(spec, 96, seed=11)
+    ro, rl = pu.run_oracle(case, "nan", rows=rows)
+    go = o[rows[:, 0], rows[:, 1], rows[:, 2]]
+    gl = lse[rows[:, 0], rows[:, 1], rows[:, 2]]
+    pu.compare(go, ro, gl, rl, spec.dtype, "nan", what=spec.name)
