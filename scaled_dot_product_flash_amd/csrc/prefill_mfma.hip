@@ -56,11 +56,19 @@ namespace {
 
 using namespace mfma;
 
-constexpr int kRows = 256;     // query rows (all heads) per workgroup
 constexpr int kBN = 64;        // keys per tile
-constexpr int kWaves = 8;
-constexpr int kThreads = 64 * kWaves;
 constexpr float kSlack = 8.f;  // lazy-rescale threshold, base-2 units
+
+// Workgroup shape per padded head dim DP: 8 waves (two per SIMD) of 32 query
+// rows; for DP = 256 a wave's Q operand, accumulators and scores need about
+// 300 registers, so 4 waves (one per SIMD, 512 registers each).  A head dim
+// D < DP that is a multiple of 8 runs padded: columns d >= D load as zeros
+// and are not stored.
+template <int DP> struct Cfg {
+    static constexpr int kWaves = DP == 256 ? 4 : 8;
+    static constexpr int kThreads = 64 * kWaves;
+    static constexpr int kRows = 32 * kWaves;   // query rows (all heads) per workgroup
+};
 
 // LDS row strides (elements).  K rows are read 16 lanes x 16 bytes at a time
 // down one column: a stride of 16 mod 256 bytes spreads them over all banks.
@@ -70,14 +78,17 @@ template <int D> struct Tile {
     static constexpr int KS = D + 8;
     static constexpr int VS = D + 32;
     static constexpr int kRowChunks = D / 8;                  // 16-byte chunks per row
-    static constexpr int kLoads = kBN * kRowChunks / kThreads;        // per thread
+    static constexpr int kLoads = kBN * kRowChunks / Cfg<D>::kThreads;   // per thread
 };
 
 template <bool kBf16, int D, bool kMask, bool kVar>
-__global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(Params p, int n_qblk, int gw,
-                                                                   int xcd_units, int mask_vec4) {
+__global__ __launch_bounds__(Cfg<D>::kThreads, 1) void prefill_mfma_kernel(Params p, int n_qblk,
+                                                                         int gw, int xcd_units,
+                                                                         int mask_vec4) {
     using M = Mma<kBf16>;
     using TL = Tile<D>;
+    constexpr int kRows = Cfg<D>::kRows, kWaves = Cfg<D>::kWaves, kThreads = Cfg<D>::kThreads;
+    const int Dt = p.D;          // true head dim (a multiple of 8, <= D)
     constexpr int KS = TL::KS, VS = TL::VS;
     constexpr int NT = D / 16;   // 16-wide d-steps of the score product
     constexpr int ND = D / 32;   // 32-row d-tiles of the output
@@ -182,8 +193,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(Params p, int
         const uint16_t* src = qg + b * p.qs.sb + h * p.qs.sh + (ok ? qrow : 0) * p.qs.sr + 8 * hh;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            i16x8 v = *reinterpret_cast<const i16x8*>(src + 16 * t);
-            qop[t] = ok ? v : i16x8{};
+            const bool in = ok && 16 * t + 8 * hh < Dt;   // padded columns are zero
+            qop[t] = in ? *reinterpret_cast<const i16x8*>(src + 16 * t) : i16x8{};
         }
     }
 
@@ -198,14 +209,16 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(Params p, int
 #pragma unroll
         for (int n = 0; n < TL::kLoads; ++n) {
             const int key = tile * kBN + st_row + n * kRowsPerPass;
-            kst[n] = load16(krs, (key * static_cast<int>(p.ks.sr) + st_col) * 2);
+            kst[n] = st_col < Dt ? load16(krs, (key * static_cast<int>(p.ks.sr) + st_col) * 2)
+                                 : i16x8{};
         }
     };
     auto fetch_v = [&](int tile) {
 #pragma unroll
         for (int n = 0; n < TL::kLoads; ++n) {
             const int key = tile * kBN + st_row + n * kRowsPerPass;
-            vst[n] = load16(vrs, (key * static_cast<int>(p.vs.sr) + st_col) * 2);
+            vst[n] = st_col < Dt ? load16(vrs, (key * static_cast<int>(p.vs.sr) + st_col) * 2)
+                                 : i16x8{};
         }
     };
     auto stash_k = [&](int buf) {
@@ -406,7 +419,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(Params p, int
 #pragma unroll
                 for (int e = 0; e < 4; ++e) o4[e] = empty ? fill : acc[d][4 * u + e] * inv;
                 const uint2 pk = {M::pack_out(o4[0], o4[1]), M::pack_out(o4[2], o4[3])};
-                *reinterpret_cast<uint2*>(og + 32 * d + 8 * u + 4 * hh) = pk;
+                if (32 * d + 8 * u + 4 * hh < Dt)
+                    *reinterpret_cast<uint2*>(og + 32 * d + 8 * u + 4 * hh) = pk;
             }
         }
         if (p.lse && hh == 0) {
@@ -416,22 +430,30 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(Params p, int
     }
 }
 
-// Query heads per workgroup: the largest of 8, 4, 2, 1 that divides the group.
-int heads_per_block(int group) {
+// Padded head dim of the kernel that runs head dim D.
+int padded_dim(int D) { return D <= 64 ? 64 : (D <= 128 ? 128 : 256); }
+
+// Query heads per workgroup: the largest of 8, 4, 2, 1 that divides the group
+// and leaves each head at least one 32-row wave.
+int heads_per_block(int group, int waves) {
     for (int gw = 8; gw > 1; gw >>= 1)
-        if (group % gw == 0) return gw;
+        if (group % gw == 0 && gw <= waves) return gw;
     return 1;
 }
 
+int waves_for(int DP) { return DP == 256 ? Cfg<256>::kWaves : Cfg<128>::kWaves; }
+
 int64_t block_count(const Params& p) {
-    const int gw = heads_per_block(p.group);
-    const int64_t n_qblk = (p.Lq + kRows / gw - 1) / (kRows / gw);
+    const int waves = waves_for(padded_dim(p.D)), rows = 32 * waves;
+    const int gw = heads_per_block(p.group, waves);
+    const int64_t n_qblk = (p.Lq + rows / gw - 1) / (rows / gw);
     return n_qblk * p.B * p.Hkv * (p.group / gw);
 }
 
 template <bool kBf16, int D>
 hipError_t launch_one(const Params& p, hipStream_t s) {
-    const int gw = heads_per_block(p.group);
+    constexpr int kRows = Cfg<D>::kRows, kThreads = Cfg<D>::kThreads;
+    const int gw = heads_per_block(p.group, Cfg<D>::kWaves);
     const int n_qblk = (p.Lq + kRows / gw - 1) / (kRows / gw);
     const int units = p.B * p.Hkv;
     const int xcd_units = (units % 8 == 0) ? units / 8 : 0;
@@ -458,7 +480,7 @@ hipError_t launch_one(const Params& p, hipStream_t s) {
 
 bool prefill_mfma_supported(const Params& p, DType dt) {
     if (dt != DType::BF16 && dt != DType::F16) return false;
-    if (p.D != 64 && p.D != 128) return false;
+    if (p.D % 8 != 0 || p.D > 256) return false;
     // 16-byte loads of Q/K/V rows and 8-byte stores of O need aligned rows.
     auto al = [](const void* ptr, const Strides& st, int a) {
         return reinterpret_cast<uintptr_t>(ptr) % (2 * a) == 0 && st.sb % a == 0 &&
@@ -476,8 +498,13 @@ bool prefill_mfma_supported(const Params& p, DType dt) {
 }
 
 hipError_t launch_prefill_mfma(const Params& p, DType dt, hipStream_t s) {
-    if (dt == DType::BF16) return p.D == 128 ? launch_one<true, 128>(p, s) : launch_one<true, 64>(p, s);
-    return p.D == 128 ? launch_one<false, 128>(p, s) : launch_one<false, 64>(p, s);
+    const int DP = padded_dim(p.D);
+    if (dt == DType::BF16) {
+        if (DP == 64) return launch_one<true, 64>(p, s);
+        return DP == 128 ? launch_one<true, 128>(p, s) : launch_one<true, 256>(p, s);
+    }
+    if (DP == 64) return launch_one<false, 64>(p, s);
+    return DP == 128 ? launch_one<false, 128>(p, s) : launch_one<false, 256>(p, s);
 }
 
 }  // namespace sdpa

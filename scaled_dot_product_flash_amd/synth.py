@@ -124,6 +124,12 @@ DOCS_BF16 = CAUSAL_GQA_BF16.replace(
     name="bf16 causal GQA prefill B4 H32/8 L4096 D128, packed documents (mean 512)",
     docs="packed", doc_mean=512, seed=11)
 
+# Head dims beyond 64 / 128 on the matrix cores (96 runs padded to 128).
+D256_BF16 = CAUSAL_GQA_BF16.replace(
+    name="bf16 causal GQA prefill B4 H32/8 L4096 D256", head_dim=256, seed=12)
+D96_BF16 = CAUSAL_GQA_BF16.replace(
+    name="bf16 causal GQA prefill B4 H32/8 L4096 D96", head_dim=96, seed=13)
+
 # Workloads of the extensions beyond the five (measured and tested the same way).
 EXTRA_WORKLOADS = {
     "chunk_f16": CHUNK_F16,
@@ -132,6 +138,8 @@ EXTRA_WORKLOADS = {
     "decode_window_f16": DECODE_WINDOW_F16,
     "decode_int8_f16": DECODE_INT8_F16,
     "docs_bf16": DOCS_BF16,
+    "d256_bf16": D256_BF16,
+    "d96_bf16": D96_BF16,
 }
 
 

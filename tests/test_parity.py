@@ -523,3 +523,58 @@ def test_docs_bf16_full_size_sampled():
     go = o[rows[:, 0], rows[:, 1], rows[:, 2]]
     gl = lse[rows[:, 0], rows[:, 1], rows[:, 2]]
     pu.compare(go, ro, gl, rl, spec.dtype, "nan", what=spec.name)
+
+
+# --------------------------------------------------------------------------
+# Head dims beyond 64 / 128 on the matrix cores (multiples of 8 run padded
+# to 64, 128 or 256; odd dims stay on the any-shape kernel).
+
+HEAD_DIMS = [
+    # D, dtype, q_len, k_len, extra
+    (8, "bf16", 130, 130, {}),
+    (32, "f16", 200, 200, {}),
+    (40, "bf16", 97, 150, dict(lens="cross", lens_zero_at=1, lens_full_at=0)),
+    (80, "f16", 150, 150, {}),
+    (96, "bf16", 150, 200, dict(local_window=40, sink="heads")),
+    (160, "f16", 100, 100, dict(softcap=10.0)),
+    (256, "bf16", 200, 200, {}),
+    (256, "f16", 70, 300, dict(causal=False, mask="keys", lens="cross", lens_zero_at=1,
+                               lens_full_at=0, mask_all_at=2)),
+    (256, "bf16", 120, 120, dict(docs="packed", doc_mean=30)),
+]
+
+
+@pytest.mark.parametrize("cfg", HEAD_DIMS, ids=lambda c: "D%d-%s-%dx%d" % c[:4])
+@pytest.mark.parametrize("policy", ["nan", "zero"])
+def test_head_dims_on_matrix_cores(cfg, policy):
+    D, dtype, lq, lk, extra = cfg
+    spec = synth.CAUSAL_GQA_BF16.replace(dtype=dtype, batch=3, q_heads=8, kv_heads=2, q_len=lq,
+                                         k_len=lk, head_dim=D, seed=50 + D, **extra)
+    case = synth.generate(spec)
+    o, lse, _ = pu.run_hip(case, policy, return_lse=True)
+    assert sdpa.last_kernel() == "prefill_mfma"
+    ro, rl = pu.run_oracle(case, policy)
+    pu.compare(o, ro, lse, rl, spec.dtype, policy, what="D=%d %s" % (D, dtype))
+
+
+def test_odd_head_dim_runs_on_the_generic_kernel():
+    spec = synth.CAUSAL_GQA_BF16.replace(dtype="f16", batch=2, q_heads=4, kv_heads=2, q_len=40,
+                                         k_len=40, head_dim=33, seed=60)
+    case = synth.generate(spec)
+    o, lse, _ = pu.run_hip(case, "nan", return_lse=True)
+    assert sdpa.last_kernel() == "generic"
+    ro, rl = pu.run_oracle(case, "nan")
+    pu.compare(o, ro, lse, rl, spec.dtype, "nan", what="D=33")
+
+
+@pytest.mark.parametrize("name", ["d256_bf16", "d96_bf16"])
+def test_head_dim_workloads_full_size_sampled(name):
+    spec = synth.EXTRA_WORKLOADS[name]
+    case = synth.generate(spec)
+    o, lse, _ = pu.run_hip(case, "nan")
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    rows = pu.sample_rows(spec, 64, seed=12)
+    ro, rl = pu.run_oracle(case, "nan", rows=rows)
+    go = o[rows[:, 0], rows[:, 1], rows[:, 2]]
+    gl = lse[rows[:, 0], rows[:, 1], rows[:, 2]]
+    pu.compare(go, ro, gl, rl, spec.dtype, "nan", what=spec.name)
