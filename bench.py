@@ -149,9 +149,11 @@ def visible_flops(case) -> float:
             hi = np.clip(i + d + 1, 0, L)
             lo = (np.clip(i + d - s.local_window, 0, None) if s.local_window >= 0
                   else np.zeros_like(i))
-            pairs += int(np.clip(hi - lo, 0, None).sum())
         else:
-            pairs += L * Lq
+            hi, lo = np.full(Lq, L, np.int64), np.zeros(Lq, np.int64)
+        if case.doc_start is not None:
+            lo = np.maximum(lo, case.doc_start[b].astype(np.int64))
+        pairs += int(np.clip(hi - lo, 0, None).sum())
     return 4.0 * s.head_dim * s.q_heads * pairs
 
 
@@ -161,13 +163,16 @@ def other_workloads(sdpa, synth, steps: int, warmup: int):
     import torch
     out = []
     specs = [synth.WORKLOADS[n] for n in ("tiny_f32", "causal_gqa_f32", "cross_mask_f16")]
-    specs += [synth.EXTRA_WORKLOADS[n] for n in ("chunk_f16", "window_bf16", "softcap_sink_bf16")]
+    specs += [synth.EXTRA_WORKLOADS[n]
+              for n in ("chunk_f16", "window_bf16", "softcap_sink_bf16", "docs_bf16", "d96_bf16",
+                        "d256_bf16")]
     for spec in specs:
         case = synth.generate(spec)
         q, k, v = (to_dev(x, spec.dtype) for x in (case.q, case.k, case.v))
         mask = None if case.mask is None else torch.from_numpy(case.mask).cuda()
         lens = None if case.key_lens is None else torch.from_numpy(case.key_lens).cuda()
         sink = None if case.head_sink is None else torch.from_numpy(case.head_sink).cuda()
+        docs = None if case.doc_start is None else torch.from_numpy(case.doc_start).cuda()
         o = torch.empty_like(q)
         for policy in (("nan", "zero") if spec.mask else ("nan",)):
             def f():
@@ -175,7 +180,7 @@ def other_workloads(sdpa, synth, steps: int, warmup: int):
                              causal=spec.causal, causal_offset=spec.causal_offset, mask=mask,
                              key_lens=lens, masked_rows=policy, return_lse=spec.lse,
                              local_window=spec.local_window, softcap=spec.softcap,
-                             sink=spec.sink is not None, head_sink=sink, out=o)
+                             sink=spec.sink is not None, head_sink=sink, doc_start=docs, out=o)
             f()
             kern = sdpa.last_kernel()
             durs, _ = time_calls(f, steps, warmup, settle_s=0.3)

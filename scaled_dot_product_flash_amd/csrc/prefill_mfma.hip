@@ -36,8 +36,9 @@
 //
 // Element-wise work that only some tiles need (the causal diagonal, the tile
 // holding the key length, the lower edge of a local window, the additive
-// mask) is done only on those tiles; the mask and the window/softcap rules
-// are compile-time variants of the kernel.  Score-rule variants follow the ONNX
+// mask) is done only on those tiles; the mask and the window / softcap /
+// document rules (with padded head dims) are compile-time variants of the
+// kernel.  Score-rule variants follow the ONNX
 // GroupQueryAttention README ("Attributes", "Inputs"): a local window starts
 // the key loop at the block's first visible tile; the softcap maps each raw
 // score before the mask is added; the sink joins the denominator at the end.
@@ -88,7 +89,10 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, 1) void prefill_mfma_kernel(Param
     using M = Mma<kBf16>;
     using TL = Tile<D>;
     constexpr int kRows = Cfg<D>::kRows, kWaves = Cfg<D>::kWaves, kThreads = Cfg<D>::kThreads;
-    const int Dt = p.D;          // true head dim (a multiple of 8, <= D)
+    // True head dim (a multiple of 8, <= D).  Padded dims run the variant
+    // kernel; in the plain one it is the compile-time D and the column guards
+    // below fold away.
+    const int Dt = kVar ? p.D : D;
     constexpr int KS = TL::KS, VS = TL::VS;
     constexpr int NT = D / 16;   // 16-wide d-steps of the score product
     constexpr int ND = D / 32;   // 32-row d-tiles of the output
@@ -460,7 +464,7 @@ hipError_t launch_one(const Params& p, hipStream_t s) {
     const int mask_vec4 = p.mask && (reinterpret_cast<uintptr_t>(p.mask) % 16 == 0) &&
                           p.ms.sb % 4 == 0 && p.ms.sh % 4 == 0 && p.ms.sr % 4 == 0;
     const dim3 grid(static_cast<uint32_t>(block_count(p)));
-    const bool var = p.softcap > 0.f || (p.causal && p.window > 0) || p.doc_start;
+    const bool var = p.softcap > 0.f || (p.causal && p.window > 0) || p.doc_start || p.D != D;
     if (p.mask && var)
         hipLaunchKernelGGL((prefill_mfma_kernel<kBf16, D, true, true>), grid, dim3(kThreads), 0, s,
                            p, n_qblk, gw, xcd_units, mask_vec4);
