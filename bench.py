@@ -327,7 +327,9 @@ def main():
             "kv_bytes": kv_bytes, "kernel": dkernel,
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-                         "traffic": None},
+                         "traffic": read_traffic("decode_splitk_f16_B64H32_cache8192D128_pmc.txt",
+                                                 kernel_source_hash(["decode.hip"])),
+                         "kernel_source_hash": kernel_source_hash(["decode.hip"])},
         }
         del dq, dk, dv, dout
 
