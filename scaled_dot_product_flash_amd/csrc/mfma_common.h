@@ -104,6 +104,14 @@ __device__ __forceinline__ i16x8 load16(__amdgpu_buffer_rsrc_t r, int byte_off) 
     return __builtin_bit_cast(i16x8, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
 }
 
+// Row maximum for the online normaliser: IEEE maximum, which propagates a
+// NaN (v_maximum3_f32 on gfx950, no per-input quieting as maxNum needs).  A
+// NaN score only occurs in a row that must end NaN anyway: the NaN maximum
+// raises nothing and the row's p and l become NaN.
+__device__ __forceinline__ float max_nan(float a, float b) {
+    return __builtin_elementwise_maximum(a, b);
+}
+
 // Combine a value with the one in lane l ^ 32 (the other half of the wave)
 // through v_permlane32_swap: with both operands x, the first result holds
 // x[l] in lanes 0..31 and x[l - 32] above, the second x[l + 32] below and
@@ -111,7 +119,7 @@ __device__ __forceinline__ i16x8 load16(__amdgpu_buffer_rsrc_t r, int byte_off) 
 __device__ __forceinline__ float halves_max(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                     false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    return max_nan(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float halves_sum(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,

@@ -339,7 +339,7 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, 1) void prefill_mfma_kernel(Param
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s_cur[kb][r], s_cur[kb][r + 1]));
+            for (int r = 0; r < 16; r += 2) mx = max_nan(mx, max_nan(s_cur[kb][r], s_cur[kb][r + 1]));
         mx = halves_max(mx);
         // -- lazy raise of the reference maximum --
         const bool raise = mx > m_ref + slack;
