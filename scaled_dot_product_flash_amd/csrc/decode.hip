@@ -25,11 +25,12 @@
 //
 // A step: K/V rows are loaded with coalesced 16-byte raw-buffer loads bounded
 // at the unit's live length (zeros past it; rows past the length are never
-// read) and prefetched into registers one step ahead, also across unit
-// boundaries; the wave stores them in its own LDS rows (no barriers) and runs
-// S^T = K Q^T and O^T += V^T P^T on 16x16x32 MFMAs with the query heads as the
-// columns.  Online normaliser with a lazily raised reference maximum; P is
-// rounded to the element type and the sum adds the rounded values.
+// read), marked non-temporal since each byte is read once, and prefetched
+// into registers one step ahead, also across unit boundaries; the wave
+// stores them in its own LDS rows (no barriers) and runs S^T = K Q^T and
+// O^T += V^T P^T on 16x16x32 MFMAs with the query heads as the columns.
+// Online normaliser with a lazily raised reference maximum; P is rounded to
+// the element type and the sum adds the rounded values.
 //
 // Score-rule variants (ONNX GroupQueryAttention README, "Attributes",
 // "Inputs"): a local window moves the start of the live range up (the range
@@ -289,8 +290,8 @@ __global__ __launch_bounds__(64) void decode_split_kernel(Params p, int n_hgrp, 
 #pragma unroll
         for (int n = 0; n < kLd; ++n) {
             const int key = j0 + n * kRpl;
-            kst[n] = load16(krs, (key * static_cast<int>(p.ks.sr) + ld_col) * kEs);
-            vst[n] = load16(vrs, (key * static_cast<int>(p.vs.sr) + ld_col) * kEs);
+            kst[n] = load16_stream(krs, (key * static_cast<int>(p.ks.sr) + ld_col) * kEs);
+            vst[n] = load16_stream(vrs, (key * static_cast<int>(p.vs.sr) + ld_col) * kEs);
         }
     };
 
@@ -440,23 +441,52 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(Params p, int n_hgr
     for (int cc = 0; cc < NPL; ++cc) A[cc] = 0.f;
     if (sb > 0) {
         const int w_lo = owner_wave(first, S), w_hi = owner_wave(first + sb - 1, S);
+        const int n = w_hi - w_lo + 1;
         const int rs = rec_stride(D);
         const float* base = static_cast<const float*>(p.ws);
+        auto rec = [&](int w) { return base + ((unit + w) * slot_heads + col) * rs; };
         // Waves with an empty share (fewer steps than waves) wrote no record.
         auto empty_share = [&](int w) {
             return S * w / kWavesTotal == S * (w + 1) / kWavesTotal;
         };
-        for (int w = w_lo; w <= w_hi; ++w)
-            if (!empty_share(w)) M = fmaxf(M, base[((unit + w) * slot_heads + col) * rs]);
-        for (int w = w_lo; w <= w_hi; ++w) {
-            if (empty_share(w)) continue;
-            const float* r = base + ((unit + w) * slot_heads + col) * rs;
-            const float f = (r[0] == kNegInf) ? 0.f : fast_exp2((r[0] - M) * c);
-            L = fmaf(r[1], f, L);
+        // Record headers are fetched 64 at a time, one per lane, so the
+        // loads overlap instead of forming a chain.
+        for (int c0 = 0; c0 < n; c0 += 64) {
+            const int w = w_lo + c0 + lane;
+            if (c0 + lane < n && !empty_share(w)) M = fmaxf(M, rec(w)[0]);
+        }
+        M = wave_max(M);
+        for (int c0 = 0; c0 < n; c0 += 64) {
+            float f = 0.f, l = 0.f;
+            {
+                const int w = w_lo + c0 + lane;
+                if (c0 + lane < n && !empty_share(w)) {
+                    const float* r = rec(w);
+                    f = (r[0] == kNegInf) ? 0.f : fast_exp2((r[0] - M) * c);
+                    l = r[1];
+                }
+            }
+            const int cnt = n - c0 < 64 ? n - c0 : 64;
+            // Accumulators: 8 records' rows loaded ahead, folded in wave order.
+            for (int i0 = 0; i0 < cnt; i0 += 8) {
+                float v[8][NPL];
 #pragma unroll
-            for (int cc = 0; cc < NPL; ++cc) {
-                const int d = lane + 64 * cc;
-                if (d < D) A[cc] = fmaf(r[4 + d], f, A[cc]);
+                for (int u = 0; u < 8; ++u)
+#pragma unroll
+                    for (int cc = 0; cc < NPL; ++cc) {
+                        const int d = lane + 64 * cc;
+                        v[u][cc] = (i0 + u < cnt && d < D) ? rec(w_lo + c0 + i0 + u)[4 + d] : 0.f;
+                    }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int i = i0 + u;
+                    if (i < cnt && !empty_share(w_lo + c0 + i)) {
+                        const float fi = __shfl(f, i, 64), li = __shfl(l, i, 64);
+                        L = fmaf(li, fi, L);
+#pragma unroll
+                        for (int cc = 0; cc < NPL; ++cc) A[cc] = fmaf(v[u][cc], fi, A[cc]);
+                    }
+                }
             }
         }
     }

@@ -104,6 +104,13 @@ __device__ __forceinline__ i16x8 load16(__amdgpu_buffer_rsrc_t r, int byte_off) 
     return __builtin_bit_cast(i16x8, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
 }
 
+// The same load with the non-temporal hint, for data read exactly once (a
+// streaming pass over a key/value cache): the lines are not kept in the
+// caches for reuse, which raises sustained read bandwidth.
+__device__ __forceinline__ i16x8 load16_stream(__amdgpu_buffer_rsrc_t r, int byte_off) {
+    return __builtin_bit_cast(i16x8, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 2));
+}
+
 // Row maximum for the online normaliser: IEEE maximum, which propagates a
 // NaN (v_maximum3_f32 on gfx950, no per-input quieting as maxNum needs).  A
 // NaN score only occurs in a row that must end NaN anyway: the NaN maximum
