@@ -1,17 +1,19 @@
 // prefill_mfma.hip -- fused attention for bf16 / fp16 inputs with fp32
-// accumulation on the gfx950 matrix cores (head_dim 64 or 128).
+// accumulation on the gfx950 matrix cores (head dims that are multiples of 8,
+// up to 256).
 //
 // Work decomposition.  A workgroup of 8 waves owns one (batch, kv head) and
 // 256 query rows that read it: gw query heads of the group (gw = 8, 4, 2 or 1,
 // the largest that divides Hq/Hkv) times 256/gw consecutive positions.  Each
 // wave owns 32 rows of one head.  One K/V tile load thus serves every query
 // head of the group that shares it (llm.istanbul "05_attention", "GQA").  The
-// keys are visited in increasing order, 64 per tile, staged through LDS
-// (double buffered, one barrier per tile) with coalesced 16-byte raw-buffer
-// loads whose range ends at the batch entry's key length, so rows past it
-// read as zeros and are never fetched.  (OneGPU "Attention", introduction and "Variants and
-// ordering": a workgroup keeps a block of query rows and walks key/value tiles
-// held in workgroup memory.)
+// keys are visited in increasing order, 64 per tile, staged through LDS (one
+// barrier per tile) by coalesced 16-byte raw-buffer loads that write LDS
+// directly, with no register round trip; the buffer's range ends at the batch
+// entry's key length, so rows past it arrive as zeros and are never fetched.
+// (OneGPU "Attention", introduction and "Variants and ordering": a workgroup
+// keeps a block of query rows and walks key/value tiles held in workgroup
+// memory.)
 //
 // Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16: the
 // output column is the query, so lane l owns query l%32 and holds 16 of its
@@ -71,15 +73,19 @@ template <int DP> struct Cfg {
     static constexpr int kRows = 32 * kWaves;   // query rows (all heads) per workgroup
 };
 
-// LDS row strides (elements).  K rows are read 16 lanes x 16 bytes at a time
-// down one column: a stride of 16 mod 256 bytes spreads them over all banks.
-// V rows are read by the transpose load, 4 rows x 64 bytes per 32 lanes: a
-// stride of 64 mod 256 bytes keeps those rows apart.
+// LDS tile layout.  K/V tiles go from HBM straight into LDS (buffer loads
+// with the LDS destination): one wave load writes 64 lanes x 16 bytes = 1 KiB
+// contiguously, lane l at byte 16 l of its block.  A 64-row tile is cut into
+// NB = D/8 such blocks, and block I holds the rows r with r % NB == I, so
+// consecutive rows land in different blocks.  K rows are read 16 lanes x 16
+// bytes down one column: blocks padded to 1040 bytes put consecutive rows 16
+// bytes mod 256 apart, over all banks.  V rows are read by the transpose
+// load, 4 rows x 64 bytes per 32 lanes: blocks padded to 1088 bytes put them
+// 64 bytes mod 256 apart.
 template <int D> struct Tile {
-    static constexpr int KS = D + 8;
-    static constexpr int VS = D + 32;
-    static constexpr int kRowChunks = D / 8;                  // 16-byte chunks per row
-    static constexpr int kLoads = kBN * kRowChunks / Cfg<D>::kThreads;   // per thread
+    static constexpr int NB = D / 8;                          // blocks = chunks per row
+    static constexpr int KB = 1040, VB = 1088;                // block strides (bytes)
+    static constexpr int RB = 2 * D;                          // row bytes
 };
 
 template <bool kBf16, int D, bool kMask, bool kVar>
@@ -93,11 +99,16 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, 1) void prefill_mfma_kernel(Param
     // kernel; in the plain one it is the compile-time D and the column guards
     // below fold away.
     const int Dt = kVar ? p.D : D;
-    constexpr int KS = TL::KS, VS = TL::VS;
     constexpr int NT = D / 16;   // 16-wide d-steps of the score product
     constexpr int ND = D / 32;   // 32-row d-tiles of the output
-    __shared__ __attribute__((aligned(16))) uint16_t k_sh[2][kBN * KS];
-    __shared__ __attribute__((aligned(16))) uint16_t v_sh[2][kBN * VS];
+    constexpr int NB = TL::NB, KB = TL::KB, VB = TL::VB, RB = TL::RB;
+    // K is triple buffered when it fits (D <= 128): K(t) lives in buffer t % 3,
+    // so the refill of iteration t (K(t+2)) never lands in the buffer the
+    // previous iteration or the prologue read.  D = 256 double buffers and
+    // puts a barrier after the prologue's score reads instead.
+    constexpr int kKBufs = D <= 128 ? 3 : 2;
+    __shared__ __attribute__((aligned(16))) uint8_t k_sh[kKBufs][NB * KB];
+    __shared__ __attribute__((aligned(16))) uint8_t v_sh[2][NB * VB];
 
     // ---- which (b, kv head, head slice, query block) this workgroup owns --
     // Heaviest causal blocks first.  When the (batch, kv-head) units split
@@ -202,50 +213,48 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, 1) void prefill_mfma_kernel(Param
         }
     }
 
-    // ---- staging: global -> registers -> LDS.  K runs one tile ahead of V:
-    // while tile t's softmax and P V run, tile t+1's scores are computed, so
-    // LDS holds K(t+1) and V(t) and the registers carry K(t+2) and V(t+1).
-    const int st_row = tid / TL::kRowChunks;                 // + n * kRowsPerPass
-    const int st_col = (tid % TL::kRowChunks) * 8;
-    constexpr int kRowsPerPass = kThreads / TL::kRowChunks;
-    i16x8 kst[TL::kLoads], vst[TL::kLoads];
-    auto fetch_k = [&](int tile) {
+    // ---- staging: HBM -> LDS.  K runs one tile ahead of V: while tile t's
+    // softmax and P V run, tile t+1's scores are computed from LDS, and the
+    // loads of K(t+2) and V(t+1) land in the free buffers; each wave waits for
+    // its own loads before the barrier that ends the tile.  Each wave loads NB / kWaves blocks per tensor per tile straight into LDS
+    // (lane l fills bytes 16 l .. 16 l + 15 of its block): in block I, lane l
+    // holds row I + NB * (l / (D/8)), 16-byte chunk l % (D/8).  Rows past the
+    // key length and padded columns (d >= true head dim) read out of the
+    // buffer's range, which writes zeros.
+    constexpr int kLoadsW = NB / kWaves;
+    const int ld_q = lane / (D / 8), ld_c = lane % (D / 8);
+    constexpr uint32_t kOutOfRange = 0x7ffffff0u;
+    auto dma = [&](__amdgpu_buffer_rsrc_t rs, int64_t sr, uint8_t* buf, int stride, int tile) {
 #pragma unroll
-        for (int n = 0; n < TL::kLoads; ++n) {
-            const int key = tile * kBN + st_row + n * kRowsPerPass;
-            kst[n] = st_col < Dt ? load16(krs, (key * static_cast<int>(p.ks.sr) + st_col) * 2)
-                                 : i16x8{};
+        for (int n = 0; n < kLoadsW; ++n) {
+            const int I = n * kWaves + w;
+            const int key = tile * kBN + I + NB * ld_q;
+            const uint32_t off =
+                8 * ld_c < Dt ? static_cast<uint32_t>((key * static_cast<int>(sr) + 8 * ld_c) * 2)
+                              : kOutOfRange;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rs, (__attribute__((address_space(3))) void*)(buf + I * stride), 16, off, 0, 0, 0);
         }
     };
-    auto fetch_v = [&](int tile) {
-#pragma unroll
-        for (int n = 0; n < TL::kLoads; ++n) {
-            const int key = tile * kBN + st_row + n * kRowsPerPass;
-            vst[n] = st_col < Dt ? load16(vrs, (key * static_cast<int>(p.vs.sr) + st_col) * 2)
-                                 : i16x8{};
-        }
-    };
-    auto stash_k = [&](int buf) {
-#pragma unroll
-        for (int n = 0; n < TL::kLoads; ++n)
-            *reinterpret_cast<i16x8*>(&k_sh[buf][(st_row + n * kRowsPerPass) * KS + st_col]) = kst[n];
-    };
-    auto stash_v = [&](int buf) {
-#pragma unroll
-        for (int n = 0; n < TL::kLoads; ++n)
-            *reinterpret_cast<i16x8*>(&v_sh[buf][(st_row + n * kRowsPerPass) * VS + st_col]) = vst[n];
-    };
+    auto kbuf = [&](int tile) { return kKBufs == 3 ? tile % 3 : tile & 1; };
+    auto fetch_k = [&](int tile) { dma(krs, p.ks.sr, k_sh[kbuf(tile)], KB, tile); };
+    auto fetch_v = [&](int tile) { dma(vrs, p.vs.sr, v_sh[tile & 1], VB, tile); };
+    // Waits for this wave's direct loads (vmcnt 0; expcnt and lgkmcnt left
+    // free), before the barrier that publishes a tile.
+    auto dma_wait = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };
     // The two 32-key blocks' MFMA chains alternate, so consecutive MFMAs are
     // independent.
     auto scores = [&](int buf, f32x16 (&s)[2]) {
-        const uint16_t* krow = &k_sh[buf][col * KS + 8 * hh];
+        // Row col + 32 kb: block col % NB, row-in-block col / NB + kb * 32 / NB
+        // (kb * 32 / NB rows = 512 bytes), chunk 2 t + hh.
+        const uint8_t* krow = &k_sh[buf][(col % NB) * KB + (col / NB) * RB + 16 * hh];
         s[0] = f32x16{};
         s[1] = f32x16{};
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-                const i16x8 a = *reinterpret_cast<const i16x8*>(krow + kb * 32 * KS + 16 * t);
+                const i16x8 a = *reinterpret_cast<const i16x8*>(krow + kb * 512 + 32 * t);
                 s[kb] = M::mfma(a, qop[t], s[kb]);
             }
         }
@@ -267,17 +276,16 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, 1) void prefill_mfma_kernel(Param
     if (t_first < n_tiles) {
         fetch_k(t_first);
         fetch_v(t_first);
-        stash_k(t_first & 1);
-        if (t_first + 1 < n_tiles) {
-            fetch_k(t_first + 1);
-            stash_k((t_first + 1) & 1);
-        }
-        stash_v(t_first & 1);
+        if (t_first + 1 < n_tiles) fetch_k(t_first + 1);
     }
+    dma_wait();
     __syncthreads();
 
     f32x16 s_cur[2];
-    if (t_first < n_tiles) scores(t_first & 1, s_cur);
+    if (t_first < n_tiles) scores(kbuf(t_first), s_cur);
+    // With two K buffers the first iteration refills this one: every wave
+    // must have read it.
+    if (kKBufs == 2) __syncthreads();
     const bool cap = kVar && p.softcap > 0.f;
     const float cap_k2 = cap ? 2.f * kLog2e * p.scale / p.softcap : 0.f;
     const float cap_back = cap ? p.softcap / p.scale : 0.f;
@@ -359,7 +367,7 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, 1) void prefill_mfma_kernel(Param
         // runs (same basic block, so the two interleave).  After the last tile
         // the buffer holds stale keys and the result is discarded.
         f32x16 s_next[2];
-        scores((tile + 1) & 1, s_next);
+        scores(kbuf(tile + 1), s_next);
         // -- p = exp2(s*c - m*c), rounded to the element type --
         i16x8 pop[2][2];
 #pragma unroll
@@ -387,20 +395,23 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, 1) void prefill_mfma_kernel(Param
         for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
             for (int st = 0; st < 2; ++st) {
-                const int row = kb * 32 + 16 * st + 4 * hh + (gi >> 2);
-                const uint16_t* v0 = &v_sh[vb][row * VS + dsub];
-                const uint16_t* v1 = v0 + 8 * VS;
+                // Rows R0 + u (u = 4 hh + gi / 4 < 8) and R0 + u + 8, R0 = 32 kb + 16 st:
+                // block (R0 % NB) + u, row-in-block R0 / NB (u + 8 wraps to the
+                // next row of the same block when NB = 8).
+                const int u = 4 * hh + (gi >> 2);
+                const int r0 = kb * 32 + 16 * st;
+                const uint8_t* v0 = &v_sh[vb][((r0 % NB) + u) * VB + (r0 / NB) * RB + 2 * dsub];
+                const uint8_t* v1 = v0 + (NB > 8 ? 8 * VB : RB);
 #pragma unroll
                 for (int d = 0; d < ND; ++d) {
-                    const i16x4 lo = tr_read(v0 + 32 * d);
-                    const i16x4 hi = tr_read(v1 + 32 * d);
+                    const i16x4 lo = tr_read(reinterpret_cast<const uint16_t*>(v0 + 64 * d));
+                    const i16x4 hi = tr_read(reinterpret_cast<const uint16_t*>(v1 + 64 * d));
                     const i16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
                     acc[d] = M::mfma(a, pop[kb][st], acc[d]);
                 }
             }
         }
-        if (more_k) stash_k(tile & 1);
-        if (more_v) stash_v((tile + 1) & 1);
+        dma_wait();
         __syncthreads();
         s_cur[0] = s_next[0];
         s_cur[1] = s_next[1];
