@@ -2,10 +2,11 @@
 // accumulation on the gfx950 matrix cores (head dims that are multiples of 8,
 // up to 256).
 //
-// Work decomposition.  A workgroup of 8 waves owns one (batch, kv head) and
-// 256 query rows that read it: gw query heads of the group (gw = 8, 4, 2 or 1,
-// the largest that divides Hq/Hkv) times 256/gw consecutive positions.  Each
-// wave owns 32 rows of one head.  One K/V tile load thus serves every query
+// Work decomposition.  A workgroup of W waves (8 for head dim 128, else 4)
+// owns one (batch, kv head) and 32 W query rows that read it: gw query heads
+// of the group (gw = 8, 4, 2 or 1, the largest that divides Hq/Hkv and is at
+// most W) times 32 W / gw consecutive positions.  Each wave owns 32 rows of
+// one head.  One K/V tile load thus serves every query
 // head of the group that shares it (llm.istanbul "05_attention", "GQA").  The
 // keys are visited in increasing order, 64 per tile, staged through LDS (one
 // barrier per tile) by coalesced 16-byte raw-buffer loads that write LDS
@@ -62,13 +63,17 @@ using namespace mfma;
 constexpr int kBN = 64;        // keys per tile
 constexpr float kSlack = 8.f;  // lazy-rescale threshold, base-2 units
 
-// Workgroup shape per padded head dim DP: 8 waves (two per SIMD) of 32 query
-// rows; for DP = 256 a wave's Q operand, accumulators and scores need about
-// 300 registers, so 4 waves (one per SIMD, 512 registers each).  A head dim
-// D < DP that is a multiple of 8 runs padded: columns d >= D load as zeros
-// and are not stored.
+// Workgroup shape per padded head dim DP, waves of 32 query rows.  DP = 128:
+// 8 waves, two per SIMD (about 230 registers each).  DP = 256: a wave's Q
+// operand, accumulators and scores need about 300 registers, so 4 waves (one
+// per SIMD, 512 registers each).  DP = 64: under 170 registers a wave, so
+// workgroups of 4 waves, three per CU -- three waves per SIMD hide more of the
+// exponentials, which weigh twice as much against the matrix work at this
+// head dim.  A head dim D < DP that is a multiple of 8 runs padded: columns
+// d >= D load as zeros and are not stored.
 template <int DP> struct Cfg {
-    static constexpr int kWaves = DP == 256 ? 4 : 8;
+    static constexpr int kWaves = DP == 128 ? 8 : 4;
+    static constexpr int kMinBlocks = DP == 64 ? 3 : 1;   // resident workgroups per CU
     static constexpr int kThreads = 64 * kWaves;
     static constexpr int kRows = 32 * kWaves;   // query rows (all heads) per workgroup
 };
@@ -89,9 +94,8 @@ template <int D> struct Tile {
 };
 
 template <bool kBf16, int D, bool kMask, bool kVar>
-__global__ __launch_bounds__(Cfg<D>::kThreads, 1) void prefill_mfma_kernel(Params p, int n_qblk,
-                                                                         int gw, int xcd_units,
-                                                                         int mask_vec4) {
+__global__ __launch_bounds__(Cfg<D>::kThreads, Cfg<D>::kMinBlocks) void prefill_mfma_kernel(
+    Params p, int n_qblk, int gw, int xcd_units, int mask_vec4) {
     using M = Mma<kBf16>;
     using TL = Tile<D>;
     constexpr int kRows = Cfg<D>::kRows, kWaves = Cfg<D>::kWaves, kThreads = Cfg<D>::kThreads;
@@ -456,7 +460,9 @@ int heads_per_block(int group, int waves) {
     return 1;
 }
 
-int waves_for(int DP) { return DP == 256 ? Cfg<256>::kWaves : Cfg<128>::kWaves; }
+int waves_for(int DP) {
+    return DP == 64 ? Cfg<64>::kWaves : (DP == 128 ? Cfg<128>::kWaves : Cfg<256>::kWaves);
+}
 
 int64_t block_count(const Params& p) {
     const int waves = waves_for(padded_dim(p.D)), rows = 32 * waves;
