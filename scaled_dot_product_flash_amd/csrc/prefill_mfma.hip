@@ -93,6 +93,48 @@ template <int D> struct Tile {
     static constexpr int RB = 2 * D;                          // row bytes
 };
 
+// Staging plan per padded head dim.  K tiles rotate over NK LDS buffers and
+// V tiles over NV (tile t uses buffer (t - first tile) mod NK, resp. NV); K
+// is loaded DK tiles ahead and V DV tiles ahead.  A buffer is refilled only
+// after the barrier that ends the last iteration reading it: that needs
+// DV <= NV - 1 and DK <= NK - 1, except that D = 256, with room for two K
+// buffers only, loads K two ahead into the buffer the prologue's score reads
+// used and puts a barrier after those reads.
+//
+// kAsm: the loads are issued as instructions the compiler does not see into
+// (see load_lds16), so it does not hold every later LDS read for them and the
+// loads overlap the next tile's work; the kernel then waits for exactly the
+// loads the next tile needs.  kTop: the loads are issued at the top of the
+// iteration (else after its mask reads).  D = 128 and 256 run with kAsm and
+// deep prefetch; D = 64 (three workgroups per CU, little LDS each) measured
+// best with compiler-visible loads at the top of the iteration.
+template <int D> struct Stage;
+template <> struct Stage<64> {
+    static constexpr int NK = 3, NV = 2, DK = 2, DV = 1;
+    static constexpr bool kPrologueBarrier = false, kAsm = false, kTop = true;
+};
+template <> struct Stage<128> {
+    static constexpr int NK = 4, NV = 4, DK = 3, DV = 3;
+    static constexpr bool kPrologueBarrier = false, kAsm = true, kTop = false;
+};
+template <> struct Stage<256> {
+    static constexpr int NK = 2, NV = 2, DK = 2, DV = 1;
+    static constexpr bool kPrologueBarrier = true, kAsm = true, kTop = false;
+};
+
+// One 16-byte-per-lane buffer load into LDS at lds_byte + 16 * lane (the
+// LDS address goes through M0; one wait state after writing M0).  Written as
+// an instruction of its own so that the compiler, which cannot tell which LDS
+// bytes such a load writes, does not hold later LDS reads of other buffers
+// for it.  The kernel waits for these loads itself (vmcnt, in issue order)
+// before the barrier that publishes a tile.
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rs, uint32_t lds_byte,
+                                           uint32_t voff) {
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(rs), "{m0}"(lds_byte));
+}
+
 template <bool kBf16, int D, bool kMask, bool kVar>
 __global__ __launch_bounds__(Cfg<D>::kThreads, Cfg<D>::kMinBlocks) void prefill_mfma_kernel(
     Params p, int n_qblk, int gw, int xcd_units, int mask_vec4) {
@@ -106,13 +148,12 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, Cfg<D>::kMinBlocks) void prefill_
     constexpr int NT = D / 16;   // 16-wide d-steps of the score product
     constexpr int ND = D / 32;   // 32-row d-tiles of the output
     constexpr int NB = TL::NB, KB = TL::KB, VB = TL::VB, RB = TL::RB;
-    // K is triple buffered when it fits (D <= 128): K(t) lives in buffer t % 3,
-    // so the refill of iteration t (K(t+2)) never lands in the buffer the
-    // previous iteration or the prologue read.  D = 256 double buffers and
-    // puts a barrier after the prologue's score reads instead.
-    constexpr int kKBufs = D <= 128 ? 3 : 2;
-    __shared__ __attribute__((aligned(16))) uint8_t k_sh[kKBufs][NB * KB];
-    __shared__ __attribute__((aligned(16))) uint8_t v_sh[2][NB * VB];
+    using SP = Stage<D>;
+    static_assert(SP::DV <= SP::NV - 1, "a V buffer would be refilled while read");
+    static_assert(SP::DK <= SP::NK - 1 || (SP::DK == SP::NK && SP::kPrologueBarrier),
+                  "a K buffer would be refilled while read");
+    __shared__ __attribute__((aligned(16))) uint8_t k_sh[SP::NK][NB * KB];
+    __shared__ __attribute__((aligned(16))) uint8_t v_sh[SP::NV][NB * VB];
 
     // ---- which (b, kv head, head slice, query block) this workgroup owns --
     // Heaviest causal blocks first.  When the (batch, kv-head) units split
@@ -217,10 +258,10 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, Cfg<D>::kMinBlocks) void prefill_
         }
     }
 
-    // ---- staging: HBM -> LDS.  K runs one tile ahead of V: while tile t's
-    // softmax and P V run, tile t+1's scores are computed from LDS, and the
-    // loads of K(t+2) and V(t+1) land in the free buffers; each wave waits for
-    // its own loads before the barrier that ends the tile.  Each wave loads NB / kWaves blocks per tensor per tile straight into LDS
+    // ---- staging: HBM -> LDS.  While tile t's softmax and P V run, tile
+    // t+1's scores are computed from LDS, and the loads of K(t+DK) and V(t+DV)
+    // land in free buffers; before the barrier that ends the tile each wave
+    // waits for its own loads that the next tile needs.  Each wave loads NB / kWaves blocks per tensor per tile straight into LDS
     // (lane l fills bytes 16 l .. 16 l + 15 of its block): in block I, lane l
     // holds row I + NB * (l / (D/8)), 16-byte chunk l % (D/8).  Rows past the
     // key length and padded columns (d >= true head dim) read out of the
@@ -236,16 +277,28 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, Cfg<D>::kMinBlocks) void prefill_
             const uint32_t off =
                 8 * ld_c < Dt ? static_cast<uint32_t>((key * static_cast<int>(sr) + 8 * ld_c) * 2)
                               : kOutOfRange;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rs, (__attribute__((address_space(3))) void*)(buf + I * stride), 16, off, 0, 0, 0);
+            if constexpr (SP::kAsm)
+                load_lds16(rs,
+                           static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+                               (__attribute__((address_space(3))) uint8_t*)(buf + I * stride))),
+                           off);
+            else
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rs, (__attribute__((address_space(3))) void*)(buf + I * stride), 16, off, 0, 0,
+                    0);
         }
     };
-    auto kbuf = [&](int tile) { return kKBufs == 3 ? tile % 3 : tile & 1; };
+    auto kbuf = [&](int tile) { return (tile - t_first) % SP::NK; };
+    auto vbuf = [&](int tile) { return (tile - t_first) % SP::NV; };
     auto fetch_k = [&](int tile) { dma(krs, p.ks.sr, k_sh[kbuf(tile)], KB, tile); };
-    auto fetch_v = [&](int tile) { dma(vrs, p.vs.sr, v_sh[tile & 1], VB, tile); };
-    // Waits for this wave's direct loads (vmcnt 0; expcnt and lgkmcnt left
-    // free), before the barrier that publishes a tile.
-    auto dma_wait = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };
+    auto fetch_v = [&](int tile) { dma(vrs, p.vs.sr, v_sh[vbuf(tile)], VB, tile); };
+    // Waits until at most n of this wave's loads are in flight (vmcnt n;
+    // expcnt and lgkmcnt left free).  Loads complete in issue order.
+    auto dma_wait_keep = [&](int n) {
+        if (n == 0) __builtin_amdgcn_s_waitcnt(0x0F70);
+        else if (n == kLoadsW) __builtin_amdgcn_s_waitcnt(0x0F70 | kLoadsW);
+        else __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * kLoadsW));
+    };
     // The two 32-key blocks' MFMA chains alternate, so consecutive MFMAs are
     // independent.
     auto scores = [&](int buf, f32x16 (&s)[2]) {
@@ -276,29 +329,28 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, Cfg<D>::kMinBlocks) void prefill_
 #pragma unroll
     for (int d = 0; d < ND; ++d) acc[d] = f32x16{};
 
-    // LDS buffers go by the parity of the absolute tile index.
-    if (t_first < n_tiles) {
-        fetch_k(t_first);
-        fetch_v(t_first);
-        if (t_first + 1 < n_tiles) fetch_k(t_first + 1);
-    }
-    dma_wait();
+    // Prologue: K of the first DK tiles and V of the first DV.
+    for (int i = 0; i < SP::DK; ++i)
+        if (t_first + i < n_tiles) fetch_k(t_first + i);
+    for (int i = 0; i < SP::DV; ++i)
+        if (t_first + i < n_tiles) fetch_v(t_first + i);
+    dma_wait_keep(0);
     __syncthreads();
 
     f32x16 s_cur[2];
     if (t_first < n_tiles) scores(kbuf(t_first), s_cur);
-    // With two K buffers the first iteration refills this one: every wave
-    // must have read it.
-    if (kKBufs == 2) __syncthreads();
+    if (SP::kPrologueBarrier) __syncthreads();
     const bool cap = kVar && p.softcap > 0.f;
     const float cap_k2 = cap ? 2.f * kLog2e * p.scale / p.softcap : 0.f;
     const float cap_back = cap ? p.softcap / p.scale : 0.f;
 
     for (int tile = t_first; tile < n_tiles; ++tile) {
-        const bool more_k = tile + 2 < n_tiles;
-        const bool more_v = tile + 1 < n_tiles;
-        if (more_k) fetch_k(tile + 2);
-        if (more_v) fetch_v(tile + 1);
+        const bool more_k = tile + SP::DK < n_tiles;
+        const bool more_v = tile + SP::DV < n_tiles;
+        if (SP::kTop) {
+            if (more_k) fetch_k(tile + SP::DK);
+            if (more_v) fetch_v(tile + SP::DV);
+        }
         const int64_t j0 = static_cast<int64_t>(tile) * kBN;
         const bool sees = j0 < wave_hi;
 
@@ -329,6 +381,12 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, Cfg<D>::kMinBlocks) void prefill_
                         s_cur[kb][4 * u + e] = fmaf(mv[e], inv_scale, s_cur[kb][4 * u + e]);
                 }
             }
+        }
+        // Loads for later tiles (K before V), after this tile's mask reads so
+        // that waiting on those does not wait on these.
+        if (!SP::kTop) {
+            if (more_k) fetch_k(tile + SP::DK);
+            if (more_v) fetch_v(tile + SP::DV);
         }
         // -- hide keys past the length / causal bound / below the window
         // (edge tiles only) --
@@ -394,7 +452,7 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, Cfg<D>::kMinBlocks) void prefill_
         // was hidden), so the products add exact zeros.
         const int gi = lane & 15;
         const int dsub = 16 * ((lane >> 4) & 1) + 4 * (gi & 3);
-        const int vb = tile & 1;
+        const int vb = vbuf(tile);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -415,7 +473,13 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, Cfg<D>::kMinBlocks) void prefill_
                 }
             }
         }
-        dma_wait();
+        // The next iteration reads K(t+2) and V(t+1); loads issued after those
+        // (this iteration's V when DV >= 2, and its K too when DK >= 3) may
+        // stay in flight.
+        int keep = 0;
+        if (SP::DV >= 2 && more_v) keep += kLoadsW;
+        if (SP::DK >= 3 && SP::DV >= 2 && more_k) keep += kLoadsW;
+        dma_wait_keep(keep);
         __syncthreads();
         s_cur[0] = s_next[0];
         s_cur[1] = s_next[1];
