@@ -263,6 +263,31 @@ def test_matrix_core_path_is_used_and_matches_generic(dtype, D, monkeypatch):
     pu.compare(o1, ro, l1, rl, dtype, "zero", what="mfma vs oracle")
 
 
+# Key ranges of 1 to 5 tiles of 64 around each head dim's staging plan (how
+# many K / V tiles are loaded ahead and into how many buffers), with ragged
+# per-entry lengths ("cross": one entry empty, one full), so that prologues
+# shorter than the prefetch distance, the last tiles' waits and the buffer
+# rotation all run; the windowed cases start the key loop past tile 0.
+STAGING = [(dt, D, Lk, win) for (dt, D) in (("f16", 64), ("bf16", 128), ("f16", 128), ("bf16", 256))
+           for Lk in (1, 64, 65, 128, 129, 192, 193, 256, 320) for win in (-1,)]
+STAGING += [("bf16", 128, 320, 70), ("f16", 64, 320, 70), ("bf16", 256, 257, 100)]
+
+
+@pytest.mark.parametrize("cfg", STAGING, ids=lambda c: "x".join(map(str, c)))
+def test_staging_tile_counts(cfg):
+    import scaled_dot_product_flash_amd as sdpa
+    dtype, D, Lk, win = cfg
+    spec = synth.Spec("staging", 4, 8, 2, 70 if win < 0 else Lk, Lk, D, dtype, seed=Lk + D,
+                      causal=win >= 0, lens="cross", lens_zero_at=1, lens_full_at=2,
+                      local_window=win, lse=True)
+    case = synth.generate(spec)
+    for policy in ("nan", "zero"):
+        o, lse, _ = pu.run_hip(case, policy)
+        assert sdpa.last_kernel() == "prefill_mfma"
+        ro, rl = pu.run_oracle(case, policy)
+        pu.compare(o, ro, lse, rl, dtype, policy, what=str(cfg))
+
+
 DECODE = [
     # dtype, B, Hq, Hkv, cap, D, lens
     ("f16", 6, 32, 8, 3000, 128, [1, 3000, 0, 257, 1024, 2999]),
