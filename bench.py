@@ -164,7 +164,8 @@ def other_workloads(sdpa, synth, steps: int, warmup: int):
     out = []
     specs = [synth.WORKLOADS[n] for n in ("tiny_f32", "causal_gqa_f32", "cross_mask_f16")]
     specs += [synth.EXTRA_WORKLOADS[n]
-              for n in ("chunk_f16", "window_bf16", "softcap_sink_bf16", "docs_bf16", "d96_bf16",
+              for n in ("chunk_f16", "long_chunk_bf16", "window_bf16", "softcap_sink_bf16",
+                        "docs_bf16", "d96_bf16",
                         "d256_bf16")]
     for spec in specs:
         case = synth.generate(spec)

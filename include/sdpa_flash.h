@@ -179,9 +179,18 @@ typedef struct attn_problem {
  *   lse        device float32 log-sum-exp of each row's scores or NULL;
  *              -inf for a row with no visible key, NaN for a NaN row.
  *   workspace  device scratch of at least attn_workspace_size(p, FORWARD)
- *              bytes (NULL allowed when that size is 0).
+ *              bytes, 16-byte aligned (NULL allowed when that size is 0).
+ *              It is needed when the query rows give too few workgroups to
+ *              fill the GPU (bf16/fp16: at most half of its resident
+ *              workgroup slots; fp32: few row blocks): the keys are then cut
+ *              into ranges whose partial (max, sum, accumulator) records go
+ *              to the workspace, and a second kernel merges each row's
+ *              ranges in order (OneGPU "Attention", "Accuracy at long key
+ *              lengths", last paragraph).  The size depends on the shape
+ *              only; the contents need no initialisation and are scratch.
  *   stream     hipStream_t to enqueue on.
- * Returns ATTN_OK, or an error with nothing enqueued.
+ * Returns ATTN_OK, or an error with nothing enqueued (ATTN_ERR_WORKSPACE
+ * when a needed workspace is missing or too small).
  */
 attn_status attn_forward(const attn_problem* p, const void* q, const void* k, const void* v,
                          void* o, const float* mask, const int32_t* key_lens, float* lse,
@@ -193,9 +202,11 @@ attn_status attn_forward(const attn_problem* p, const void* q, const void* k, co
  * GroupQueryAttention README, split-K decode variants and BNSH caches).
  * Same arguments and semantics as attn_forward, with p->q_len == 1 and
  * p->k_len the cache capacity; key_lens gives the live length of each batch
- * entry.  The keys are cut into fixed ranges (a function of the shape only);
- * each range's partial (max, sum, accumulator) goes to the workspace and a
- * second kernel merges them in range order.
+ * entry.  The live keys of all (batch entry, kv head) pairs are cut, on the
+ * device from key_lens, into equal contiguous shares over a fixed set of
+ * waves; each share's partial (max, sum, accumulator) goes to the workspace
+ * (whose size depends on the shape only) and a second kernel merges a row's
+ * partials in key order.
  */
 attn_status attn_decode(const attn_problem* p, const void* q, const void* k, const void* v,
                         void* o, const float* mask, const int32_t* key_lens, float* lse,

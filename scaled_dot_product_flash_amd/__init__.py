@@ -108,6 +108,15 @@ def last_kernel() -> str:
     return load_library().attn_last_kernel().decode()
 
 
+_last_ws = 0
+
+
+def last_workspace_bytes() -> int:
+    """Workspace bytes the last forward/decode call of this module asked the
+    library for (nonzero when it split the keys into ranges)."""
+    return _last_ws
+
+
 def _check(status: int):
     if status != OK:
         raise AttnError(status, last_error())
@@ -244,7 +253,9 @@ def _run(op: int, q, k, v, *, layout: str, kv_layout: str | None, causal: bool,
         lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device)
         p.lse = Layout(0, Hq * Lq, Lq, 1)
     lib = load_library()
+    global _last_ws
     ws_bytes = workspace_size(p, op)
+    _last_ws = ws_bytes
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
     with torch.cuda.device(q.device):
         s = stream if stream is not None else torch.cuda.current_stream(q.device)

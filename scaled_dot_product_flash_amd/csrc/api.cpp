@@ -115,6 +115,7 @@ attn_status validate(const attn_problem* p, bool check_ptrs, const void* q, cons
 sdpa::Params make_params(const attn_problem* p, const void* q, const void* k, const void* v,
                          void* o, const float* mask, const int32_t* key_lens, float* lse) {
     sdpa::Params r{};
+    r.n_split = 1;
     const size_t es = elem_size(p->dtype);
     auto adv = [&](const void* base, int64_t off) -> const void* {
         return base ? static_cast<const char*>(base) + off * static_cast<int64_t>(es) : nullptr;
@@ -191,13 +192,17 @@ size_t decode_ws(const attn_problem* p) {
                     : 0;
 }
 
-// Workspace of the fp32 prefill path (key-range split); shape only.
+// Workspace of the prefill paths' key-range splits (fp32 kernel; bf16/fp16
+// matrix-core kernel on small grids); shape only.
 size_t forward_ws(const attn_problem* p) {
-    const bool shape_ok = p->dtype == ATTN_DTYPE_F32 &&
-                          (p->head_dim == 32 || p->head_dim == 64 || p->head_dim == 128);
-    return shape_ok ? sdpa::prefill_f32_workspace_bytes(p->batch, p->q_heads, p->q_len, p->k_len,
-                                                        p->head_dim)
-                    : 0;
+    if (p->dtype == ATTN_DTYPE_F32) {
+        const bool shape_ok = p->head_dim == 32 || p->head_dim == 64 || p->head_dim == 128;
+        return shape_ok ? sdpa::prefill_f32_workspace_bytes(p->batch, p->q_heads, p->q_len,
+                                                            p->k_len, p->head_dim)
+                        : 0;
+    }
+    return sdpa::prefill_mfma_workspace_bytes(p->batch, p->q_heads, p->kv_heads, p->q_len,
+                                              p->k_len, p->head_dim);
 }
 
 attn_status attn_workspace_size(const attn_problem* p, int32_t op, size_t* bytes) {
@@ -226,9 +231,24 @@ attn_status attn_forward(const attn_problem* p, const void* q, const void* k, co
     sdpa::Params prm = make_params(p, q, k, v, o, mask, key_lens, lse);
     const auto dt = static_cast<sdpa::DType>(p->dtype);
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    if (!force_generic() && sdpa::prefill_mfma_supported(prm, dt)) {
-        g_kernel = "prefill_mfma";
-        return launched(sdpa::launch_prefill_mfma(prm, dt, s));
+    if (!force_generic() && (dt == sdpa::DType::BF16 || dt == sdpa::DType::F16)) {
+        sdpa::prefill_mfma_plan(p->batch, p->q_heads, p->kv_heads, p->q_len, p->k_len,
+                                p->head_dim, &prm.split_len, &prm.n_split);
+        if (sdpa::prefill_mfma_supported(prm, dt)) {
+            if (prm.n_split > 1) {
+                const size_t need = forward_ws(p);
+                if (!workspace || workspace_bytes < need)
+                    return fail(ATTN_ERR_WORKSPACE, "forward needs %zu workspace bytes, got %zu",
+                                need, workspace ? workspace_bytes : size_t(0));
+                if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+                    return fail(ATTN_ERR_INVALID, "workspace must be 16-byte aligned");
+                prm.ws = workspace;
+            }
+            g_kernel = "prefill_mfma";
+            return launched(sdpa::launch_prefill_mfma(prm, dt, s));
+        }
+        prm.n_split = 1;
+        prm.split_len = 0;
     }
     sdpa::prefill_f32_plan(p->batch, p->q_heads, p->q_len, p->k_len, &prm.split_len, &prm.n_split);
     if (!force_generic() && sdpa::prefill_f32_supported(prm, dt)) {

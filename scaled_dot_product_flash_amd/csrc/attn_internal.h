@@ -42,8 +42,8 @@ struct Params {
     const float* k_scale;
     const float* v_scale;
     const int32_t* doc_start;   // nullable: per (b, i) first visible key
-    int32_t n_split;       // key ranges per (b, h) for the fp32 split kernel
-    int32_t split_len;     // keys per range (multiple of the tile)
+    int32_t n_split;       // key ranges per row block (1: no split); 16-byte aligned ws
+    int32_t split_len;     // keys per range (multiple of the kernel's tile)
 };
 
 enum class DType : int { F32 = 0, F16 = 1, BF16 = 2 };
@@ -51,6 +51,9 @@ enum class DType : int { F32 = 0, F16 = 1, BF16 = 2 };
 // Launchers return the hipError_t of the launch.
 hipError_t launch_generic(const Params& p, DType dt, hipStream_t s);
 
+void prefill_mfma_plan(int B, int Hq, int Hkv, int Lq, int Lk, int D, int* split_len,
+                       int* n_split);
+size_t prefill_mfma_workspace_bytes(int B, int Hq, int Hkv, int Lq, int Lk, int D);
 bool prefill_mfma_supported(const Params& p, DType dt);
 bool decode_split_supported(const Params& p, DType dt);
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int D);

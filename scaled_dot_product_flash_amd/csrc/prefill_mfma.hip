@@ -64,7 +64,7 @@ constexpr int kBN = 64;        // keys per tile
 constexpr float kSlack = 8.f;  // lazy-rescale threshold, base-2 units
 
 // Workgroup shape per padded head dim DP, waves of 32 query rows.  DP = 128:
-// 8 waves, two per SIMD (about 230 registers each).  DP = 256: a wave's Q
+// 8 waves, two per SIMD (about 205 registers each).  DP = 256: a wave's Q
 // operand, accumulators and scores need about 300 registers, so 4 waves (one
 // per SIMD, 512 registers each).  DP = 64: under 170 registers a wave, so
 // workgroups of 4 waves, three per CU -- three waves per SIMD hide more of the
@@ -160,9 +160,12 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, Cfg<D>::kMinBlocks) void prefill_
     // evenly over the 8 XCDs (consecutive workgroups go to consecutive XCDs),
     // each XCD keeps whole units so the workgroups sharing K/V share its L2.
     const int n_slice = p.group / gw;           // head slices per kv head
+    // With a key-range split (small grids), consecutive workgroups take the
+    // ranges of one query block.
+    const int rng = static_cast<int>(blockIdx.x) % p.n_split;
     int b, g, slice, qb;
     {
-        const int L = blockIdx.x;
+        const int L = static_cast<int>(blockIdx.x) / p.n_split;
         if (xcd_units > 0) {
             const int xcd = L & 7, slot = L >> 3;
             const int per = xcd_units * n_slice;
@@ -209,7 +212,7 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, Cfg<D>::kMinBlocks) void prefill_
         wave_hi = wb < 0 ? 0 : (wb < wave_hi ? wb : wave_hi);
     }
     if (qw0 >= p.Lq) wave_hi = 0;
-    const int n_tiles = static_cast<int>((blk_hi + kBN - 1) / kBN);
+    int n_tiles = static_cast<int>((blk_hi + kBN - 1) / kBN);
     // Under a local window the block's first row sees the lowest keys, and a
     // tile below the wave's last row's window edge needs the element test.
     // Lower key bounds (local window, document starts; variant kernel only):
@@ -238,6 +241,12 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, Cfg<D>::kMinBlocks) void prefill_
 #pragma unroll
         for (int i = 0; i < kWaves; ++i) bm = min(bm, blk_min[i]);
         t_first = bm == INT32_MAX ? n_tiles : bm / kBN;
+    }
+
+    if (p.n_split > 1) {   // this workgroup's key range: tiles [r_lo, r_hi)
+        const int r_lo = rng * (p.split_len / kBN), r_hi = r_lo + p.split_len / kBN;
+        t_first = t_first > r_lo ? t_first : r_lo;
+        n_tiles = n_tiles < r_hi ? n_tiles : r_hi;
     }
 
     const uint16_t* qg = static_cast<const uint16_t*>(p.q);
@@ -487,6 +496,30 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, Cfg<D>::kMinBlocks) void prefill_
 
     // ---- epilogue: O = acc / l (or the masked-row policy), LSE = m + log l --
     float l_tot = halves_sum(l_sum);
+    if (p.n_split > 1) {
+        // Partial record of this key range, (m, l, acc) in raw-score units
+        // with acc unnormalised; the merge folds a row's ranges in order and
+        // applies the sink, the masked-row policy and the LSE.
+        if (qrow < p.Lq) {
+            // Range-major records: [range][b][h][row][m, l, -, -, acc[D]].
+            const int RS = p.D + 4;
+            float* rec = static_cast<float*>(p.ws) +
+                         (((static_cast<int64_t>(rng) * p.B + b) * p.Hq + h) * p.Lq + qrow) * RS;
+#pragma unroll
+            for (int d = 0; d < ND; ++d)
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    if (32 * d + 8 * u + 4 * hh < Dt)
+                        *reinterpret_cast<f32x4*>(rec + 4 + 32 * d + 8 * u + 4 * hh) =
+                            f32x4{acc[d][4 * u], acc[d][4 * u + 1], acc[d][4 * u + 2],
+                                  acc[d][4 * u + 3]};
+            if (hh == 0) {
+                rec[0] = m_ref;
+                rec[1] = l_tot;
+            }
+        }
+        return;
+    }
     float m2 = m_ref * c;                       // base-2 reference (-inf stays -inf)
     const float fs = fold_sink(p, h, m2, l_tot);
     if (qrow < p.Lq) {
@@ -511,6 +544,55 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, Cfg<D>::kMinBlocks) void prefill_
             p.lse[b * p.ls.sb + h * p.ls.sh + qrow * p.ls.sr] = lse;
         }
     }
+}
+
+// One thread per (b, h, row, d): fold the row's key-range records in range
+// order (OneGPU "Attention", "Accuracy at long key lengths", last paragraph),
+// then the sink, the masked-row policy and the LSE as the kernel's own
+// epilogue does.
+template <typename T>
+__global__ __launch_bounds__(256) void prefill_mfma_merge_kernel(Params p) {
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    const int64_t total = static_cast<int64_t>(p.B) * p.Hq * p.Lq * p.D;
+    if (t >= total) return;
+    const int d = static_cast<int>(t % p.D);
+    const int64_t row = t / p.D;                     // (b, h, i) flattened
+    const int64_t i = row % p.Lq;
+    const int h = static_cast<int>((row / p.Lq) % p.Hq);
+    const int b = static_cast<int>(row / (static_cast<int64_t>(p.Lq) * p.Hq));
+    const int RS = p.D + 4;
+    const int64_t range_stride = total / p.D * RS;  // records of one range
+    const float* recs = static_cast<const float*>(p.ws) + row * RS;
+    const float c = p.scale_log2;
+    float M = kNegInf;
+    for (int r = 0; r < p.n_split; ++r) M = fmaxf(M, recs[r * range_stride]);
+    // Folded in range order, four records' loads issued ahead of their use.
+    float L = 0.f, A = 0.f;
+    for (int r0 = 0; r0 < p.n_split; r0 += 4) {
+        float m4[4], l4[4], a4[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const bool in = r0 + u < p.n_split;
+            const float* rec = recs + (in ? r0 + u : 0) * range_stride;
+            m4[u] = in ? rec[0] : kNegInf;
+            l4[u] = in ? rec[1] : 0.f;
+            a4[u] = in ? rec[4 + d] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (r0 + u >= p.n_split) break;
+            const float f = (m4[u] == kNegInf) ? 0.f : fast_exp2((m4[u] - M) * c);
+            L = fmaf(l4[u], f, L);
+            A = fmaf(a4[u], f, A);
+        }
+    }
+    float m2 = M * c;                            // base-2 reference (-inf stays -inf)
+    const float fs = fold_sink(p, h, m2, L);
+    const bool empty = (L == 0.f);
+    const float o = empty ? (p.masked_zero ? 0.f : __builtin_nanf("")) : A * (fs / L);
+    Elem<T>::store(p.o, b * p.os.sb + h * p.os.sh + i * p.os.sr + d, o);
+    if (p.lse && d == 0)
+        p.lse[b * p.ls.sb + h * p.ls.sh + i * p.ls.sr] = empty ? kNegInf : (m2 + fast_log2(L)) * kLn2;
 }
 
 // Padded head dim of the kernel that runs head dim D.
@@ -541,10 +623,10 @@ hipError_t launch_one(const Params& p, hipStream_t s) {
     const int gw = heads_per_block(p.group, Cfg<D>::kWaves);
     const int n_qblk = (p.Lq + kRows / gw - 1) / (kRows / gw);
     const int units = p.B * p.Hkv;
-    const int xcd_units = (units % 8 == 0) ? units / 8 : 0;
+    const int xcd_units = (units % 8 == 0 && p.n_split == 1) ? units / 8 : 0;
     const int mask_vec4 = p.mask && (reinterpret_cast<uintptr_t>(p.mask) % 16 == 0) &&
                           p.ms.sb % 4 == 0 && p.ms.sh % 4 == 0 && p.ms.sr % 4 == 0;
-    const dim3 grid(static_cast<uint32_t>(block_count(p)));
+    const dim3 grid(static_cast<uint32_t>(block_count(p) * p.n_split));
     const bool var = p.softcap > 0.f || (p.causal && p.window > 0) || p.doc_start || p.D != D;
     if (p.mask && var)
         hipLaunchKernelGGL((prefill_mfma_kernel<kBf16, D, true, true>), grid, dim3(kThreads), 0, s,
@@ -558,10 +640,53 @@ hipError_t launch_one(const Params& p, hipStream_t s) {
     else
         hipLaunchKernelGGL((prefill_mfma_kernel<kBf16, D, false, false>), grid, dim3(kThreads), 0,
                            s, p, n_qblk, gw, xcd_units, mask_vec4);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || p.n_split == 1) return e;
+    const int64_t total = static_cast<int64_t>(p.B) * p.Hq * p.Lq * p.D;
+    const dim3 mgrid(static_cast<uint32_t>((total + 255) / 256));
+    if (kBf16)
+        hipLaunchKernelGGL((prefill_mfma_merge_kernel<bf16_t>), mgrid, dim3(256), 0, s, p);
+    else
+        hipLaunchKernelGGL((prefill_mfma_merge_kernel<_Float16>), mgrid, dim3(256), 0, s, p);
     return hipGetLastError();
 }
 
 }  // namespace
+
+// Key ranges for small grids (shape only): when the query blocks would leave
+// at least half of the GPU's resident workgroup slots empty (256 CUs of an
+// MI355X; three slots per CU at head dim 64), each block's keys are cut into
+// ranges of a whole number of tiles, at least 4 tiles each and at most 32
+// ranges, aiming at two workgroups per slot.  Each range writes its rows'
+// (m, l, acc) records, which costs about as much HBM traffic as the output
+// per range, so grids that already fill the GPU are not split.
+void prefill_mfma_plan(int B, int Hq, int Hkv, int Lq, int Lk, int D, int* split_len,
+                       int* n_split) {
+    *split_len = 0;
+    *n_split = 1;
+    if (B <= 0 || Hkv <= 0 || Hq % Hkv != 0 || Lq <= 0 || Lk <= 0 || D % 8 != 0 || D > 256) return;
+    const int DP = padded_dim(D), waves = waves_for(DP), rows = 32 * waves;
+    const int group = Hq / Hkv, gw = heads_per_block(group, waves);
+    const int64_t blocks = static_cast<int64_t>((Lq + rows / gw - 1) / (rows / gw)) * B * Hkv *
+                           (group / gw);
+    const int64_t slots = 256 * (DP == 64 ? Cfg<64>::kMinBlocks : 1);
+    const int64_t tiles = (static_cast<int64_t>(Lk) + kBN - 1) / kBN;
+    if (2 * blocks > slots || tiles < 8) return;
+    int64_t n = (2 * slots + blocks - 1) / blocks;
+    if (n > tiles / 4) n = tiles / 4;
+    if (n > 32) n = 32;
+    if (n < 2) return;
+    const int64_t per = (tiles + n - 1) / n;          // tiles per range
+    *split_len = static_cast<int>(per * kBN);
+    *n_split = static_cast<int>((tiles + per - 1) / per);
+}
+
+size_t prefill_mfma_workspace_bytes(int B, int Hq, int Hkv, int Lq, int Lk, int D) {
+    int len, n;
+    prefill_mfma_plan(B, Hq, Hkv, Lq, Lk, D, &len, &n);
+    if (n <= 1) return 0;
+    return static_cast<size_t>(B) * Hq * Lq * n * (D + 4) * sizeof(float);
+}
 
 bool prefill_mfma_supported(const Params& p, DType dt) {
     if (dt != DType::BF16 && dt != DType::F16) return false;
@@ -579,7 +704,7 @@ bool prefill_mfma_supported(const Params& p, DType dt) {
     if ((static_cast<int64_t>(p.Lk) + kBN) * p.ks.sr * 2 >= (int64_t(1) << 31) ||
         (static_cast<int64_t>(p.Lk) + kBN) * p.vs.sr * 2 >= (int64_t(1) << 31))
         return false;
-    return block_count(p) < (int64_t(1) << 31);
+    return block_count(p) * p.n_split < (int64_t(1) << 31);
 }
 
 hipError_t launch_prefill_mfma(const Params& p, DType dt, hipStream_t s) {

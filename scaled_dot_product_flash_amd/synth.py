@@ -124,6 +124,13 @@ DOCS_BF16 = CAUSAL_GQA_BF16.replace(
     name="bf16 causal GQA prefill B4 H32/8 L4096 D128, packed documents (mean 512)",
     docs="packed", doc_mean=512, seed=11)
 
+# One long sequence: a chunk of 512 new rows at the end of a 32768-key cache
+# (64 query blocks, a quarter of the GPU's workgroup slots: the keys are cut
+# into ranges).
+LONG_CHUNK_BF16 = Spec("bf16 chunked prefill B1 H32/8 Lq512 cache32768 D128", 1, 32, 8, 512,
+                       32768, 128, "bf16", seed=14, kv_layout="bhsd", causal=True,
+                       causal_offset="end", lse=True)
+
 # Head dims beyond 64 / 128 on the matrix cores (96 runs padded to 128).
 D256_BF16 = CAUSAL_GQA_BF16.replace(
     name="bf16 causal GQA prefill B4 H32/8 L4096 D256", head_dim=256, seed=12)
@@ -133,6 +140,7 @@ D96_BF16 = CAUSAL_GQA_BF16.replace(
 # Workloads of the extensions beyond the five (measured and tested the same way).
 EXTRA_WORKLOADS = {
     "chunk_f16": CHUNK_F16,
+    "long_chunk_bf16": LONG_CHUNK_BF16,
     "window_bf16": WINDOW_BF16,
     "softcap_sink_bf16": SOFTCAP_SINK_BF16,
     "decode_window_f16": DECODE_WINDOW_F16,

@@ -153,7 +153,10 @@ def test_decode_workspace_is_checked_before_launch():
         setattr(p, lay, sdpa.Layout(0, L * H * 128, 128, H * 128))
     need = sdpa.workspace_size(p, sdpa.OP_DECODE)
     assert need > 0
-    assert sdpa.workspace_size(p, sdpa.OP_FORWARD) == 0
+    # As a forward problem the same shape is one small workgroup, whose keys
+    # are cut into ranges: whole records of (m, l, acc[128]) per query row.
+    fwd = sdpa.workspace_size(p, sdpa.OP_FORWARD)
+    assert fwd > 0 and fwd % (4 * 1 * (128 + 4) * 4) == 0
     rc = lib.attn_decode(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, None, None, None, 0, None)
     assert rc == sdpa.ERR_WORKSPACE
     rc = lib.attn_decode(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, None, None, FAKE,
@@ -174,6 +177,30 @@ def test_fp32_forward_split_needs_workspace():
     assert need > 0
     rc = lib.attn_forward(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, None, None, None, 0, None)
     assert rc == sdpa.ERR_WORKSPACE
+
+
+def test_matrix_core_forward_split_workspace():
+    """bf16/fp16 prefill with too few query blocks for the GPU cuts the keys
+    into ranges (shape only) and needs a 16-byte aligned workspace, checked
+    before anything is launched; the full-size prefill shape needs none."""
+    lib = sdpa.load_library()
+    p = _problem(batch=1, q_heads=8, kv_heads=2, q_len=100, k_len=8192, head_dim=128, causal=1)
+    for lay, H, L in (("q", 8, 100), ("k", 2, 8192), ("v", 2, 8192), ("o", 8, 100)):
+        setattr(p, lay, sdpa.Layout(0, L * H * 128, 128, H * 128))
+    need = sdpa.workspace_size(p, sdpa.OP_FORWARD)
+    per_range = 1 * 8 * 100 * (128 + 4) * 4
+    assert need > 0 and need % per_range == 0 and 2 <= need // per_range <= 32
+    rc = lib.attn_forward(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, None, None, None, 0, None)
+    assert rc == sdpa.ERR_WORKSPACE
+    odd = ctypes.c_void_p(0x1004)
+    rc = lib.attn_forward(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, None, None, odd, need,
+                          None)
+    assert rc == sdpa.ERR_INVALID and b"aligned" in lib.attn_last_error()
+    big = _problem(batch=4, q_heads=32, kv_heads=8, q_len=4096, k_len=4096, head_dim=128,
+                   causal=1)
+    for lay, H in (("q", 32), ("k", 8), ("v", 8), ("o", 32)):
+        setattr(big, lay, sdpa.Layout(0, 4096 * H * 128, 128, H * 128))
+    assert sdpa.workspace_size(big, sdpa.OP_FORWARD) == 0
 
 
 def test_offset_sentinels_match_c(tmp_path):

@@ -86,6 +86,22 @@ def test_chunk_f16_full_size_sampled():
     pu.compare(go, ro, gl, rl, spec.dtype, "nan", what="fp16 chunk 16x32x128 cache 8192")
 
 
+def test_long_chunk_bf16_full_size_sampled():
+    """512 new rows at the end of a 32768-key cache, batch 1: too few query
+    blocks for the GPU, so the keys are cut into ranges and merged."""
+    import scaled_dot_product_flash_amd as sdpa
+    spec = synth.EXTRA_WORKLOADS["long_chunk_bf16"]
+    case = synth.generate(spec)
+    o, lse, _ = pu.run_hip(case, "nan")
+    assert sdpa.last_workspace_bytes() > 0
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    rows = pu.sample_rows(spec, 48, seed=14)
+    ro, rl = pu.run_oracle(case, "nan", rows=rows)
+    go = o[rows[:, 0], rows[:, 1], rows[:, 2]]
+    gl = lse[rows[:, 0], rows[:, 1], rows[:, 2]]
+    pu.compare(go, ro, gl, rl, spec.dtype, "nan", what="bf16 chunk 1x32x512 cache 32768")
+
+
 def test_decode_f16_full_size_every_row():
     spec, case = _full_case("decode_f16")
     o, lse, _ = pu.run_hip(case, "nan", return_lse=True)
@@ -286,6 +302,43 @@ def test_staging_tile_counts(cfg):
         assert sdpa.last_kernel() == "prefill_mfma"
         ro, rl = pu.run_oracle(case, policy)
         pu.compare(o, ro, lse, rl, dtype, policy, what=str(cfg))
+
+
+# Prefill grids too small for the GPU: each row block's keys are cut into
+# ranges whose partial records a second kernel merges in order (checked to be
+# the path taken through the workspace the call asked for).  Long caches,
+# ragged and zero lengths, both policies, mask, window, sink and documents.
+SPLIT = {
+    "bf16_D128_chunk_end": synth.CHUNK_F16.replace(dtype="bf16", batch=2, q_heads=8, kv_heads=2,
+                                                   q_len=100, k_len=8192, lens="cross",
+                                                   lens_zero_at=1, seed=41),
+    "f16_D64_mask_lens": synth.CROSS_MASK_F16.replace(batch=2, q_heads=4, kv_heads=4, q_len=300,
+                                                      k_len=3000, seed=42),
+    "bf16_D256_window_sink": synth.CHUNK_F16.replace(dtype="bf16", batch=1, q_heads=2,
+                                                     kv_heads=1, q_len=64, k_len=2048,
+                                                     head_dim=256, lens=None, local_window=700,
+                                                     sink="heads", seed=43),
+    "bf16_D96_docs": synth.CAUSAL_GQA_BF16.replace(batch=1, q_heads=4, kv_heads=1, q_len=1500,
+                                                   k_len=1500, head_dim=96, docs="packed",
+                                                   doc_mean=300, seed=44),
+    "f16_D128_softcap_sink_zero": synth.CHUNK_F16.replace(batch=3, q_heads=4, kv_heads=1,
+                                                          q_len=1, k_len=5000, softcap=10.0,
+                                                          sink="zero", lens="cross",
+                                                          lens_zero_at=0, seed=45),
+}
+
+
+@pytest.mark.parametrize("policy", ["nan", "zero"])
+@pytest.mark.parametrize("name", sorted(SPLIT))
+def test_prefill_key_range_split(name, policy):
+    import scaled_dot_product_flash_amd as sdpa
+    spec = SPLIT[name]
+    case = synth.generate(spec)
+    o, lse, _ = pu.run_hip(case, policy)
+    assert sdpa.last_kernel() == "prefill_mfma"
+    assert sdpa.last_workspace_bytes() > 0
+    ro, rl = pu.run_oracle(case, policy)
+    pu.compare(o, ro, lse, rl, spec.dtype, policy, what=name)
 
 
 DECODE = [
