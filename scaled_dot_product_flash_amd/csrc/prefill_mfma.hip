@@ -155,34 +155,34 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, Cfg<D>::kMinBlocks) void prefill_
     __shared__ __attribute__((aligned(16))) uint8_t k_sh[SP::NK][NB * KB];
     __shared__ __attribute__((aligned(16))) uint8_t v_sh[SP::NV][NB * VB];
 
-    // ---- which (b, kv head, head slice, query block) this workgroup owns --
-    // Heaviest causal blocks first.  When the (batch, kv-head) units split
-    // evenly over the 8 XCDs (consecutive workgroups go to consecutive XCDs),
-    // each XCD keeps whole units so the workgroups sharing K/V share its L2.
+    // ---- which (b, kv head, key range, head slice, query block) this
+    // workgroup owns.  Heaviest causal blocks first.  Units are (batch, kv
+    // head, key range) triples; without a key-range split there is one range.
+    // When the units split evenly over the 8 XCDs (consecutive workgroups go
+    // to consecutive XCDs), each XCD keeps whole units, so the workgroups
+    // reading the same K/V tiles share its L2.
     const int n_slice = p.group / gw;           // head slices per kv head
-    // With a key-range split (small grids), consecutive workgroups take the
-    // ranges of one query block.
-    const int rng = static_cast<int>(blockIdx.x) % p.n_split;
-    int b, g, slice, qb;
+    int b, g, slice, qb, rng;
     {
-        const int L = static_cast<int>(blockIdx.x) / p.n_split;
+        const int L = blockIdx.x;
+        int unit;
         if (xcd_units > 0) {
             const int xcd = L & 7, slot = L >> 3;
             const int per = xcd_units * n_slice;
             qb = n_qblk - 1 - slot / per;
             const int rem = slot % per;
-            const int unit = xcd * xcd_units + rem / n_slice;
-            b = unit / p.Hkv;
-            g = unit % p.Hkv;
+            unit = xcd * xcd_units + rem / n_slice;
             slice = rem % n_slice;
         } else {
-            const int per = p.B * p.Hkv * n_slice;
+            const int per = p.B * p.Hkv * p.n_split * n_slice;
             qb = n_qblk - 1 - L / per;
             const int rem = L % per;
-            b = rem / (p.Hkv * n_slice);
-            g = (rem / n_slice) % p.Hkv;
+            unit = rem / n_slice;
             slice = rem % n_slice;
         }
+        rng = unit % p.n_split;
+        b = unit / p.n_split / p.Hkv;
+        g = unit / p.n_split % p.Hkv;
     }
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -622,8 +622,8 @@ hipError_t launch_one(const Params& p, hipStream_t s) {
     constexpr int kRows = Cfg<D>::kRows, kThreads = Cfg<D>::kThreads;
     const int gw = heads_per_block(p.group, Cfg<D>::kWaves);
     const int n_qblk = (p.Lq + kRows / gw - 1) / (kRows / gw);
-    const int units = p.B * p.Hkv;
-    const int xcd_units = (units % 8 == 0 && p.n_split == 1) ? units / 8 : 0;
+    const int units = p.B * p.Hkv * p.n_split;
+    const int xcd_units = (units % 8 == 0) ? units / 8 : 0;
     const int mask_vec4 = p.mask && (reinterpret_cast<uintptr_t>(p.mask) % 16 == 0) &&
                           p.ms.sb % 4 == 0 && p.ms.sh % 4 == 0 && p.ms.sr % 4 == 0;
     const dim3 grid(static_cast<uint32_t>(block_count(p) * p.n_split));
