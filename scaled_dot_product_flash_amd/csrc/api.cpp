@@ -202,7 +202,8 @@ size_t forward_ws(const attn_problem* p) {
                         : 0;
     }
     return sdpa::prefill_mfma_workspace_bytes(p->batch, p->q_heads, p->kv_heads, p->q_len,
-                                              p->k_len, p->head_dim);
+                                              p->k_len, p->head_dim,
+                                              p->causal && p->window > 0, p->doc_start != nullptr);
 }
 
 attn_status attn_workspace_size(const attn_problem* p, int32_t op, size_t* bytes) {
@@ -233,7 +234,8 @@ attn_status attn_forward(const attn_problem* p, const void* q, const void* k, co
     const hipStream_t s = static_cast<hipStream_t>(stream);
     if (!force_generic() && (dt == sdpa::DType::BF16 || dt == sdpa::DType::F16)) {
         sdpa::prefill_mfma_plan(p->batch, p->q_heads, p->kv_heads, p->q_len, p->k_len,
-                                p->head_dim, &prm.split_len, &prm.n_split);
+                                p->head_dim, p->causal && p->window > 0, p->doc_start != nullptr,
+                                &prm.split_len, &prm.n_split);
         if (sdpa::prefill_mfma_supported(prm, dt)) {
             if (prm.n_split > 1) {
                 const size_t need = forward_ws(p);

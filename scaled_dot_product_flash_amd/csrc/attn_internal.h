@@ -51,9 +51,11 @@ enum class DType : int { F32 = 0, F16 = 1, BF16 = 2 };
 // Launchers return the hipError_t of the launch.
 hipError_t launch_generic(const Params& p, DType dt, hipStream_t s);
 
-void prefill_mfma_plan(int B, int Hq, int Hkv, int Lq, int Lk, int D, int* split_len,
-                       int* n_split);
-size_t prefill_mfma_workspace_bytes(int B, int Hq, int Hkv, int Lq, int Lk, int D);
+// window: a causal local window is set; docs: document starts are given.
+void prefill_mfma_plan(int B, int Hq, int Hkv, int Lq, int Lk, int D, bool window, bool docs,
+                       int* split_len, int* n_split);
+size_t prefill_mfma_workspace_bytes(int B, int Hq, int Hkv, int Lq, int Lk, int D, bool window,
+                                    bool docs);
 bool prefill_mfma_supported(const Params& p, DType dt);
 bool decode_split_supported(const Params& p, DType dt);
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int D);

@@ -69,11 +69,15 @@ constexpr float kSlack = 8.f;  // lazy-rescale threshold, base-2 units
 // per SIMD, 512 registers each).  DP = 64: under 170 registers a wave, so
 // workgroups of 4 waves, three per CU -- three waves per SIMD hide more of the
 // exponentials, which weigh twice as much against the matrix work at this
-// head dim.  A head dim D < DP that is a multiple of 8 runs padded: columns
-// d >= D load as zeros and are not stored.
-template <int DP> struct Cfg {
-    static constexpr int kWaves = DP == 128 ? 8 : 4;
-    static constexpr int kMinBlocks = DP == 64 ? 3 : 1;   // resident workgroups per CU
+// head dim.  kShort (DP = 128 under a local window or document starts, where
+// each workgroup walks few key tiles): 4 waves, two workgroups per CU, so one
+// workgroup's prologue and epilogue overlap the other's tiles.  A head dim
+// D < DP that is a multiple of 8 runs padded: columns d >= D load as zeros
+// and are not stored.
+template <int DP, bool kShort = false> struct Cfg {
+    static constexpr int kWaves = (DP == 128 && !kShort) ? 8 : 4;
+    static constexpr int kMinBlocks =
+        DP == 64 ? 3 : (DP == 128 && kShort ? 2 : 1);   // resident workgroups per CU
     static constexpr int kThreads = 64 * kWaves;
     static constexpr int kRows = 32 * kWaves;   // query rows (all heads) per workgroup
 };
@@ -108,7 +112,7 @@ template <int D> struct Tile {
 // iteration (else after its mask reads).  D = 128 and 256 run with kAsm and
 // deep prefetch; D = 64 (three workgroups per CU, little LDS each) measured
 // best with compiler-visible loads at the top of the iteration.
-template <int D> struct Stage;
+template <int D, bool kShort = false> struct Stage;
 template <> struct Stage<64> {
     static constexpr int NK = 3, NV = 2, DK = 2, DV = 1;
     static constexpr bool kPrologueBarrier = false, kAsm = false, kTop = true;
@@ -118,6 +122,11 @@ template <> struct Stage<128> {
     static constexpr bool kPrologueBarrier = false, kAsm = true, kTop = false;
 };
 template <> struct Stage<256> {
+    static constexpr int NK = 2, NV = 2, DK = 2, DV = 1;
+    static constexpr bool kPrologueBarrier = true, kAsm = true, kTop = false;
+};
+// Two workgroups per CU leave each 80 KiB: two buffers per tensor.
+template <> struct Stage<128, true> {
     static constexpr int NK = 2, NV = 2, DK = 2, DV = 1;
     static constexpr bool kPrologueBarrier = true, kAsm = true, kTop = false;
 };
@@ -135,12 +144,14 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rs, uint32_t l
                  : "v"(voff), "s"(rs), "{m0}"(lds_byte));
 }
 
-template <bool kBf16, int D, bool kMask, bool kVar>
-__global__ __launch_bounds__(Cfg<D>::kThreads, Cfg<D>::kMinBlocks) void prefill_mfma_kernel(
+template <bool kBf16, int D, bool kMask, bool kVar, bool kShort>
+__global__ __launch_bounds__((Cfg<D, kShort>::kThreads), (Cfg<D, kShort>::kMinBlocks)) void
+prefill_mfma_kernel(
     Params p, int n_qblk, int gw, int xcd_units, int mask_vec4) {
     using M = Mma<kBf16>;
     using TL = Tile<D>;
-    constexpr int kRows = Cfg<D>::kRows, kWaves = Cfg<D>::kWaves, kThreads = Cfg<D>::kThreads;
+    using CF = Cfg<D, kShort>;
+    constexpr int kRows = CF::kRows, kWaves = CF::kWaves, kThreads = CF::kThreads;
     // True head dim (a multiple of 8, <= D).  Padded dims run the variant
     // kernel; in the plain one it is the compile-time D and the column guards
     // below fold away.
@@ -148,7 +159,7 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, Cfg<D>::kMinBlocks) void prefill_
     constexpr int NT = D / 16;   // 16-wide d-steps of the score product
     constexpr int ND = D / 32;   // 32-row d-tiles of the output
     constexpr int NB = TL::NB, KB = TL::KB, VB = TL::VB, RB = TL::RB;
-    using SP = Stage<D>;
+    using SP = Stage<D, kShort>;
     static_assert(SP::DV <= SP::NV - 1, "a V buffer would be refilled while read");
     static_assert(SP::DK <= SP::NK - 1 || (SP::DK == SP::NK && SP::kPrologueBarrier),
                   "a K buffer would be refilled while read");
@@ -606,40 +617,58 @@ int heads_per_block(int group, int waves) {
     return 1;
 }
 
-int waves_for(int DP) {
-    return DP == 64 ? Cfg<64>::kWaves : (DP == 128 ? Cfg<128>::kWaves : Cfg<256>::kWaves);
+// Workgroups whose key range is cut short by a local window or document
+// starts (head dim 128 runs them on the kShort shape).
+bool short_rows(bool window, bool docs) { return window || docs; }
+
+int waves_for(int DP, bool shrt) {
+    if (DP == 128) return shrt ? Cfg<128, true>::kWaves : Cfg<128>::kWaves;
+    return DP == 64 ? Cfg<64>::kWaves : Cfg<256>::kWaves;
 }
+int blocks_per_cu(int DP, bool shrt) {
+    if (DP == 128) return shrt ? Cfg<128, true>::kMinBlocks : Cfg<128>::kMinBlocks;
+    return DP == 64 ? Cfg<64>::kMinBlocks : Cfg<256>::kMinBlocks;
+}
+bool short_rows(const Params& p) { return short_rows(p.causal && p.window > 0, p.doc_start); }
 
 int64_t block_count(const Params& p) {
-    const int waves = waves_for(padded_dim(p.D)), rows = 32 * waves;
+    const int waves = waves_for(padded_dim(p.D), short_rows(p)), rows = 32 * waves;
     const int gw = heads_per_block(p.group, waves);
     const int64_t n_qblk = (p.Lq + rows / gw - 1) / (rows / gw);
     return n_qblk * p.B * p.Hkv * (p.group / gw);
 }
 
-template <bool kBf16, int D>
-hipError_t launch_one(const Params& p, hipStream_t s) {
-    constexpr int kRows = Cfg<D>::kRows, kThreads = Cfg<D>::kThreads;
-    const int gw = heads_per_block(p.group, Cfg<D>::kWaves);
-    const int n_qblk = (p.Lq + kRows / gw - 1) / (kRows / gw);
+template <bool kBf16, int D, bool kShort>
+hipError_t launch_shape(const Params& p, hipStream_t s) {
+    using CF = Cfg<D, kShort>;
+    const int gw = heads_per_block(p.group, CF::kWaves);
+    const int n_qblk = (p.Lq + CF::kRows / gw - 1) / (CF::kRows / gw);
     const int units = p.B * p.Hkv * p.n_split;
     const int xcd_units = (units % 8 == 0) ? units / 8 : 0;
     const int mask_vec4 = p.mask && (reinterpret_cast<uintptr_t>(p.mask) % 16 == 0) &&
                           p.ms.sb % 4 == 0 && p.ms.sh % 4 == 0 && p.ms.sr % 4 == 0;
-    const dim3 grid(static_cast<uint32_t>(block_count(p) * p.n_split));
+    const dim3 grid(static_cast<uint32_t>(block_count(p) * p.n_split)), blk(CF::kThreads);
     const bool var = p.softcap > 0.f || (p.causal && p.window > 0) || p.doc_start || p.D != D;
-    if (p.mask && var)
-        hipLaunchKernelGGL((prefill_mfma_kernel<kBf16, D, true, true>), grid, dim3(kThreads), 0, s,
+    if (kShort) {   // a window or document starts: always the variant kernel
+        if (p.mask)
+            hipLaunchKernelGGL((prefill_mfma_kernel<kBf16, D, true, true, kShort>), grid, blk, 0, s,
+                               p, n_qblk, gw, xcd_units, mask_vec4);
+        else
+            hipLaunchKernelGGL((prefill_mfma_kernel<kBf16, D, false, true, kShort>), grid, blk, 0,
+                               s, p, n_qblk, gw, xcd_units, mask_vec4);
+    } else if (p.mask && var) {
+        hipLaunchKernelGGL((prefill_mfma_kernel<kBf16, D, true, true, false>), grid, blk, 0, s, p,
+                           n_qblk, gw, xcd_units, mask_vec4);
+    } else if (p.mask) {
+        hipLaunchKernelGGL((prefill_mfma_kernel<kBf16, D, true, false, false>), grid, blk, 0, s, p,
+                           n_qblk, gw, xcd_units, mask_vec4);
+    } else if (var) {
+        hipLaunchKernelGGL((prefill_mfma_kernel<kBf16, D, false, true, false>), grid, blk, 0, s, p,
+                           n_qblk, gw, xcd_units, mask_vec4);
+    } else {
+        hipLaunchKernelGGL((prefill_mfma_kernel<kBf16, D, false, false, false>), grid, blk, 0, s,
                            p, n_qblk, gw, xcd_units, mask_vec4);
-    else if (p.mask)
-        hipLaunchKernelGGL((prefill_mfma_kernel<kBf16, D, true, false>), grid, dim3(kThreads), 0,
-                           s, p, n_qblk, gw, xcd_units, mask_vec4);
-    else if (var)
-        hipLaunchKernelGGL((prefill_mfma_kernel<kBf16, D, false, true>), grid, dim3(kThreads), 0,
-                           s, p, n_qblk, gw, xcd_units, mask_vec4);
-    else
-        hipLaunchKernelGGL((prefill_mfma_kernel<kBf16, D, false, false>), grid, dim3(kThreads), 0,
-                           s, p, n_qblk, gw, xcd_units, mask_vec4);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.n_split == 1) return e;
     const int64_t total = static_cast<int64_t>(p.B) * p.Hq * p.Lq * p.D;
@@ -651,6 +680,13 @@ hipError_t launch_one(const Params& p, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <bool kBf16, int D>
+hipError_t launch_one(const Params& p, hipStream_t s) {
+    if constexpr (D == 128)
+        if (short_rows(p)) return launch_shape<kBf16, D, true>(p, s);
+    return launch_shape<kBf16, D, false>(p, s);
+}
+
 }  // namespace
 
 // Key ranges for small grids (shape only): when the query blocks would leave
@@ -660,16 +696,17 @@ hipError_t launch_one(const Params& p, hipStream_t s) {
 // ranges, aiming at two workgroups per slot.  Each range writes its rows'
 // (m, l, acc) records, which costs about as much HBM traffic as the output
 // per range, so grids that already fill the GPU are not split.
-void prefill_mfma_plan(int B, int Hq, int Hkv, int Lq, int Lk, int D, int* split_len,
-                       int* n_split) {
+void prefill_mfma_plan(int B, int Hq, int Hkv, int Lq, int Lk, int D, bool window, bool docs,
+                       int* split_len, int* n_split) {
     *split_len = 0;
     *n_split = 1;
     if (B <= 0 || Hkv <= 0 || Hq % Hkv != 0 || Lq <= 0 || Lk <= 0 || D % 8 != 0 || D > 256) return;
-    const int DP = padded_dim(D), waves = waves_for(DP), rows = 32 * waves;
+    const bool shrt = short_rows(window, docs);
+    const int DP = padded_dim(D), waves = waves_for(DP, shrt), rows = 32 * waves;
     const int group = Hq / Hkv, gw = heads_per_block(group, waves);
     const int64_t blocks = static_cast<int64_t>((Lq + rows / gw - 1) / (rows / gw)) * B * Hkv *
                            (group / gw);
-    const int64_t slots = 256 * (DP == 64 ? Cfg<64>::kMinBlocks : 1);
+    const int64_t slots = 256 * blocks_per_cu(DP, shrt);
     const int64_t tiles = (static_cast<int64_t>(Lk) + kBN - 1) / kBN;
     if (2 * blocks > slots || tiles < 8) return;
     int64_t n = (2 * slots + blocks - 1) / blocks;
@@ -681,9 +718,10 @@ void prefill_mfma_plan(int B, int Hq, int Hkv, int Lq, int Lk, int D, int* split
     *n_split = static_cast<int>((tiles + per - 1) / per);
 }
 
-size_t prefill_mfma_workspace_bytes(int B, int Hq, int Hkv, int Lq, int Lk, int D) {
+size_t prefill_mfma_workspace_bytes(int B, int Hq, int Hkv, int Lq, int Lk, int D, bool window,
+                                    bool docs) {
     int len, n;
-    prefill_mfma_plan(B, Hq, Hkv, Lq, Lk, D, &len, &n);
+    prefill_mfma_plan(B, Hq, Hkv, Lq, Lk, D, window, docs, &len, &n);
     if (n <= 1) return 0;
     return static_cast<size_t>(B) * Hq * Lq * n * (D + 4) * sizeof(float);
 }
