@@ -50,6 +50,8 @@
 // a row whose reference max is still -inf uses 0 as the exponent base, so
 // exp2(-inf) = 0 and never exp2(-inf - -inf); a row with no visible key ends
 // with l == 0 and follows the masked-row policy; NaN / +inf scores make l NaN.
+#include <type_traits>
+
 #include "attn_internal.h"
 #include "device_common.h"
 #include "mfma_common.h"
@@ -144,7 +146,9 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rs, uint32_t l
                  : "v"(voff), "s"(rs), "{m0}"(lds_byte));
 }
 
-template <bool kBf16, int D, bool kMask, bool kVar, bool kShort>
+// kSplit: the workgroup covers one key range and writes partial records (a
+// compile-time variant, so kernels that do not split carry no record code).
+template <bool kBf16, int D, bool kMask, bool kVar, bool kShort, bool kSplit>
 __global__ __launch_bounds__((Cfg<D, kShort>::kThreads), (Cfg<D, kShort>::kMinBlocks)) void
 prefill_mfma_kernel(
     Params p, int n_qblk, int gw, int xcd_units, int mask_vec4) {
@@ -173,6 +177,7 @@ prefill_mfma_kernel(
     // to consecutive XCDs), each XCD keeps whole units, so the workgroups
     // reading the same K/V tiles share its L2.
     const int n_slice = p.group / gw;           // head slices per kv head
+    const int ns = kSplit ? p.n_split : 1;
     int b, g, slice, qb, rng;
     {
         const int L = blockIdx.x;
@@ -185,15 +190,15 @@ prefill_mfma_kernel(
             unit = xcd * xcd_units + rem / n_slice;
             slice = rem % n_slice;
         } else {
-            const int per = p.B * p.Hkv * p.n_split * n_slice;
+            const int per = p.B * p.Hkv * ns * n_slice;
             qb = n_qblk - 1 - L / per;
             const int rem = L % per;
             unit = rem / n_slice;
             slice = rem % n_slice;
         }
-        rng = unit % p.n_split;
-        b = unit / p.n_split / p.Hkv;
-        g = unit / p.n_split % p.Hkv;
+        rng = unit % ns;
+        b = unit / ns / p.Hkv;
+        g = unit / ns % p.Hkv;
     }
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -254,7 +259,7 @@ prefill_mfma_kernel(
         t_first = bm == INT32_MAX ? n_tiles : bm / kBN;
     }
 
-    if (p.n_split > 1) {   // this workgroup's key range: tiles [r_lo, r_hi)
+    if (kSplit) {   // this workgroup's key range: tiles [r_lo, r_hi)
         const int r_lo = rng * (p.split_len / kBN), r_hi = r_lo + p.split_len / kBN;
         t_first = t_first > r_lo ? t_first : r_lo;
         n_tiles = n_tiles < r_hi ? n_tiles : r_hi;
@@ -507,7 +512,7 @@ prefill_mfma_kernel(
 
     // ---- epilogue: O = acc / l (or the masked-row policy), LSE = m + log l --
     float l_tot = halves_sum(l_sum);
-    if (p.n_split > 1) {
+    if constexpr (kSplit) {
         // Partial record of this key range, (m, l, acc) in raw-score units
         // with acc unnormalised; the merge folds a row's ranges in order and
         // applies the sink, the masked-row policy and the LSE.
@@ -649,25 +654,29 @@ hipError_t launch_shape(const Params& p, hipStream_t s) {
                           p.ms.sb % 4 == 0 && p.ms.sh % 4 == 0 && p.ms.sr % 4 == 0;
     const dim3 grid(static_cast<uint32_t>(block_count(p) * p.n_split)), blk(CF::kThreads);
     const bool var = p.softcap > 0.f || (p.causal && p.window > 0) || p.doc_start || p.D != D;
+    auto go = [&](auto mask_c, auto var_c, auto split_c) {
+        constexpr bool kM = decltype(mask_c)::value, kV = decltype(var_c)::value;
+        constexpr bool kS = decltype(split_c)::value;
+        hipLaunchKernelGGL((prefill_mfma_kernel<kBf16, D, kM, kV, kShort, kS>), grid, blk, 0, s, p,
+                           n_qblk, gw, xcd_units, mask_vec4);
+    };
+    using T = std::true_type;
+    using F = std::false_type;
+    auto by_split = [&](auto mask_c, auto var_c) {
+        if (p.n_split > 1) go(mask_c, var_c, T{});
+        else go(mask_c, var_c, F{});
+    };
     if (kShort) {   // a window or document starts: always the variant kernel
-        if (p.mask)
-            hipLaunchKernelGGL((prefill_mfma_kernel<kBf16, D, true, true, kShort>), grid, blk, 0, s,
-                               p, n_qblk, gw, xcd_units, mask_vec4);
-        else
-            hipLaunchKernelGGL((prefill_mfma_kernel<kBf16, D, false, true, kShort>), grid, blk, 0,
-                               s, p, n_qblk, gw, xcd_units, mask_vec4);
+        if (p.mask) by_split(T{}, T{});
+        else by_split(F{}, T{});
     } else if (p.mask && var) {
-        hipLaunchKernelGGL((prefill_mfma_kernel<kBf16, D, true, true, false>), grid, blk, 0, s, p,
-                           n_qblk, gw, xcd_units, mask_vec4);
+        by_split(T{}, T{});
     } else if (p.mask) {
-        hipLaunchKernelGGL((prefill_mfma_kernel<kBf16, D, true, false, false>), grid, blk, 0, s, p,
-                           n_qblk, gw, xcd_units, mask_vec4);
+        by_split(T{}, F{});
     } else if (var) {
-        hipLaunchKernelGGL((prefill_mfma_kernel<kBf16, D, false, true, false>), grid, blk, 0, s, p,
-                           n_qblk, gw, xcd_units, mask_vec4);
+        by_split(F{}, T{});
     } else {
-        hipLaunchKernelGGL((prefill_mfma_kernel<kBf16, D, false, false, false>), grid, blk, 0, s,
-                           p, n_qblk, gw, xcd_units, mask_vec4);
+        by_split(F{}, F{});
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.n_split == 1) return e;
