@@ -171,15 +171,52 @@ prefill_mfma_kernel(
     __shared__ __attribute__((aligned(16))) uint8_t v_sh[SP::NV][NB * VB];
 
     // ---- which (b, kv head, key range, head slice, query block) this
-    // workgroup owns.  Heaviest causal blocks first.  Units are (batch, kv
-    // head, key range) triples; without a key-range split there is one range.
+    // workgroup owns.  Heaviest causal blocks first; without causality but
+    // with per-entry key lengths, longest entries first (below).  Units are
+    // (batch, kv head, key range) triples; without a key-range split there is
+    // one range.
     // When the units split evenly over the 8 XCDs (consecutive workgroups go
     // to consecutive XCDs), each XCD keeps whole units, so the workgroups
     // reading the same K/V tiles share its L2.
     const int n_slice = p.group / gw;           // head slices per kv head
     const int ns = kSplit ? p.n_split : 1;
     int b, g, slice, qb, rng;
-    {
+    const bool by_len = !p.causal && p.lens != nullptr && p.B <= 64;
+    if (by_len) {
+        // Non-causal rows with per-entry key lengths: every query block of an
+        // entry costs about its length, so the units go longest entry first
+        // (dealt round-robin over the XCDs), the query blocks inside a unit.
+        const int L = blockIdx.x;
+        const int per_unit = n_qblk * n_slice;
+        int k, rem;
+        if (xcd_units > 0) {
+            const int xcd = L & 7, slot = L >> 3;
+            k = (slot / per_unit) * 8 + xcd;
+            rem = slot % per_unit;
+        } else {
+            k = L / per_unit;
+            rem = L % per_unit;
+        }
+        qb = n_qblk - 1 - rem / n_slice;
+        slice = rem % n_slice;
+        // Rank of each entry by clamped length, longest first, ties by index.
+        const int ln = threadIdx.x & 63;
+        auto clamped = [&](int j) {
+            const int64_t v = p.lens[j];
+            return v < 0 ? int64_t(0) : (v > p.Lk ? int64_t(p.Lk) : v);
+        };
+        const int64_t li = ln < p.B ? clamped(ln) : -1;
+        int rank = 0;
+        for (int j = 0; j < p.B; ++j) {
+            const int64_t lj = clamped(j);
+            rank += (lj > li) || (lj == li && j < ln);
+        }
+        const int br = k / (p.Hkv * ns);
+        const uint64_t hit = __builtin_amdgcn_ballot_w64(ln < p.B && rank == br);
+        b = static_cast<int>(__builtin_ctzll(hit));
+        g = (k / ns) % p.Hkv;
+        rng = k % ns;
+    } else {
         const int L = blockIdx.x;
         int unit;
         if (xcd_units > 0) {

@@ -4,6 +4,8 @@ Reduced versions of the five workloads (several tiles and a ragged tail each)
 are compared in full; the full-size workloads are compared on sampled rows
 the oracle computes one by one, plus properties that hold at any size.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -339,6 +341,33 @@ def test_prefill_key_range_split(name, policy):
     assert sdpa.last_workspace_bytes() > 0
     ro, rl = pu.run_oracle(case, policy)
     pu.compare(o, ro, lse, rl, spec.dtype, policy, what=name)
+
+
+# Without causality, workgroups with per-entry key lengths are ordered
+# longest entry first (ranks computed on the device; ties by index): tied and
+# zero lengths, unit counts that do and do not split over the 8 XCDs, and
+# more than 64 entries (the plain order).
+LEN_ORDER = [
+    ("f16", 64, [300, 300, 0]),
+    ("bf16", 128, [5, 300, 300, 1, 0, 299, 64, 65]),
+    ("f16", 128, [17, 300, 0, 0, 250, 300, 1, 128, 129]),
+    ("bf16", 64, list(np.random.default_rng(3).integers(0, 301, size=65))),
+]
+
+
+@pytest.mark.parametrize("cfg", LEN_ORDER, ids=lambda c: "%s_D%d_B%d" % (c[0], c[1], len(c[2])))
+def test_length_ordered_workgroups(cfg):
+    import scaled_dot_product_flash_amd as sdpa
+    dtype, D, lens = cfg
+    spec = synth.Spec("lenorder", len(lens), 4, 2, 200, 300, D, dtype, seed=len(lens) + D,
+                      lens="uniform", lse=True)
+    case = synth.generate(spec)
+    case = dataclasses.replace(case, key_lens=np.asarray(lens, dtype=np.int32))
+    for policy in ("nan", "zero"):
+        o, lse, _ = pu.run_hip(case, policy)
+        assert sdpa.last_kernel() == "prefill_mfma"
+        ro, rl = pu.run_oracle(case, policy)
+        pu.compare(o, ro, lse, rl, dtype, policy, what=str(lens))
 
 
 DECODE = [
