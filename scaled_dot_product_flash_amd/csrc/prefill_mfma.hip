@@ -146,9 +146,12 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rs, uint32_t l
                  : "v"(voff), "s"(rs), "{m0}"(lds_byte));
 }
 
-// kSplit: the workgroup covers one key range and writes partial records (a
-// compile-time variant, so kernels that do not split carry no record code).
-template <bool kBf16, int D, bool kMask, bool kVar, bool kShort, bool kSplit>
+// kSplit: the workgroup covers one key range and writes partial records.
+// kOrder: workgroups take their units longest batch entry first (non-causal
+// problems with per-entry key lengths).  Both are compile-time variants, so
+// kernels without them carry none of their code (which would change the
+// register allocation and schedule of the tile loop).
+template <bool kBf16, int D, bool kMask, bool kVar, bool kShort, bool kSplit, bool kOrder>
 __global__ __launch_bounds__((Cfg<D, kShort>::kThreads), (Cfg<D, kShort>::kMinBlocks)) void
 prefill_mfma_kernel(
     Params p, int n_qblk, int gw, int xcd_units, int mask_vec4) {
@@ -181,8 +184,7 @@ prefill_mfma_kernel(
     const int n_slice = p.group / gw;           // head slices per kv head
     const int ns = kSplit ? p.n_split : 1;
     int b, g, slice, qb, rng;
-    const bool by_len = !p.causal && p.lens != nullptr && p.B <= 64;
-    if (by_len) {
+    if constexpr (kOrder) {
         // Non-causal rows with per-entry key lengths: every query block of an
         // entry costs about its length, so the units go longest entry first
         // (dealt round-robin over the XCDs), the query blocks inside a unit.
@@ -691,29 +693,34 @@ hipError_t launch_shape(const Params& p, hipStream_t s) {
                           p.ms.sb % 4 == 0 && p.ms.sh % 4 == 0 && p.ms.sr % 4 == 0;
     const dim3 grid(static_cast<uint32_t>(block_count(p) * p.n_split)), blk(CF::kThreads);
     const bool var = p.softcap > 0.f || (p.causal && p.window > 0) || p.doc_start || p.D != D;
-    auto go = [&](auto mask_c, auto var_c, auto split_c) {
+    auto go = [&](auto mask_c, auto var_c, auto split_c, auto order_c) {
         constexpr bool kM = decltype(mask_c)::value, kV = decltype(var_c)::value;
-        constexpr bool kS = decltype(split_c)::value;
-        hipLaunchKernelGGL((prefill_mfma_kernel<kBf16, D, kM, kV, kShort, kS>), grid, blk, 0, s, p,
-                           n_qblk, gw, xcd_units, mask_vec4);
+        constexpr bool kS = decltype(split_c)::value, kO = decltype(order_c)::value;
+        hipLaunchKernelGGL((prefill_mfma_kernel<kBf16, D, kM, kV, kShort, kS, kO>), grid, blk, 0, s,
+                           p, n_qblk, gw, xcd_units, mask_vec4);
     };
     using T = std::true_type;
     using F = std::false_type;
-    auto by_split = [&](auto mask_c, auto var_c) {
-        if (p.n_split > 1) go(mask_c, var_c, T{});
-        else go(mask_c, var_c, F{});
+    auto by_split = [&](auto mask_c, auto var_c, auto order_c) {
+        if (p.n_split > 1) go(mask_c, var_c, T{}, order_c);
+        else go(mask_c, var_c, F{}, order_c);
     };
+    // Longest entries first: non-causal with per-entry lengths (up to 64
+    // entries), on the kernels without score-rule variants.
+    const bool order = !p.causal && p.lens != nullptr && p.B <= 64;
     if (kShort) {   // a window or document starts: always the variant kernel
-        if (p.mask) by_split(T{}, T{});
-        else by_split(F{}, T{});
+        if (p.mask) by_split(T{}, T{}, F{});
+        else by_split(F{}, T{}, F{});
     } else if (p.mask && var) {
-        by_split(T{}, T{});
+        by_split(T{}, T{}, F{});
     } else if (p.mask) {
-        by_split(T{}, F{});
+        if (order) by_split(T{}, F{}, T{});
+        else by_split(T{}, F{}, F{});
     } else if (var) {
-        by_split(F{}, T{});
+        by_split(F{}, T{}, F{});
     } else {
-        by_split(F{}, F{});
+        if (order) by_split(F{}, F{}, T{});
+        else by_split(F{}, F{}, F{});
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.n_split == 1) return e;
