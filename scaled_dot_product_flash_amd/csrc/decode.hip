@@ -94,13 +94,14 @@ __device__ __forceinline__ void widen_i8(uint4 raw, i16x8& lo, i16x8& hi) {
         }
     } else {
         // fp16 0x6400 | u is 1024 + u for a byte u; u = x + 128 (x ^ 0x80),
-        // then one packed subtract of 1152 gives x.
+        // then one packed subtract of 1152 gives x.  One byte permute builds
+        // two such halves from bytes of u and the constant 0x64.
         const f16x2 bias = {static_cast<_Float16>(1152.f), static_cast<_Float16>(1152.f)};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const uint32_t u = w[i] ^ 0x80808080u;
-            const uint32_t a = 0x64006400u | (u & 0x000000ffu) | ((u & 0x0000ff00u) << 8);
-            const uint32_t b = 0x64006400u | ((u >> 16) & 0x000000ffu) | ((u >> 8) & 0x00ff0000u);
+            const uint32_t a = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u);   // bytes 0, 1
+            const uint32_t b = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);   // bytes 2, 3
             out[2 * i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, a) - bias);
             out[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, b) - bias);
         }
