@@ -2,19 +2,23 @@
 // accumulation on the gfx950 matrix cores (head dims that are multiples of 8,
 // up to 256).
 //
-// Work decomposition.  A workgroup of W waves (8 for head dim 128, else 4)
-// owns one (batch, kv head) and 32 W query rows that read it: gw query heads
-// of the group (gw = 8, 4, 2 or 1, the largest that divides Hq/Hkv and is at
-// most W) times 32 W / gw consecutive positions.  Each wave owns 32 rows of
-// one head.  One K/V tile load thus serves every query
-// head of the group that shares it (llm.istanbul "05_attention", "GQA").  The
-// keys are visited in increasing order, 64 per tile, staged through LDS (one
-// barrier per tile) by coalesced 16-byte raw-buffer loads that write LDS
-// directly, with no register round trip; the buffer's range ends at the batch
-// entry's key length, so rows past it arrive as zeros and are never fetched.
+// Work decomposition.  A workgroup of W waves (8 for head dim 128, else 4;
+// see Cfg) owns one (batch, kv head) and 32 W query rows that read it: gw
+// query heads of the group (gw = 8, 4, 2 or 1, the largest that divides
+// Hq/Hkv and is at most W) times 32 W / gw consecutive positions.  Each wave
+// owns 32 rows of one head.  One K/V tile load thus serves every query head of
+// the group that shares it (llm.istanbul "05_attention", "GQA").  The keys are
+// visited in increasing order, 64 per tile, staged through LDS (one barrier
+// per tile) by coalesced 16-byte raw-buffer loads that write LDS directly,
+// with no register round trip; the buffer's range ends at the batch entry's
+// key length, so rows past it arrive as zeros and are never fetched.
 // (OneGPU "Attention", introduction and "Variants and ordering": a workgroup
 // keeps a block of query rows and walks key/value tiles held in workgroup
-// memory.)
+// memory.)  When the query blocks would leave half of the GPU idle, each
+// block's keys are cut into ranges whose partial records a second kernel
+// merges in range order (OneGPU "Attention", "Accuracy at long key lengths").
+// Workgroups run heaviest causal block first, or, without causality but with
+// key lengths, longest batch entry first.
 //
 // Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16: the
 // output column is the query, so lane l owns query l%32 and holds 16 of its
@@ -39,9 +43,10 @@
 //
 // Element-wise work that only some tiles need (the causal diagonal, the tile
 // holding the key length, the lower edge of a local window, the additive
-// mask) is done only on those tiles; the mask and the window / softcap /
-// document rules (with padded head dims) are compile-time variants of the
-// kernel.  Score-rule variants follow the ONNX
+// mask) is done only on those tiles; the mask, the window / softcap /
+// document rules (with padded head dims), the short-row shape, the key-range
+// split and the length order are compile-time variants of the kernel, so a
+// kernel carries only the code it runs.  Score-rule variants follow the ONNX
 // GroupQueryAttention README ("Attributes", "Inputs"): a local window starts
 // the key loop at the block's first visible tile; the softcap maps each raw
 // score before the mask is added; the sink joins the denominator at the end.
