@@ -287,6 +287,8 @@ attn_status attn_decode(const attn_problem* p, const void* q, const void* k, con
         if (!workspace || workspace_bytes < need)
             return fail(ATTN_ERR_WORKSPACE, "decode needs %zu workspace bytes, got %zu", need,
                         workspace ? workspace_bytes : size_t(0));
+        if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+            return fail(ATTN_ERR_INVALID, "workspace must be 16-byte aligned");
         prm.ws = workspace;
         g_kernel = p->kv_int8 ? "decode_splitk_int8" : "decode_splitk";
         return launched(sdpa::launch_decode_split(prm, dt, s));

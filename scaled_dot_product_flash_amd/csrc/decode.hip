@@ -163,7 +163,7 @@ __device__ __forceinline__ int owner_wave(int64_t x, int64_t S) {
 }
 
 template <bool kBf16, int D, bool kCap, bool kI8>
-__global__ __launch_bounds__(64) void decode_split_kernel(Params p, int n_hgrp, int slot_heads) {
+__global__ __launch_bounds__(64, 2) void decode_split_kernel(Params p, int n_hgrp, int slot_heads) {
     using M = Mma<kBf16>;
     using LY = DLay<D>;
     constexpr int KS = LY::KS, VS = LY::VS;

@@ -163,6 +163,11 @@ def test_decode_workspace_is_checked_before_launch():
                          need - 4, None)
     assert rc == sdpa.ERR_WORKSPACE
     assert b"workspace" in lib.attn_last_error()
+    # The partial records are written 16 bytes at a time.
+    odd = ctypes.c_void_p(0x1008)
+    rc = lib.attn_decode(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, None, None, odd, need,
+                         None)
+    assert rc == sdpa.ERR_INVALID and b"aligned" in lib.attn_last_error()
 
 
 def test_fp32_forward_split_needs_workspace():
