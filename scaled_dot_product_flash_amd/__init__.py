@@ -258,10 +258,18 @@ def _run(op: int, q, k, v, *, layout: str, kv_layout: str | None, causal: bool,
     _last_ws = ws_bytes
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
     with torch.cuda.device(q.device):
-        s = stream if stream is not None else torch.cuda.current_stream(q.device)
+        cur = torch.cuda.current_stream(q.device)
+        s = stream if stream is not None else cur
         fn = lib.attn_forward if op == OP_FORWARD else lib.attn_decode
         _check(fn(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(mask),
                   _ptr(key_lens), _ptr(lse), _ptr(ws), ws_bytes, ctypes.c_void_p(s.cuda_stream)))
+        if s != cur:
+            # Blocks allocated here (workspace, contiguous copies, outputs) were
+            # taken on the current stream; keep them from being reused there
+            # before the work on `s` has finished.
+            for t in (ws, out, lse, mask, key_lens, head_sink, doc_start, k_scale, v_scale):
+                if t is not None:
+                    t.record_stream(s)
     return (out, lse) if return_lse else out
 
 
