@@ -450,16 +450,39 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(Params p, int n_hgr
         auto empty_share = [&](int w) {
             return S * w / kWavesTotal == S * (w + 1) / kWavesTotal;
         };
-        // Record headers are fetched 64 at a time, one per lane, so the
-        // loads overlap instead of forming a chain.
-        for (int c0 = 0; c0 < n; c0 += 64) {
+        // Record headers are fetched one per lane (64 at a time), so the
+        // loads overlap instead of forming a chain; the first 64 headers and
+        // the first eight records' rows are fetched together, since their
+        // addresses do not depend on the headers' values.
+        float mh = kNegInf, lh = 0.f;            // header of record w_lo + lane
+        float v0[8][NPL];
+        {
+            const int w = w_lo + lane;
+            if (lane < n && !empty_share(w)) {
+                const float* r = rec(w);
+                mh = r[0];
+                lh = r[1];
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+#pragma unroll
+                for (int cc = 0; cc < NPL; ++cc) {
+                    const int d = lane + 64 * cc;
+                    v0[u][cc] = (u < n && d < D) ? rec(w_lo + u)[4 + d] : 0.f;
+                }
+        }
+        M = mh;
+        for (int c0 = 64; c0 < n; c0 += 64) {
             const int w = w_lo + c0 + lane;
             if (c0 + lane < n && !empty_share(w)) M = fmaxf(M, rec(w)[0]);
         }
         M = wave_max(M);
         for (int c0 = 0; c0 < n; c0 += 64) {
             float f = 0.f, l = 0.f;
-            {
+            if (c0 == 0) {
+                f = (mh == kNegInf) ? 0.f : fast_exp2((mh - M) * c);
+                l = lh;
+            } else {
                 const int w = w_lo + c0 + lane;
                 if (c0 + lane < n && !empty_share(w)) {
                     const float* r = rec(w);
@@ -471,13 +494,21 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(Params p, int n_hgr
             // Accumulators: 8 records' rows loaded ahead, folded in wave order.
             for (int i0 = 0; i0 < cnt; i0 += 8) {
                 float v[8][NPL];
+                if (c0 == 0 && i0 == 0) {
 #pragma unroll
-                for (int u = 0; u < 8; ++u)
+                    for (int u = 0; u < 8; ++u)
 #pragma unroll
-                    for (int cc = 0; cc < NPL; ++cc) {
-                        const int d = lane + 64 * cc;
-                        v[u][cc] = (i0 + u < cnt && d < D) ? rec(w_lo + c0 + i0 + u)[4 + d] : 0.f;
-                    }
+                        for (int cc = 0; cc < NPL; ++cc) v[u][cc] = v0[u][cc];
+                } else {
+#pragma unroll
+                    for (int u = 0; u < 8; ++u)
+#pragma unroll
+                        for (int cc = 0; cc < NPL; ++cc) {
+                            const int d = lane + 64 * cc;
+                            v[u][cc] = (i0 + u < cnt && d < D) ? rec(w_lo + c0 + i0 + u)[4 + d]
+                                                               : 0.f;
+                        }
+                }
 #pragma unroll
                 for (int u = 0; u < 8; ++u) {
                     const int i = i0 + u;
