@@ -252,7 +252,8 @@ attn_status attn_forward(const attn_problem* p, const void* q, const void* k, co
         prm.n_split = 1;
         prm.split_len = 0;
     }
-    sdpa::prefill_f32_plan(p->batch, p->q_heads, p->q_len, p->k_len, &prm.split_len, &prm.n_split);
+    sdpa::prefill_f32_plan(p->batch, p->q_heads, p->q_len, p->k_len, p->head_dim, &prm.split_len,
+                           &prm.n_split);
     if (!force_generic() && sdpa::prefill_f32_supported(prm, dt)) {
         if (prm.n_split > 1) {
             const size_t need = forward_ws(p);

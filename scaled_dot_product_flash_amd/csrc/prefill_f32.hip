@@ -1,16 +1,21 @@
 // prefill_f32.hip -- fused attention for float32 inputs on the vector FMA
 // units (head_dim 32, 64 or 128).
 //
-// Four neighbouring lanes own one query row, each a quarter of the head
+// Four neighbouring lanes own a query row, each a quarter of the head
 // dimension: a score is four partial dot products added by two quad
 // exchanges (DPP), so every lane of the quad holds the same score and takes
 // the same softmax decisions (OneGPU "Attention", "Variants and ordering":
 // the `pairs` variant splits the head dimension over neighbouring threads and
-// joins the halves with a shuffle).  A wave therefore owns 16 rows of one
-// (batch, head).  Keys are folded in increasing order, 32 per tile, from the
-// wave's own LDS rows (coalesced 16-byte loads, next tile prefetched into
-// registers), with the online normaliser and a lazily raised reference max
-// as in the matrix-core kernel; in float32 the probabilities are not rounded.
+// joins the halves with a shuffle).  For head dims up to 64 each quad owns
+// two rows (16 apart), so every K/V value read from LDS feeds two FMAs: one
+// read per FMA would leave the loop bound by LDS bandwidth, not by the FMA
+// units.  A wave therefore owns 32 rows (16 at head dim 128) of one (batch,
+// head).  Keys are folded in increasing order, 16 per tile (32 at head dim
+// 128), from the wave's own LDS rows (coalesced 16-byte loads, next tile
+// prefetched into registers), with the online normaliser and a lazily raised
+// reference max as in the matrix-core kernel; in float32 the probabilities
+// are not rounded.  (Two rows per quad with 32-key tiles, or four rows, need
+// more than 256 registers and leave one wave per SIMD: both measured slower.)
 //
 // When the query blocks are too few to fill the GPU, the keys are cut into
 // contiguous ranges (a multiple of 32 keys, at least 128, at most 16 ranges);
@@ -24,8 +29,14 @@ namespace sdpa {
 
 namespace {
 
-constexpr int kTile = 32;        // keys per tile
-constexpr int kRowsPerWave = 16;
+constexpr int kRangeQuantum = 32;   // key ranges are multiples of this
+
+// Rows per lane quad, and rows per wave.
+__host__ __device__ constexpr int rows_per_quad(int D) { return D <= 64 ? 2 : 1; }
+__host__ __device__ constexpr int rows_per_wave(int D) { return 16 * rows_per_quad(D); }
+// Keys per tile: 16 when a quad owns two rows, so the scores fit beside the
+// prefetched tile in 256 registers (two waves per SIMD).
+__host__ __device__ constexpr int tile_of(int D) { return rows_per_quad(D) == 2 ? 16 : 32; }
 constexpr float kSlack = 8.f;    // lazy-rescale threshold, base-2 units
 
 // Quad sum: both exchange steps add the same two numbers on each partner, so
@@ -37,6 +48,7 @@ __device__ __forceinline__ float quad_sum(float x) {
 }
 
 template <int D> struct F32Lay {
+    static constexpr int kTile = tile_of(D);
     static constexpr int DQ = D / 4;                  // dims per lane
     static constexpr int kRowF4 = D / 4;              // float4 per row
     static constexpr int kLoads = kTile * kRowF4 / 64;   // float4 loads per lane per tensor
@@ -47,6 +59,9 @@ template <int D, bool kMask, bool kSplit>
 __global__ __launch_bounds__(64) void prefill_f32_kernel(Params p, int n_rblk) {
     using LY = F32Lay<D>;
     constexpr int DQ = LY::DQ;
+    constexpr int R = rows_per_quad(D);
+    constexpr int RW = rows_per_wave(D);
+    constexpr int kTile = LY::kTile;
     __shared__ __attribute__((aligned(16))) float k_sh[kTile * D];
     __shared__ __attribute__((aligned(16))) float v_sh[kTile * D];
 
@@ -58,46 +73,57 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(Params p, int n_rblk) {
     const int g = h / p.group;
     const int lane = threadIdx.x;
     const int quad = lane >> 2, qd = lane & 3;
-    const int64_t i = static_cast<int64_t>(rb) * kRowsPerWave + quad;   // this lane's row
 
     int64_t kv_len = p.Lk;
     if (p.lens) {
         const int64_t L = p.lens[b];
         kv_len = L < 0 ? 0 : (L > p.Lk ? p.Lk : L);
     }
+    const int64_t delta = causal_delta(p, kv_len);
     // Keys the block can see, and this range of them.
     int64_t blk_hi = kv_len;
     if (p.causal) {
-        const int64_t last = (static_cast<int64_t>(rb + 1) * kRowsPerWave < p.Lq
-                                  ? static_cast<int64_t>(rb + 1) * kRowsPerWave : p.Lq) - 1;
-        const int64_t bb = last + causal_delta(p, kv_len) + 1;
+        const int64_t last = (static_cast<int64_t>(rb + 1) * RW < p.Lq
+                                  ? static_cast<int64_t>(rb + 1) * RW : p.Lq) - 1;
+        const int64_t bb = last + delta + 1;
         blk_hi = bb < 0 ? 0 : (bb < blk_hi ? bb : blk_hi);
     }
     const int64_t j_begin = kSplit ? static_cast<int64_t>(rng) * p.split_len : 0;
     int64_t j_end = blk_hi;
     if (kSplit && j_begin + p.split_len < j_end) j_end = j_begin + p.split_len;
     if (kSplit && j_begin >= blk_hi) return;   // no row of the block sees this range
-    const int64_t row_hi = p.causal ? i + causal_delta(p, kv_len) + 1 : kv_len;   // key < row_hi visible
     const int n_tiles = j_end > j_begin ? static_cast<int>((j_end - j_begin + kTile - 1) / kTile) : 0;
+
+    // This lane's rows: rb * RW + 16 r + quad, r < R.
+    int64_t row[R], row_hi[R];
+    bool row_ok[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        row[r] = static_cast<int64_t>(rb) * RW + 16 * r + quad;
+        row_ok[r] = row[r] < p.Lq;
+        row_hi[r] = p.causal ? row[r] + delta + 1 : kv_len;   // key < row_hi visible
+    }
 
     const float* qg = static_cast<const float*>(p.q);
     const float* kg = static_cast<const float*>(p.k) + b * p.ks.sb + g * p.ks.sh;
     const float* vg = static_cast<const float*>(p.v) + b * p.vs.sb + g * p.vs.sh;
-    const bool row_ok = i < p.Lq;
 
-    float q[DQ];
-    {
-        const float* src = qg + b * p.qs.sb + h * p.qs.sh + (row_ok ? i : 0) * p.qs.sr + qd * DQ;
+    float q[R][DQ];
+    const float* mrow[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const float* src = qg + b * p.qs.sb + h * p.qs.sh + (row_ok[r] ? row[r] : 0) * p.qs.sr + qd * DQ;
 #pragma unroll
         for (int d = 0; d < DQ; d += 4) {
             const float4 v = *reinterpret_cast<const float4*>(src + d);
-            q[d] = row_ok ? v.x : 0.f;
-            q[d + 1] = row_ok ? v.y : 0.f;
-            q[d + 2] = row_ok ? v.z : 0.f;
-            q[d + 3] = row_ok ? v.w : 0.f;
+            q[r][d] = row_ok[r] ? v.x : 0.f;
+            q[r][d + 1] = row_ok[r] ? v.y : 0.f;
+            q[r][d + 2] = row_ok[r] ? v.z : 0.f;
+            q[r][d + 3] = row_ok[r] ? v.w : 0.f;
         }
+        mrow[r] = (kMask && row_ok[r]) ? p.mask + b * p.ms.sb + h * p.ms.sh + row[r] * p.ms.sr
+                                       : nullptr;
     }
-    const float* mrow = (kMask && row_ok) ? p.mask + b * p.ms.sb + h * p.ms.sh + i * p.ms.sr : nullptr;
 
     const int ld_row = lane / LY::kRowF4;
     const int ld_col = (lane % LY::kRowF4) * 4;
@@ -119,9 +145,14 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(Params p, int n_rblk) {
     const float c = p.scale_log2;
     const float slack = kSlack / c;
     const float inv_scale = kLog2e / c;
-    float m_ref = kNegInf, l_sum = 0.f, acc[DQ];
+    float m_ref[R], l_sum[R], acc[R][DQ];
 #pragma unroll
-    for (int d = 0; d < DQ; ++d) acc[d] = 0.f;
+    for (int r = 0; r < R; ++r) {
+        m_ref[r] = kNegInf;
+        l_sum[r] = 0.f;
+#pragma unroll
+        for (int d = 0; d < DQ; ++d) acc[r][d] = 0.f;
+    }
 
     if (n_tiles > 0) fetch(0);
     for (int tile = 0; tile < n_tiles; ++tile) {
@@ -129,99 +160,120 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(Params p, int n_rblk) {
         // in-order LDS queue, so one buffer suffices.
 #pragma unroll
         for (int n = 0; n < LY::kLoads; ++n) {
-            const int r = n * LY::kRowsPerLoad + ld_row;
-            *reinterpret_cast<float4*>(&k_sh[r * D + ld_col]) = kst[n];
-            *reinterpret_cast<float4*>(&v_sh[r * D + ld_col]) = vst[n];
+            const int rr = n * LY::kRowsPerLoad + ld_row;
+            *reinterpret_cast<float4*>(&k_sh[rr * D + ld_col]) = kst[n];
+            *reinterpret_cast<float4*>(&v_sh[rr * D + ld_col]) = vst[n];
         }
         if (tile + 1 < n_tiles) fetch(tile + 1);
         const int64_t j0 = j_begin + static_cast<int64_t>(tile) * kTile;
 
-        float s[kTile];
+        float s[R][kTile];
 #pragma unroll
         for (int j = 0; j < kTile; ++j) {
             const float* kr = &k_sh[j * D + qd * DQ];
-            float part = 0.f;
+            float part[R];
+#pragma unroll
+            for (int r = 0; r < R; ++r) part[r] = 0.f;
 #pragma unroll
             for (int d = 0; d < DQ; d += 4) {
                 const float4 kv = *reinterpret_cast<const float4*>(kr + d);
-                part = fmaf(q[d], kv.x, part);
-                part = fmaf(q[d + 1], kv.y, part);
-                part = fmaf(q[d + 2], kv.z, part);
-                part = fmaf(q[d + 3], kv.w, part);
-            }
-            s[j] = quad_sum(part);
-        }
-        if (kMask && mrow) {
 #pragma unroll
-            for (int j = 0; j < kTile; ++j)
-                if (j0 + j < j_end) s[j] = fmaf(mrow[j0 + j], inv_scale, s[j]);
+                for (int r = 0; r < R; ++r) {
+                    part[r] = fmaf(q[r][d], kv.x, part[r]);
+                    part[r] = fmaf(q[r][d + 1], kv.y, part[r]);
+                    part[r] = fmaf(q[r][d + 2], kv.z, part[r]);
+                    part[r] = fmaf(q[r][d + 3], kv.w, part[r]);
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < R; ++r) s[r][j] = quad_sum(part[r]);
         }
-        const bool partial = (j0 + kTile > j_end) || (j0 + kTile > row_hi) || !row_ok;
-        if (partial) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            if (kMask && mrow[r]) {
+#pragma unroll
+                for (int j = 0; j < kTile; ++j)
+                    if (j0 + j < j_end) s[r][j] = fmaf(mrow[r][j0 + j], inv_scale, s[r][j]);
+            }
+            const bool partial = (j0 + kTile > j_end) || (j0 + kTile > row_hi[r]) || !row_ok[r];
+            if (partial) {
+#pragma unroll
+                for (int j = 0; j < kTile; ++j) {
+                    const int64_t key = j0 + j;
+                    if (key >= j_end || key >= row_hi[r] || key >= kv_len || !row_ok[r])
+                        s[r][j] = kNegInf;
+                }
+            }
+            float mx = kNegInf;
+#pragma unroll
+            for (int j = 0; j < kTile; j += 2) mx = fmaxf(mx, fmaxf(s[r][j], s[r][j + 1]));
+            const bool raise = mx > m_ref[r] + slack;
+            if (__builtin_amdgcn_ballot_w64(raise)) {
+                const float m_new = raise ? mx : m_ref[r];
+                const float alpha = raise ? fast_exp2((m_ref[r] - m_new) * c) : 1.f;   // 0 when m_ref = -inf
+                l_sum[r] *= alpha;
+#pragma unroll
+                for (int d = 0; d < DQ; ++d) acc[r][d] *= alpha;
+                m_ref[r] = m_new;
+            }
+            // (s - m) * c rather than fma(s, c, -m*c): the subtraction is
+            // exact for the row maximum, so its weight is exactly 1 (p is not
+            // rounded to a narrower type on this path).
+            const float base = (m_ref[r] == kNegInf) ? 0.f : m_ref[r];
 #pragma unroll
             for (int j = 0; j < kTile; ++j) {
-                const int64_t key = j0 + j;
-                if (key >= j_end || key >= row_hi || key >= kv_len || !row_ok) s[j] = kNegInf;
+                s[r][j] = fast_exp2((s[r][j] - base) * c);
+                l_sum[r] += s[r][j];
             }
         }
-        float mx = kNegInf;
-#pragma unroll
-        for (int j = 0; j < kTile; j += 2) mx = fmaxf(mx, fmaxf(s[j], s[j + 1]));
-        const bool raise = mx > m_ref + slack;
-        if (__builtin_amdgcn_ballot_w64(raise)) {
-            const float m_new = raise ? mx : m_ref;
-            const float alpha = raise ? fast_exp2((m_ref - m_new) * c) : 1.f;   // 0 when m_ref = -inf
-            l_sum *= alpha;
-#pragma unroll
-            for (int d = 0; d < DQ; ++d) acc[d] *= alpha;
-            m_ref = m_new;
-        }
-        // (s - m) * c rather than fma(s, c, -m*c): the subtraction is exact
-        // for the row maximum, so its weight is exactly 1 (p is not rounded
-        // to a narrower type on this path).
-        const float base = (m_ref == kNegInf) ? 0.f : m_ref;
 #pragma unroll
         for (int j = 0; j < kTile; ++j) {
-            const float pj = fast_exp2((s[j] - base) * c);
-            l_sum += pj;
             const float* vr = &v_sh[j * D + qd * DQ];
 #pragma unroll
             for (int d = 0; d < DQ; d += 4) {
                 const float4 vv = *reinterpret_cast<const float4*>(vr + d);
-                acc[d] = fmaf(pj, vv.x, acc[d]);
-                acc[d + 1] = fmaf(pj, vv.y, acc[d + 1]);
-                acc[d + 2] = fmaf(pj, vv.z, acc[d + 2]);
-                acc[d + 3] = fmaf(pj, vv.w, acc[d + 3]);
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    acc[r][d] = fmaf(s[r][j], vv.x, acc[r][d]);
+                    acc[r][d + 1] = fmaf(s[r][j], vv.y, acc[r][d + 1]);
+                    acc[r][d + 2] = fmaf(s[r][j], vv.z, acc[r][d + 2]);
+                    acc[r][d + 3] = fmaf(s[r][j], vv.w, acc[r][d + 3]);
+                }
             }
         }
     }
 
-    if (!row_ok) return;
-    if (kSplit) {
-        float* rec = static_cast<float*>(p.ws) +
-                     (((static_cast<int64_t>(b) * p.Hq + h) * p.Lq + i) * p.n_split + rng) * (D + 4);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        if (!row_ok[r]) continue;
+        const int64_t i = row[r];
+        if (kSplit) {
+            float* rec = static_cast<float*>(p.ws) +
+                         (((static_cast<int64_t>(b) * p.Hq + h) * p.Lq + i) * p.n_split + rng) * (D + 4);
+#pragma unroll
+            for (int d = 0; d < DQ; d += 4)
+                *reinterpret_cast<float4*>(rec + 4 + qd * DQ + d) =
+                    make_float4(acc[r][d], acc[r][d + 1], acc[r][d + 2], acc[r][d + 3]);
+            if (qd == 0) {
+                rec[0] = m_ref[r];
+                rec[1] = l_sum[r];
+            }
+            continue;
+        }
+        const bool empty = (l_sum[r] == 0.f);
+        const float inv = 1.f / l_sum[r];
+        const float fill = p.masked_zero ? 0.f : __builtin_nanf("");
+        float* og = static_cast<float*>(p.o) + b * p.os.sb + h * p.os.sh + i * p.os.sr + qd * DQ;
 #pragma unroll
         for (int d = 0; d < DQ; d += 4)
-            *reinterpret_cast<float4*>(rec + 4 + qd * DQ + d) =
-                make_float4(acc[d], acc[d + 1], acc[d + 2], acc[d + 3]);
-        if (qd == 0) {
-            rec[0] = m_ref;
-            rec[1] = l_sum;
-        }
-        return;
+            *reinterpret_cast<float4*>(og + d) =
+                empty ? make_float4(fill, fill, fill, fill)
+                      : make_float4(acc[r][d] * inv, acc[r][d + 1] * inv, acc[r][d + 2] * inv,
+                                    acc[r][d + 3] * inv);
+        if (p.lse && qd == 0)
+            p.lse[b * p.ls.sb + h * p.ls.sh + i * p.ls.sr] =
+                empty ? kNegInf : (m_ref[r] * c + fast_log2(l_sum[r])) * kLn2;
     }
-    const bool empty = (l_sum == 0.f);
-    const float inv = 1.f / l_sum;
-    const float fill = p.masked_zero ? 0.f : __builtin_nanf("");
-    float* og = static_cast<float*>(p.o) + b * p.os.sb + h * p.os.sh + i * p.os.sr + qd * DQ;
-#pragma unroll
-    for (int d = 0; d < DQ; d += 4)
-        *reinterpret_cast<float4*>(og + d) =
-            empty ? make_float4(fill, fill, fill, fill)
-                  : make_float4(acc[d] * inv, acc[d + 1] * inv, acc[d + 2] * inv, acc[d + 3] * inv);
-    if (p.lse && qd == 0)
-        p.lse[b * p.ls.sb + h * p.ls.sh + i * p.ls.sr] =
-            empty ? kNegInf : (m_ref * c + fast_log2(l_sum)) * kLn2;
 }
 
 // One thread per (b, h, row, dim): merge the row's live ranges in order.
@@ -266,7 +318,7 @@ __global__ __launch_bounds__(256) void prefill_f32_merge_kernel(Params p) {
 
 template <int D>
 hipError_t launch_d(const Params& p, hipStream_t s) {
-    const int n_rblk = (p.Lq + kRowsPerWave - 1) / kRowsPerWave;
+    const int n_rblk = (p.Lq + rows_per_wave(D) - 1) / rows_per_wave(D);
     const dim3 grid(n_rblk, p.Hq, p.B * p.n_split);
     const bool split = p.n_split > 1;
     if (p.mask) {
@@ -288,8 +340,9 @@ hipError_t launch_d(const Params& p, hipStream_t s) {
 
 // Key ranges for the fp32 kernel: only when the row blocks give fewer than
 // ~2048 waves; ranges are multiples of 32 keys, at least 128, at most 16.
-void prefill_f32_plan(int B, int Hq, int Lq, int Lk, int* split_len, int* n_split) {
-    const int64_t units = static_cast<int64_t>((Lq + kRowsPerWave - 1) / kRowsPerWave) * Hq * B;
+void prefill_f32_plan(int B, int Hq, int Lq, int Lk, int D, int* split_len, int* n_split) {
+    const int rw = rows_per_wave(D);
+    const int64_t units = static_cast<int64_t>((Lq + rw - 1) / rw) * Hq * B;
     int n = 1;
     if (units < 2048 && Lk >= 256) {
         const int64_t want = (2048 + units - 1) / units;
@@ -299,8 +352,8 @@ void prefill_f32_plan(int B, int Hq, int Lq, int Lk, int* split_len, int* n_spli
         if (n < 1) n = 1;
     }
     int len = (Lk + n - 1) / n;
-    len = (len + kTile - 1) / kTile * kTile;
-    if (len < kTile) len = kTile;
+    len = (len + kRangeQuantum - 1) / kRangeQuantum * kRangeQuantum;
+    if (len < kRangeQuantum) len = kRangeQuantum;
     *split_len = len;
     *n_split = Lk > 0 ? (Lk + len - 1) / len : 1;
     if (*n_split < 1) *n_split = 1;
@@ -308,7 +361,7 @@ void prefill_f32_plan(int B, int Hq, int Lq, int Lk, int* split_len, int* n_spli
 
 size_t prefill_f32_workspace_bytes(int B, int Hq, int Lq, int Lk, int D) {
     int len, n;
-    prefill_f32_plan(B, Hq, Lq, Lk, &len, &n);
+    prefill_f32_plan(B, Hq, Lq, Lk, D, &len, &n);
     if (n <= 1) return 0;
     return static_cast<size_t>(B) * Hq * Lq * n * (D + 4) * sizeof(float);
 }
