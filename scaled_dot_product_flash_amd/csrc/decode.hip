@@ -113,14 +113,29 @@ __device__ __forceinline__ void widen_i8(uint4 raw, i16x8& lo, i16x8& hi) {
 // Partial record of one (slot, head): [m, l, -, -, acc[0..D)], floats.
 __host__ __device__ constexpr int rec_stride(int D) { return D + 4; }
 
+// A value every lane holds alike, moved to scalar registers.  The entry
+// index, lengths and step counts below are wave-uniform, but the compiler
+// cannot tell for values loaded from memory or summed across lanes; without
+// this, every K/V load built from them is wrapped in a per-lane loop over
+// buffer descriptors.
+__device__ __forceinline__ int32_t uniform32(int32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(static_cast<uint64_t>(v) >> 32));
+    return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
 // Live keys of batch entry b: [lo, lo + n).  The one query row is i = 0.
+// kUniform: b is the same in every active lane (the loaded values go to
+// scalar registers); otherwise each lane asks for its own entry.
 struct LiveRange {
     int64_t lo, n;
 };
-__device__ __forceinline__ LiveRange live_range(const Params& p, int b) {
+template <bool kUniform>
+__device__ __forceinline__ LiveRange live_range_t(const Params& p, int b) {
     int64_t kv = p.Lk;
     if (p.lens) {
-        const int64_t L = p.lens[b];
+        const int64_t L = kUniform ? uniform32(p.lens[b]) : p.lens[b];
         kv = L < 0 ? 0 : (L > p.Lk ? p.Lk : L);
     }
     int64_t hi = kv, lo = 0;
@@ -131,14 +146,21 @@ __device__ __forceinline__ LiveRange live_range(const Params& p, int b) {
         lo = window_lo(p, 0, delta);
     }
     if (p.doc_start) {               // the row's document start (q_len == 1)
-        const int64_t d = p.doc_start[b];
+        const int64_t d = kUniform ? uniform32(p.doc_start[b]) : p.doc_start[b];
         lo = d > lo ? d : lo;
     }
     return {lo < hi ? lo : hi, lo < hi ? hi - lo : 0};
 }
 
-__device__ __forceinline__ int64_t steps_of(const Params& p, int b) {
-    return (live_range(p, b).n + kStep - 1) / kStep;
+__device__ __forceinline__ LiveRange live_range(const Params& p, int b) {   // b wave-uniform
+    return live_range_t<true>(p, b);
+}
+
+__device__ __forceinline__ int64_t steps_of(const Params& p, int b) {        // b wave-uniform
+    return (live_range_t<true>(p, b).n + kStep - 1) / kStep;
+}
+__device__ __forceinline__ int64_t steps_of_lane(const Params& p, int b) {   // b per lane
+    return (live_range_t<false>(p, b).n + kStep - 1) / kStep;
 }
 
 // Steps before batch entry b (all kv heads and slices of entries < b), summed
@@ -148,12 +170,12 @@ __device__ int64_t steps_before(const Params& p, int b, int per_b_units) {
     int64_t total = 0;
     for (int b0 = 0; b0 < b; b0 += 64) {
         const int bb = b0 + lane;
-        int64_t v = (bb < b) ? steps_of(p, bb) : 0;
+        int64_t v = (bb < b) ? steps_of_lane(p, bb) : 0;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) v += __shfl_xor(v, off, 64);
         total += v;
     }
-    return total * per_b_units;
+    return uniform64(total * per_b_units);
 }
 
 // Wave that owns flattened step x when S steps are cut into W equal shares
@@ -184,7 +206,7 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(Params p, int n_hgr
     int b = 0;
     int64_t base_b = 0;                          // first step of entry b
     int64_t sb = steps_of(p, 0);
-    while (base_b + sb * per_b <= a) {
+    while (b < p.B - 1 && base_b + sb * per_b <= a) {
         base_b += sb * per_b;
         ++b;
         sb = steps_of(p, b);
