@@ -471,6 +471,26 @@ def test_decode_tiny_totals(lens):
         pu.compare(o, ro, lse, rl, "bf16", policy, what="decode tiny %s" % lens)
 
 
+@pytest.mark.parametrize("B,cap", [(150, 300), (300, 2000)])
+def test_decode_many_entries_trailing_empty(B, cap):
+    """More entries than one wave's lanes (the per-entry step sums run in
+    chunks of 64), about a third of them empty, the last ones included, with
+    fewer (150 x 300) and more (300 x 2000) live steps than decode waves."""
+    spec = synth.Spec("decode-many", B, 4, 2, 1, cap, 64, "f16", seed=B, kv_layout="bhsd",
+                      causal=True, decode=True, lens="uniform", lse=True)
+    case = synth.generate(spec)
+    rng = np.random.default_rng(B)
+    lens = rng.integers(1, cap + 1, size=B).astype(np.int32)
+    lens[rng.random(B) < 0.3] = 0
+    lens[-5:] = 0
+    lens[0] = cap
+    case.key_lens[:] = lens
+    for policy in ("nan", "zero"):
+        o, lse, _ = pu.run_hip(case, policy)
+        ro, rl = pu.run_oracle(case, policy)
+        pu.compare(o, ro, lse, rl, "f16", policy, what="decode many %d" % B)
+
+
 # --------------------------------------------------------------------------
 # Score-rule variants: local window, softcap, sink (GroupQueryAttention
 # README attributes), on every kernel that runs them.
