@@ -202,14 +202,30 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(Params p, int n_hgr
     const int64_t a = S * wave / kWavesTotal, e = S * (wave + 1) / kWavesTotal;
     if (a >= e) return;
 
-    // Locate the unit holding step a: batch entry by a scan over the entries.
+    // Locate the unit holding step a: 64 entries per round, one per lane;
+    // an inclusive prefix sum over the lanes finds the first entry whose
+    // steps end past a (a < S, so some round finds it).
     int b = 0;
     int64_t base_b = 0;                          // first step of entry b
-    int64_t sb = steps_of(p, 0);
-    while (b < p.B - 1 && base_b + sb * per_b <= a) {
-        base_b += sb * per_b;
-        ++b;
-        sb = steps_of(p, b);
+    int64_t sb = 0;                              // steps of each unit of entry b
+    for (int b0 = 0; b0 < p.B; b0 += 64) {
+        const int bb = b0 + lane;
+        const int64_t st = bb < p.B ? steps_of_lane(p, bb) : 0;
+        int64_t incl = st * per_b;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int64_t y = __shfl_up(incl, off, 64);
+            if (lane >= off) incl += y;
+        }
+        const uint64_t hit = __builtin_amdgcn_ballot_w64(base_b + incl > a);
+        if (hit) {
+            const int l = __builtin_ctzll(hit);
+            b = b0 + l;
+            sb = uniform64(__shfl(st, l, 64));
+            base_b = uniform64(base_b + __shfl(incl, l, 64) - sb * per_b);
+            break;
+        }
+        base_b = uniform64(base_b + __shfl(incl, 63, 64));
     }
     int uu = static_cast<int>((a - base_b) / sb);   // unit within the entry
     int64_t ls = (a - base_b) % sb;                 // step within the unit

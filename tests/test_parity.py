@@ -491,6 +491,26 @@ def test_decode_many_entries_trailing_empty(B, cap):
         pu.compare(o, ro, lse, rl, "f16", policy, what="decode many %d" % B)
 
 
+@pytest.mark.parametrize("which", ["decode_f16", "prefill_bf16", "prefill_f32"])
+def test_largest_batch(which):
+    """The largest batch the library accepts (65535 entries; the fp32 kernel's
+    grid depth is exactly its limit), short rows, a third of the key lengths
+    zero."""
+    B = 65535
+    if which == "decode_f16":
+        spec = synth.Spec("max-batch", B, 2, 1, 1, 40, 64, "f16", seed=91, kv_layout="bhsd",
+                          causal=True, decode=True, lens="uniform", lse=True)
+    else:
+        spec = synth.Spec("max-batch", B, 2, 1, 5, 7, 64, which[-4:].lstrip("_"), seed=92,
+                          causal=True, causal_offset="end", lens="uniform", lse=True)
+    case = synth.generate(spec)
+    rng = np.random.default_rng(93)
+    case.key_lens[rng.random(B) < 0.33] = 0
+    o, lse, _ = pu.run_hip(case, "nan")
+    ro, rl = pu.run_oracle(case, "nan")
+    pu.compare(o, ro, lse, rl, spec.dtype, "nan", what="largest batch %s" % which)
+
+
 # --------------------------------------------------------------------------
 # Score-rule variants: local window, softcap, sink (GroupQueryAttention
 # README attributes), on every kernel that runs them.
