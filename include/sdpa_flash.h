@@ -98,7 +98,10 @@ typedef enum attn_op {
  * Positions-first [B, L, H, D] contiguous: batch_stride = L*H*D,
  *   head_stride = D, row_stride = H*D.
  * Heads-first [B, H, L, D] contiguous: batch_stride = H*L*D,
- *   head_stride = L*D, row_stride = D.                                        */
+ *   head_stride = L*D, row_stride = D.
+ * Offsets and strides are in elements and must be >= 0; a layout (Q/K/V/O,
+ * and the mask and LSE when given) whose largest element index reaches 2^62
+ * is rejected with ATTN_ERR_INVALID.                                          */
 typedef struct attn_layout {
     int64_t offset;
     int64_t batch_stride;

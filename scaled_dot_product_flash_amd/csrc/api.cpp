@@ -39,11 +39,13 @@ bool nonneg(const attn_layout& l) {
     return l.offset >= 0 && l.batch_stride >= 0 && l.head_stride >= 0 && l.row_stride >= 0;
 }
 
-// Largest element index a layout touches for (B, H, L, width), +1.
-int64_t extent(const attn_layout& l, int64_t B, int64_t H, int64_t L, int64_t width) {
+// Largest element index a layout touches for (B, H, L, width), +1; in 128
+// bits, so that no stride a caller passes can wrap it past the limit check.
+__int128 extent(const attn_layout& l, int64_t B, int64_t H, int64_t L, int64_t width) {
     if (B == 0 || H == 0 || L == 0 || width == 0) return 0;
-    return l.offset + (B - 1) * l.batch_stride + (H - 1) * l.head_stride +
-           (L - 1) * l.row_stride + width;
+    return static_cast<__int128>(l.offset) + static_cast<__int128>(B - 1) * l.batch_stride +
+           static_cast<__int128>(H - 1) * l.head_stride +
+           static_cast<__int128>(L - 1) * l.row_stride + width;
 }
 
 // check_ptrs = false validates the problem alone (for attn_workspace_size).
@@ -103,12 +105,16 @@ attn_status validate(const attn_problem* p, bool check_ptrs, const void* q, cons
         return fail(ATTN_ERR_INVALID, "k and v must be non-NULL when k_len > 0");
     const int64_t D = p->head_dim;
     // 64-bit element offsets are used everywhere; reject extents past 2^62.
-    const int64_t lim = int64_t(1) << 62;
+    const __int128 lim = static_cast<__int128>(1) << 62;
     if (extent(p->q, p->batch, p->q_heads, p->q_len, D) > lim ||
         extent(p->o, p->batch, p->q_heads, p->q_len, D) > lim ||
         extent(p->k, p->batch, p->kv_heads, p->k_len, D) > lim ||
         extent(p->v, p->batch, p->kv_heads, p->k_len, D) > lim)
         return fail(ATTN_ERR_INVALID, "tensor extent too large");
+    if (mask && extent(p->mask, p->batch, p->q_heads, p->q_len, p->k_len) > lim)
+        return fail(ATTN_ERR_INVALID, "mask extent too large");
+    if (lse && extent(p->lse, p->batch, p->q_heads, p->q_len, 1) > lim)
+        return fail(ATTN_ERR_INVALID, "lse extent too large");
     return ATTN_OK;
 }
 

@@ -91,6 +91,10 @@ FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation rejects first
     (dict(softcap=float("nan")), sdpa.ERR_INVALID),
     (dict(sink=2), sdpa.ERR_INVALID),
     (dict(head_sink=0x1000), sdpa.ERR_INVALID),      # values without sink = 1
+    (dict(q_heads=70000, kv_heads=2), sdpa.ERR_UNSUPPORTED),
+    (dict(k=sdpa.Layout(0, 0, 64, 1 << 60)), sdpa.ERR_INVALID),     # extent past 2^62
+    (dict(k=sdpa.Layout(0, 0, 64, 1 << 62)), sdpa.ERR_INVALID),     # 7 * 2^62 would wrap int64
+    (dict(causal=0, window=0, doc_start=None, k_scale=0x1000), sdpa.ERR_INVALID),  # scale, no int8
 ])
 def test_invalid_problem_rejected_before_launch(change, status):
     lib = sdpa.load_library()
@@ -115,6 +119,27 @@ def test_null_pointers_rejected():
     assert lib.attn_workspace_size(ctypes.byref(p), 0, None) == sdpa.ERR_INVALID
     assert lib.attn_workspace_size(ctypes.byref(p), 9, ctypes.byref(ctypes.c_size_t())) \
         == sdpa.ERR_INVALID
+
+
+def test_negative_mask_and_lse_strides_rejected():
+    lib = sdpa.load_library()
+    p = _problem()
+    p.mask = sdpa.Layout(0, 0, -8, 8)
+    rc = lib.attn_forward(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, 0, None)
+    assert rc == sdpa.ERR_INVALID and b"mask" in lib.attn_last_error()
+    p = _problem()
+    p.lse = sdpa.Layout(0, -1, 8, 1)
+    rc = lib.attn_forward(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, None, FAKE, None, 0, None)
+    assert rc == sdpa.ERR_INVALID and b"lse" in lib.attn_last_error()
+    # Strides whose products would wrap 64-bit offsets.
+    p = _problem()
+    p.mask = sdpa.Layout(0, 0, 0, 1 << 62)
+    rc = lib.attn_forward(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, 0, None)
+    assert rc == sdpa.ERR_INVALID and b"mask" in lib.attn_last_error()
+    p = _problem()
+    p.lse = sdpa.Layout(0, 0, 1 << 62, 1)
+    rc = lib.attn_forward(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, None, FAKE, None, 0, None)
+    assert rc == sdpa.ERR_INVALID and b"lse" in lib.attn_last_error()
 
 
 def test_decode_requires_one_query_row():
