@@ -299,14 +299,36 @@ __global__ __launch_bounds__(256) void prefill_f32_merge_kernel(Params p) {
     }
     const int n_live = static_cast<int>((hi + p.split_len - 1) / p.split_len);
     const float* recs = static_cast<const float*>(p.ws) + row * p.n_split * (D + 4);
-    float M = kNegInf;
-    for (int r = 0; r < n_live; ++r) M = fmaxf(M, recs[r * (D + 4)]);
-    float L = 0.f, A = 0.f;
-    for (int r = 0; r < n_live; ++r) {
-        const float* rec = recs + r * (D + 4);
-        const float f = (rec[0] == kNegInf) ? 0.f : fast_exp2((rec[0] - M) * p.scale_log2);
-        L = fmaf(rec[1], f, L);
-        A = fmaf(rec[4 + d], f, A);
+    // Eight ranges' (m, l, acc[d]) are fetched together per round; the
+    // reference maximum is the largest seen so far, so up to eight ranges
+    // fold in one round exactly as a separate maximum pass would.
+    float M = kNegInf, L = 0.f, A = 0.f;
+    for (int r0 = 0; r0 < n_live; r0 += 8) {
+        float m8[8], l8[8], a8[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const bool in = r0 + u < n_live;
+            const float* rec = recs + (in ? r0 + u : 0) * (D + 4);
+            m8[u] = in ? rec[0] : kNegInf;
+            l8[u] = in ? rec[1] : 0.f;
+            a8[u] = in ? rec[4 + d] : 0.f;
+        }
+        float Mn = M;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) Mn = fmaxf(Mn, m8[u]);
+        if (Mn != M) {   // raise the reference (from -inf: nothing folded yet)
+            const float al = (M == kNegInf) ? 0.f : fast_exp2((M - Mn) * p.scale_log2);
+            L *= al;
+            A *= al;
+            M = Mn;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            if (r0 + u >= n_live) break;
+            const float f = (m8[u] == kNegInf) ? 0.f : fast_exp2((m8[u] - M) * p.scale_log2);
+            L = fmaf(l8[u], f, L);
+            A = fmaf(a8[u], f, A);
+        }
     }
     const bool empty = (L == 0.f);
     const float o = empty ? (p.masked_zero ? 0.f : __builtin_nanf("")) : A / L;
