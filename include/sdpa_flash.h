@@ -209,7 +209,9 @@ attn_status attn_forward(const attn_problem* p, const void* q, const void* k, co
  * device from key_lens, into equal contiguous shares over a fixed set of
  * waves; each share's partial (max, sum, accumulator) goes to the workspace
  * (whose size depends on the shape only) and a second kernel merges a row's
- * partials in key order.
+ * partials in key order.  Shapes or buffers that path does not take (head
+ * dims other than 64 and 128, fp32, unaligned rows) run as attn_forward
+ * would; attn_workspace_size(p, ATTN_OP_DECODE) covers both.
  */
 attn_status attn_decode(const attn_problem* p, const void* q, const void* k, const void* v,
                         void* o, const float* mask, const int32_t* key_lens, float* lse,

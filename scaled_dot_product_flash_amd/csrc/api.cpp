@@ -190,7 +190,7 @@ const char* attn_last_kernel(void) { return g_kernel; }
 const char* attn_version(void) { return "sdpa_flash 0.1 (gfx950)"; }
 
 // Workspace of the split decode path; depends on the shape only.
-size_t decode_ws(const attn_problem* p) {
+size_t decode_split_ws(const attn_problem* p) {
     const bool shape_ok = (p->dtype == ATTN_DTYPE_BF16 || p->dtype == ATTN_DTYPE_F16) &&
                           (p->head_dim == 64 || p->head_dim == 128) && p->q_len == 1 &&
                           p->k_len > 0;
@@ -210,6 +210,14 @@ size_t forward_ws(const attn_problem* p) {
     return sdpa::prefill_mfma_workspace_bytes(p->batch, p->q_heads, p->kv_heads, p->q_len,
                                               p->k_len, p->head_dim,
                                               p->causal && p->window > 0, p->doc_start != nullptr);
+}
+
+// attn_decode runs the split decode path when the shape and the buffers allow
+// it and the forward path otherwise, so its workspace covers both (shape only).
+size_t decode_ws(const attn_problem* p) {
+    const size_t a = decode_split_ws(p);
+    const size_t b = p->kv_int8 ? 0 : forward_ws(p);
+    return a > b ? a : b;
 }
 
 attn_status attn_workspace_size(const attn_problem* p, int32_t op, size_t* bytes) {
@@ -290,7 +298,7 @@ attn_status attn_decode(const attn_problem* p, const void* q, const void* k, con
     const auto dt = static_cast<sdpa::DType>(p->dtype);
     const hipStream_t s = static_cast<hipStream_t>(stream);
     if (!force_generic() && sdpa::decode_split_supported(prm, dt)) {
-        const size_t need = decode_ws(p);
+        const size_t need = decode_split_ws(p);
         if (!workspace || workspace_bytes < need)
             return fail(ATTN_ERR_WORKSPACE, "decode needs %zu workspace bytes, got %zu", need,
                         workspace ? workspace_bytes : size_t(0));

@@ -195,6 +195,22 @@ def test_decode_workspace_is_checked_before_launch():
     assert rc == sdpa.ERR_INVALID and b"aligned" in lib.attn_last_error()
 
 
+def test_decode_workspace_covers_the_forward_fallback():
+    """A decode shape the split decode path does not take (head dim 256) runs
+    as a forward call, whose few query blocks split the keys: the decode
+    workspace size covers that call."""
+    lib = sdpa.load_library()
+    p = _problem(batch=2, q_heads=12, kv_heads=3, q_len=1, k_len=681, head_dim=256,
+                 dtype=sdpa.DTYPE_BF16, causal=1)
+    for lay, H, L in (("q", 12, 1), ("k", 3, 681), ("v", 3, 681), ("o", 12, 1)):
+        setattr(p, lay, sdpa.Layout(0, L * H * 256, 256, H * 256))
+    fwd = sdpa.workspace_size(p, sdpa.OP_FORWARD)
+    assert fwd > 0
+    assert sdpa.workspace_size(p, sdpa.OP_DECODE) >= fwd
+    rc = lib.attn_decode(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, None, None, None, 0, None)
+    assert rc == sdpa.ERR_WORKSPACE
+
+
 def test_fp32_forward_split_needs_workspace():
     """The fp32 causal GQA shape (few row blocks) is cut into key ranges and
     needs a workspace; without it the call fails before launching."""
