@@ -3,8 +3,9 @@
 Each case draws, from its own fixed seed: the dtype, head dim (multiples of 8
 and odd ones), grouped heads, layouts, lengths, causal offset, additive mask,
 score-rule variants (local window, softcap, sink), document starts, and
-decode against a cache. Both masked-row policies alternate over the cases.
-A failure names its case index, which reproduces it exactly.
+decode against a cache (fp16/bf16, or int8 with scales). Both masked-row
+policies alternate over the cases. A failure names its case index, which
+reproduces it exactly.
 """
 import numpy as np
 import pytest
@@ -14,7 +15,7 @@ import parity_util as pu
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 48
+N_CASES = 96
 
 
 def draw(i: int) -> synth.Spec:
@@ -25,15 +26,16 @@ def draw(i: int) -> synth.Spec:
     Hkv = pick([1, 2, 3, 4])
     Hq = Hkv * pick([1, 2, 3, 4, 8])
     D = pick([8, 16, 24, 32, 40, 64, 72, 96, 128, 136, 192, 256, 17, 33, 100])
-    B = int(rng.integers(1, 5))
+    big = i >= 48                      # the second half draws longer rows and more entries
+    B = int(rng.integers(1, 7 if big else 5))
     kw = dict(q_layout=pick(["bshd", "bhsd"]), lse=True, masked_rows=pick(["nan", "zero"]))
     if decode:
-        Lk = int(rng.integers(1, 700))
+        Lk = int(rng.integers(1, 1200 if big else 700))
         spec = synth.Spec("random %d" % i, B, Hq, Hkv, 1, Lk, D, dtype, seed=i, kv_layout="bhsd",
                           causal=True, decode=True, lens="uniform", **kw)
     else:
-        Lq = int(rng.integers(1, 300))
-        Lk = int(rng.integers(0, 400)) if rng.random() < 0.9 else 0
+        Lq = int(rng.integers(1, 600 if big else 300))
+        Lk = int(rng.integers(0, 1000 if big else 400)) if rng.random() < 0.9 else 0
         causal = bool(rng.random() < 0.6)
         off = None
         if causal:
@@ -53,6 +55,8 @@ def draw(i: int) -> synth.Spec:
             var["docs"] = "random"
         if not decode and rng.random() < 0.25:
             var["mask"] = "keys"
+    if decode and D in (64, 128) and rng.random() < 0.35:
+        var["kv_quant"] = pick(["tensor", "channel", "mixed"])
     return spec.replace(**var)
 
 
