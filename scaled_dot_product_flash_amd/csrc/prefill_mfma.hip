@@ -624,26 +624,35 @@ __global__ __launch_bounds__(256) void prefill_mfma_merge_kernel(Params p) {
     const int64_t range_stride = total / p.D * RS;  // records of one range
     const float* recs = static_cast<const float*>(p.ws) + row * RS;
     const float c = p.scale_log2;
-    float M = kNegInf;
-    for (int r = 0; r < p.n_split; ++r) M = fmaxf(M, recs[r * range_stride]);
-    // Folded in range order, four records' loads issued ahead of their use.
-    float L = 0.f, A = 0.f;
-    for (int r0 = 0; r0 < p.n_split; r0 += 4) {
-        float m4[4], l4[4], a4[4];
+    // Folded in range order; eight ranges' (m, l, acc[d]) are fetched per
+    // round, and the reference maximum is the largest seen so far, so up to
+    // eight ranges fold in one round exactly as after a separate maximum pass.
+    float M = kNegInf, L = 0.f, A = 0.f;
+    for (int r0 = 0; r0 < p.n_split; r0 += 8) {
+        float m8[8], l8[8], a8[8];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < 8; ++u) {
             const bool in = r0 + u < p.n_split;
             const float* rec = recs + (in ? r0 + u : 0) * range_stride;
-            m4[u] = in ? rec[0] : kNegInf;
-            l4[u] = in ? rec[1] : 0.f;
-            a4[u] = in ? rec[4 + d] : 0.f;
+            m8[u] = in ? rec[0] : kNegInf;
+            l8[u] = in ? rec[1] : 0.f;
+            a8[u] = in ? rec[4 + d] : 0.f;
+        }
+        float Mn = M;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) Mn = fmaxf(Mn, m8[u]);
+        if (Mn != M) {   // raise the reference (from -inf: nothing folded yet)
+            const float al = (M == kNegInf) ? 0.f : fast_exp2((M - Mn) * c);
+            L *= al;
+            A *= al;
+            M = Mn;
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < 8; ++u) {
             if (r0 + u >= p.n_split) break;
-            const float f = (m4[u] == kNegInf) ? 0.f : fast_exp2((m4[u] - M) * c);
-            L = fmaf(l4[u], f, L);
-            A = fmaf(a4[u], f, A);
+            const float f = (m8[u] == kNegInf) ? 0.f : fast_exp2((m8[u] - M) * c);
+            L = fmaf(l8[u], f, L);
+            A = fmaf(a8[u], f, A);
         }
     }
     float m2 = M * c;                            // base-2 reference (-inf stays -inf)
