@@ -462,14 +462,26 @@ prefill_mfma_kernel(
         const bool partial = (j0 + kBN > kv_len) || (p.causal && j0 + kBN - 1 > qw0 + delta) ||
                              (kVar && j0 < wave_lo);
         if (partial) {
-            const int64_t qlim = p.causal ? qrow + delta : kv_len;
+            // Score (kb, r) holds key j0 + 4 hh + o, o = 32 kb + 8 (r / 4) + r % 4
+            // (a constant below 64): it is visible iff lo <= o < hi, with the
+            // lane's key bounds taken relative to j0 + 4 hh and clamped to
+            // [0, 64], which changes no comparison and fits 32 bits.
+            const int64_t base = j0 + 4 * hh;
+            int64_t top = kv_len;
+            if (p.causal && qrow + delta + 1 < top) top = qrow + delta + 1;
+            const int64_t th = top - base;
+            const int hi = static_cast<int>(th < 0 ? 0 : (th > 64 ? 64 : th));
+            int lo = 0;
+            if (kVar) {
+                const int64_t tl = row_lo - base;
+                lo = static_cast<int>(tl < 0 ? 0 : (tl > 64 ? 64 : tl));
+            }
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int64_t key = j0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-                    if (key >= kv_len || key > qlim || (kVar && key < row_lo))
-                        s_cur[kb][r] = kNegInf;
+                    const int o = kb * 32 + 8 * (r >> 2) + (r & 3);
+                    if (o >= hi || (kVar && o < lo)) s_cur[kb][r] = kNegInf;
                 }
         }
 
