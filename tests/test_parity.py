@@ -725,3 +725,20 @@ def test_head_dim_workloads_full_size_sampled(name):
     go = o[rows[:, 0], rows[:, 1], rows[:, 2]]
     gl = lse[rows[:, 0], rows[:, 1], rows[:, 2]]
     pu.compare(go, ro, gl, rl, spec.dtype, "nan", what=spec.name)
+
+
+# Causal offsets that put each row's key bounds far outside the tile or on
+# either side of a 64-key tile edge, with ragged lengths and tails, with and
+# without a local window: the per-score visibility test compares each score's
+# offset inside its tile with the lane's bounds clamped to [0, 64].
+@pytest.mark.parametrize("window", [-1, 37])
+@pytest.mark.parametrize("off", [-(1 << 40), -151, -150, -149, -65, -64, -63, -1, 0, 1, 63, 64,
+                                 65, 127, 1 << 40])
+def test_causal_offsets_at_tile_edges(off, window):
+    spec = synth.Spec("offset %d window %d" % (off, window), 2, 8, 2, 150, 203, 128, "bf16",
+                      seed=31, causal=True, causal_offset=off, lens="uniform", lse=True,
+                      local_window=window, masked_rows="zero")
+    case = synth.generate(spec)
+    o, lse, _ = pu.run_hip(case, "zero")
+    ro, rl = pu.run_oracle(case, "zero")
+    pu.compare(o, ro, lse, rl, "bf16", "zero", what=str(spec))
