@@ -21,7 +21,7 @@
  * section "GQA", and line-by-line step 1).
  * LSE = m + log(l) (llm.istanbul, "Online Softmax Algoritmasi", final step).
  *
- * Readings taken where the pages are silent (listed again in the design doc):
+ * Readings taken where the pages are silent:
  *   - key lengths are clamped to [0, KLen]; the default causal offset is
  *     relative to the problem's KLen, not the per-batch length;
  *   - the end-aligned offset (mode 2) is, per batch entry, the clamped key
@@ -38,7 +38,7 @@
  *     rule are never evaluated (so garbage there cannot leak in).
  *
  * Score-rule variants (ONNX GroupQueryAttention README, "Attributes" and
- * "Inputs"; readings, listed again in the design doc):
+ * "Inputs"; readings):
  *   - local window W >= 0 (causal only): the row at position p = i + offset
  *     also needs j >= p - W, i.e. W keys to its left and itself ("left window
  *     size for causal local attention"); -1 disables it;
