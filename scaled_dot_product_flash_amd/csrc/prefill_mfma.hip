@@ -431,7 +431,24 @@ prefill_mfma_kernel(
                 for (int r = 0; r < 16; ++r) s_cur[kb][r] = softcap_raw(s_cur[kb][r], cap_k2, cap_back);
         }
         // -- additive mask, folded into raw-score units --
-        if (kMask && mrow && sees) {
+        if (kMask && mrow && sees && mask_vec4 && j0 + kBN <= kv_len) {
+            // The whole tile lies inside the length: eight 16-byte loads.
+            float4 m4[2][4];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    m4[kb][u] = *reinterpret_cast<const float4*>(mrow + j0 + kb * 32 + 8 * u + 4 * hh);
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    s_cur[kb][4 * u] = fmaf(m4[kb][u].x, inv_scale, s_cur[kb][4 * u]);
+                    s_cur[kb][4 * u + 1] = fmaf(m4[kb][u].y, inv_scale, s_cur[kb][4 * u + 1]);
+                    s_cur[kb][4 * u + 2] = fmaf(m4[kb][u].z, inv_scale, s_cur[kb][4 * u + 2]);
+                    s_cur[kb][4 * u + 3] = fmaf(m4[kb][u].w, inv_scale, s_cur[kb][4 * u + 3]);
+                }
+        } else if (kMask && mrow && sees) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
