@@ -74,7 +74,8 @@ def settle(fn, seconds: float = 1.0):
 def time_calls(fn, steps: int, warmup: int, settle_s: float = 1.0):
     """Per-call HIP event durations (ms) on the current stream, plus wall time."""
     import torch
-    settle(fn, settle_s)
+    if settle_s > 0:
+        settle(fn, settle_s)
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -242,6 +243,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-others", action="store_true",
                     help="skip the tiny fp32, fp32 causal GQA and fp16 cross-attention lines")
+    ap.add_argument("--settle", type=float, default=1.0,
+                    help="seconds of untimed calls before each workload's warmup (clock ramp)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device copy (reference for HBM counters)")
     args = ap.parse_args()
@@ -275,7 +278,7 @@ def main():
 
     step()
     kernel = sdpa.last_kernel()
-    durs, wall = time_calls(step, args.steps, args.warmup)
+    durs, wall = time_calls(step, args.steps, args.warmup, args.settle)
     ms = float(np.mean(durs))
     tflops = spec.flops / (ms * 1e-3) / 1e12
     src_hash = kernel_source_hash(["prefill_mfma.hip"])
@@ -316,7 +319,7 @@ def main():
 
         dstep()
         dkernel = sdpa.last_kernel()
-        ddurs, _ = time_calls(dstep, args.steps, args.warmup)
+        ddurs, _ = time_calls(dstep, args.steps, args.warmup, args.settle)
         dms = float(np.mean(ddurs))
         kv_bytes = float(np.sum(dcase.key_lens.astype(np.float64))) * dspec.kv_heads * \
             dspec.head_dim * 2 * 2

@@ -274,6 +274,8 @@ attn_status attn_forward(const attn_problem* p, const void* q, const void* k, co
             if (!workspace || workspace_bytes < need)
                 return fail(ATTN_ERR_WORKSPACE, "forward needs %zu workspace bytes, got %zu", need,
                             workspace ? workspace_bytes : size_t(0));
+            if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+                return fail(ATTN_ERR_INVALID, "workspace must be 16-byte aligned");
             prm.ws = workspace;
         }
         g_kernel = "prefill_f32";

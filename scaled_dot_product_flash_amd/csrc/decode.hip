@@ -30,7 +30,9 @@
 // stores them in its own LDS rows (no barriers) and runs S^T = K Q^T and
 // O^T += V^T P^T on 16x16x32 MFMAs with the query heads as the columns.
 // Online normaliser with a lazily raised reference maximum; P is rounded to
-// the element type and the sum adds the rounded values.
+// the element type and the sum adds the rounded values.  Scores are raw
+// (q.k) without a mask and natural (scale * q.k + mask, the mask added as
+// given) with one, so a large finite mask value stays finite.
 //
 // Score-rule variants (ONNX GroupQueryAttention README, "Attributes",
 // "Inputs"): a local window moves the start of the live range up (the range
@@ -227,6 +229,9 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(Params p, int n_hgr
         }
         base_b = uniform64(base_b + __shfl(incl, 63, 64));
     }
+    // The scan and steps_before count the same steps, so an entry is always
+    // found; a wave that found none (sb == 0) has nothing to do.
+    if (sb <= 0) return;
     int uu = static_cast<int>((a - base_b) / sb);   // unit within the entry
     int64_t ls = (a - base_b) % sb;                 // step within the unit
 
@@ -235,11 +240,14 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(Params p, int n_hgr
     const int ld_row = kI8 ? lane / L8::kRowChunks : lane / LY::kRowChunks;
     const int ld_col = kI8 ? (lane % L8::kRowChunks) * 16 : (lane % LY::kRowChunks) * 8;
     // Raw scores are q.k with the K integers; a per-tensor K scale joins c.
+    // With a mask the scores are natural: sc = scale (times that K scale)
+    // maps raw to natural, and c = log2(e).
     const float kscale = (kI8 && p.k_quant == 1) ? p.k_scale[0] : 1.f;
     const bool k_chan = kI8 && p.k_quant == 2;
-    const float c = p.scale_log2 * kscale;
+    const bool nat = p.mask != nullptr;
+    const float sc = p.scale * kscale;
+    const float c = nat ? kLog2e : p.scale_log2 * kscale;
     const float slack = kSlack / c;
-    const float inv_scale = kLog2e / c;
     const float cap_k2 = kCap ? 2.f * kLog2e * p.scale * kscale / p.softcap : 0.f;
     const float cap_back = kCap ? p.softcap / (p.scale * kscale) : 0.f;
 
@@ -392,7 +400,8 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(Params p, int n_hgr
                 const int64_t key0 = j0 + kb * 16 + 4 * q4;
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    if (key0 + r < kv_hi) s[kb][r] = fmaf(mrow[key0 + r], inv_scale, s[kb][r]);
+                    s[kb][r] = (key0 + r < kv_hi) ? fmaf(s[kb][r], sc, mrow[key0 + r])
+                                                  : s[kb][r] * sc;
             }
         }
         if (j0 + kStep > kv_hi) {
@@ -418,15 +427,19 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(Params p, int n_hgr
                 for (int r = 0; r < 4; ++r) acc[d][r] *= alpha;
             m_ref = m_new;
         }
-        const float neg_mc = (m_ref == kNegInf) ? 0.f : -m_ref * c;
+        // exp2(s*c - m*c), or exp2((s - m)*c) with a mask: a reference far
+        // from zero (a large finite mask value) can neither overflow the
+        // product nor round away the scores' differences.
+        const float neg_mc = (m_ref == kNegInf || nat) ? 0.f : -m_ref * c;
+        const float sub = (m_ref == kNegInf || !nat) ? 0.f : m_ref;
         // P^T operand (16x16x32 B layout): k = 8*q4 + e <-> key (e < 4 ? 4*q4 + e : 16 + 4*q4 + e - 4).
         uint32_t w4[4];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
             for (int e2 = 0; e2 < 2; ++e2) {
-                w4[2 * kb + e2] = M::pack_out(fast_exp2(fmaf(s[kb][2 * e2], c, neg_mc)),
-                                              fast_exp2(fmaf(s[kb][2 * e2 + 1], c, neg_mc)));
+                w4[2 * kb + e2] = M::pack_out(fast_exp2(fmaf(s[kb][2 * e2] - sub, c, neg_mc)),
+                                              fast_exp2(fmaf(s[kb][2 * e2 + 1] - sub, c, neg_mc)));
                 l_sum = M::sum2(w4[2 * kb + e2], l_sum);
             }
         }
@@ -472,9 +485,11 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(Params p, int n_hgr
     const int64_t unit = static_cast<int64_t>(b) * per_b + uu;
     const int64_t first = steps_before(p, b, per_b) + uu * sb;   // first step of the unit
     constexpr int NPL = (D + 63) / 64;
-    // Records are in raw-score units: with a per-tensor int8 K scale, c
-    // carries it (as in the split kernel).
-    const float c = p.scale_log2 * ((p.kv_int8 && p.k_quant == 1) ? p.k_scale[0] : 1.f);
+    // Records are in the split kernel's score units: raw (a per-tensor int8
+    // K scale joins c and to_nat), or natural with a mask.
+    const float ksc = (p.kv_int8 && p.k_quant == 1) ? p.k_scale[0] : 1.f;
+    const float c = p.mask ? kLog2e : p.scale_log2 * ksc;
+    const float to_nat = p.mask ? 1.f : p.scale * ksc;
     float M = kNegInf, L = 0.f, A[NPL];
 #pragma unroll
     for (int cc = 0; cc < NPL; ++cc) A[cc] = 0.f;
@@ -560,8 +575,8 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(Params p, int n_hgr
             }
         }
     }
-    float m2 = M * c;                            // base-2 reference (-inf stays -inf)
-    const float fs = fold_sink(p, h, m2, L);
+    float m_nat = M * to_nat;                    // natural units (-inf stays -inf)
+    const float fs = fold_sink(p, h, m_nat, L);
     const bool empty = (L == 0.f);
     const float inv = fs / L;
     const int64_t orow = b * p.os.sb + h * p.os.sh;
@@ -576,8 +591,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(Params p, int n_hgr
         }
     }
     if (p.lse && lane == 0)
-        p.lse[b * p.ls.sb + h * p.ls.sh] =
-            empty ? kNegInf : (m2 + fast_log2(L)) * kLn2;
+        p.lse[b * p.ls.sb + h * p.ls.sh] = empty ? kNegInf : row_lse(m_nat, L);
 }
 
 int slice_count(int group) { return (group + 15) / 16; }

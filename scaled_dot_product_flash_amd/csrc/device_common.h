@@ -86,21 +86,29 @@ __device__ __forceinline__ float softcap_raw(float s, float k2, float back) {
     return back * (1.f - 2.f * __builtin_amdgcn_rcpf(e + 1.f));
 }
 
-// Folds the sink term of query head h into a row's final state: m2 is the
-// base-2 reference of the accumulated terms (-inf when none) and l their sum.
-// Returns the factor for the accumulator; m2 and l become those of the full
-// denominator (GroupQueryAttention README, "Inputs": a per-head smooth factor
-// added to the softmax denominator).  A -inf sink is no term; a NaN or +inf
-// sink makes l NaN.
-__device__ __forceinline__ float fold_sink(const Params& p, int h, float& m2, float& l) {
+// Folds the sink term of query head h into a row's final state, in natural
+// units (scores scale * q.k + mask): m is the reference of the accumulated
+// terms (-inf when none) and l their sum relative to it.  Returns the factor
+// for the accumulator; m and l become those of the full denominator
+// (GroupQueryAttention README, "Inputs": a per-head smooth factor added to
+// the softmax denominator).  Differences are taken before scaling, so a
+// reference anywhere in the float range cannot overflow.  A -inf sink is no
+// term; a NaN or +inf sink makes l NaN.
+__device__ __forceinline__ float fold_sink(const Params& p, int h, float& m, float& l) {
     if (!p.sink) return 1.f;
-    const float s2 = (p.head_sink ? p.head_sink[h] : 0.f) * kLog2e;
-    if (s2 == kNegInf) return 1.f;
-    const float M = fmaxf(m2, s2);
-    const float f = (m2 == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m2 - M);
-    l = l * f + __builtin_amdgcn_exp2f(s2 - M);
-    m2 = M;
+    const float s = p.head_sink ? p.head_sink[h] : 0.f;
+    if (s == kNegInf) return 1.f;
+    const float M = fmaxf(m, s);
+    const float f = (m == kNegInf) ? 0.f : __builtin_amdgcn_exp2f((m - M) * kLog2e);
+    l = l * f + __builtin_amdgcn_exp2f((s - M) * kLog2e);
+    m = M;
     return f;
+}
+
+// LSE of a row whose reference m (natural units) and sum l are final and
+// l > 0: m + ln l.
+__device__ __forceinline__ float row_lse(float m, float l) {
+    return fmaf(__builtin_amdgcn_logf(l), kLn2, m);
 }
 
 // IEEE maxNum: a NaN operand is ignored (NaN reaches the output through exp2).

@@ -49,8 +49,10 @@ __global__ __launch_bounds__(256) void generic_kernel(Params p) {
     const int64_t vbase = b * p.vs.sb + static_cast<int64_t>(g) * p.vs.sh;
     const float* mrow = p.mask ? p.mask + b * p.ms.sb + h * p.ms.sh + i * p.ms.sr : nullptr;
 
-    float m = kNegInf;   // running max, base-2 units
-    float l = 0.f;       // running sum of exp2(t - m)
+    // Scores in natural units, t = scale * q.k (softcapped) + mask, so a large
+    // finite mask value stays finite; p = exp2((t - m) * log2 e).
+    float m = kNegInf;   // running max
+    float l = 0.f;       // running sum of exp(t - m)
     float acc[kMaxD / 64];
 #pragma unroll
     for (int c = 0; c < kMaxD / 64; ++c) acc[c] = 0.f;
@@ -62,16 +64,16 @@ __global__ __launch_bounds__(256) void generic_kernel(Params p) {
             const int64_t kr = kbase + j * p.ks.sr;
             float dot = 0.f;
             for (int d = 0; d < D; ++d) dot = fmaf(q_sh[w][d], Elem<T>::load(p.k, kr + d), dot);
-            const float madd = mrow ? mrow[j] * kLog2e : 0.f;
+            const float madd = mrow ? mrow[j] : 0.f;
             if (p.softcap > 0.f)   // softcap on the scaled score, then the mask
-                t = fmaf(p.softcap * tanhf(dot * p.scale / p.softcap), kLog2e, madd);
+                t = p.softcap * tanhf(dot * p.scale / p.softcap) + madd;
             else
-                t = fmaf(dot, p.scale_log2, madd);
+                t = fmaf(dot, p.scale, madd);
         }
         const float m_new = fmaxf(m, wave_max(t));
         const float base = (m_new == kNegInf) ? 0.f : m_new;   // all hidden so far: exp2(-inf) = 0
-        const float pj = fast_exp2(t - base);
-        const float alpha = fast_exp2(m - base);
+        const float pj = fast_exp2((t - base) * kLog2e);
+        const float alpha = fast_exp2((m - base) * kLog2e);
         l = l * alpha + wave_sum(pj);
 #pragma unroll
         for (int c = 0; c < kMaxD / 64; ++c) acc[c] *= alpha;
@@ -103,7 +105,7 @@ __global__ __launch_bounds__(256) void generic_kernel(Params p) {
         }
     }
     if (p.lse && lane == 0) {
-        const float lse = empty ? kNegInf : (m + fast_log2(l)) * kLn2;
+        const float lse = empty ? kNegInf : row_lse(m, l);
         p.lse[b * p.ls.sb + h * p.ls.sh + i * p.ls.sr] = lse;
     }
 }

@@ -142,9 +142,11 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(Params p, int n_rblk) {
         }
     };
 
-    const float c = p.scale_log2;
+    // Score units: raw q.k without a mask; natural (scale * q.k + mask, the
+    // mask added as given, so a large finite value stays finite) with one.
+    const float c = kMask ? kLog2e : p.scale_log2;   // score units -> base 2
+    const float to_nat = kMask ? 1.f : p.scale;       // score units -> natural
     const float slack = kSlack / c;
-    const float inv_scale = kLog2e / c;
     float m_ref[R], l_sum[R], acc[R][DQ];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -193,7 +195,8 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(Params p, int n_rblk) {
             if (kMask && mrow[r]) {
 #pragma unroll
                 for (int j = 0; j < kTile; ++j)
-                    if (j0 + j < j_end) s[r][j] = fmaf(mrow[r][j0 + j], inv_scale, s[r][j]);
+                    s[r][j] = (j0 + j < j_end) ? fmaf(s[r][j], p.scale, mrow[r][j0 + j])
+                                               : s[r][j] * p.scale;
             }
             const bool partial = (j0 + kTile > j_end) || (j0 + kTile > row_hi[r]) || !row_ok[r];
             if (partial) {
@@ -272,13 +275,15 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(Params p, int n_rblk) {
                                     acc[r][d + 3] * inv);
         if (p.lse && qd == 0)
             p.lse[b * p.ls.sb + h * p.ls.sh + i * p.ls.sr] =
-                empty ? kNegInf : (m_ref[r] * c + fast_log2(l_sum[r])) * kLn2;
+                empty ? kNegInf : row_lse(m_ref[r] * to_nat, l_sum[r]);
     }
 }
 
 // One thread per (b, h, row, dim): merge the row's live ranges in order.
+// Records are in the main kernel's score units: c converts a difference of
+// them to base 2, to_nat a value to natural units.
 template <int D>
-__global__ __launch_bounds__(256) void prefill_f32_merge_kernel(Params p) {
+__global__ __launch_bounds__(256) void prefill_f32_merge_kernel(Params p, float c, float to_nat) {
     const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
     const int64_t total = static_cast<int64_t>(p.B) * p.Hq * p.Lq * D;
     if (t >= total) return;
@@ -317,7 +322,7 @@ __global__ __launch_bounds__(256) void prefill_f32_merge_kernel(Params p) {
 #pragma unroll
         for (int u = 0; u < 8; ++u) Mn = fmaxf(Mn, m8[u]);
         if (Mn != M) {   // raise the reference (from -inf: nothing folded yet)
-            const float al = (M == kNegInf) ? 0.f : fast_exp2((M - Mn) * p.scale_log2);
+            const float al = (M == kNegInf) ? 0.f : fast_exp2((M - Mn) * c);
             L *= al;
             A *= al;
             M = Mn;
@@ -325,7 +330,7 @@ __global__ __launch_bounds__(256) void prefill_f32_merge_kernel(Params p) {
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             if (r0 + u >= n_live) break;
-            const float f = (m8[u] == kNegInf) ? 0.f : fast_exp2((m8[u] - M) * p.scale_log2);
+            const float f = (m8[u] == kNegInf) ? 0.f : fast_exp2((m8[u] - M) * c);
             L = fmaf(l8[u], f, L);
             A = fmaf(a8[u], f, A);
         }
@@ -334,8 +339,7 @@ __global__ __launch_bounds__(256) void prefill_f32_merge_kernel(Params p) {
     const float o = empty ? (p.masked_zero ? 0.f : __builtin_nanf("")) : A / L;
     static_cast<float*>(p.o)[b * p.os.sb + h * p.os.sh + i * p.os.sr + d] = o;
     if (p.lse && d == 0)
-        p.lse[b * p.ls.sb + h * p.ls.sh + i * p.ls.sr] =
-            empty ? kNegInf : (M * p.scale_log2 + fast_log2(L)) * kLn2;
+        p.lse[b * p.ls.sb + h * p.ls.sh + i * p.ls.sr] = empty ? kNegInf : row_lse(M * to_nat, L);
 }
 
 template <int D>
@@ -353,8 +357,9 @@ hipError_t launch_d(const Params& p, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !split) return e;
     const int64_t total = static_cast<int64_t>(p.B) * p.Hq * p.Lq * D;
+    const float c = p.mask ? kLog2e : p.scale_log2, to_nat = p.mask ? 1.f : p.scale;
     hipLaunchKernelGGL((prefill_f32_merge_kernel<D>), dim3(static_cast<uint32_t>((total + 255) / 256)),
-                       dim3(256), 0, s, p);
+                       dim3(256), 0, s, p, c, to_nat);
     return hipGetLastError();
 }
 

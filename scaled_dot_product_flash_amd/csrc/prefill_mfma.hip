@@ -27,10 +27,13 @@
 // kernel": scores transposed so one lane keeps one row).
 //
 // Online normaliser (OneGPU "Attention", introduction; llm.istanbul
-// "05_attention", "Online Softmax Algoritmasi") kept in raw-score units: with
-// c = scale*log2(e), p = exp2(s*c - m*c) is one FMA and one exp2 per score.
-// The reference maximum m is raised lazily, only when a tile's maximum
-// exceeds it by more than 8/c (so p <= 2^8), and the accumulators are
+// "05_attention", "Online Softmax Algoritmasi").  Without a mask the scores
+// stay raw (s = q.k): with c = scale*log2(e), p = exp2(s*c - m*c) is one FMA
+// and one exp2 per score.  With a mask they are natural, s = scale*q.k +
+// mask (one FMA, the mask added as given), and c = log2(e): folding the mask
+// into raw units instead (mask / scale) would turn a large finite mask value
+// into -inf.  The reference maximum m is raised lazily, only when a tile's
+// maximum exceeds it by more than 8/c (so p <= 2^8), and the accumulators are
 // rescaled only then (OneGPU "Apple simdgroup kernel", reference maximum).
 // Raising is a per-row decision taken identically in both lanes of the row.
 //
@@ -388,9 +391,11 @@ prefill_mfma_kernel(
 
     const float* mrow = nullptr;
     if (kMask && qrow < p.Lq) mrow = p.mask + b * p.ms.sb + h * p.ms.sh + qrow * p.ms.sr;
-    const float c = p.scale_log2;          // > 0
-    const float slack = kSlack / c;        // lazy threshold in raw-score units
-    const float inv_scale = kLog2e / c;    // mask (natural units) -> raw-score units
+    // Score units: natural with a mask, raw without (see the file comment).
+    const float c = kMask ? kLog2e : p.scale_log2;   // score units -> base 2 (> 0)
+    const float to_nat = kMask ? 1.f : p.scale;       // score units -> natural
+    const float slack = kSlack / c;                   // lazy threshold in score units
+    const float sc = p.scale;                         // raw -> natural
 
     float m_ref = kNegInf;   // reference maximum of this lane's row, raw-score units
     float l_sum = 0.f;       // this lane's share of the sum of rounded p
@@ -443,10 +448,10 @@ prefill_mfma_kernel(
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
-                    s_cur[kb][4 * u] = fmaf(m4[kb][u].x, inv_scale, s_cur[kb][4 * u]);
-                    s_cur[kb][4 * u + 1] = fmaf(m4[kb][u].y, inv_scale, s_cur[kb][4 * u + 1]);
-                    s_cur[kb][4 * u + 2] = fmaf(m4[kb][u].z, inv_scale, s_cur[kb][4 * u + 2]);
-                    s_cur[kb][4 * u + 3] = fmaf(m4[kb][u].w, inv_scale, s_cur[kb][4 * u + 3]);
+                    s_cur[kb][4 * u] = fmaf(s_cur[kb][4 * u], sc, m4[kb][u].x);
+                    s_cur[kb][4 * u + 1] = fmaf(s_cur[kb][4 * u + 1], sc, m4[kb][u].y);
+                    s_cur[kb][4 * u + 2] = fmaf(s_cur[kb][4 * u + 2], sc, m4[kb][u].z);
+                    s_cur[kb][4 * u + 3] = fmaf(s_cur[kb][4 * u + 3], sc, m4[kb][u].w);
                 }
         } else if (kMask && mrow && sees) {
 #pragma unroll
@@ -464,7 +469,7 @@ prefill_mfma_kernel(
                     }
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        s_cur[kb][4 * u + e] = fmaf(mv[e], inv_scale, s_cur[kb][4 * u + e]);
+                        s_cur[kb][4 * u + e] = fmaf(s_cur[kb][4 * u + e], sc, mv[e]);
                 }
             }
         }
@@ -522,7 +527,21 @@ prefill_mfma_kernel(
                 for (int r = 0; r < 16; ++r) acc[d][r] *= alpha;
             m_ref = m_new;
         }
-        const float neg_mc = (m_ref == kNegInf) ? 0.f : -m_ref * c;
+        float neg_mc = (m_ref == kNegInf) ? 0.f : -m_ref * c;
+        if constexpr (kMask) {
+            // A reference far from zero (a large finite mask on every key seen
+            // so far): subtract it from the scores first, exactly for scores
+            // near it, so the exponent argument neither overflows nor loses
+            // the scores' differences in the rounding of m*c.
+            const bool far = fabsf(neg_mc) >= 4096.f;
+            if (__builtin_amdgcn_ballot_w64(far) && far) {
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) s_cur[kb][r] -= m_ref;
+                neg_mc = 0.f;
+            }
+        }
         // -- next tile's scores on the matrix core while this tile's softmax
         // runs (same basic block, so the two interleave).  After the last tile
         // the buffer holds stale keys and the result is discarded.
@@ -603,14 +622,14 @@ prefill_mfma_kernel(
                             f32x4{acc[d][4 * u], acc[d][4 * u + 1], acc[d][4 * u + 2],
                                   acc[d][4 * u + 3]};
             if (hh == 0) {
-                rec[0] = m_ref;
+                rec[0] = m_ref;   // score units (the merge gets the same c and to_nat)
                 rec[1] = l_tot;
             }
         }
         return;
     }
-    float m2 = m_ref * c;                       // base-2 reference (-inf stays -inf)
-    const float fs = fold_sink(p, h, m2, l_tot);
+    float m_nat = m_ref * to_nat;               // natural units (-inf stays -inf)
+    const float fs = fold_sink(p, h, m_nat, l_tot);
     if (qrow < p.Lq) {
         const bool empty = (l_tot == 0.f);
         const float inv = fs / l_tot;
@@ -629,7 +648,7 @@ prefill_mfma_kernel(
             }
         }
         if (p.lse && hh == 0) {
-            const float lse = empty ? kNegInf : (m2 + fast_log2(l_tot)) * kLn2;
+            const float lse = empty ? kNegInf : row_lse(m_nat, l_tot);
             p.lse[b * p.ls.sb + h * p.ls.sh + qrow * p.ls.sr] = lse;
         }
     }
@@ -639,8 +658,10 @@ prefill_mfma_kernel(
 // order (OneGPU "Attention", "Accuracy at long key lengths", last paragraph),
 // then the sink, the masked-row policy and the LSE as the kernel's own
 // epilogue does.
+// Records are in the main kernel's score units: c converts a difference of
+// them to base 2, to_nat a value to natural units.
 template <typename T>
-__global__ __launch_bounds__(256) void prefill_mfma_merge_kernel(Params p) {
+__global__ __launch_bounds__(256) void prefill_mfma_merge_kernel(Params p, float c, float to_nat) {
     const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
     const int64_t total = static_cast<int64_t>(p.B) * p.Hq * p.Lq * p.D;
     if (t >= total) return;
@@ -652,7 +673,6 @@ __global__ __launch_bounds__(256) void prefill_mfma_merge_kernel(Params p) {
     const int RS = p.D + 4;
     const int64_t range_stride = total / p.D * RS;  // records of one range
     const float* recs = static_cast<const float*>(p.ws) + row * RS;
-    const float c = p.scale_log2;
     // Folded in range order; eight ranges' (m, l, acc[d]) are fetched per
     // round, and the reference maximum is the largest seen so far, so up to
     // eight ranges fold in one round exactly as after a separate maximum pass.
@@ -684,13 +704,13 @@ __global__ __launch_bounds__(256) void prefill_mfma_merge_kernel(Params p) {
             A = fmaf(a8[u], f, A);
         }
     }
-    float m2 = M * c;                            // base-2 reference (-inf stays -inf)
-    const float fs = fold_sink(p, h, m2, L);
+    float m_nat = M * to_nat;                    // natural units (-inf stays -inf)
+    const float fs = fold_sink(p, h, m_nat, L);
     const bool empty = (L == 0.f);
     const float o = empty ? (p.masked_zero ? 0.f : __builtin_nanf("")) : A * (fs / L);
     Elem<T>::store(p.o, b * p.os.sb + h * p.os.sh + i * p.os.sr + d, o);
     if (p.lse && d == 0)
-        p.lse[b * p.ls.sb + h * p.ls.sh + i * p.ls.sr] = empty ? kNegInf : (m2 + fast_log2(L)) * kLn2;
+        p.lse[b * p.ls.sb + h * p.ls.sh + i * p.ls.sr] = empty ? kNegInf : row_lse(m_nat, L);
 }
 
 // Padded head dim of the kernel that runs head dim D.
@@ -769,10 +789,13 @@ hipError_t launch_shape(const Params& p, hipStream_t s) {
     if (e != hipSuccess || p.n_split == 1) return e;
     const int64_t total = static_cast<int64_t>(p.B) * p.Hq * p.Lq * p.D;
     const dim3 mgrid(static_cast<uint32_t>((total + 255) / 256));
+    // The records' score units (natural with a mask, raw without).
+    const float c = p.mask ? kLog2e : p.scale_log2, to_nat = p.mask ? 1.f : p.scale;
     if (kBf16)
-        hipLaunchKernelGGL((prefill_mfma_merge_kernel<bf16_t>), mgrid, dim3(256), 0, s, p);
+        hipLaunchKernelGGL((prefill_mfma_merge_kernel<bf16_t>), mgrid, dim3(256), 0, s, p, c, to_nat);
     else
-        hipLaunchKernelGGL((prefill_mfma_merge_kernel<_Float16>), mgrid, dim3(256), 0, s, p);
+        hipLaunchKernelGGL((prefill_mfma_merge_kernel<_Float16>), mgrid, dim3(256), 0, s, p, c,
+                           to_nat);
     return hipGetLastError();
 }
 

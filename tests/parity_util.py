@@ -7,7 +7,17 @@ the HIP path through the binding, run the oracle, and compare by the rule
   * otherwise             -> GPU finite and |GPU - oracle| <= tol
 
 with tol = 1e-4 (fp32), 5e-3 (fp16), 2e-2 (bf16) max-abs on unit-variance
-inputs.  LSE uses the same tolerance as its dtype's outputs.
+inputs.
+
+LSE has bounds of its own, derived from the arithmetic rather than from the
+output tolerance.  On the bf16/fp16 paths the running sum l adds the
+probabilities after they are rounded to the element type (OneGPU "Attention",
+"Matrix hardware": numerator and denominator see the same rounded p), so
+l_gpu = sum_j p_j (1 + e_j) with |e_j| <= 2^-9 (bf16) or 2^-12 (fp16), and
+|LSE_gpu - LSE| <= -ln(1 - 2^-9) = 1.96e-3 (bf16), 2.4e-4 (fp16), plus fp32
+rounding of the sums and of exp2/log2.  The rounding of m*c cancels between
+the exponents and the epilogue's m*c + log2 l.  The bounds below are those
+figures with 2x (bf16) and 4x (fp16) slack; fp32 does not round p.
 """
 from __future__ import annotations
 
@@ -18,6 +28,17 @@ import scaled_dot_product_flash_amd as sdpa
 from scaled_dot_product_flash_amd import synth
 
 TOL = {"f32": 1e-4, "f16": 5e-3, "bf16": 2e-2}
+LSE_TOL = {"f32": 1e-4, "f16": 1e-3, "bf16": 4e-3}
+
+# Largest errors seen in this session, per dtype (reported by conftest.py at
+# the end of a run, so the measured margins can be quoted).
+MAX_SEEN = {"o": {}, "lse": {}}
+
+
+def _note(kind: str, dtype: str, err: float):
+    d = MAX_SEEN[kind]
+    if err > d.get(dtype, 0.0):
+        d[dtype] = float(err)
 
 
 def torch_mod():
@@ -106,6 +127,7 @@ def compare(gpu_o, ref_o, gpu_lse, ref_lse, dtype: str, policy: str, what: str =
     if not np.isfinite(gpu_o[fin]).all():
         raise AssertionError("%s: non-finite outputs where the oracle is finite" % what)
     err = np.abs(gpu_o[fin] - ref_o[fin]).max(initial=0.0)
+    _note("o", dtype, err)
     if err > tol:
         idx = np.unravel_index(np.argmax(np.where(fin, np.abs(gpu_o - ref_o), -1)), ref_o.shape)
         raise AssertionError("%s: max |gpu - oracle| = %.3g > %.1g at %s (gpu %r, oracle %r)"
@@ -125,8 +147,9 @@ def compare(gpu_o, ref_o, gpu_lse, ref_lse, dtype: str, policy: str, what: str =
             if not np.isfinite(gpu_lse[ok]).all():
                 raise AssertionError("%s: non-finite LSE where the oracle is finite" % what)
             lerr = np.abs(gpu_lse[ok] - ref_lse[ok]).max(initial=0.0)
-            if lerr > tol:
-                raise AssertionError("%s: LSE error %.3g > %.1g" % (what, lerr, tol))
+            _note("lse", dtype, lerr)
+            if lerr > LSE_TOL[dtype]:
+                raise AssertionError("%s: LSE error %.3g > %.1g" % (what, lerr, LSE_TOL[dtype]))
     return err
 
 

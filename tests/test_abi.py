@@ -223,6 +223,11 @@ def test_fp32_forward_split_needs_workspace():
     assert need > 0
     rc = lib.attn_forward(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, None, None, None, 0, None)
     assert rc == sdpa.ERR_WORKSPACE
+    # The split writes 16-byte records: a misaligned workspace is refused too.
+    odd = ctypes.c_void_p(0x1004)
+    rc = lib.attn_forward(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, None, None, odd, need,
+                          None)
+    assert rc == sdpa.ERR_INVALID and b"aligned" in lib.attn_last_error()
 
 
 def test_matrix_core_forward_split_workspace():

@@ -742,3 +742,82 @@ def test_causal_offsets_at_tile_edges(off, window):
     o, lse, _ = pu.run_hip(case, "zero")
     ro, rl = pu.run_oracle(case, "zero")
     pu.compare(o, ro, lse, rl, "bf16", "zero", what=str(spec))
+
+
+# Large finite mask values (the float32-minimum "masked" convention, -1e30,
+# a huge positive entry): they are values, not -inf, so a row whose visible
+# keys all carry the same such value is the plain mean of those V rows
+# (OneGPU "Attention", "Special values": only -inf keys weigh nothing), and a
+# row mixing them with ordinary keys gives them weight 0.  Every kernel:
+# matrix-core prefill (one pass and key-range split), fp32, decode and the
+# any-shape kernel.
+FMIN = np.finfo(np.float32).min
+
+
+def _large_mask_rows(rng, n_rows, Lk):
+    m = (rng.standard_normal((n_rows, Lk)) * 2).astype(np.float32)
+    pats = [np.full(Lk, FMIN, np.float32),                                  # all finfo.min
+            np.where(np.arange(Lk) % 2 == 0, 0.0, FMIN).astype(np.float32), # half of them
+            np.full(Lk, -1e30, np.float32),                                 # all -1e30
+            np.where(np.arange(Lk) % 3 == 0, -np.inf, FMIN).astype(np.float32),
+            np.full(Lk, -np.inf, np.float32),                               # empty row
+            np.where(np.arange(Lk) == Lk // 3, 3e38, 0.0).astype(np.float32)]
+    for r, pat in enumerate(pats):
+        if r < n_rows:
+            m[r] = pat
+    return m
+
+
+def _compare_large(o, lse, ro, rl, dtype, policy, what):
+    pu.compare(o, ro, None, None, dtype, policy, what=what)
+    # LSE of rows near the float range: fp32 cannot hold ln(count) beside
+    # 3.4e38, so those compare relatively.
+    fin = np.isfinite(rl)
+    assert (np.isnan(lse) == np.isnan(rl)).all() and (lse[rl == -np.inf] == -np.inf).all()
+    err = np.abs(lse[fin] - rl[fin])
+    assert (err <= pu.LSE_TOL[dtype] + 2.0 ** -22 * np.abs(rl[fin])).all(), what
+
+
+LARGE = [("bf16", 128, "mfma"), ("f16", 64, "mfma"), ("f16", 128, "split"),
+         ("f32", 64, "f32"), ("f32", 64, "f32split"), ("bf16", 72, "generic")]
+
+
+@pytest.mark.parametrize("cfg", LARGE, ids=lambda c: "_".join(map(str, c)))
+def test_large_finite_mask(cfg, monkeypatch):
+    import scaled_dot_product_flash_amd as sdpa
+    dtype, D, path = cfg
+    Lq, Lk = (100, 3000) if path == "split" else ((40, 700) if path == "f32split" else (70, 200))
+    B, Hq, Hkv = (1, 4, 4) if path in ("split", "f32split") else (2, 4, 2)
+    spec = synth.Spec("large", B, Hq, Hkv, Lq, Lk, D, dtype, seed=51 + D, lse=True)
+    case = synth.generate(spec)
+    rng = np.random.default_rng(77)
+    mask = _large_mask_rows(rng, Lq, Lk)[None, None].repeat(B, axis=0)
+    case = synth.Case(spec, case.q, case.k, case.v, None, np.ascontiguousarray(mask))
+    if path == "generic":
+        monkeypatch.setenv("SDPA_FLASH_KERNEL", "generic")
+    for policy in ("nan", "zero"):
+        o, lse, _ = pu.run_hip(case, policy, return_lse=True)
+        want = {"mfma": "prefill_mfma", "split": "prefill_mfma", "f32": "prefill_f32",
+                "f32split": "prefill_f32", "generic": "generic"}[path]
+        assert sdpa.last_kernel() == want
+        if path in ("split", "f32split"):
+            assert sdpa.last_workspace_bytes() > 0
+        ro, rl = pu.run_oracle(case, policy)
+        assert np.isfinite(ro[:, :, :4]).all() and np.isfinite(ro[:, :, 5]).all()
+        _compare_large(o, lse, ro, rl, dtype, policy, what="%s %s" % (cfg, policy))
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_large_finite_mask_decode(dtype):
+    import scaled_dot_product_flash_amd as sdpa
+    spec = synth.DECODE_F16.replace(dtype=dtype, batch=6, k_len=300, seed=61)
+    case = synth.generate(spec)
+    case.key_lens[:] = [300, 150, 77, 300, 33, 256]
+    rng = np.random.default_rng(78)
+    mask = _large_mask_rows(rng, 6, 300)[:, None, None, :]
+    case = synth.Case(spec, case.q, case.k, case.v, case.key_lens, np.ascontiguousarray(mask))
+    for policy in ("nan", "zero"):
+        o, lse, _ = pu.run_hip(case, policy, return_lse=True)
+        assert sdpa.last_kernel() == "decode_splitk"
+        ro, rl = pu.run_oracle(case, policy)
+        _compare_large(o, lse, ro, rl, dtype, policy, what="decode %s %s" % (dtype, policy))
