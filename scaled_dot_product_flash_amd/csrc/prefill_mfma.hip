@@ -154,6 +154,22 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rs, uint32_t l
                  : "v"(voff), "s"(rs), "{m0}"(lds_byte));
 }
 
+// Maximum of the 32 scores a lane holds for its row (NaN-propagating), as a
+// tree of three-way maxima four levels deep.
+__device__ __forceinline__ float row_max32(const f32x16 (&s)[2]) {
+    float a[11];
+#pragma unroll
+    for (int i = 0; i < 10; ++i) {
+        const int j = 3 * i;   // values j, j+1, j+2 of the 32 (kb = j / 16)
+        a[i] = max_nan(max_nan(s[j / 16][j % 16], s[(j + 1) / 16][(j + 1) % 16]),
+                       s[(j + 2) / 16][(j + 2) % 16]);
+    }
+    a[10] = max_nan(s[1][14], s[1][15]);
+    const float b0 = max_nan(max_nan(a[0], a[1]), a[2]), b1 = max_nan(max_nan(a[3], a[4]), a[5]);
+    const float b2 = max_nan(max_nan(a[6], a[7]), a[8]), b3 = max_nan(a[9], a[10]);
+    return max_nan(max_nan(b0, b1), max_nan(b2, b3));
+}
+
 // kSplit: the workgroup covers one key range and writes partial records.
 // kOrder: workgroups take their units longest batch entry first (non-causal
 // problems with per-entry key lengths).  Both are compile-time variants, so
@@ -411,14 +427,17 @@ prefill_mfma_kernel(
     dma_wait_keep(0);
     __syncthreads();
 
-    f32x16 s_cur[2];
-    if (t_first < n_tiles) scores(kbuf(t_first), s_cur);
+    f32x16 s_a[2], s_b[2];
+    if (t_first < n_tiles) scores(kbuf(t_first), s_a);
     if (SP::kPrologueBarrier) __syncthreads();
     const bool cap = kVar && p.softcap > 0.f;
     const float cap_k2 = cap ? 2.f * kLog2e * p.scale / p.softcap : 0.f;
     const float cap_back = cap ? p.softcap / p.scale : 0.f;
 
-    for (int tile = t_first; tile < n_tiles; ++tile) {
+    // One tile; s_cur holds its scores, s_next receives the next tile's.  The
+    // loop below runs it twice per trip with the two score sets swapping
+    // roles, so no scores are copied between tiles.
+    auto step = [&](int tile, f32x16 (&s_cur)[2], f32x16 (&s_next)[2]) {
         const bool more_k = tile + SP::DK < n_tiles;
         const bool more_v = tile + SP::DV < n_tiles;
         if (SP::kTop) {
@@ -507,13 +526,9 @@ prefill_mfma_kernel(
                 }
         }
 
-        // -- row maximum: 32 values in-lane, then the partner lane --
-        float mx = kNegInf;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; r += 2) mx = max_nan(mx, max_nan(s_cur[kb][r], s_cur[kb][r + 1]));
-        mx = halves_max(mx);
+        // -- row maximum: 32 values in-lane (a tree of three-way maxima, four
+        // levels deep), then the partner lane --
+        float mx = halves_max(row_max32(s_cur));
         // -- lazy raise of the reference maximum --
         const bool raise = mx > m_ref + slack;
         if (__builtin_amdgcn_ballot_w64(raise)) {
@@ -545,25 +560,29 @@ prefill_mfma_kernel(
         // -- next tile's scores on the matrix core while this tile's softmax
         // runs (same basic block, so the two interleave).  After the last tile
         // the buffer holds stale keys and the result is discarded.
-        f32x16 s_next[2];
         scores(kbuf(tile + 1), s_next);
-        // -- p = exp2(s*c - m*c), rounded to the element type --
+        // -- p = exp2(s*c - m*c), rounded to the element type; the tile's sum
+        // of the rounded p in four independent chains (short dependences) --
         i16x8 pop[2][2];
+        float l_part[2][2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
             for (int st = 0; st < 2; ++st) {
                 uint32_t w4[4];
+                float lp = 0.f;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = 8 * st + 2 * e;
                     w4[e] = M::pack_out(fast_exp2(fmaf(s_cur[kb][r], c, neg_mc)),
                                         fast_exp2(fmaf(s_cur[kb][r + 1], c, neg_mc)));
-                    l_sum = M::sum2(w4[e], l_sum);
+                    lp = M::sum2(w4[e], lp);
                 }
+                l_part[kb][st] = lp;
                 pop[kb][st] = __builtin_bit_cast(i16x8, (uint4){w4[0], w4[1], w4[2], w4[3]});
             }
         }
+        l_sum += (l_part[0][0] + l_part[0][1]) + (l_part[1][0] + l_part[1][1]);
         // -- O^T += V^T P^T (V^T by transpose read) --
         // A wave whose rows cannot see this tile has all p = 0 here (every score
         // was hidden), so the products add exact zeros.
@@ -598,8 +617,10 @@ prefill_mfma_kernel(
         if (SP::DK >= 3 && SP::DV >= 2 && more_k) keep += kLoadsW;
         dma_wait_keep(keep);
         __syncthreads();
-        s_cur[0] = s_next[0];
-        s_cur[1] = s_next[1];
+    };
+    for (int tile = t_first; tile < n_tiles; tile += 2) {
+        step(tile, s_a, s_b);
+        if (tile + 1 < n_tiles) step(tile + 1, s_b, s_a);
     }
 
     // ---- epilogue: O = acc / l (or the masked-row policy), LSE = m + log l --
