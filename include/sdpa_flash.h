@@ -218,6 +218,24 @@ attn_status attn_decode(const attn_problem* p, const void* q, const void* k, con
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * attn_decode_noalloc -- attn_decode for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments and results as attn_decode without the
+ * workspace: the partial records go to a fixed 32 MiB device array that the
+ * library keeps on every GPU it runs on until the process ends (its address
+ * is looked up once per device, on the first call there, with that device
+ * current).  The call allocates nothing.  A problem whose
+ * attn_workspace_size(p, ATTN_OP_DECODE) exceeds 32 MiB returns
+ * ATTN_ERR_WORKSPACE.  All calls on one GPU share the array and need no
+ * clearing between them (every record is written before it is read), but
+ * calls that overlap in time on one GPU -- on different streams, or from
+ * different threads -- race on it and must be serialised by the caller.
+ */
+attn_status attn_decode_noalloc(const attn_problem* p, const void* q, const void* k,
+                                const void* v, void* o, const float* mask,
+                                const int32_t* key_lens, float* lse, void* stream);
+
+/*
  * attn_workspace_size -- bytes of device workspace the call `op` needs for
  * problem p (0 when it needs none).  Host-only: touches no device.
  * Returns ATTN_ERR_INVALID for a malformed problem.

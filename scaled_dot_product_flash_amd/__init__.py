@@ -17,21 +17,22 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["forward", "decode", "workspace_size", "AttnError", "lib_path", "load_library",
+__all__ = ["forward", "decode", "decode_noalloc", "workspace_size", "AttnError", "lib_path", "load_library",
            "Problem", "Layout", "SYMBOLS"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libsdpa_flash.so")
 
 # Every symbol include/sdpa_flash.h declares.
-SYMBOLS = ("attn_forward", "attn_decode", "attn_workspace_size", "attn_last_error",
-           "attn_last_kernel", "attn_version")
+SYMBOLS = ("attn_forward", "attn_decode", "attn_decode_noalloc", "attn_workspace_size",
+           "attn_last_error", "attn_last_kernel", "attn_version")
 
 OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 DTYPE_F32, DTYPE_F16, DTYPE_BF16 = 0, 1, 2
 MASKED_NAN, MASKED_ZERO = 0, 1
 QUANT_PER_TENSOR, QUANT_PER_CHANNEL = 1, 2
 OP_FORWARD, OP_DECODE = 0, 1
+_OP_DECODE_NOALLOC = 2     # binding-side tag: attn_decode_noalloc (no workspace argument)
 CAUSAL_OFFSET_DEFAULT = -(1 << 63)
 CAUSAL_OFFSET_KEY_END = -(1 << 63) + 1
 
@@ -86,6 +87,8 @@ def load_library():
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = call
+    lib.attn_decode_noalloc.restype = ctypes.c_int
+    lib.attn_decode_noalloc.argtypes = [ctypes.POINTER(Problem), vp, vp, vp, vp, vp, vp, vp, vp]
     lib.attn_workspace_size.restype = ctypes.c_int
     lib.attn_workspace_size.argtypes = [ctypes.POINTER(Problem), ctypes.c_int32,
                                         ctypes.POINTER(ctypes.c_size_t)]
@@ -254,15 +257,23 @@ def _run(op: int, q, k, v, *, layout: str, kv_layout: str | None, causal: bool,
         p.lse = Layout(0, Hq * Lq, Lq, 1)
     lib = load_library()
     global _last_ws
-    ws_bytes = workspace_size(p, op)
-    _last_ws = ws_bytes
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
+    ws = None
+    if op != _OP_DECODE_NOALLOC:
+        ws_bytes = workspace_size(p, op)
+        _last_ws = ws_bytes
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
     with torch.cuda.device(q.device):
         cur = torch.cuda.current_stream(q.device)
         s = stream if stream is not None else cur
-        fn = lib.attn_forward if op == OP_FORWARD else lib.attn_decode
-        _check(fn(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(mask),
-                  _ptr(key_lens), _ptr(lse), _ptr(ws), ws_bytes, ctypes.c_void_p(s.cuda_stream)))
+        if op == _OP_DECODE_NOALLOC:
+            _check(lib.attn_decode_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                           _ptr(mask), _ptr(key_lens), _ptr(lse),
+                                           ctypes.c_void_p(s.cuda_stream)))
+        else:
+            fn = lib.attn_forward if op == OP_FORWARD else lib.attn_decode
+            _check(fn(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(mask),
+                      _ptr(key_lens), _ptr(lse), _ptr(ws), ws_bytes,
+                      ctypes.c_void_p(s.cuda_stream)))
         if s != cur:
             # Blocks allocated here (workspace, contiguous copies, outputs) were
             # taken on the current stream; keep them from being reused there
@@ -309,6 +320,22 @@ def decode(q, k_cache, v_cache, key_lens=None, *, layout: str = "bshd", kv_layou
     (k_cache / v_cache int8) takes float32 k_scale / v_scale of 1 value (per
     tensor) or Hkv*D values (per channel, index g*D + d)."""
     return _run(OP_DECODE, q, k_cache, v_cache, layout=layout, kv_layout=kv_layout,
+                causal=True, causal_offset="end", scale=scale, mask=mask, key_lens=key_lens,
+                masked_rows=masked_rows, return_lse=return_lse, local_window=local_window,
+                softcap=softcap, sink=sink, head_sink=head_sink, k_scale=k_scale,
+                v_scale=v_scale, doc_start=doc_start, out=out, stream=stream)
+
+
+def decode_noalloc(q, k_cache, v_cache, key_lens=None, *, layout: str = "bshd",
+                   kv_layout: str = "bhsd", scale: float | None = None, mask=None,
+                   masked_rows: str = "nan", return_lse: bool = False, local_window: int = -1,
+                   softcap: float = 0.0, sink: bool = False, head_sink=None, k_scale=None,
+                   v_scale=None, doc_start=None, out=None, stream=None):
+    """decode() through attn_decode_noalloc: the library takes no workspace
+    and allocates nothing (its partial records go to a fixed device array it
+    holds per GPU).  Pass ``out`` (and no ``return_lse``) for a call that
+    allocates nothing on the torch side either."""
+    return _run(_OP_DECODE_NOALLOC, q, k_cache, v_cache, layout=layout, kv_layout=kv_layout,
                 causal=True, causal_offset="end", scale=scale, mask=mask, key_lens=key_lens,
                 masked_rows=masked_rows, return_lse=return_lse, local_window=local_window,
                 softcap=softcap, sink=sink, head_sink=head_sink, k_scale=k_scale,

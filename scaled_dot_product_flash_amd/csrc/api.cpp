@@ -181,6 +181,14 @@ attn_status launched(hipError_t e) {
 
 }  // namespace
 
+attn_status sdpa::set_error(attn_status status, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return status;
+}
+
 extern "C" {
 
 const char* attn_last_error(void) { return g_err; }

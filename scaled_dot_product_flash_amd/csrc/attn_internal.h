@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "sdpa_flash.h"
+
 namespace sdpa {
 
 // Element strides of one tensor: (b, h, r) -> b*sb + h*sh + r*sr (+ d).
@@ -47,6 +49,10 @@ struct Params {
 };
 
 enum class DType : int { F32 = 0, F16 = 1, BF16 = 2 };
+
+// Records a printf-style message for attn_last_error() on this thread and
+// returns `status`.
+attn_status set_error(attn_status status, const char* fmt, ...);
 
 // Launchers return the hipError_t of the launch.
 hipError_t launch_generic(const Params& p, DType dt, hipStream_t s);
