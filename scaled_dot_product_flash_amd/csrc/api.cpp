@@ -209,12 +209,9 @@ size_t decode_split_ws(const attn_problem* p) {
 // Workspace of the prefill paths' key-range splits (fp32 kernel; bf16/fp16
 // matrix-core kernel on small grids); shape only.
 size_t forward_ws(const attn_problem* p) {
-    if (p->dtype == ATTN_DTYPE_F32) {
-        const bool shape_ok = p->head_dim == 32 || p->head_dim == 64 || p->head_dim == 128;
-        return shape_ok ? sdpa::prefill_f32_workspace_bytes(p->batch, p->q_heads, p->q_len,
-                                                            p->k_len, p->head_dim)
-                        : 0;
-    }
+    if (p->dtype == ATTN_DTYPE_F32)
+        return sdpa::prefill_f32_workspace_bytes(p->batch, p->q_heads, p->q_len, p->k_len,
+                                                 p->head_dim);
     return sdpa::prefill_mfma_workspace_bytes(p->batch, p->q_heads, p->kv_heads, p->q_len,
                                               p->k_len, p->head_dim,
                                               p->causal && p->window > 0, p->doc_start != nullptr);

@@ -430,6 +430,17 @@ F32 = [
     (1, 4, 1, 100, 700, 128, True, None, True, True),
     (3, 2, 2, 17, 1000, 64, False, None, True, True),
     (1, 1, 1, 1, 1, 32, True, None, False, False),
+    # head dims padded to 32 / 64 / 96 / 128 / 256, odd ones (per-element
+    # loads), and the key-range split at several paddings
+    (2, 4, 2, 70, 70, 1, True, None, False, False),
+    (2, 4, 2, 90, 130, 17, False, None, True, True),
+    (2, 6, 3, 100, 100, 33, True, 0, True, False),
+    (2, 12, 4, 512, 512, 80, True, 0, False, False),
+    (2, 12, 4, 512, 512, 96, True, 0, False, False),
+    (1, 4, 2, 60, 900, 100, True, None, True, True),
+    (2, 4, 2, 130, 130, 160, True, None, False, False),
+    (1, 4, 4, 50, 700, 256, False, None, True, True),
+    (2, 4, 2, 100, 100, 256, True, 0, False, False),
 ]
 
 
@@ -532,7 +543,13 @@ VARIANTS = {
         sink="zero", seed=25), "prefill_mfma"),
     "window_cap_sink_f32": (synth.CAUSAL_GQA_F32.replace(
         batch=1, q_heads=4, kv_heads=2, q_len=100, k_len=100, local_window=10, softcap=3.0,
-        sink="heads", seed=26), "generic"),
+        sink="heads", seed=26), "prefill_f32"),
+    "window_docs_f32_D96_split": (synth.CAUSAL_GQA_F32.replace(
+        batch=1, q_heads=4, kv_heads=2, q_len=60, k_len=900, head_dim=96, local_window=300,
+        causal_offset=None, docs="random", sink="zero", seed=30), "prefill_f32"),
+    "softcap_f32_D256_mask_lens": (synth.CROSS_MASK_F16.replace(
+        dtype="f32", batch=3, q_heads=4, kv_heads=4, q_len=70, k_len=200, head_dim=256,
+        softcap=4.0, lens_zero_at=1, lens_full_at=0, mask_all_at=2, seed=31), "prefill_f32"),
     "decode_window_cap_sink": (synth.DECODE_F16.replace(
         batch=8, k_len=1000, local_window=100, softcap=30.0, sink="heads", seed=27),
         "decode_splitk"),
@@ -641,9 +658,12 @@ DOCS = {
         local_window=50, sink="heads", seed=43), "prefill_mfma"),
     "docs_noncausal_f16_mask": (synth.CROSS_MASK_F16.replace(
         q_len=100, k_len=300, docs="random", seed=44), "prefill_mfma"),
-    "docs_f32_generic": (synth.CAUSAL_GQA_F32.replace(
+    "docs_f32": (synth.CAUSAL_GQA_F32.replace(
         batch=2, q_heads=4, kv_heads=2, q_len=90, k_len=90, docs="packed", doc_mean=12,
-        seed=45), "generic"),
+        seed=45), "prefill_f32"),
+    "docs_f32_D33_sink_split": (synth.CAUSAL_GQA_F32.replace(
+        batch=1, q_heads=2, kv_heads=1, q_len=40, k_len=800, head_dim=33, docs="random",
+        causal_offset=None, sink="heads", seed=47), "prefill_f32"),
     "docs_decode": (synth.DECODE_F16.replace(
         batch=8, k_len=700, docs="random", seed=46), "decode_splitk"),
 }
@@ -821,3 +841,26 @@ def test_large_finite_mask_decode(dtype):
         assert sdpa.last_kernel() == "decode_splitk"
         ro, rl = pu.run_oracle(case, policy)
         _compare_large(o, lse, ro, rl, dtype, policy, what="decode %s %s" % (dtype, policy))
+
+
+# fp32 at long key lengths (OneGPU "Attention", "Accuracy at long key
+# lengths": a single running sum lost accuracy at thousands of keys; the fp32
+# kernel sums each tile into zero-started partials).  Q is scaled so the
+# scores spread with standard deviation 3 to 12 (natural units).  The scaled
+# error (max |gpu - oracle| / max |oracle|) is printed beside the page's 1e-5
+# fp32 figure; the bound is the fp32 tolerance.
+@pytest.mark.parametrize("lk,spread", [(4096, 3.0), (4096, 12.0), (8192, 6.0)])
+def test_fp32_long_keys_accuracy(lk, spread):
+    import scaled_dot_product_flash_amd as sdpa
+    spec = synth.Spec("f32-long", 1, 4, 2, 64, lk, 64, "f32", seed=70 + lk % 97, causal=False,
+                      lse=True)
+    case = synth.generate(spec)
+    # score std = |q| |k| scale: scale q so that scale * |q| * |k| ~ spread
+    q = (case.q * np.float32(spread)).astype(np.float32)
+    case = synth.Case(spec, q, case.k, case.v, None, None)
+    o, lse, _ = pu.run_hip(case, "nan", return_lse=True)
+    assert sdpa.last_kernel() == "prefill_f32"
+    ro, rl = pu.run_oracle(case, "nan")
+    err = pu.compare(o, ro, lse, rl, "f32", "nan", what="f32 Lk=%d spread %g" % (lk, spread))
+    print("fp32 Lk=%d score std %.0f: max|err| %.3g, scaled %.3g (page: 1e-5 bound)"
+          % (lk, spread, err, err / np.abs(ro).max()))
