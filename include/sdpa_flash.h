@@ -189,8 +189,11 @@ typedef struct attn_problem {
  *              into ranges whose partial (max, sum, accumulator) records go
  *              to the workspace, and a second kernel merges each row's
  *              ranges in order (OneGPU "Attention", "Accuracy at long key
- *              lengths", last paragraph).  The size depends on the shape
- *              only; the contents need no initialisation and are scratch.
+ *              lengths", last paragraph).  bf16/fp16 head dims that are not
+ *              a multiple of 8 also keep copies of K and V there, padded to
+ *              one (OneGPU "Attention", "What it covers": other head dims
+ *              are padded up).  The size depends on the shape only; the
+ *              contents need no initialisation and are scratch.
  *   stream     hipStream_t to enqueue on.
  * Returns ATTN_OK, or an error with nothing enqueued (ATTN_ERR_WORKSPACE
  * when a needed workspace is missing or too small).

@@ -212,7 +212,10 @@ size_t forward_ws(const attn_problem* p) {
     if (p->dtype == ATTN_DTYPE_F32)
         return sdpa::prefill_f32_workspace_bytes(p->batch, p->q_heads, p->q_len, p->k_len,
                                                  p->head_dim);
-    return sdpa::prefill_mfma_workspace_bytes(p->batch, p->q_heads, p->kv_heads, p->q_len,
+    // Staged K/V copies (head dims not a multiple of 8) first, then the
+    // key-range split's records.
+    return sdpa::prefill_mfma_stage_bytes(p->batch, p->kv_heads, p->k_len, p->head_dim) +
+           sdpa::prefill_mfma_workspace_bytes(p->batch, p->q_heads, p->kv_heads, p->q_len,
                                               p->k_len, p->head_dim,
                                               p->causal && p->window > 0, p->doc_start != nullptr);
 }
@@ -256,14 +259,17 @@ attn_status attn_forward(const attn_problem* p, const void* q, const void* k, co
                                 p->head_dim, p->causal && p->window > 0, p->doc_start != nullptr,
                                 &prm.split_len, &prm.n_split);
         if (sdpa::prefill_mfma_supported(prm, dt)) {
-            if (prm.n_split > 1) {
-                const size_t need = forward_ws(p);
+            const size_t need = forward_ws(p);
+            if (need > 0) {
                 if (!workspace || workspace_bytes < need)
                     return fail(ATTN_ERR_WORKSPACE, "forward needs %zu workspace bytes, got %zu",
                                 need, workspace ? workspace_bytes : size_t(0));
                 if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
                     return fail(ATTN_ERR_INVALID, "workspace must be 16-byte aligned");
-                prm.ws = workspace;
+                const size_t stage =
+                    sdpa::prefill_mfma_stage_bytes(p->batch, p->kv_heads, p->k_len, p->head_dim);
+                prm.stage = workspace;
+                prm.ws = static_cast<char*>(workspace) + stage;
             }
             g_kernel = "prefill_mfma";
             return launched(sdpa::launch_prefill_mfma(prm, dt, s));

@@ -44,6 +44,7 @@ struct Params {
     const float* k_scale;
     const float* v_scale;
     const int32_t* doc_start;   // nullable: per (b, i) first visible key
+    void* stage;           // workspace part for staged K/V copies (head dims not a multiple of 8)
     int32_t n_split;       // key ranges per row block (1: no split); 16-byte aligned ws
     int32_t split_len;     // keys per range (multiple of the kernel's tile)
 };
@@ -62,6 +63,7 @@ void prefill_mfma_plan(int B, int Hq, int Hkv, int Lq, int Lk, int D, bool windo
                        int* split_len, int* n_split);
 size_t prefill_mfma_workspace_bytes(int B, int Hq, int Hkv, int Lq, int Lk, int D, bool window,
                                     bool docs);
+size_t prefill_mfma_stage_bytes(int B, int Hkv, int Lk, int D);
 bool prefill_mfma_supported(const Params& p, DType dt);
 bool decode_split_supported(const Params& p, DType dt);
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int D);

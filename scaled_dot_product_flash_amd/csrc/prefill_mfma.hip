@@ -1,6 +1,7 @@
 // prefill_mfma.hip -- fused attention for bf16 / fp16 inputs with fp32
-// accumulation on the gfx950 matrix cores (head dims that are multiples of 8,
-// up to 256).
+// accumulation on the gfx950 matrix cores, head dims 1..256 (padded to 64,
+// 128 or 256; a head dim that is not a multiple of 8 first has its K/V rows
+// staged into the workspace as copies padded to one).
 //
 // Work decomposition.  A workgroup of W waves (8 for head dim 128, else 4;
 // see Cfg) owns one (batch, kv head) and 32 W query rows that read it: gw
@@ -72,6 +73,10 @@ using namespace mfma;
 
 constexpr int kBN = 64;        // keys per tile
 constexpr float kSlack = 8.f;  // lazy-rescale threshold, base-2 units
+
+// Floats per partial record of the key-range split: m, l, two pads, then the
+// accumulator padded to whole float4.
+__host__ __device__ constexpr int record_stride(int D) { return (D + 3) / 4 * 4 + 4; }
 
 // Workgroup shape per padded head dim DP, waves of 32 query rows.  DP = 128:
 // 8 waves, two per SIMD (about 205 registers each).  DP = 256: a wave's Q
@@ -187,6 +192,11 @@ prefill_mfma_kernel(
     // kernel; in the plain one it is the compile-time D and the column guards
     // below fold away.
     const int Dt = kVar ? p.D : D;
+    // K/V columns per row: a head dim that is not a multiple of 8 reads
+    // copies padded to one (zeros past Dt), staged into the workspace first;
+    // its Q rows are then read and O rows written per element.
+    const int Dkv = kVar ? (p.D + 7) & ~7 : D;
+    const bool elem = kVar && (p.D & 7) != 0;
     constexpr int NT = D / 16;   // 16-wide d-steps of the score product
     constexpr int ND = D / 32;   // 32-row d-tiles of the output
     constexpr int NB = TL::NB, KB = TL::KB, VB = TL::VB, RB = TL::RB;
@@ -342,7 +352,15 @@ prefill_mfma_kernel(
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             const bool in = ok && 16 * t + 8 * hh < Dt;   // padded columns are zero
-            qop[t] = in ? *reinterpret_cast<const i16x8*>(src + 16 * t) : i16x8{};
+            if (elem) {
+                i16x8 v{};
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    v[e] = (ok && 16 * t + 8 * hh + e < Dt) ? static_cast<short>(src[16 * t + e]) : short(0);
+                qop[t] = v;
+            } else {
+                qop[t] = in ? *reinterpret_cast<const i16x8*>(src + 16 * t) : i16x8{};
+            }
         }
     }
 
@@ -363,7 +381,7 @@ prefill_mfma_kernel(
             const int I = n * kWaves + w;
             const int key = tile * kBN + I + NB * ld_q;
             const uint32_t off =
-                8 * ld_c < Dt ? static_cast<uint32_t>((key * static_cast<int>(sr) + 8 * ld_c) * 2)
+                8 * ld_c < Dkv ? static_cast<uint32_t>((key * static_cast<int>(sr) + 8 * ld_c) * 2)
                               : kOutOfRange;
             if constexpr (SP::kAsm)
                 load_lds16(rs,
@@ -631,7 +649,7 @@ prefill_mfma_kernel(
         // applies the sink, the masked-row policy and the LSE.
         if (qrow < p.Lq) {
             // Range-major records: [range][b][h][row][m, l, -, -, acc[D]].
-            const int RS = p.D + 4;
+            const int RS = record_stride(p.D);
             float* rec = static_cast<float*>(p.ws) +
                          (((static_cast<int64_t>(rng) * p.B + b) * p.Hq + h) * p.Lq + qrow) * RS;
 #pragma unroll
@@ -664,8 +682,15 @@ prefill_mfma_kernel(
 #pragma unroll
                 for (int e = 0; e < 4; ++e) o4[e] = empty ? fill : acc[d][4 * u + e] * inv;
                 const uint2 pk = {M::pack_out(o4[0], o4[1]), M::pack_out(o4[2], o4[3])};
-                if (32 * d + 8 * u + 4 * hh < Dt)
-                    *reinterpret_cast<uint2*>(og + 32 * d + 8 * u + 4 * hh) = pk;
+                const int c0 = 32 * d + 8 * u + 4 * hh;
+                if (elem) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (c0 + e < Dt)
+                            og[c0 + e] = static_cast<uint16_t>(((e < 2 ? pk.x : pk.y) >> (16 * (e & 1))) & 0xffffu);
+                } else if (c0 < Dt) {
+                    *reinterpret_cast<uint2*>(og + c0) = pk;
+                }
             }
         }
         if (p.lse && hh == 0) {
@@ -691,7 +716,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_merge_kernel(Params p, float
     const int64_t i = row % p.Lq;
     const int h = static_cast<int>((row / p.Lq) % p.Hq);
     const int b = static_cast<int>(row / (static_cast<int64_t>(p.Lq) * p.Hq));
-    const int RS = p.D + 4;
+    const int RS = record_stride(p.D);
     const int64_t range_stride = total / p.D * RS;  // records of one range
     const float* recs = static_cast<const float*>(p.ws) + row * RS;
     // Folded in range order; eight ranges' (m, l, acc[d]) are fetched per
@@ -732,6 +757,44 @@ __global__ __launch_bounds__(256) void prefill_mfma_merge_kernel(Params p, float
     Elem<T>::store(p.o, b * p.os.sb + h * p.os.sh + i * p.os.sr + d, o);
     if (p.lse && d == 0)
         p.lse[b * p.ls.sb + h * p.ls.sh + i * p.ls.sr] = empty ? kNegInf : row_lse(m_nat, L);
+}
+
+// Head dims that are not a multiple of 8 (rows not made of whole 16-byte
+// chunks): one thread per 8-element chunk copies K and V rows into the
+// workspace with the head dim padded to a multiple of 8 (zeros), so the main
+// kernel's 16-byte loads apply.  Rows at or past a batch entry's key length
+// are written as zeros, not read.
+__global__ __launch_bounds__(256) void prefill_stage_kv_kernel(Params p, uint16_t* kd, uint16_t* vd,
+                                                               int dp8) {
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    const int cpr = dp8 / 8;                                   // chunks per row
+    const int64_t total = static_cast<int64_t>(p.B) * p.Hkv * p.Lk * cpr;
+    if (t >= total) return;
+    const int cch = static_cast<int>(t % cpr);
+    const int64_t rowi = t / cpr;                              // (b, g, j) flattened
+    const int64_t j = rowi % p.Lk;
+    const int g = static_cast<int>((rowi / p.Lk) % p.Hkv);
+    const int b = static_cast<int>(rowi / (static_cast<int64_t>(p.Lk) * p.Hkv));
+    int64_t kv_len = p.Lk;
+    if (p.lens) {
+        const int64_t L = p.lens[b];
+        kv_len = L < 0 ? 0 : (L > p.Lk ? p.Lk : L);
+    }
+    const uint16_t* ks = static_cast<const uint16_t*>(p.k) + b * p.ks.sb + g * p.ks.sh + j * p.ks.sr;
+    const uint16_t* vs = static_cast<const uint16_t*>(p.v) + b * p.vs.sb + g * p.vs.sh + j * p.vs.sr;
+    uint16_t kx[8], vx[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int col = 8 * cch + e;
+        const bool in = j < kv_len && col < p.D;
+        kx[e] = in ? ks[col] : uint16_t(0);
+        vx[e] = in ? vs[col] : uint16_t(0);
+    }
+    const int64_t o = rowi * dp8 + 8 * cch;
+    *reinterpret_cast<uint4*>(kd + o) = make_uint4(kx[0] | (uint32_t(kx[1]) << 16), kx[2] | (uint32_t(kx[3]) << 16),
+                                                   kx[4] | (uint32_t(kx[5]) << 16), kx[6] | (uint32_t(kx[7]) << 16));
+    *reinterpret_cast<uint4*>(vd + o) = make_uint4(vx[0] | (uint32_t(vx[1]) << 16), vx[2] | (uint32_t(vx[3]) << 16),
+                                                   vx[4] | (uint32_t(vx[5]) << 16), vx[6] | (uint32_t(vx[7]) << 16));
 }
 
 // Padded head dim of the kernel that runs head dim D.
@@ -840,7 +903,7 @@ void prefill_mfma_plan(int B, int Hq, int Hkv, int Lq, int Lk, int D, bool windo
                        int* split_len, int* n_split) {
     *split_len = 0;
     *n_split = 1;
-    if (B <= 0 || Hkv <= 0 || Hq % Hkv != 0 || Lq <= 0 || Lk <= 0 || D % 8 != 0 || D > 256) return;
+    if (B <= 0 || Hkv <= 0 || Hq % Hkv != 0 || Lq <= 0 || Lk <= 0 || D < 1 || D > 256) return;
     const bool shrt = short_rows(window, docs);
     const int DP = padded_dim(D), waves = waves_for(DP, shrt), rows = 32 * waves;
     const int group = Hq / Hkv, gw = heads_per_block(group, waves);
@@ -863,29 +926,59 @@ size_t prefill_mfma_workspace_bytes(int B, int Hq, int Hkv, int Lq, int Lk, int 
     int len, n;
     prefill_mfma_plan(B, Hq, Hkv, Lq, Lk, D, window, docs, &len, &n);
     if (n <= 1) return 0;
-    return static_cast<size_t>(B) * Hq * Lq * n * (D + 4) * sizeof(float);
+    return static_cast<size_t>(B) * Hq * Lq * n * record_stride(D) * sizeof(float);
+}
+
+// Workspace bytes of the staged K/V copies (head dims that are not a
+// multiple of 8; 0 otherwise), shape only; 256-byte multiple.
+size_t prefill_mfma_stage_bytes(int B, int Hkv, int Lk, int D) {
+    if (D % 8 == 0 || Lk == 0) return 0;
+    const size_t one = static_cast<size_t>(B) * Hkv * Lk * ((D + 7) / 8 * 8) * 2;
+    return (2 * one + 255) / 256 * 256;
 }
 
 bool prefill_mfma_supported(const Params& p, DType dt) {
     if (dt != DType::BF16 && dt != DType::F16) return false;
-    if (p.D % 8 != 0 || p.D > 256) return false;
-    // 16-byte loads of Q/K/V rows and 8-byte stores of O need aligned rows.
+    if (p.D < 1 || p.D > 256) return false;
+    const bool staged = p.D % 8 != 0;
+    // 16-byte loads of Q/K/V rows and 8-byte stores of O need aligned rows;
+    // a staged problem reads Q and writes O per element and reads K/V from
+    // its aligned copies.
     auto al = [](const void* ptr, const Strides& st, int a) {
         return reinterpret_cast<uintptr_t>(ptr) % (2 * a) == 0 && st.sb % a == 0 &&
                st.sh % a == 0 && st.sr % a == 0;
     };
-    if (!al(p.q, p.qs, 8) || !al(p.o, p.os, 4)) return false;
-    if (p.Lk > 0 && (!al(p.k, p.ks, 8) || !al(p.v, p.vs, 8))) return false;
+    if (!staged) {
+        if (!al(p.q, p.qs, 8) || !al(p.o, p.os, 4)) return false;
+        if (p.Lk > 0 && (!al(p.k, p.ks, 8) || !al(p.v, p.vs, 8))) return false;
+    }
     // Buffer offsets within one (b, kv head) slice are 32-bit, including the
     // up-to-one-tile overrun past the key length.
-    if (p.ks.sr >= (1 << 24) || p.vs.sr >= (1 << 24)) return false;
-    if ((static_cast<int64_t>(p.Lk) + kBN) * p.ks.sr * 2 >= (int64_t(1) << 31) ||
-        (static_cast<int64_t>(p.Lk) + kBN) * p.vs.sr * 2 >= (int64_t(1) << 31))
+    const int64_t ksr = staged ? (p.D + 7) / 8 * 8 : p.ks.sr;
+    const int64_t vsr = staged ? (p.D + 7) / 8 * 8 : p.vs.sr;
+    if (ksr >= (1 << 24) || vsr >= (1 << 24)) return false;
+    if ((static_cast<int64_t>(p.Lk) + kBN) * ksr * 2 >= (int64_t(1) << 31) ||
+        (static_cast<int64_t>(p.Lk) + kBN) * vsr * 2 >= (int64_t(1) << 31))
         return false;
     return block_count(p) * p.n_split < (int64_t(1) << 31);
 }
 
-hipError_t launch_prefill_mfma(const Params& p, DType dt, hipStream_t s) {
+hipError_t launch_prefill_mfma(const Params& p_in, DType dt, hipStream_t s) {
+    Params p = p_in;
+    if (p.D % 8 != 0 && p.Lk > 0) {   // stage K/V with the head dim padded to a multiple of 8
+        const int dp8 = (p.D + 7) / 8 * 8;
+        uint16_t* kd = static_cast<uint16_t*>(p.stage);
+        uint16_t* vd = kd + static_cast<int64_t>(p.B) * p.Hkv * p.Lk * dp8;
+        const int64_t chunks = static_cast<int64_t>(p.B) * p.Hkv * p.Lk * (dp8 / 8);
+        hipLaunchKernelGGL(prefill_stage_kv_kernel, dim3(static_cast<uint32_t>((chunks + 255) / 256)),
+                           dim3(256), 0, s, p, kd, vd, dp8);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        p.k = kd;
+        p.v = vd;
+        p.ks = {static_cast<int64_t>(p.Hkv) * p.Lk * dp8, static_cast<int64_t>(p.Lk) * dp8, dp8};
+        p.vs = p.ks;
+    }
     const int DP = padded_dim(p.D);
     if (dt == DType::BF16) {
         if (DP == 64) return launch_one<true, 64>(p, s);

@@ -724,14 +724,45 @@ def test_head_dims_on_matrix_cores(cfg, policy):
     pu.compare(o, ro, lse, rl, spec.dtype, policy, what="D=%d %s" % (D, dtype))
 
 
-def test_odd_head_dim_runs_on_the_generic_kernel():
-    spec = synth.CAUSAL_GQA_BF16.replace(dtype="f16", batch=2, q_heads=4, kv_heads=2, q_len=40,
-                                         k_len=40, head_dim=33, seed=60)
+# Head dims that are not a multiple of 8: K/V staged into the workspace
+# padded to one, Q read and O written per element, then the matrix-core
+# kernel at the padded dim (OneGPU "Attention", "What it covers").
+ODD_DIMS = [
+    # D, dtype, B, Hq, Hkv, Lq, Lk, extra
+    (1, "bf16", 2, 4, 2, 70, 70, {}),
+    (17, "bf16", 3, 8, 2, 150, 150, dict(lens="cross", lens_zero_at=1, lens_full_at=0)),
+    (33, "f16", 2, 4, 2, 40, 40, {}),
+    (100, "bf16", 2, 8, 2, 200, 260, dict(local_window=60, sink="heads")),
+    (100, "f16", 2, 4, 4, 90, 300, dict(causal=False, mask="keys", lens="cross",
+                                        lens_zero_at=1, lens_full_at=0, mask_all_at=5)),
+    (255, "bf16", 2, 4, 2, 100, 100, dict(docs="packed", doc_mean=20, softcap=8.0)),
+    (130, "f16", 1, 8, 2, 64, 2000, dict(causal_offset=None)),   # key-range split
+]
+
+
+@pytest.mark.parametrize("cfg", ODD_DIMS, ids=lambda c: "D%d-%s-%dx%d" % (c[0], c[1], c[5], c[6]))
+@pytest.mark.parametrize("policy", ["nan", "zero"])
+def test_odd_head_dims_on_matrix_cores(cfg, policy):
+    D, dtype, B, Hq, Hkv, lq, lk, extra = cfg
+    spec = synth.CAUSAL_GQA_BF16.replace(dtype=dtype, batch=B, q_heads=Hq, kv_heads=Hkv,
+                                         q_len=lq, k_len=lk, head_dim=D, seed=60 + D, **extra)
+    case = synth.generate(spec)
+    o, lse, _ = pu.run_hip(case, policy, return_lse=True)
+    assert sdpa.last_kernel() == "prefill_mfma"
+    assert sdpa.last_workspace_bytes() > 0      # the staged K/V copies
+    ro, rl = pu.run_oracle(case, policy)
+    pu.compare(o, ro, lse, rl, spec.dtype, policy, what="D=%d %s" % (D, dtype))
+
+
+def test_odd_head_dim_decode_runs_staged():
+    """Decode at a head dim the split decode path does not take runs as the
+    forward path does, staged K/V included."""
+    spec = synth.DECODE_F16.replace(batch=8, k_len=700, head_dim=100, seed=67)
     case = synth.generate(spec)
     o, lse, _ = pu.run_hip(case, "nan", return_lse=True)
-    assert sdpa.last_kernel() == "generic"
+    assert sdpa.last_kernel() == "prefill_mfma"
     ro, rl = pu.run_oracle(case, "nan")
-    pu.compare(o, ro, lse, rl, spec.dtype, "nan", what="D=33")
+    pu.compare(o, ro, lse, rl, spec.dtype, "nan", what="decode D=100")
 
 
 @pytest.mark.parametrize("name", ["d256_bf16", "d96_bf16"])
