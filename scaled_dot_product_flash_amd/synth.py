@@ -51,7 +51,7 @@ class Spec:
     causal_offset: Optional[Union[int, str]] = None   # None, an int or 'end'
     lse: bool = False
     decode: bool = False
-    lens: Optional[str] = None        # None, 'uniform' (in [1, k_len]), 'cross' or
+    lens: Optional[str] = None        # None, 'uniform' (in [1, k_len]), 'full', 'cross' or
                                       # 'chunk' (in [q_len, k_len]: the chunk fits)
     mask: Optional[str] = None        # None or 'keys' ([B,1,1,Lk], 10% -inf)
     masked_rows: str = "nan"
@@ -137,6 +137,13 @@ D256_BF16 = CAUSAL_GQA_BF16.replace(
 D96_BF16 = CAUSAL_GQA_BF16.replace(
     name="bf16 causal GQA prefill B4 H32/8 L4096 D96", head_dim=96, seed=13)
 
+# Head dims that are not a multiple of 8 (bf16, run padded to 128 with K/V
+# staged) and an fp32 head dim between the fp32 kernel's tiles (96 -> 128).
+D100_BF16 = CAUSAL_GQA_BF16.replace(
+    name="bf16 causal GQA prefill B4 H32/8 L4096 D100", head_dim=100, seed=15)
+D96_F32 = CAUSAL_GQA_BF16.replace(
+    name="fp32 causal GQA prefill B4 H32/8 L4096 D96", dtype="f32", head_dim=96, seed=16)
+
 # Workloads of the extensions beyond the five (measured and tested the same way).
 EXTRA_WORKLOADS = {
     "chunk_f16": CHUNK_F16,
@@ -148,7 +155,32 @@ EXTRA_WORKLOADS = {
     "docs_bf16": DOCS_BF16,
     "d256_bf16": D256_BF16,
     "d96_bf16": D96_BF16,
+    "d100_bf16": D100_BF16,
+    "d96_f32": D96_F32,
 }
+
+# The model shapes the OneGPU "Attention" page times (its "Performance"
+# tables): 12 heads throughout, no mask; MiniLM with head dim 32, BERT-base
+# and Whisper-small with 64.  The page does not state the Whisper batch;
+# 1 is taken.  The Whisper decoder row is read as one new query row against
+# 448 cached keys, the cross-attention row as one query row against the
+# encoder's 1500 keys.  Random inputs of those shapes: no trained weights.
+MINILM_B8 = Spec("MiniLM B8 S128 H12 D32", 8, 12, 12, 128, 128, 32, "f32", seed=20)
+BERT_B8_S512 = Spec("BERT-base B8 S512 H12 D64", 8, 12, 12, 512, 512, 64, "f32", seed=21)
+WHISPER_ENC = Spec("Whisper-small encoder B1 H12 L1500 D64", 1, 12, 12, 1500, 1500, 64, "f32",
+                   seed=22)
+WHISPER_DEC = Spec("Whisper-small decoder step B1 H12 cache448 D64", 1, 12, 12, 1, 448, 64,
+                   "f32", seed=23, kv_layout="bhsd", causal=True, decode=True, lens="full")
+WHISPER_CROSS = Spec("Whisper-small cross-attention B1 H12 Lq1 Lk1500 D64", 1, 12, 12, 1, 1500,
+                     64, "f32", seed=24)
+
+
+def _both(spec: Spec):
+    return [spec, spec.replace(name=spec.name + " fp16", dtype="f16", seed=spec.seed + 100)]
+
+
+PAGE_SHAPES = {s.name: s for base in (MINILM_B8, BERT_B8_S512, WHISPER_ENC, WHISPER_DEC,
+                                      WHISPER_CROSS) for s in _both(base)}
 
 
 def round_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -223,6 +255,8 @@ def generate(spec: Spec) -> Case:
             lens[spec.lens_zero_at] = 0
         if spec.lens_full_at < spec.batch:
             lens[spec.lens_full_at] = spec.k_len
+    elif spec.lens == "full":
+        lens = np.full(spec.batch, spec.k_len, dtype=np.int32)
     elif spec.lens == "chunk":
         lens = rng.integers(min(spec.q_len, spec.k_len), spec.k_len + 1,
                             size=spec.batch).astype(np.int32)

@@ -765,11 +765,15 @@ def test_odd_head_dim_decode_runs_staged():
     pu.compare(o, ro, lse, rl, spec.dtype, "nan", what="decode D=100")
 
 
-@pytest.mark.parametrize("name", ["d256_bf16", "d96_bf16"])
-def test_head_dim_workloads_full_size_sampled(name):
+@pytest.mark.parametrize("name,kernel", [("d256_bf16", "prefill_mfma"),
+                                         ("d96_bf16", "prefill_mfma"),
+                                         ("d100_bf16", "prefill_mfma"),
+                                         ("d96_f32", "prefill_f32")])
+def test_head_dim_workloads_full_size_sampled(name, kernel):
     spec = synth.EXTRA_WORKLOADS[name]
     case = synth.generate(spec)
     o, lse, _ = pu.run_hip(case, "nan")
+    assert sdpa.last_kernel() == kernel
     assert np.isfinite(o).all() and np.isfinite(lse).all()
     rows = pu.sample_rows(spec, 64, seed=12)
     ro, rl = pu.run_oracle(case, "nan", rows=rows)
@@ -895,3 +899,17 @@ def test_fp32_long_keys_accuracy(lk, spread):
     err = pu.compare(o, ro, lse, rl, "f32", "nan", what="f32 Lk=%d spread %g" % (lk, spread))
     print("fp32 Lk=%d score std %.0f: max|err| %.3g, scaled %.3g (page: 1e-5 bound)"
           % (lk, spread, err, err / np.abs(ro).max()))
+
+
+# The model shapes the OneGPU "Attention" page times ("Performance"), fp32
+# and fp16, compared in full against the oracle: MiniLM (head 32), BERT-base
+# B8 S512, the Whisper-small encoder (1500 keys), a decoder step against 448
+# cached keys and one-query cross-attention over the 1500 encoder keys.
+@pytest.mark.parametrize("name", sorted(synth.PAGE_SHAPES))
+def test_page_model_shapes(name):
+    spec = synth.PAGE_SHAPES[name]
+    case = synth.generate(spec)
+    o, lse, _ = pu.run_hip(case, "nan", return_lse=True)
+    assert sdpa.last_kernel() != "generic"
+    ro, rl = pu.run_oracle(case, "nan")
+    pu.compare(o, ro, lse, rl, spec.dtype, "nan", what=name)
