@@ -210,8 +210,8 @@ size_t decode_split_ws(const attn_problem* p) {
 // matrix-core kernel on small grids); shape only.
 size_t forward_ws(const attn_problem* p) {
     if (p->dtype == ATTN_DTYPE_F32)
-        return sdpa::prefill_f32_workspace_bytes(p->batch, p->q_heads, p->q_len, p->k_len,
-                                                 p->head_dim);
+        return sdpa::prefill_f32_workspace_bytes(p->batch, p->q_heads, p->kv_heads, p->q_len,
+                                                 p->k_len, p->head_dim);
     // Staged K/V copies (head dims not a multiple of 8) first, then the
     // key-range split's records.
     return sdpa::prefill_mfma_stage_bytes(p->batch, p->kv_heads, p->k_len, p->head_dim) +
@@ -277,8 +277,8 @@ attn_status attn_forward(const attn_problem* p, const void* q, const void* k, co
         prm.n_split = 1;
         prm.split_len = 0;
     }
-    sdpa::prefill_f32_plan(p->batch, p->q_heads, p->q_len, p->k_len, p->head_dim, &prm.split_len,
-                           &prm.n_split);
+    sdpa::prefill_f32_plan(p->batch, p->q_heads, p->kv_heads, p->q_len, p->k_len, p->head_dim,
+                           &prm.split_len, &prm.n_split);
     if (!force_generic() && sdpa::prefill_f32_supported(prm, dt)) {
         if (prm.n_split > 1) {
             const size_t need = forward_ws(p);

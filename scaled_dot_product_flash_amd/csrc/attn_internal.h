@@ -69,8 +69,9 @@ bool decode_split_supported(const Params& p, DType dt);
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int D);
 hipError_t launch_decode_split(const Params& p, DType dt, hipStream_t s);
 
-void prefill_f32_plan(int B, int Hq, int Lq, int Lk, int D, int* split_len, int* n_split);
-size_t prefill_f32_workspace_bytes(int B, int Hq, int Lq, int Lk, int D);
+void prefill_f32_plan(int B, int Hq, int Hkv, int Lq, int Lk, int D, int* split_len,
+                      int* n_split);
+size_t prefill_f32_workspace_bytes(int B, int Hq, int Hkv, int Lq, int Lk, int D);
 bool prefill_f32_supported(const Params& p, DType dt);
 hipError_t launch_prefill_f32(const Params& p, DType dt, hipStream_t s);
 hipError_t launch_prefill_mfma(const Params& p, DType dt, hipStream_t s);

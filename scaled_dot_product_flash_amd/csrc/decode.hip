@@ -9,9 +9,10 @@
 // causal bound of the one query row) form ceil(len/32) steps of 32 keys.
 //
 // Load balance.  Per-batch lengths differ widely, so cutting each unit into
-// fixed ranges leaves the GPU half idle at the end.  Instead a fixed number of
-// waves W (2048: eight per CU of an MI355X) each take an equal contiguous
-// share of the concatenated steps of all units, in unit order; every wave
+// fixed ranges leaves the GPU half idle at the end.  Instead W waves (2048:
+// eight per CU of an MI355X; as many as there are steps when there are
+// fewer) each take an equal contiguous share of the concatenated steps of
+// all units, in unit order; every wave
 // computes the same per-batch prefix sums from the lengths, so the cut needs
 // no host round trip.  A wave writes one partial record (reference max, sum,
 // unnormalised accumulator) for each unit it touches, at slot (unit + wave):
@@ -180,10 +181,15 @@ __device__ int64_t steps_before(const Params& p, int b, int per_b_units) {
     return uniform64(total * per_b_units);
 }
 
+// Waves that share S steps: every wave gets at least one.
+__device__ __forceinline__ int64_t share_waves(int64_t S) {
+    return S < kWavesTotal ? S : kWavesTotal;
+}
+
 // Wave that owns flattened step x when S steps are cut into W equal shares
 // (share w = [floor(S*w/W), floor(S*(w+1)/W))).
-__device__ __forceinline__ int owner_wave(int64_t x, int64_t S) {
-    return static_cast<int>(((x + 1) * kWavesTotal - 1) / S);
+__device__ __forceinline__ int owner_wave(int64_t x, int64_t S, int64_t W) {
+    return static_cast<int>(((x + 1) * W - 1) / S);
 }
 
 template <bool kBf16, int D, bool kCap, bool kI8>
@@ -201,7 +207,9 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(Params p, int n_hgr
     const int wave = blockIdx.x;
     const int per_b = p.Hkv * n_hgrp;            // units per batch entry
     const int64_t S = steps_before(p, p.B, per_b);
-    const int64_t a = S * wave / kWavesTotal, e = S * (wave + 1) / kWavesTotal;
+    const int64_t W = share_waves(S);
+    if (wave >= W) return;
+    const int64_t a = S * wave / W, e = S * (wave + 1) / W;
     if (a >= e) return;
 
     // Locate the unit holding step a: 64 entries per round, one per lane;
@@ -494,15 +502,14 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(Params p, int n_hgr
 #pragma unroll
     for (int cc = 0; cc < NPL; ++cc) A[cc] = 0.f;
     if (sb > 0) {
-        const int w_lo = owner_wave(first, S), w_hi = owner_wave(first + sb - 1, S);
+        const int64_t W = share_waves(S);
+        const int w_lo = owner_wave(first, S, W), w_hi = owner_wave(first + sb - 1, S, W);
         const int n = w_hi - w_lo + 1;
         const int rs = rec_stride(D);
         const float* base = static_cast<const float*>(p.ws);
         auto rec = [&](int w) { return base + ((unit + w) * slot_heads + col) * rs; };
-        // Waves with an empty share (fewer steps than waves) wrote no record.
-        auto empty_share = [&](int w) {
-            return S * w / kWavesTotal == S * (w + 1) / kWavesTotal;
-        };
+        // A wave with an empty share wrote no record (none while W <= S).
+        auto empty_share = [&](int w) { return S * w / W == S * (w + 1) / W; };
         // Record headers are fetched one per lane (64 at a time), so the
         // loads overlap instead of forming a chain; the first 64 headers and
         // the first eight records' rows are fetched together, since their

@@ -1,90 +1,119 @@
-// prefill_f32.hip -- fused attention for float32 inputs on the vector FMA
-// units, head dims 1..256 (padded to 32, 64, 96, 128 or 256; padded columns
-// load as zeros and are not stored).
+// prefill_f32.hip -- fused attention for float32 inputs on the gfx950 matrix
+// cores (v_mfma_f32_32x32x2_f32: float32 operands and accumulation), head
+// dims 1..256 (padded to 32, 64, 96, 128 or 256; padded columns load as zeros
+// and are not stored).
 //
-// A group of G neighbouring lanes (G = 4, or 8 at the 256 padding) owns a
-// query row, each lane DP / G of its columns: a score is G partial dot
-// products added by exchanges inside the group, so every lane of the group
-// holds the same score and takes the same softmax decisions (OneGPU
-// "Attention", "Variants and ordering": the `pairs` variant splits the head
-// dimension over neighbouring threads and joins the parts with a shuffle).
-// For paddings up to 64 each group owns two rows (16 apart), so every K/V
-// value read from LDS feeds two FMAs: one read per FMA would leave the loop
-// bound by LDS bandwidth.  Keys are folded in increasing order, 16 per tile (8
-// at the 256 padding), from the wave's own LDS rows (coalesced loads, next
-// tile prefetched into registers), with the online normaliser and a lazily
-// raised reference max as in the matrix-core kernel; in float32 the
-// probabilities are not rounded.
-//
+// A workgroup of four waves owns 128 query rows of one kv head's group
+// (4 heads x 32 positions, 2 x 64 or 1 x 128, the most heads that divide the
+// group), each wave 32 rows.  Keys come in tiles of 32, loaded by all four
+// waves straight from HBM into LDS (4-byte buffer loads into LDS: any head
+// dim and row stride, zeros past the key length and the head dim), double
+// buffered.  Per tile and wave:
+//   S^T = K Q^T    -- DP/2 matrix ops; lane l holds query row l%32 and Q's
+//                     columns h DP/2 .. h DP/2 + DP/2 - 1 (h = l/32) in
+//                     registers, K's matching columns come from LDS;
+//   softmax        -- the lane owns its row's 16 keys 8(r/4) + 4h + r%4 of
+//                     the tile (the other 16 are in lane l^32): lazily raised
+//                     reference max, p = 2^((s - m) c), not rounded (fp32);
+//   O^T += V^T P^T -- P^T is the score accumulator itself (register r is the
+//                     operand of step r), V^T read per lane from LDS.
 // Blockwise summation (OneGPU "Attention", "Accuracy at long key lengths"):
-// each tile's products and probabilities are summed into zero-started
-// partials, which are then added to the running accumulator and sum once, so
-// a long row adds one value per tile to the running totals instead of one per
-// key.
+// each tile's products go to a zero-started accumulator and its
+// probabilities to a zero-started sum, which are added to the running ones
+// once per tile.
 //
 // Score-rule variants (ONNX GroupQueryAttention README, "Attributes",
 // "Inputs") and document masks (llm.istanbul "05_attention", "Phase 0" and
-// "K-block iteration") in the kVar kernel: each row's first visible key (local
-// window, document start) bounds it from below and the tiles below the
-// block's smallest bound are skipped; the softcap maps the raw score before
-// the mask; the sink joins the denominator at the end.
+// "K-block iteration") in the kVar kernel: each row's first visible key
+// (local window, document start) bounds it from below and the tiles below
+// the workgroup's smallest bound are skipped; the softcap maps the raw score
+// before the mask; the sink joins the denominator at the end.  A wave skips
+// the matrix work of a tile none of its rows can see.
 //
-// When the query blocks are too few to fill the GPU, the keys are cut into
-// contiguous ranges (a multiple of 32 keys, at least 128, at most 16 ranges);
-// each (rows, range) wave writes its partial (m, l, acc) and a second kernel
-// merges the ranges of each row in range order (OneGPU "Attention", "Accuracy
-// at long key lengths", last paragraph).  The cut depends only on the shape.
+// When the workgroups are too few to fill the GPU, the keys are cut into
+// contiguous ranges (whole tiles); each (rows, range) wave writes its partial
+// (m, l, acc) and a second kernel merges the ranges of each row in range
+// order (OneGPU "Attention", "Accuracy at long key lengths", last paragraph).
+// The cut depends only on the shape.
 #include <type_traits>
 
 #include "attn_internal.h"
 #include "device_common.h"
+#include "mfma_common.h"
 
 namespace sdpa {
 
 namespace {
 
-constexpr int kRangeQuantum = 32;   // key ranges are multiples of this
-constexpr float kSlack = 8.f;       // lazy-rescale threshold, base-2 units
+using mfma::f32x16;
+using mfma::f32x4;
+using mfma::halves_max;
+using mfma::halves_sum;
+using mfma::make_rsrc;
+using mfma::max_nan;
 
-// Layout per padded head dim DP: G lanes per row, R rows per lane group,
-// T keys per tile.
-template <int DP> struct F32Lay {
-    static constexpr int G = DP == 256 ? 8 : 4;
-    static constexpr int R = DP <= 64 ? 2 : 1;
-    static constexpr int DQ = DP / G;                 // columns per lane
-    static constexpr int kGroups = 64 / G;            // lane groups per wave
-    static constexpr int RW = kGroups * R;            // rows per wave
-    static constexpr int T = DP == 256 ? 8 : 16;      // keys per tile
-    static constexpr int kRowF4 = DP / 4;             // float4 per padded row
-    static constexpr int kLoads = T * kRowF4 / 64;    // float4 per lane per tensor
-    static_assert(T * kRowF4 % 64 == 0, "tile loads must cover the wave");
-    static_assert(DQ % 4 == 0, "a lane's columns are whole float4");
+constexpr int kTileN = 32;          // keys per tile
+constexpr int kRangeQuantum = 64;   // key ranges are multiples of this (two tiles)
+constexpr int kWavesF = 4;          // waves per workgroup
+constexpr float kSlack = 8.f;       // lazy-rescale threshold, base-2 units
+constexpr uint32_t kOutOfRange = 0x80000000u;   // a buffer offset past any tensor
+
+// Padded head dim DP: LDS rows of DP + 4 floats (the 16-byte shift per row
+// keeps the 16-byte column reads of 16 rows on distinct banks).
+template <int DP> struct F32Cfg {
+    static constexpr int kRowF = DP + 4;                    // floats per LDS row
+    static constexpr int kTileF = kTileN * kRowF;           // floats per tile buffer
+    static constexpr int kLoads = kTileF / 64;              // 64-float DMA rows per tile
+    static constexpr int kHalf = DP / 2;                    // Q columns per lane
+    static constexpr int kBlk = DP / 32;                    // 32-column output blocks
+    static constexpr int kMinWg = DP <= 128 ? 2 : 1;        // workgroups per CU (registers)
+    static_assert(kTileF % 64 == 0, "a tile buffer is whole DMA rows");
+    static_assert(kHalf % 4 == 0, "Q halves are whole 16-byte LDS reads");
 };
 
-// Sum over the G lanes of a group: every step adds the same two numbers on
-// each partner, so all lanes end with identical bits.
-template <int G> __device__ __forceinline__ float group_sum(float x) {
-    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));  // ^1
-    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));  // ^2
-    if constexpr (G == 8) x += __shfl_xor(x, 4, 64);
-    return x;
+// One 4-byte-per-lane buffer load into LDS at lds_byte + 4 * lane (M0 holds
+// the LDS address; one wait state after writing it).  An instruction of its
+// own, so the compiler does not hold later LDS reads of the other buffer for
+// it; the kernel waits for these loads itself before the barrier that
+// publishes a tile.
+__device__ __forceinline__ void load_lds4(__amdgpu_buffer_rsrc_t rs, uint32_t lds_byte,
+                                          uint32_t voff) {
+    asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(rs), "{m0}"(lds_byte));
+}
+
+__device__ __forceinline__ void dma_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Key offset (within a 32-key tile) of accumulator register r in lane half h:
+// the 32x32 accumulator puts rows 8(r/4) + 4h + r%4 in register r.
+__device__ __forceinline__ constexpr int key_of(int r, int h) {
+    return 8 * (r / 4) + 4 * h + (r % 4);
 }
 
 template <int DP, bool kMask, bool kSplit, bool kVar>
-__global__ __launch_bounds__(64) void prefill_f32_kernel(Params p, int n_rblk, int vec) {
-    using LY = F32Lay<DP>;
-    constexpr int G = LY::G, R = LY::R, DQ = LY::DQ, RW = LY::RW, kTile = LY::T;
-    __shared__ __attribute__((aligned(16))) float k_sh[kTile * DP];
-    __shared__ __attribute__((aligned(16))) float v_sh[kTile * DP];
+__global__ __launch_bounds__(256, F32Cfg<DP>::kMinWg) void prefill_f32_kernel(Params p,
+                                                                                int n_qblk,
+                                                                                int gw) {
+    using CF = F32Cfg<DP>;
+    __shared__ __attribute__((aligned(16))) float k_sh[2][CF::kTileF];
+    __shared__ __attribute__((aligned(16))) float v_sh[2][CF::kTileF];
+    __shared__ int64_t wg_bounds[2 * kWavesF];
 
-    // blockIdx.x: row block (heaviest causal blocks first); y: head; z: batch * ranges.
-    const int rb = n_rblk - 1 - static_cast<int>(blockIdx.x);
-    const int h = blockIdx.y;
+    // blockIdx.x: query block (heaviest causal blocks first); y: (kv head,
+    // head slice); z: batch * ranges.
+    const int qb = n_qblk - 1 - static_cast<int>(blockIdx.x);
+    const int n_slice = p.group / gw;
+    const int g = static_cast<int>(blockIdx.y) / n_slice;
+    const int slice = static_cast<int>(blockIdx.y) % n_slice;
     const int b = static_cast<int>(blockIdx.z) / p.n_split;
     const int rng = static_cast<int>(blockIdx.z) % p.n_split;
-    const int g = h / p.group;
-    const int lane = threadIdx.x;
-    const int grp = lane / G, gl = lane % G;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int hh = lane >> 5, col = lane & 31;
+    const int wph = kWavesF / gw;                 // waves per head
+    const int h = g * p.group + slice * gw + w / wph;
+    const int64_t row = static_cast<int64_t>(qb) * (32 * wph) + 32 * (w % wph) + col;
+    const bool row_ok = row < p.Lq;
     const int D = p.D;
 
     int64_t kv_len = p.Lk;
@@ -93,85 +122,88 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(Params p, int n_rblk, i
         kv_len = L < 0 ? 0 : (L > p.Lk ? p.Lk : L);
     }
     const int64_t delta = causal_delta(p, kv_len);
-
-    // This lane's rows: rb * RW + kGroups r + grp, r < R; keys [row_lo, row_hi)
-    // are visible to row r (before the mask).
-    int64_t row[R], row_hi[R], row_lo[R];
-    bool row_ok[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        row[r] = static_cast<int64_t>(rb) * RW + LY::kGroups * r + grp;
-        row_ok[r] = row[r] < p.Lq;
-        int64_t hi = kv_len;
-        if (p.causal) {
-            const int64_t bb = row[r] + delta + 1;   // keys j <= i + delta
-            hi = bb < hi ? bb : hi;
-        }
-        row_hi[r] = row_ok[r] ? hi : 0;
-        row_lo[r] = (kVar && row_ok[r]) ? first_key(p, b, row[r], delta) : 0;
+    // Keys [row_lo, row_hi) are visible to this lane's row (before the mask).
+    int64_t row_hi = kv_len, row_lo = 0;
+    if (p.causal) {
+        const int64_t bb = row + delta + 1;
+        row_hi = bb < row_hi ? bb : row_hi;
     }
-    // Keys the block can see: [blk_lo, blk_hi); this range of them.
+    if (row_hi < 0 || !row_ok) row_hi = 0;
+    if (kVar && row_ok) row_lo = first_key(p, b, row, delta);
+
+    // The wave's bounds (max of hi, min of lo over its valid rows), then the
+    // workgroup's.
+    int64_t w_hi = row_hi, w_lo = row_ok ? row_lo : INT64_MAX;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int64_t oh = __shfl_xor(w_hi, off, 64), ol = __shfl_xor(w_lo, off, 64);
+        w_hi = oh > w_hi ? oh : w_hi;
+        w_lo = ol < w_lo ? ol : w_lo;
+    }
+    if (lane == 0) {
+        wg_bounds[2 * w] = w_hi;
+        wg_bounds[2 * w + 1] = w_lo;
+    }
+    __syncthreads();
     int64_t blk_hi = 0, blk_lo = INT64_MAX;
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-        if (!row_ok[r]) continue;
-        blk_hi = row_hi[r] > blk_hi ? row_hi[r] : blk_hi;
-        blk_lo = row_lo[r] < blk_lo ? row_lo[r] : blk_lo;
+    for (int i = 0; i < kWavesF; ++i) {
+        blk_hi = wg_bounds[2 * i] > blk_hi ? wg_bounds[2 * i] : blk_hi;
+        blk_lo = wg_bounds[2 * i + 1] < blk_lo ? wg_bounds[2 * i + 1] : blk_lo;
     }
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {   // wave-wide max / min
-        const int64_t oh = __shfl_xor(blk_hi, off, 64), ol = __shfl_xor(blk_lo, off, 64);
-        blk_hi = oh > blk_hi ? oh : blk_hi;
-        blk_lo = ol < blk_lo ? ol : blk_lo;
-    }
-    int64_t j_begin = kSplit ? static_cast<int64_t>(rng) * p.split_len : 0;
+    const int64_t r_begin = kSplit ? static_cast<int64_t>(rng) * p.split_len : 0;
+    // A range at or past the workgroup's bound: no wave has a record to write.
+    if (kSplit && r_begin >= blk_hi) return;
+    int64_t j_begin = r_begin;
     int64_t j_end = blk_hi;
     if (kSplit && j_begin + p.split_len < j_end) j_end = j_begin + p.split_len;
     if (kVar && blk_lo != INT64_MAX && blk_lo > j_begin)   // whole tiles below every row's bound
-        j_begin += (blk_lo - j_begin) / kTile * kTile;
-    const int n_tiles = j_end > j_begin ? static_cast<int>((j_end - j_begin + kTile - 1) / kTile) : 0;
+        j_begin += (blk_lo - j_begin) / kTileN * kTileN;
+    const int n_tiles =
+        j_end > j_begin ? static_cast<int>((j_end - j_begin + kTileN - 1) / kTileN) : 0;
 
-    const float* qg = static_cast<const float*>(p.q);
     const float* kg = static_cast<const float*>(p.k) + b * p.ks.sb + g * p.ks.sh;
     const float* vg = static_cast<const float*>(p.v) + b * p.vs.sb + g * p.vs.sh;
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(kg, kv_len * p.ks.sr * 4);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vg, kv_len * p.vs.sr * 4);
 
-    // Columns gl * DQ .. gl * DQ + DQ - 1 of the padded row; columns >= D are 0.
-    float q[R][DQ];
-    const float* mrow[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const float* src = qg + b * p.qs.sb + h * p.qs.sh + (row_ok[r] ? row[r] : 0) * p.qs.sr;
-#pragma unroll
-        for (int d = 0; d < DQ; ++d) {
-            const int cix = gl * DQ + d;
-            q[r][d] = (row_ok[r] && cix < D) ? src[cix] : 0.f;
+    // Tile loads: float f = i * 64 + lane of a tile buffer is key f / kRowF,
+    // column f % kRowF; columns >= D and keys past the length load as zeros.
+    // DMA rows i = w, w + 4, ... are this wave's.
+    auto dma = [&](int tile, int buf) {
+        const int64_t key0 = j_begin + static_cast<int64_t>(tile) * kTileN;
+        for (int i = w; i < CF::kLoads; i += kWavesF) {
+            const int f = i * 64 + lane;
+            const int r = f / CF::kRowF, cc = f % CF::kRowF;
+            const int64_t key = key0 + r;
+            const bool in = cc < D && key < kv_len;
+            const uint32_t ko = in ? static_cast<uint32_t>((key * p.ks.sr + cc) * 4) : kOutOfRange;
+            const uint32_t vo = in ? static_cast<uint32_t>((key * p.vs.sr + cc) * 4) : kOutOfRange;
+            load_lds4(krs,
+                      static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+                          (__attribute__((address_space(3))) float*)(&k_sh[buf][i * 64]))),
+                      ko);
+            load_lds4(vrs,
+                      static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+                          (__attribute__((address_space(3))) float*)(&v_sh[buf][i * 64]))),
+                      vo);
         }
-        mrow[r] = (kMask && row_ok[r]) ? p.mask + b * p.ms.sb + h * p.ms.sh + row[r] * p.ms.sr
-                                       : nullptr;
+    };
+    if (n_tiles > 0) dma(0, 0);
+
+    // Q columns hh * DP/2 + t of this lane's row, zeros past D.
+    float q[CF::kHalf];
+    {
+        const float* src = static_cast<const float*>(p.q) + b * p.qs.sb + h * p.qs.sh +
+                           (row_ok ? row : 0) * p.qs.sr;
+#pragma unroll
+        for (int t = 0; t < CF::kHalf; ++t) {
+            const int d = hh * CF::kHalf + t;
+            q[t] = (row_ok && d < D) ? src[d] : 0.f;
+        }
     }
-
-    // Tile loads: float4 f = n * 64 + lane of the tile is row f / kRowF4,
-    // columns 4 (f % kRowF4) .. + 3; keys past the range and columns past D
-    // load as zeros.
-    float4 kst[LY::kLoads], vst[LY::kLoads];
-    auto ld4 = [&](const float* base, int64_t sr, int64_t key, int c4, bool in) {
-        if (!in) return make_float4(0.f, 0.f, 0.f, 0.f);
-        const float* src = base + key * sr + c4;
-        if (vec && c4 + 3 < D) return *reinterpret_cast<const float4*>(src);
-        return make_float4(c4 < D ? src[0] : 0.f, c4 + 1 < D ? src[1] : 0.f,
-                           c4 + 2 < D ? src[2] : 0.f, c4 + 3 < D ? src[3] : 0.f);
-    };
-    auto fetch = [&](int tile) {
-#pragma unroll
-        for (int n = 0; n < LY::kLoads; ++n) {
-            const int f = n * 64 + lane;
-            const int64_t key = j_begin + static_cast<int64_t>(tile) * kTile + f / LY::kRowF4;
-            const int c4 = 4 * (f % LY::kRowF4);
-            const bool in = key < j_end;
-            kst[n] = ld4(kg, p.ks.sr, key, c4, in);
-            vst[n] = ld4(vg, p.vs.sr, key, c4, in);
-        }
-    };
+    const float* mrow = (kMask && row_ok) ? p.mask + b * p.ms.sb + h * p.ms.sh + row * p.ms.sr
+                                          : nullptr;
 
     // Score units: raw q.k without a mask; natural (scale * q.k + mask, the
     // mask added as given, so a large finite value stays finite) with one.
@@ -181,169 +213,165 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(Params p, int n_rblk, i
     const bool cap = kVar && p.softcap > 0.f;
     const float cap_k2 = cap ? 2.f * kLog2e * p.scale / p.softcap : 0.f;
     const float cap_back = cap ? p.softcap / p.scale : 0.f;
-    float m_ref[R], l_sum[R], acc[R][DQ];
+    float m_ref = kNegInf, l_sum = 0.f;
+    f32x16 acc[CF::kBlk];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-        m_ref[r] = kNegInf;
-        l_sum[r] = 0.f;
-#pragma unroll
-        for (int d = 0; d < DQ; ++d) acc[r][d] = 0.f;
-    }
+    for (int j = 0; j < CF::kBlk; ++j) acc[j] = f32x16{};
 
-    if (n_tiles > 0) fetch(0);
+    // The Q loads are complete before the loop: left pending, the compiler's
+    // wait for them at their first use inside the loop would wait, on every
+    // tile, for the next tile's loads too.
+#pragma unroll
+    for (int t = 0; t < CF::kHalf; ++t) asm volatile("" ::"v"(q[t]));
+    dma_wait_all();
+    __syncthreads();
     for (int tile = 0; tile < n_tiles; ++tile) {
-        // The previous tile's LDS reads precede these writes in this wave's
-        // in-order LDS queue, so one buffer suffices.
+        const int buf = tile & 1;
+        // With a mask, the next tile's loads go out after this tile's mask
+        // values are in: the wait for those (the compiler's, which counts
+        // only its own loads) would otherwise wait for the tile loads too.
+        if (!kMask && tile + 1 < n_tiles) dma(tile + 1, buf ^ 1);
+        const int64_t j0 = j_begin + static_cast<int64_t>(tile) * kTileN;
+        // Matrix work only if one of the wave's rows sees a key of the tile.
+        if (j0 < w_hi && (!kVar || j0 + kTileN > w_lo)) {
+            float mv[16];
+            if (kMask) {
 #pragma unroll
-        for (int n = 0; n < LY::kLoads; ++n) {
-            const int f = n * 64 + lane;
-            const int rr = f / LY::kRowF4, c4 = 4 * (f % LY::kRowF4);
-            *reinterpret_cast<float4*>(&k_sh[rr * DP + c4]) = kst[n];
-            *reinterpret_cast<float4*>(&v_sh[rr * DP + c4]) = vst[n];
-        }
-        if (tile + 1 < n_tiles) fetch(tile + 1);
-        const int64_t j0 = j_begin + static_cast<int64_t>(tile) * kTile;
-
-        float s[R][kTile];
-#pragma unroll
-        for (int j = 0; j < kTile; ++j) {
-            const float* kr = &k_sh[j * DP + gl * DQ];
-            float part[R];
-#pragma unroll
-            for (int r = 0; r < R; ++r) part[r] = 0.f;
-#pragma unroll
-            for (int d = 0; d < DQ; d += 4) {
-                const float4 kv = *reinterpret_cast<const float4*>(kr + d);
-#pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    part[r] = fmaf(q[r][d], kv.x, part[r]);
-                    part[r] = fmaf(q[r][d + 1], kv.y, part[r]);
-                    part[r] = fmaf(q[r][d + 2], kv.z, part[r]);
-                    part[r] = fmaf(q[r][d + 3], kv.w, part[r]);
+                for (int r = 0; r < 16; ++r) {
+                    const int64_t key = j0 + key_of(r, hh);
+                    mv[r] = (mrow && key < row_hi) ? mrow[key] : 0.f;
                 }
             }
+            // -- S^T = K Q^T: one accumulation chain (dependent fp32 matrix
+            // ops issue back to back at full rate on gfx950).
+            f32x16 s = f32x16{};
+            const float* krow = &k_sh[buf][col * CF::kRowF + hh * CF::kHalf];
 #pragma unroll
-            for (int r = 0; r < R; ++r) s[r][j] = group_sum<G>(part[r]);
-        }
-        float tacc[R][DQ];   // this tile's products (blockwise summation)
+            for (int u = 0; u < CF::kHalf / 4; ++u) {
+                const f32x4 kv = *reinterpret_cast<const f32x4*>(krow + 4 * u);
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
+                for (int e = 0; e < 4; ++e)
+                    s = __builtin_amdgcn_mfma_f32_32x32x2f32(kv[e], q[4 * u + e], s, 0, 0, 0);
+            }
+
+            // -- score rule: softcap on the raw score, the mask, visibility.
             if (cap) {
 #pragma unroll
-                for (int j = 0; j < kTile; ++j) s[r][j] = softcap_raw(s[r][j], cap_k2, cap_back);
+                for (int r = 0; r < 16; ++r) s[r] = softcap_raw(s[r], cap_k2, cap_back);
             }
-            if (kMask && mrow[r]) {
+            if (kMask) {
 #pragma unroll
-                for (int j = 0; j < kTile; ++j)
-                    s[r][j] = (j0 + j < j_end) ? fmaf(s[r][j], p.scale, mrow[r][j0 + j])
-                                               : s[r][j] * p.scale;
+                for (int r = 0; r < 16; ++r) s[r] = fmaf(s[r], p.scale, mv[r]);
             }
-            const bool partial = (j0 + kTile > j_end) || (j0 + kTile > row_hi[r]) ||
-                                 (kVar && j0 < row_lo[r]) || !row_ok[r];
-            if (partial) {
+            const bool partial = (j0 + kTileN > row_hi) || (kVar && j0 < row_lo);
+            if (__builtin_amdgcn_ballot_w64(partial)) {
 #pragma unroll
-                for (int j = 0; j < kTile; ++j) {
-                    const int64_t key = j0 + j;
-                    if (key >= j_end || key >= row_hi[r] || (kVar && key < row_lo[r]))
-                        s[r][j] = kNegInf;
+                for (int r = 0; r < 16; ++r) {
+                    const int64_t key = j0 + key_of(r, hh);
+                    if (key >= row_hi || (kVar && key < row_lo)) s[r] = kNegInf;
                 }
             }
+            // -- online normaliser (lazy reference), this tile's p and sum.
             float mx = kNegInf;
 #pragma unroll
-            for (int j = 0; j < kTile; j += 2) mx = fmaxf(mx, fmaxf(s[r][j], s[r][j + 1]));
-            const bool raise = mx > m_ref[r] + slack;
+            for (int r = 0; r < 16; r += 2) mx = max_nan(mx, max_nan(s[r], s[r + 1]));
+            mx = halves_max(mx);
+            const bool raise = mx > m_ref + slack;
             if (__builtin_amdgcn_ballot_w64(raise)) {
-                const float m_new = raise ? mx : m_ref[r];
-                const float alpha = raise ? fast_exp2((m_ref[r] - m_new) * c) : 1.f;   // 0 when m_ref = -inf
-                l_sum[r] *= alpha;
+                const float m_new = raise ? mx : m_ref;
+                const float alpha = raise ? fast_exp2((m_ref - m_new) * c) : 1.f;   // 0 from -inf
+                l_sum *= alpha;
 #pragma unroll
-                for (int d = 0; d < DQ; ++d) acc[r][d] *= alpha;
-                m_ref[r] = m_new;
+                for (int j = 0; j < CF::kBlk; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[j][r] *= alpha;
+                m_ref = m_new;
             }
-            // (s - m) * c rather than fma(s, c, -m*c): the subtraction is
-            // exact for the row maximum, so its weight is exactly 1 (p is not
-            // rounded to a narrower type on this path).
-            const float base = (m_ref[r] == kNegInf) ? 0.f : m_ref[r];
+            // (s - m) * c: exact 0 for the row maximum, so its weight is 1.
+            const float base = (m_ref == kNegInf) ? 0.f : m_ref;
             float tl = 0.f;
 #pragma unroll
-            for (int j = 0; j < kTile; ++j) {
-                s[r][j] = fast_exp2((s[r][j] - base) * c);
-                tl += s[r][j];
+            for (int r = 0; r < 16; ++r) {
+                s[r] = fast_exp2((s[r] - base) * c);
+                tl += s[r];
             }
-            l_sum[r] += tl;
+            l_sum += tl;
+            if (kMask && tile + 1 < n_tiles) dma(tile + 1, buf ^ 1);
+            // -- O^T += V^T P^T per 32-column block, each tile's into a
+            // zero-started partial.
 #pragma unroll
-            for (int d = 0; d < DQ; ++d) tacc[r][d] = 0.f;
-        }
+            for (int j = 0; j < CF::kBlk; ++j) {
+                f32x16 t = f32x16{};
+                const float* vcol = &v_sh[buf][32 * j + col];
 #pragma unroll
-        for (int j = 0; j < kTile; ++j) {
-            const float* vr = &v_sh[j * DP + gl * DQ];
+                for (int r = 0; r < 16; ++r)
+                    t = __builtin_amdgcn_mfma_f32_32x32x2f32(vcol[key_of(r, hh) * CF::kRowF], s[r],
+                                                             t, 0, 0, 0);
 #pragma unroll
-            for (int d = 0; d < DQ; d += 4) {
-                const float4 vv = *reinterpret_cast<const float4*>(vr + d);
-#pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    tacc[r][d] = fmaf(s[r][j], vv.x, tacc[r][d]);
-                    tacc[r][d + 1] = fmaf(s[r][j], vv.y, tacc[r][d + 1]);
-                    tacc[r][d + 2] = fmaf(s[r][j], vv.z, tacc[r][d + 2]);
-                    tacc[r][d + 3] = fmaf(s[r][j], vv.w, tacc[r][d + 3]);
-                }
+                for (int r = 0; r < 16; ++r) acc[j][r] += t[r];
             }
+        } else if (kMask && tile + 1 < n_tiles) {
+            dma(tile + 1, buf ^ 1);   // a wave with no work in this tile
         }
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-            for (int d = 0; d < DQ; ++d) acc[r][d] += tacc[r][d];
+        // The next tile's loads have landed in every wave before any wave
+        // reads them, and this tile's buffer is free for the loads after next.
+        dma_wait_all();
+        __syncthreads();
     }
 
+    if (!row_ok) return;
+    // Lane l holds columns 32 j + 8 (r/4) + 4 hh + r%4 of its row.
+    const float l_tot = halves_sum(l_sum);
+    if (kSplit) {
+        if (r_begin >= w_hi) return;     // past the wave's bound: the merge reads no record
+        float* rec = static_cast<float*>(p.ws) +
+                     (((static_cast<int64_t>(b) * p.Hq + h) * p.Lq + row) * p.n_split + rng) *
+                         (DP + 4);
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-        if (!row_ok[r]) continue;
-        const int64_t i = row[r];
-        if (kSplit) {
-            float* rec = static_cast<float*>(p.ws) +
-                         (((static_cast<int64_t>(b) * p.Hq + h) * p.Lq + i) * p.n_split + rng) * (DP + 4);
+        for (int j = 0; j < CF::kBlk; ++j)
 #pragma unroll
-            for (int d = 0; d < DQ; d += 4)
-                *reinterpret_cast<float4*>(rec + 4 + gl * DQ + d) =
-                    make_float4(acc[r][d], acc[r][d + 1], acc[r][d + 2], acc[r][d + 3]);
-            if (gl == 0) {
-                rec[0] = m_ref[r];
-                rec[1] = l_sum[r];
-            }
-            continue;
+            for (int u = 0; u < 4; ++u)
+                *reinterpret_cast<float4*>(rec + 4 + 32 * j + 8 * u + 4 * hh) =
+                    make_float4(acc[j][4 * u], acc[j][4 * u + 1], acc[j][4 * u + 2],
+                                acc[j][4 * u + 3]);
+        if (hh == 0) {
+            rec[0] = m_ref;
+            rec[1] = l_tot;
         }
-        float m_nat = m_ref[r] * to_nat;          // natural units (-inf stays -inf)
-        float l_tot = l_sum[r];
-        const float fs = fold_sink(p, h, m_nat, l_tot);
-        const bool empty = (l_tot == 0.f);
-        const float inv = fs / l_tot;
-        const float fill = p.masked_zero ? 0.f : __builtin_nanf("");
-        float* og = static_cast<float*>(p.o) + b * p.os.sb + h * p.os.sh + i * p.os.sr;
-#pragma unroll
-        for (int d = 0; d < DQ; ++d) {
-            const int cix = gl * DQ + d;
-            if (cix < D) og[cix] = empty ? fill : acc[r][d] * inv;
-        }
-        if (p.lse && gl == 0)
-            p.lse[b * p.ls.sb + h * p.ls.sh + i * p.ls.sr] = empty ? kNegInf : row_lse(m_nat, l_tot);
+        return;
     }
+    float m_nat = m_ref * to_nat;          // natural units (-inf stays -inf)
+    float l_f = l_tot;
+    const float fs = fold_sink(p, h, m_nat, l_f);
+    const bool empty = (l_f == 0.f);
+    const float inv = fs / l_f;
+    const float fill = p.masked_zero ? 0.f : __builtin_nanf("");
+    float* og = static_cast<float*>(p.o) + b * p.os.sb + h * p.os.sh + row * p.os.sr;
+#pragma unroll
+    for (int j = 0; j < CF::kBlk; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int d = 32 * j + key_of(r, hh);
+            if (d < D) og[d] = empty ? fill : acc[j][r] * inv;
+        }
+    if (p.lse && hh == 0)
+        p.lse[b * p.ls.sb + h * p.ls.sh + row * p.ls.sr] = empty ? kNegInf : row_lse(m_nat, l_f);
 }
 
-// Rows per wave of the kernel that runs head dim D.
+// The head dim a problem runs at.
 int f32_padded(int D) {
     return D <= 32 ? 32 : (D <= 64 ? 64 : (D <= 96 ? 96 : (D <= 128 ? 128 : 256)));
 }
-int f32_rows_per_wave(int D) {
-    switch (f32_padded(D)) {
-    case 32: return F32Lay<32>::RW;
-    case 64: return F32Lay<64>::RW;
-    case 96: return F32Lay<96>::RW;
-    case 128: return F32Lay<128>::RW;
-    default: return F32Lay<256>::RW;
-    }
+
+// Heads per workgroup: the most of 4, 2, 1 that divides the group.
+int f32_heads_per_wg(int group) { return group % 4 == 0 ? 4 : (group % 2 == 0 ? 2 : 1); }
+
+int f32_n_qblk(int Lq, int gw) {
+    const int P = 32 * (kWavesF / gw);
+    return (Lq + P - 1) / P;
 }
 
-// One thread per (b, h, row, dim): merge the ranges the row's block wrote, in
+// One thread per (b, h, row, dim): merge the ranges the row's wave wrote, in
 // order, then the sink, the masked-row policy and the LSE as the main
 // kernel's epilogue does.  Records are in the main kernel's score units: c
 // converts a difference of them to base 2, to_nat a value to natural units.
@@ -362,12 +390,11 @@ __global__ __launch_bounds__(256) void prefill_f32_merge_kernel(Params p, float 
         const int64_t L = p.lens[b];
         kv_len = L < 0 ? 0 : (L > p.Lk ? p.Lk : L);
     }
-    // The ranges below the block's causal bound are the ones its wave wrote
-    // (a range past it returned before writing).
-    constexpr int rw = F32Lay<DP>::RW;
+    // The ranges below the causal bound of the row's wave (its 32 positions)
+    // are the ones that wave wrote.
     int64_t blk_hi = kv_len;
     if (p.causal) {
-        const int64_t last = ((i / rw + 1) * rw < p.Lq ? (i / rw + 1) * rw : p.Lq) - 1;
+        const int64_t last = ((i / 32 + 1) * 32 < p.Lq ? (i / 32 + 1) * 32 : p.Lq) - 1;
         const int64_t bb = last + causal_delta(p, kv_len) + 1;
         blk_hi = bb < 0 ? 0 : (bb < blk_hi ? bb : blk_hi);
     }
@@ -419,19 +446,15 @@ bool f32_var(const Params& p) {
 
 template <int DP>
 hipError_t launch_d(const Params& p, hipStream_t s) {
-    const int n_rblk = (p.Lq + F32Lay<DP>::RW - 1) / F32Lay<DP>::RW;
-    const dim3 grid(n_rblk, p.Hq, p.B * p.n_split);
+    const int gw = f32_heads_per_wg(p.group);
+    const int n_qblk = f32_n_qblk(p.Lq, gw);
+    const dim3 grid(n_qblk, p.Hkv * (p.group / gw), p.B * p.n_split);
     const bool split = p.n_split > 1;
-    // 16-byte K/V loads when every row starts 16-byte aligned and holds whole float4s.
-    auto al = [](const void* ptr, const Strides& st) {
-        return reinterpret_cast<uintptr_t>(ptr) % 16 == 0 && st.sb % 4 == 0 && st.sh % 4 == 0 &&
-               st.sr % 4 == 0;
-    };
-    const int vec = (p.D % 4 == 0) && (p.Lk == 0 || (al(p.k, p.ks) && al(p.v, p.vs)));
     auto go = [&](auto mask_c, auto split_c, auto var_c) {
         constexpr bool kM = decltype(mask_c)::value, kS = decltype(split_c)::value;
         constexpr bool kV = decltype(var_c)::value;
-        hipLaunchKernelGGL((prefill_f32_kernel<DP, kM, kS, kV>), grid, dim3(64), 0, s, p, n_rblk, vec);
+        hipLaunchKernelGGL((prefill_f32_kernel<DP, kM, kS, kV>), grid, dim3(64 * kWavesF), 0, s,
+                           p, n_qblk, gw);
     };
     using T = std::true_type;
     using F = std::false_type;
@@ -449,24 +472,30 @@ hipError_t launch_d(const Params& p, hipStream_t s) {
     if (e != hipSuccess || !split) return e;
     const int64_t total = static_cast<int64_t>(p.B) * p.Hq * p.Lq * p.D;
     const float c = p.mask ? kLog2e : p.scale_log2, to_nat = p.mask ? 1.f : p.scale;
-    hipLaunchKernelGGL((prefill_f32_merge_kernel<DP>), dim3(static_cast<uint32_t>((total + 255) / 256)),
-                       dim3(256), 0, s, p, c, to_nat);
+    hipLaunchKernelGGL((prefill_f32_merge_kernel<DP>),
+                       dim3(static_cast<uint32_t>((total + 255) / 256)), dim3(256), 0, s, p, c,
+                       to_nat);
     return hipGetLastError();
 }
 
 }  // namespace
 
-// Key ranges for the fp32 kernel: only when the row blocks give fewer than
-// ~2048 waves; ranges are multiples of 32 keys, at least 128, at most 16.
-void prefill_f32_plan(int B, int Hq, int Lq, int Lk, int D, int* split_len, int* n_split) {
-    const int rw = f32_rows_per_wave(D);
-    const int64_t units = static_cast<int64_t>((Lq + rw - 1) / rw) * Hq * B;
+// Key ranges for the fp32 kernel: only when the workgroups are fewer than
+// two per CU and the keys span at least four tiles; ranges are multiples of
+// 64 keys, at most 32 of them.
+void prefill_f32_plan(int B, int Hq, int Hkv, int Lq, int Lk, int D, int* split_len,
+                      int* n_split) {
+    (void)D;
+    const int group = (Hkv > 0 && Hq % Hkv == 0) ? Hq / Hkv : 1;
+    const int gw = f32_heads_per_wg(group);
+    const int64_t wgs = static_cast<int64_t>(f32_n_qblk(Lq, gw)) * (Hq / gw) * B;
     int n = 1;
-    if (units < 2048 && Lk >= 256) {
-        const int64_t want = (2048 + units - 1) / units;
-        const int64_t most = Lk / 128;
+    const int64_t target = 512;
+    if (wgs > 0 && wgs < target && Lk >= 4 * kTileN) {
+        const int64_t want = (target + wgs - 1) / wgs;
+        const int64_t most = Lk / kRangeQuantum;
         n = static_cast<int>(want < most ? want : most);
-        if (n > 16) n = 16;
+        if (n > 32) n = 32;
         if (n < 1) n = 1;
     }
     int len = (Lk + n - 1) / n;
@@ -477,9 +506,9 @@ void prefill_f32_plan(int B, int Hq, int Lq, int Lk, int D, int* split_len, int*
     if (*n_split < 1) *n_split = 1;
 }
 
-size_t prefill_f32_workspace_bytes(int B, int Hq, int Lq, int Lk, int D) {
+size_t prefill_f32_workspace_bytes(int B, int Hq, int Hkv, int Lq, int Lk, int D) {
     int len, n;
-    prefill_f32_plan(B, Hq, Lq, Lk, D, &len, &n);
+    prefill_f32_plan(B, Hq, Hkv, Lq, Lk, D, &len, &n);
     if (n <= 1) return 0;
     return static_cast<size_t>(B) * Hq * Lq * n * (f32_padded(D) + 4) * sizeof(float);
 }
@@ -487,9 +516,14 @@ size_t prefill_f32_workspace_bytes(int B, int Hq, int Lq, int Lk, int D) {
 bool prefill_f32_supported(const Params& p, DType dt) {
     if (dt != DType::F32) return false;
     if (p.D < 1 || p.D > 256) return false;
-    // Q, O and the mask are read and written per element; K and V per
-    // float4 when aligned, else per element (the launch picks).
-    return p.Hq <= 65535 && static_cast<int64_t>(p.B) * p.n_split <= 65535;
+    const int gw = f32_heads_per_wg(p.group);
+    // Buffer resources and their offsets are 32-bit: one (batch, kv head)
+    // slice of K and of V must span less than 2 GiB.
+    const int64_t lim = INT32_MAX;
+    if (static_cast<int64_t>(p.Lk) * p.ks.sr * 4 >= lim) return false;
+    if (static_cast<int64_t>(p.Lk) * p.vs.sr * 4 >= lim) return false;
+    return static_cast<int64_t>(p.Hkv) * (p.group / gw) <= 65535 &&
+           static_cast<int64_t>(p.B) * p.n_split <= 65535;
 }
 
 hipError_t launch_prefill_f32(const Params& p, DType, hipStream_t s) {
