@@ -188,9 +188,8 @@ prefill_mfma_kernel(
     using TL = Tile<D>;
     using CF = Cfg<D, kShort>;
     constexpr int kRows = CF::kRows, kWaves = CF::kWaves, kThreads = CF::kThreads;
-    // True head dim (a multiple of 8, <= D).  Padded dims run the variant
-    // kernel; in the plain one it is the compile-time D and the column guards
-    // below fold away.
+    // True head dim (<= D).  Padded dims run the variant kernel; in the plain
+    // one it is the compile-time D and the column guards below fold away.
     const int Dt = kVar ? p.D : D;
     // K/V columns per row: a head dim that is not a multiple of 8 reads
     // copies padded to one (zeros past Dt), staged into the workspace first;
@@ -455,6 +454,9 @@ prefill_mfma_kernel(
     // One tile; s_cur holds its scores, s_next receives the next tile's.  The
     // loop below runs it twice per trip with the two score sets swapping
     // roles, so no scores are copied between tiles.
+    // D = 256 issues the V loads just before P V rather than with the K
+    // loads (measured 2.5% faster there; no difference at D = 128).
+    constexpr bool kVLate = D == 256;
     auto step = [&](int tile, f32x16 (&s_cur)[2], f32x16 (&s_next)[2]) {
         const bool more_k = tile + SP::DK < n_tiles;
         const bool more_v = tile + SP::DV < n_tiles;
@@ -514,7 +516,7 @@ prefill_mfma_kernel(
         // that waiting on those does not wait on these.
         if (!SP::kTop) {
             if (more_k) fetch_k(tile + SP::DK);
-            if (more_v) fetch_v(tile + SP::DV);
+            if (more_v && !kVLate) fetch_v(tile + SP::DV);
         }
         // -- hide keys past the length / causal bound / below the window
         // (edge tiles only) --
@@ -601,6 +603,7 @@ prefill_mfma_kernel(
             }
         }
         l_sum += (l_part[0][0] + l_part[0][1]) + (l_part[1][0] + l_part[1][1]);
+        if (!SP::kTop && kVLate && more_v) fetch_v(tile + SP::DV);
         // -- O^T += V^T P^T (V^T by transpose read) --
         // A wave whose rows cannot see this tile has all p = 0 here (every score
         // was hidden), so the products add exact zeros.
