@@ -371,17 +371,17 @@ int f32_n_qblk(int Lq, int gw) {
     return (Lq + P - 1) / P;
 }
 
-// One thread per (b, h, row, dim): merge the ranges the row's wave wrote, in
-// order, then the sink, the masked-row policy and the LSE as the main
-// kernel's epilogue does.  Records are in the main kernel's score units: c
-// converts a difference of them to base 2, to_nat a value to natural units.
+// One wave per (b, h, row), lanes over the head dim: merge the ranges the
+// row's wave wrote, in order, then the sink, the masked-row policy and the
+// LSE as the main kernel's epilogue does.  Records are in the main kernel's
+// score units: c converts a difference of them to base 2, to_nat a value to
+// natural units.
 template <int DP>
 __global__ __launch_bounds__(256) void prefill_f32_merge_kernel(Params p, float c, float to_nat) {
-    const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-    const int64_t total = static_cast<int64_t>(p.B) * p.Hq * p.Lq * p.D;
-    if (t >= total) return;
-    const int d = static_cast<int>(t % p.D);
-    const int64_t row = t / p.D;                     // (b, h, i) flattened
+    const int lane = threadIdx.x & 63;
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);   // (b, h, i)
+    const int64_t rows = static_cast<int64_t>(p.B) * p.Hq * p.Lq;
+    if (row >= rows) return;
     const int64_t i = row % p.Lq;
     const int h = static_cast<int>((row / p.Lq) % p.Hq);
     const int b = static_cast<int>(row / (static_cast<int64_t>(p.Lq) * p.Hq));
@@ -400,19 +400,26 @@ __global__ __launch_bounds__(256) void prefill_f32_merge_kernel(Params p, float 
     }
     const int n_live = static_cast<int>((blk_hi + p.split_len - 1) / p.split_len);
     const float* recs = static_cast<const float*>(p.ws) + row * p.n_split * (DP + 4);
-    // Eight ranges' (m, l, acc[d]) are fetched together per round; the
-    // reference maximum is the largest seen so far, so up to eight ranges
-    // fold in one round exactly as a separate maximum pass would.
-    float M = kNegInf, L = 0.f, A = 0.f;
+    constexpr int NPL = (DP + 63) / 64;              // head-dim values per lane
+    // Eight ranges' (m, l, acc) are fetched per round; the reference maximum
+    // is the largest seen so far, so up to eight ranges fold in one round
+    // exactly as a separate maximum pass would.
+    float M = kNegInf, L = 0.f, A[NPL];
+#pragma unroll
+    for (int k = 0; k < NPL; ++k) A[k] = 0.f;
     for (int r0 = 0; r0 < n_live; r0 += 8) {
-        float m8[8], l8[8], a8[8];
+        float m8[8], l8[8], a8[8][NPL];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const bool in = r0 + u < n_live;
             const float* rec = recs + (in ? r0 + u : 0) * (DP + 4);
             m8[u] = in ? rec[0] : kNegInf;
             l8[u] = in ? rec[1] : 0.f;
-            a8[u] = in ? rec[4 + d] : 0.f;
+#pragma unroll
+            for (int k = 0; k < NPL; ++k) {
+                const int d = lane + 64 * k;
+                a8[u][k] = (in && d < p.D) ? rec[4 + d] : 0.f;
+            }
         }
         float Mn = M;
 #pragma unroll
@@ -420,7 +427,8 @@ __global__ __launch_bounds__(256) void prefill_f32_merge_kernel(Params p, float 
         if (Mn != M) {   // raise the reference (from -inf: nothing folded yet)
             const float al = (M == kNegInf) ? 0.f : fast_exp2((M - Mn) * c);
             L *= al;
-            A *= al;
+#pragma unroll
+            for (int k = 0; k < NPL; ++k) A[k] *= al;
             M = Mn;
         }
 #pragma unroll
@@ -428,15 +436,22 @@ __global__ __launch_bounds__(256) void prefill_f32_merge_kernel(Params p, float 
             if (r0 + u >= n_live) break;
             const float f = (m8[u] == kNegInf) ? 0.f : fast_exp2((m8[u] - M) * c);
             L = fmaf(l8[u], f, L);
-            A = fmaf(a8[u], f, A);
+#pragma unroll
+            for (int k = 0; k < NPL; ++k) A[k] = fmaf(a8[u][k], f, A[k]);
         }
     }
     float m_nat = M * to_nat;
     const float fs = fold_sink(p, h, m_nat, L);
     const bool empty = (L == 0.f);
-    const float o = empty ? (p.masked_zero ? 0.f : __builtin_nanf("")) : A * (fs / L);
-    static_cast<float*>(p.o)[b * p.os.sb + h * p.os.sh + i * p.os.sr + d] = o;
-    if (p.lse && d == 0)
+    const float inv = fs / L;
+    const float fill = p.masked_zero ? 0.f : __builtin_nanf("");
+    float* og = static_cast<float*>(p.o) + b * p.os.sb + h * p.os.sh + i * p.os.sr;
+#pragma unroll
+    for (int k = 0; k < NPL; ++k) {
+        const int d = lane + 64 * k;
+        if (d < p.D) og[d] = empty ? fill : A[k] * inv;
+    }
+    if (p.lse && lane == 0)
         p.lse[b * p.ls.sb + h * p.ls.sh + i * p.ls.sr] = empty ? kNegInf : row_lse(m_nat, L);
 }
 
@@ -470,10 +485,10 @@ hipError_t launch_d(const Params& p, hipStream_t s) {
     else by_split(F{});
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !split) return e;
-    const int64_t total = static_cast<int64_t>(p.B) * p.Hq * p.Lq * p.D;
+    const int64_t rows = static_cast<int64_t>(p.B) * p.Hq * p.Lq;
     const float c = p.mask ? kLog2e : p.scale_log2, to_nat = p.mask ? 1.f : p.scale;
     hipLaunchKernelGGL((prefill_f32_merge_kernel<DP>),
-                       dim3(static_cast<uint32_t>((total + 255) / 256)), dim3(256), 0, s, p, c,
+                       dim3(static_cast<uint32_t>((rows + 3) / 4)), dim3(256), 0, s, p, c,
                        to_nat);
     return hipGetLastError();
 }
