@@ -62,23 +62,34 @@ constexpr uint32_t kOutOfRange = 0x80000000u;   // a buffer offset past any tens
 // keeps the 16-byte column reads of 16 rows on distinct banks).
 template <int DP> struct F32Cfg {
     static constexpr int kRowF = DP + 4;                    // floats per LDS row
-    static constexpr int kTileF = kTileN * kRowF;           // floats per tile buffer
-    static constexpr int kLoads = kTileF / 64;              // 64-float DMA rows per tile
+    static constexpr int kTileF = kTileN * kRowF;           // floats of a tile
+    static constexpr int kLoads = kTileF / 64;              // 4-byte DMA rows per tile
+    static constexpr int kLoads16 = (kTileF + 255) / 256;   // 16-byte DMA rows per tile
+    static constexpr int kBufF = kLoads16 * 256;            // floats per tile buffer
     static constexpr int kHalf = DP / 2;                    // Q columns per lane
     static constexpr int kBlk = DP / 32;                    // 32-column output blocks
     static constexpr int kMinWg = DP <= 128 ? 2 : 1;        // workgroups per CU (registers)
+    // Up to 64 columns, three workgroups per CU where the registers allow
+    // it without spills (not the key-range split kernels): 3-4% faster.
+    static constexpr int kMinWg3 = DP <= 64 ? 3 : kMinWg;
     static_assert(kTileF % 64 == 0, "a tile buffer is whole DMA rows");
     static_assert(kHalf % 4 == 0, "Q halves are whole 16-byte LDS reads");
 };
 
 // One 4-byte-per-lane buffer load into LDS at lds_byte + 4 * lane (M0 holds
-// the LDS address; one wait state after writing it).  An instruction of its
-// own, so the compiler does not hold later LDS reads of the other buffer for
-// it; the kernel waits for these loads itself before the barrier that
-// publishes a tile.
+// the LDS address; one wait state after writing it), and the 16-byte form at
+// lds_byte + 16 * lane.  Instructions of their own, so the compiler does not
+// hold later LDS reads of the other buffer for them; the kernel waits for
+// these loads itself before the barrier that publishes a tile.
 __device__ __forceinline__ void load_lds4(__amdgpu_buffer_rsrc_t rs, uint32_t lds_byte,
                                           uint32_t voff) {
     asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(rs), "{m0}"(lds_byte));
+}
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rs, uint32_t lds_byte,
+                                           uint32_t voff) {
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                  :
                  : "v"(voff), "s"(rs), "{m0}"(lds_byte));
 }
@@ -92,12 +103,13 @@ __device__ __forceinline__ constexpr int key_of(int r, int h) {
 }
 
 template <int DP, bool kMask, bool kSplit, bool kVar>
-__global__ __launch_bounds__(256, F32Cfg<DP>::kMinWg) void prefill_f32_kernel(Params p,
+__global__ __launch_bounds__(256, kSplit ? F32Cfg<DP>::kMinWg : F32Cfg<DP>::kMinWg3) void prefill_f32_kernel(Params p,
                                                                                 int n_qblk,
-                                                                                int gw) {
+                                                                                int gw,
+                                                                                int vec) {
     using CF = F32Cfg<DP>;
-    __shared__ __attribute__((aligned(16))) float k_sh[2][CF::kTileF];
-    __shared__ __attribute__((aligned(16))) float v_sh[2][CF::kTileF];
+    __shared__ __attribute__((aligned(16))) float k_sh[2][CF::kBufF];
+    __shared__ __attribute__((aligned(16))) float v_sh[2][CF::kBufF];
     __shared__ int64_t wg_bounds[2 * kWavesF];
 
     // blockIdx.x: query block (heaviest causal blocks first); y: (kv head,
@@ -108,7 +120,8 @@ __global__ __launch_bounds__(256, F32Cfg<DP>::kMinWg) void prefill_f32_kernel(Pa
     const int slice = static_cast<int>(blockIdx.y) % n_slice;
     const int b = static_cast<int>(blockIdx.z) / p.n_split;
     const int rng = static_cast<int>(blockIdx.z) % p.n_split;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int hh = lane >> 5, col = lane & 31;
     const int wph = kWavesF / gw;                 // waves per head
     const int h = g * p.group + slice * gw + w / wph;
@@ -167,11 +180,33 @@ __global__ __launch_bounds__(256, F32Cfg<DP>::kMinWg) void prefill_f32_kernel(Pa
     const __amdgpu_buffer_rsrc_t krs = make_rsrc(kg, kv_len * p.ks.sr * 4);
     const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vg, kv_len * p.vs.sr * 4);
 
-    // Tile loads: float f = i * 64 + lane of a tile buffer is key f / kRowF,
-    // column f % kRowF; columns >= D and keys past the length load as zeros.
-    // DMA rows i = w, w + 4, ... are this wave's.
+    // Tile loads: float f of a tile buffer is key f / kRowF, column
+    // f % kRowF; columns >= D and keys past the length load as zeros.  With
+    // rows of whole, 16-byte aligned float4s (vec), lane l of DMA row i
+    // loads floats 4 (i * 64 + l) .. + 3 (the last row runs into the buffer's
+    // padding); else 4-byte loads, float i * 64 + l.  DMA rows i = w, w + 4,
+    // ... are this wave's.
     auto dma = [&](int tile, int buf) {
         const int64_t key0 = j_begin + static_cast<int64_t>(tile) * kTileN;
+        if (vec) {
+            for (int i = w; i < CF::kLoads16; i += kWavesF) {
+                const int f = 4 * (i * 64 + lane);
+                const int r = f / CF::kRowF, cc = f % CF::kRowF;
+                const int64_t key = key0 + r;
+                const bool in = r < kTileN && cc < D && key < kv_len;
+                const uint32_t ko = in ? static_cast<uint32_t>((key * p.ks.sr + cc) * 4) : kOutOfRange;
+                const uint32_t vo = in ? static_cast<uint32_t>((key * p.vs.sr + cc) * 4) : kOutOfRange;
+                load_lds16(krs,
+                           static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+                               (__attribute__((address_space(3))) float*)(&k_sh[buf][i * 256]))),
+                           ko);
+                load_lds16(vrs,
+                           static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+                               (__attribute__((address_space(3))) float*)(&v_sh[buf][i * 256]))),
+                           vo);
+            }
+            return;
+        }
         for (int i = w; i < CF::kLoads; i += kWavesF) {
             const int f = i * 64 + lane;
             const int r = f / CF::kRowF, cc = f % CF::kRowF;
@@ -461,6 +496,13 @@ bool f32_var(const Params& p) {
 
 template <int DP>
 hipError_t launch_d(const Params& p, hipStream_t s) {
+    // 16-byte tile loads when every K and V row starts 16-byte aligned and
+    // holds whole float4s.
+    auto al = [](const void* ptr, const Strides& st) {
+        return reinterpret_cast<uintptr_t>(ptr) % 16 == 0 && st.sb % 4 == 0 && st.sh % 4 == 0 &&
+               st.sr % 4 == 0;
+    };
+    const int vec = p.D % 4 == 0 && (p.Lk == 0 || (al(p.k, p.ks) && al(p.v, p.vs)));
     const int gw = f32_heads_per_wg(p.group);
     const int n_qblk = f32_n_qblk(p.Lq, gw);
     const dim3 grid(n_qblk, p.Hkv * (p.group / gw), p.B * p.n_split);
@@ -469,7 +511,7 @@ hipError_t launch_d(const Params& p, hipStream_t s) {
         constexpr bool kM = decltype(mask_c)::value, kS = decltype(split_c)::value;
         constexpr bool kV = decltype(var_c)::value;
         hipLaunchKernelGGL((prefill_f32_kernel<DP, kM, kS, kV>), grid, dim3(64 * kWavesF), 0, s,
-                           p, n_qblk, gw);
+                           p, n_qblk, gw, vec);
     };
     using T = std::true_type;
     using F = std::false_type;
