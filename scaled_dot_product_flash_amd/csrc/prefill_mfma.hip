@@ -344,21 +344,84 @@ prefill_mfma_kernel(
     const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vg, kv_len * p.vs.sr * 2);
 
     // ---- Q^T operand, resident in registers -------------------------------
+    // Rows whose length is not a multiple of 8 elements (no 16-byte access
+    // applies).  D >= 128: Q comes in and O goes out through LDS, each wave
+    // owning 32 rows of D elements at the front of the K buffers, free before
+    // the first tile loads and after the last tile's barrier; global accesses
+    // then go one row at a time with lanes over consecutive columns
+    // (c = lane + 64 k), instead of each lane walking its own row, where
+    // per-lane 2-byte accesses down 32 rows cost a memory transaction per
+    // lane per instruction.  D = 64 (three workgroups per CU at the register
+    // cap, where the staging code's registers would spill inside the tile
+    // loop): per-lane element accesses, all Q loads issued before any is used.
+    constexpr bool kRowStage = D >= 128;
+    static_assert(!kRowStage || kRows * D * 2 <= SP::NK * NB * KB, "the row-staging area does not fit");
+    uint16_t* const xrow = reinterpret_cast<uint16_t*>(&k_sh[0][0]) + w * 32 * D;
+    constexpr int kColIt = D / 64;   // column steps of 64 per row
+
+    // ---- Q^T operand, resident in registers -------------------------------
     i16x8 qop[NT];
     {
         const bool ok = qrow < p.Lq;
-        const uint16_t* src = qg + b * p.qs.sb + h * p.qs.sh + (ok ? qrow : 0) * p.qs.sr + 8 * hh;
+        if (elem && !kRowStage) {
+            const uint16_t* row = qg + b * p.qs.sb + h * p.qs.sh + (ok ? qrow : 0) * p.qs.sr;
+            short e16[NT][8];
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            const bool in = ok && 16 * t + 8 * hh < Dt;   // padded columns are zero
-            if (elem) {
-                i16x8 v{};
+            for (int t = 0; t < NT; ++t)
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    v[e] = (ok && 16 * t + 8 * hh + e < Dt) ? static_cast<short>(src[16 * t + e]) : short(0);
+                for (int e = 0; e < 8; ++e) {
+                    const int c = 16 * t + 8 * hh + e;   // clamped into the row, zeroed below
+                    e16[t][e] = static_cast<short>(row[c < Dt ? c : Dt - 1]);
+                }
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                i16x8 v;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = (ok && 16 * t + 8 * hh + e < Dt) ? e16[t][e] : short(0);
                 qop[t] = v;
-            } else {
-                qop[t] = in ? *reinterpret_cast<const i16x8*>(src + 16 * t) : i16x8{};
+            }
+        } else if (elem) {
+            // Every load issued before any is stored, none conditional: the
+            // row and column are clamped into the tensor and the values
+            // outside it are zeroed when the operand is read back.
+            // Sixteen rows per round (registers for 32 rows would spill).
+            const uint16_t* qb = qg + b * p.qs.sb + h * p.qs.sh;
+#pragma unroll
+            for (int r0 = 0; r0 < 32; r0 += 16) {
+                short qv[16][kColIt];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int64_t qr = qw0 + r0 + r;
+                    const uint16_t* src = qb + (qr < p.Lq ? qr : p.Lq - 1) * p.qs.sr;
+#pragma unroll
+                    for (int k = 0; k < kColIt; ++k) {
+                        const int c = lane + 64 * k;
+                        qv[r][k] = static_cast<short>(src[c < Dt ? c : Dt - 1]);
+                    }
+                }
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+#pragma unroll
+                    for (int k = 0; k < kColIt; ++k)
+                        xrow[(r0 + r) * D + lane + 64 * k] = static_cast<uint16_t>(qv[r][k]);
+            }
+            // The wave reads back what it wrote (LDS keeps one wave's
+            // accesses in order).
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const i16x8 raw = *reinterpret_cast<const i16x8*>(xrow + col * D + 16 * t + 8 * hh);
+                i16x8 v;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = (ok && 16 * t + 8 * hh + e < Dt) ? raw[e] : short(0);
+                qop[t] = v;
+            }
+            __syncthreads();   // before any wave's tile loads overwrite the area
+        } else {
+            const uint16_t* row = qg + b * p.qs.sb + h * p.qs.sh + (ok ? qrow : 0) * p.qs.sr;
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const bool in = ok && 16 * t + 8 * hh < Dt;   // padded columns are zero
+                qop[t] = in ? *reinterpret_cast<const i16x8*>(row + 8 * hh + 16 * t) : i16x8{};
             }
         }
     }
@@ -672,6 +735,50 @@ prefill_mfma_kernel(
     }
     float m_nat = m_ref * to_nat;               // natural units (-inf stays -inf)
     const float fs = fold_sink(p, h, m_nat, l_tot);
+    if (kRowStage && elem) {
+        // Through the wave's LDS rows (see the Q load): the last tile's
+        // barrier has ended every read of the K buffers.
+        const bool empty = (l_tot == 0.f);
+        const float inv = fs / l_tot;
+        const float fill = p.masked_zero ? 0.f : __builtin_nanf("");
+#pragma unroll
+        for (int d = 0; d < ND; ++d)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                float o4[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o4[e] = empty ? fill : acc[d][4 * u + e] * inv;
+                *reinterpret_cast<uint2*>(xrow + col * D + 32 * d + 8 * u + 4 * hh) =
+                    uint2{M::pack_out(o4[0], o4[1]), M::pack_out(o4[2], o4[3])};
+            }
+        // Eight rows at a time: their LDS reads first, then the
+        // (conditional) stores.
+        uint16_t* ob = static_cast<uint16_t*>(p.o) + b * p.os.sb + h * p.os.sh;
+        // A loop kept rolled: unrolled, the compiler hoists the 32 rows'
+        // addresses above the tile loop, where they would spill.
+#pragma unroll 1
+        for (int r0 = 0; r0 < 32; r0 += 8) {
+            uint16_t ov[8][kColIt];
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+#pragma unroll
+                for (int k = 0; k < kColIt; ++k) ov[r][k] = xrow[(r0 + r) * D + lane + 64 * k];
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                const int64_t qr = qw0 + r0 + r;
+#pragma unroll
+                for (int k = 0; k < kColIt; ++k) {
+                    const int c = lane + 64 * k;
+                    if (qr < p.Lq && c < Dt) ob[qr * p.os.sr + c] = ov[r][k];
+                }
+            }
+        }
+        if (p.lse && hh == 0 && qrow < p.Lq) {
+            const float lse = empty ? kNegInf : row_lse(m_nat, l_tot);
+            p.lse[b * p.ls.sb + h * p.ls.sh + qrow * p.ls.sr] = lse;
+        }
+        return;
+    }
     if (qrow < p.Lq) {
         const bool empty = (l_tot == 0.f);
         const float inv = fs / l_tot;
@@ -779,6 +886,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_merge_kernel(Params p, float
 // workspace with the head dim padded to a multiple of 8 (zeros), so the main
 // kernel's 16-byte loads apply.  Rows at or past a batch entry's key length
 // are written as zeros, not read.
+template <int W>
 __global__ __launch_bounds__(256) void prefill_stage_kv_kernel(Params p, uint16_t* kd, uint16_t* vd,
                                                                int dp8) {
     const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
@@ -797,13 +905,27 @@ __global__ __launch_bounds__(256) void prefill_stage_kv_kernel(Params p, uint16_
     }
     const uint16_t* ks = static_cast<const uint16_t*>(p.k) + b * p.ks.sb + g * p.ks.sh + j * p.ks.sr;
     const uint16_t* vs = static_cast<const uint16_t*>(p.v) + b * p.vs.sb + g * p.vs.sh + j * p.vs.sr;
+    // W elements per load (W divides D and the rows are aligned to 2 W
+    // bytes), so a group is wholly inside the row or wholly past it.
     uint16_t kx[8], vx[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const int col = 8 * cch + e;
+    for (int e0 = 0; e0 < 8; e0 += W) {
+        const int col = 8 * cch + e0;
         const bool in = j < kv_len && col < p.D;
-        kx[e] = in ? ks[col] : uint16_t(0);
-        vx[e] = in ? vs[col] : uint16_t(0);
+        if constexpr (W == 4) {
+            const uint2 kw = in ? *reinterpret_cast<const uint2*>(ks + col) : uint2{0, 0};
+            const uint2 vw = in ? *reinterpret_cast<const uint2*>(vs + col) : uint2{0, 0};
+            kx[e0] = kw.x & 0xffffu; kx[e0 + 1] = kw.x >> 16; kx[e0 + 2] = kw.y & 0xffffu; kx[e0 + 3] = kw.y >> 16;
+            vx[e0] = vw.x & 0xffffu; vx[e0 + 1] = vw.x >> 16; vx[e0 + 2] = vw.y & 0xffffu; vx[e0 + 3] = vw.y >> 16;
+        } else if constexpr (W == 2) {
+            const uint32_t kw = in ? *reinterpret_cast<const uint32_t*>(ks + col) : 0u;
+            const uint32_t vw = in ? *reinterpret_cast<const uint32_t*>(vs + col) : 0u;
+            kx[e0] = kw & 0xffffu; kx[e0 + 1] = kw >> 16;
+            vx[e0] = vw & 0xffffu; vx[e0 + 1] = vw >> 16;
+        } else {
+            kx[e0] = in ? ks[col] : uint16_t(0);
+            vx[e0] = in ? vs[col] : uint16_t(0);
+        }
     }
     const int64_t o = rowi * dp8 + 8 * cch;
     *reinterpret_cast<uint4*>(kd + o) = make_uint4(kx[0] | (uint32_t(kx[1]) << 16), kx[2] | (uint32_t(kx[3]) << 16),
@@ -985,8 +1107,21 @@ hipError_t launch_prefill_mfma(const Params& p_in, DType dt, hipStream_t s) {
         uint16_t* kd = static_cast<uint16_t*>(p.stage);
         uint16_t* vd = kd + static_cast<int64_t>(p.B) * p.Hkv * p.Lk * dp8;
         const int64_t chunks = static_cast<int64_t>(p.B) * p.Hkv * p.Lk * (dp8 / 8);
-        hipLaunchKernelGGL(prefill_stage_kv_kernel, dim3(static_cast<uint32_t>((chunks + 255) / 256)),
-                           dim3(256), 0, s, p, kd, vd, dp8);
+        // Widest element group that divides D and keeps every access aligned.
+        auto fits = [&](int w) {
+            auto al = [&](const void* ptr, const Strides& st) {
+                return reinterpret_cast<uintptr_t>(ptr) % (2 * w) == 0 && st.sb % w == 0 &&
+                       st.sh % w == 0 && st.sr % w == 0;
+            };
+            return p.D % w == 0 && al(p.k, p.ks) && al(p.v, p.vs);
+        };
+        const dim3 grid(static_cast<uint32_t>((chunks + 255) / 256));
+        if (fits(4))
+            hipLaunchKernelGGL(prefill_stage_kv_kernel<4>, grid, dim3(256), 0, s, p, kd, vd, dp8);
+        else if (fits(2))
+            hipLaunchKernelGGL(prefill_stage_kv_kernel<2>, grid, dim3(256), 0, s, p, kd, vd, dp8);
+        else
+            hipLaunchKernelGGL(prefill_stage_kv_kernel<1>, grid, dim3(256), 0, s, p, kd, vd, dp8);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         p.k = kd;

@@ -725,7 +725,8 @@ def test_head_dims_on_matrix_cores(cfg, policy):
 
 
 # Head dims that are not a multiple of 8: K/V staged into the workspace
-# padded to one, Q read and O written per element, then the matrix-core
+# padded to one, Q read and O written per element (through LDS, one row at
+# a time, at the padded dims 128 and 256), then the matrix-core
 # kernel at the padded dim (OneGPU "Attention", "What it covers").
 ODD_DIMS = [
     # D, dtype, B, Hq, Hkv, Lq, Lk, extra
