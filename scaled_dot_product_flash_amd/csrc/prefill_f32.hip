@@ -188,7 +188,7 @@ __global__ __launch_bounds__(256, kSplit ? F32Cfg<DP>::kMinWg : F32Cfg<DP>::kMin
     // ... are this wave's.
     auto dma = [&](int tile, int buf) {
         const int64_t key0 = j_begin + static_cast<int64_t>(tile) * kTileN;
-        if (vec) {
+        if (vec & 1) {
             for (int i = w; i < CF::kLoads16; i += kWavesF) {
                 const int f = 4 * (i * 64 + lane);
                 const int r = f / CF::kRowF, cc = f % CF::kRowF;
@@ -226,15 +226,33 @@ __global__ __launch_bounds__(256, kSplit ? F32Cfg<DP>::kMinWg : F32Cfg<DP>::kMin
     };
     if (n_tiles > 0) dma(0, 0);
 
-    // Q columns hh * DP/2 + t of this lane's row, zeros past D.
+    // Q columns hh * DP/2 + t of this lane's row, zeros past D.  With rows
+    // of whole, 16-byte aligned float4s (vec bit 1): 16-byte loads, each
+    // instruction touching a quarter as many cache lines as 4-byte loads.
     float q[CF::kHalf];
     {
         const float* src = static_cast<const float*>(p.q) + b * p.qs.sb + h * p.qs.sh +
                            (row_ok ? row : 0) * p.qs.sr;
+        // Every load unconditional (column clamped into the row, the value
+        // zeroed after), so none waits behind a branch.
+        if (vec & 2) {
 #pragma unroll
-        for (int t = 0; t < CF::kHalf; ++t) {
-            const int d = hh * CF::kHalf + t;
-            q[t] = (row_ok && d < D) ? src[d] : 0.f;
+            for (int t = 0; t < CF::kHalf; t += 4) {
+                const int d = hh * CF::kHalf + t;
+                const float4 v = *reinterpret_cast<const float4*>(src + (d < D ? d : 0));
+                const bool in = row_ok && d < D;
+                q[t] = in ? v.x : 0.f;
+                q[t + 1] = in ? v.y : 0.f;
+                q[t + 2] = in ? v.z : 0.f;
+                q[t + 3] = in ? v.w : 0.f;
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < CF::kHalf; ++t) {
+                const int d = hh * CF::kHalf + t;
+                const float v = src[d < D ? d : 0];
+                q[t] = (row_ok && d < D) ? v : 0.f;
+            }
         }
     }
     const float* mrow = (kMask && row_ok) ? p.mask + b * p.ms.sb + h * p.ms.sh + row * p.ms.sr
@@ -382,13 +400,27 @@ __global__ __launch_bounds__(256, kSplit ? F32Cfg<DP>::kMinWg : F32Cfg<DP>::kMin
     const float inv = fs / l_f;
     const float fill = p.masked_zero ? 0.f : __builtin_nanf("");
     float* og = static_cast<float*>(p.o) + b * p.os.sb + h * p.os.sh + row * p.os.sr;
+    if (vec & 2) {   // registers 4u .. 4u + 3 hold four consecutive columns
 #pragma unroll
-    for (int j = 0; j < CF::kBlk; ++j)
+        for (int j = 0; j < CF::kBlk; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int d = 32 * j + key_of(r, hh);
-            if (d < D) og[d] = empty ? fill : acc[j][r] * inv;
-        }
+            for (int u = 0; u < 4; ++u) {
+                const int d = 32 * j + key_of(4 * u, hh);
+                if (d < D)
+                    *reinterpret_cast<float4*>(og + d) =
+                        empty ? make_float4(fill, fill, fill, fill)
+                              : make_float4(acc[j][4 * u] * inv, acc[j][4 * u + 1] * inv,
+                                            acc[j][4 * u + 2] * inv, acc[j][4 * u + 3] * inv);
+            }
+    } else {
+#pragma unroll
+        for (int j = 0; j < CF::kBlk; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int d = 32 * j + key_of(r, hh);
+                if (d < D) og[d] = empty ? fill : acc[j][r] * inv;
+            }
+    }
     if (p.lse && hh == 0)
         p.lse[b * p.ls.sb + h * p.ls.sh + row * p.ls.sr] = empty ? kNegInf : row_lse(m_nat, l_f);
 }
@@ -502,7 +534,9 @@ hipError_t launch_d(const Params& p, hipStream_t s) {
         return reinterpret_cast<uintptr_t>(ptr) % 16 == 0 && st.sb % 4 == 0 && st.sh % 4 == 0 &&
                st.sr % 4 == 0;
     };
-    const int vec = p.D % 4 == 0 && (p.Lk == 0 || (al(p.k, p.ks) && al(p.v, p.vs)));
+    // Bit 0: K/V rows; bit 1: Q and O rows (16-byte loads and stores).
+    const int vec = (p.D % 4 == 0 && (p.Lk == 0 || (al(p.k, p.ks) && al(p.v, p.vs))) ? 1 : 0) |
+                    (p.D % 4 == 0 && al(p.q, p.qs) && al(p.o, p.os) ? 2 : 0);
     const int gw = f32_heads_per_wg(p.group);
     const int n_qblk = f32_n_qblk(p.Lq, gw);
     const dim3 grid(n_qblk, p.Hkv * (p.group / gw), p.B * p.n_split);
