@@ -42,7 +42,9 @@
 //
 // Int8 cache (GroupQueryAttention README, "Inputs": k_scale / v_scale): rows
 // are read as 16-byte loads of 16 int8 values -- half the bytes of fp16 --
-// and widened to the element type on their way into LDS (exact: |x| <= 128).
+// stored in LDS as they are, and widened to the element type as the MFMA
+// operands are read (exact: |x| <= 128): K rows by 8-byte reads, V columns
+// by the 8-bit transpose read, half the LDS bytes of widened rows.
 // A per-tensor K scale multiplies the exponent constant (exact); a
 // per-channel K scale is folded into the query row, rounded to the element
 // type.  V scales apply per output element in the merge, where they factor
@@ -58,6 +60,7 @@ namespace {
 using namespace mfma;
 
 constexpr int kStep = 32;          // keys per wave step (two 16-key MFMA blocks)
+
 constexpr int kWavesTotal = 2048;  // persistent waves: 8 per CU on 256 CUs
 constexpr float kSlack = 8.f;      // lazy-rescale threshold, base-2 units
 
@@ -73,11 +76,15 @@ template <int D> struct DLay {
     static constexpr int kWaveBytes = kStep * (KS + VS) * 2;
 };
 
-// Int8 rows: 16 values per 16-byte load.
+// Int8 rows: 16 values per 16-byte load, kept as int8 in LDS (rows of RS
+// bytes, K and V alike; 16 bytes of padding keep the 8-byte K reads and the
+// transposing V reads within two-way bank conflicts).
 template <int D> struct I8Lay {
     static constexpr int kRowChunks = D / 16;
     static constexpr int kRowsPerLoad = 64 / kRowChunks;
     static constexpr int kLoads = kStep / kRowsPerLoad;
+    static constexpr int RS = D + 16;
+    static constexpr int kWaveBytes = kStep * 2 * RS;
 };
 
 // 16 signed bytes -> 16 elements of the MFMA type, exactly.
@@ -111,6 +118,14 @@ __device__ __forceinline__ void widen_i8(uint4 raw, i16x8& lo, i16x8& hi) {
     }
     lo = __builtin_bit_cast(i16x8, (uint4){out[0], out[1], out[2], out[3]});
     hi = __builtin_bit_cast(i16x8, (uint4){out[4], out[5], out[6], out[7]});
+}
+
+// 8 signed bytes -> 8 elements of the MFMA type, exactly (as widen_i8).
+template <bool kBf16>
+__device__ __forceinline__ i16x8 widen8_i8(uint2 raw) {
+    i16x8 lo, hi;
+    widen_i8<kBf16>(make_uint4(raw.x, raw.y, 0u, 0u), lo, hi);
+    return lo;
 }
 
 // Partial record of one (slot, head): [m, l, -, -, acc[0..D)], floats.
@@ -199,9 +214,12 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(Params p, int n_hgr
     constexpr int KS = LY::KS, VS = LY::VS;
     constexpr int NT = D / 32;       // 32-wide d-steps of the score product
     constexpr int ND = D / 16;       // 16-row d-tiles of the output
-    __shared__ __attribute__((aligned(16))) uint8_t smem[LY::kWaveBytes];
+    using L8 = I8Lay<D>;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kI8 ? L8::kWaveBytes : LY::kWaveBytes];
     uint16_t* const k_sh = reinterpret_cast<uint16_t*>(smem);
     uint16_t* const v_sh = k_sh + kStep * KS;
+    uint8_t* const k8 = smem;                         // int8 cache: rows of L8::RS bytes
+    uint8_t* const v8 = smem + kStep * L8::RS;
 
     const int lane = threadIdx.x;
     const int wave = blockIdx.x;
@@ -244,7 +262,6 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(Params p, int n_hgr
     int64_t ls = (a - base_b) % sb;                 // step within the unit
 
     const int col = lane & 15, q4 = lane >> 4;
-    using L8 = I8Lay<D>;
     const int ld_row = kI8 ? lane / L8::kRowChunks : lane / LY::kRowChunks;
     const int ld_col = kI8 ? (lane % L8::kRowChunks) * 16 : (lane % LY::kRowChunks) * 8;
     // Raw scores are q.k with the K integers; a per-tensor K scale joins c.
@@ -371,13 +388,8 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(Params p, int n_hgr
         for (int n = 0; n < kLd; ++n) {
             const int row = n * kRpl + ld_row;
             if (kI8) {
-                i16x8 a0, a1, b0, b1;
-                widen_i8<kBf16>(__builtin_bit_cast(uint4, kst[n]), a0, a1);
-                widen_i8<kBf16>(__builtin_bit_cast(uint4, vst[n]), b0, b1);
-                *reinterpret_cast<i16x8*>(&k_sh[row * KS + ld_col]) = a0;
-                *reinterpret_cast<i16x8*>(&k_sh[row * KS + ld_col + 8]) = a1;
-                *reinterpret_cast<i16x8*>(&v_sh[row * VS + ld_col]) = b0;
-                *reinterpret_cast<i16x8*>(&v_sh[row * VS + ld_col + 8]) = b1;
+                *reinterpret_cast<i16x8*>(&k8[row * L8::RS + ld_col]) = kst[n];
+                *reinterpret_cast<i16x8*>(&v8[row * L8::RS + ld_col]) = vst[n];
             } else {
                 *reinterpret_cast<i16x8*>(&k_sh[row * KS + ld_col]) = kst[n];
                 *reinterpret_cast<i16x8*>(&v_sh[row * VS + ld_col]) = vst[n];
@@ -386,15 +398,28 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(Params p, int n_hgr
         if (x + 1 < e) fetch(nb, nuu, nls);
         const int64_t j0 = ls * kStep;
 
-        // S^T = K Q^T: two 16-key blocks; lane holds keys kb*16 + 4*q4 + r of column col.
+        // S^T = K Q^T: two 16-key blocks; lane holds keys key_at(kb, r) of column col.
+        // fp16/bf16 rows: block kb holds keys kb*16 + 4*q4 + r.  Int8 rows: the
+        // A operand's row m of block kb is key 8*(m/4) + 4*kb + m%4, so that
+        // lane q4 ends up with the eight consecutive keys 8*q4 + 4*kb + r,
+        // which the transposing 8-bit V read delivers as one operand.
+        auto key_at = [&](int kb, int r) { return kI8 ? 8 * q4 + 4 * kb + r : 16 * kb + 4 * q4 + r; };
         f32x4 s[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             s[kb] = f32x4{};
-            const uint16_t* krow = &k_sh[(kb * 16 + col) * KS + 8 * q4];
+            if constexpr (kI8) {
+                const uint8_t* krow = &k8[(8 * (col >> 2) + 4 * kb + (col & 3)) * L8::RS + 8 * q4];
 #pragma unroll
-            for (int t = 0; t < NT; ++t)
-                s[kb] = M::mfma16(*reinterpret_cast<const i16x8*>(krow + 32 * t), qop[t], s[kb]);
+                for (int t = 0; t < NT; ++t)
+                    s[kb] = M::mfma16(widen8_i8<kBf16>(*reinterpret_cast<const uint2*>(krow + 32 * t)),
+                                      qop[t], s[kb]);
+            } else {
+                const uint16_t* krow = &k_sh[(kb * 16 + col) * KS + 8 * q4];
+#pragma unroll
+                for (int t = 0; t < NT; ++t)
+                    s[kb] = M::mfma16(*reinterpret_cast<const i16x8*>(krow + 32 * t), qop[t], s[kb]);
+            }
         }
         if (kCap) {
 #pragma unroll
@@ -405,7 +430,7 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(Params p, int n_hgr
         if (mrow) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-                const int64_t key0 = j0 + kb * 16 + 4 * q4;
+                const int64_t key0 = j0 + key_at(kb, 0);
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     s[kb][r] = (key0 + r < kv_hi) ? fmaf(s[kb][r], sc, mrow[key0 + r])
@@ -417,7 +442,7 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(Params p, int n_hgr
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    if (j0 + kb * 16 + 4 * q4 + r >= kv_hi) s[kb][r] = kNegInf;
+                    if (j0 + key_at(kb, r) >= kv_hi) s[kb][r] = kNegInf;
         }
         // Row maximum over the 4 lanes that share column col.
         float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
@@ -440,7 +465,8 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(Params p, int n_hgr
         // product nor round away the scores' differences.
         const float neg_mc = (m_ref == kNegInf || nat) ? 0.f : -m_ref * c;
         const float sub = (m_ref == kNegInf || !nat) ? 0.f : m_ref;
-        // P^T operand (16x16x32 B layout): k = 8*q4 + e <-> key (e < 4 ? 4*q4 + e : 16 + 4*q4 + e - 4).
+        // P^T operand (16x16x32 B layout): k = 8*q4 + e <-> key key_at(e / 4, e % 4)
+        // (fp16/bf16 rows: e < 4 ? 4*q4 + e : 16 + 4*q4 + e - 4; int8 rows: 8*q4 + e).
         uint32_t w4[4];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
@@ -452,16 +478,28 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(Params p, int n_hgr
             }
         }
         const i16x8 pop = __builtin_bit_cast(i16x8, (uint4){w4[0], w4[1], w4[2], w4[3]});
-        // O^T += V^T P^T; V^T from the transpose read: rows 4*q4 + i/4 (+16), cols 16*dt + 4*(i%4).
+        // O^T += V^T P^T.  fp16/bf16 rows: V^T from the 16-bit transpose read,
+        // rows 4*q4 + i/4 (+16), cols 16*dt + 4*(i%4).  Int8 rows: one 8-bit
+        // transpose read per d-tile: lane 2k + h of each 16-lane group points
+        // at row 8*q4 + k, bytes 16*dt + 8*h .. + 7, and lane 8*h + i receives
+        // byte i of those eight rows, i.e. column 16*dt + (lane % 16) of keys
+        // 8*q4 .. 8*q4 + 7, the P^T operand's keys.
         const int gi = lane & 15;
-        const uint16_t* v0 = &v_sh[(4 * q4 + (gi >> 2)) * VS + 4 * (gi & 3)];
-        const uint16_t* v1 = v0 + 16 * VS;
+        if constexpr (kI8) {
+            const uint8_t* vr = &v8[(8 * q4 + (gi >> 1)) * L8::RS + 8 * (gi & 1)];
 #pragma unroll
-        for (int d = 0; d < ND; ++d) {
-            const i16x4 lo = tr_read(v0 + 16 * d);
-            const i16x4 hi = tr_read(v1 + 16 * d);
-            const i16x8 av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            acc[d] = M::mfma16(av, pop, acc[d]);
+            for (int d = 0; d < ND; ++d)
+                acc[d] = M::mfma16(widen8_i8<kBf16>(tr_read8(vr + 16 * d)), pop, acc[d]);
+        } else {
+            const uint16_t* v0 = &v_sh[(4 * q4 + (gi >> 2)) * VS + 4 * (gi & 3)];
+            const uint16_t* v1 = v0 + 16 * VS;
+#pragma unroll
+            for (int d = 0; d < ND; ++d) {
+                const i16x4 lo = tr_read(v0 + 16 * d);
+                const i16x4 hi = tr_read(v1 + 16 * d);
+                const i16x8 av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                acc[d] = M::mfma16(av, pop, acc[d]);
+            }
         }
 
         if (nb != b || nuu != uu || x + 1 == e) {

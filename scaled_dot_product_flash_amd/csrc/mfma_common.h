@@ -140,5 +140,15 @@ __device__ __forceinline__ i16x4 tr_read(const uint16_t* p) {
             (__attribute__((address_space(3))) uint16_t*)(p)));
 }
 
+// Eight bytes by the 8-bit transpose read: lane 8h + i of each 16-lane group
+// receives byte i of the 8 bytes that lanes 2k + h (k = 0..7) point at, in
+// k order (a layout checked on the GPU).
+__device__ __forceinline__ uint2 tr_read8(const uint8_t* p) {
+    typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
+    const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+        (i32x2 __attribute__((address_space(3)))*)((__attribute__((address_space(3))) uint8_t*)(p)));
+    return make_uint2(static_cast<uint32_t>(v[0]), static_cast<uint32_t>(v[1]));
+}
+
 }  // namespace mfma
 }  // namespace sdpa
