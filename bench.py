@@ -40,8 +40,8 @@ METRIC = "attention TFLOP/s (prefill) + KV GB/s (decode), % of MI355X roofline"
 
 # Sources whose text decides each kernel's code: a committed counter summary
 # is used only while their hash matches the one stamped in it.
-PREFILL_SOURCES = ["prefill_mfma.hip", "device_common.h", "attn_internal.h"]
-DECODE_SOURCES = ["decode.hip", "device_common.h", "attn_internal.h"]
+PREFILL_SOURCES = ["prefill_mfma.hip", "mfma_common.h", "device_common.h", "attn_internal.h"]
+DECODE_SOURCES = ["decode.hip", "mfma_common.h", "device_common.h", "attn_internal.h"]
 PREFILL_TAG = "prefill_mfma_bf16_causal_B4H32L4096D128"
 DECODE_TAG = "decode_splitk_f16_B64H32_cache8192D128"
 
