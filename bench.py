@@ -46,11 +46,36 @@ PREFILL_TAG = "prefill_mfma_bf16_causal_B4H32L4096D128"
 DECODE_TAG = "decode_splitk_f16_B64H32_cache8192D128"
 
 
+def code_text(src: str) -> str:
+    """C/C++ source with comments removed and whitespace runs collapsed, so
+    that comment and layout edits do not change a kernel's source hash."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":                      # string or character literal, copied whole
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash(names) -> str:
     h = hashlib.sha256()
     for n in names:
-        with open(os.path.join(ROOT, "scaled_dot_product_flash_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "scaled_dot_product_flash_amd", "csrc", n)) as f:
+            h.update(code_text(f.read()).encode())
     return h.hexdigest()[:16]
 
 

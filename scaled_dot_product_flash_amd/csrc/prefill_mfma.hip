@@ -193,7 +193,8 @@ prefill_mfma_kernel(
     const int Dt = kVar ? p.D : D;
     // K/V columns per row: a head dim that is not a multiple of 8 reads
     // copies padded to one (zeros past Dt), staged into the workspace first;
-    // its Q rows are then read and O rows written per element.
+    // its Q rows are then read and O rows written without 16-byte accesses
+    // (see the row staging below).
     const int Dkv = kVar ? (p.D + 7) & ~7 : D;
     const bool elem = kVar && (p.D & 7) != 0;
     constexpr int NT = D / 16;   // 16-wide d-steps of the score product
@@ -1079,7 +1080,7 @@ bool prefill_mfma_supported(const Params& p, DType dt) {
     if (p.D < 1 || p.D > 256) return false;
     const bool staged = p.D % 8 != 0;
     // 16-byte loads of Q/K/V rows and 8-byte stores of O need aligned rows;
-    // a staged problem reads Q and writes O per element and reads K/V from
+    // a staged problem reads Q and writes O in 2-byte elements and reads K/V from
     // its aligned copies.
     auto al = [](const void* ptr, const Strides& st, int a) {
         return reinterpret_cast<uintptr_t>(ptr) % (2 * a) == 0 && st.sb % a == 0 &&

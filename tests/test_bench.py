@@ -100,3 +100,13 @@ def test_visible_flops_causal_square():
     case = synth.generate(spec)
     pairs = 8 * 9 // 2
     assert bench.visible_flops(case) == 4.0 * spec.head_dim * 2 * pairs
+
+
+def test_source_hash_ignores_comments_only():
+    """Counter summaries are keyed to the kernels' code: comment and layout
+    edits keep the hash, a changed token or string literal does not."""
+    a = 'int f(int x) { // add one\n  return x + 1; /* done */ }\nconst char* s = "a // b";\n'
+    b = 'int f(int x) {\n    return x + 1;\n}\n// trailing note\nconst char* s = "a // b";'
+    assert bench.code_text(a) == bench.code_text(b)
+    assert bench.code_text(a) != bench.code_text(a.replace("x + 1", "x + 2"))
+    assert bench.code_text(a) != bench.code_text(a.replace('"a // b"', '"a / b"'))
