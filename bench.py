@@ -515,7 +515,9 @@ def _counter_means(dirs, match: str):
 
 def summarize(args):
     """Write a profiles/ summary from rocprofv3 CSV output directories."""
-    srcs = {"prefill": PREFILL_SOURCES, "decode": DECODE_SOURCES}.get(args.sources)
+    all_srcs = sorted(f for f in os.listdir(os.path.join(ROOT, "scaled_dot_product_flash_amd", "csrc"))
+                      if f.endswith((".hip", ".h", ".cpp")))
+    srcs = {"prefill": PREFILL_SOURCES, "decode": DECODE_SOURCES, "all": all_srcs}.get(args.sources)
     lines = ["# " + t for t in args.title]
     lines += ["#", "# Commands (from the repository root, TMPDIR=/tmp):"]
     lines += ["#   " + c for c in args.command]
@@ -526,10 +528,10 @@ def summarize(args):
     if args.kind == "stats":
         rows = list(_csv_rows(args.dirs, "kernel_stats.csv"))
         rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
-        lines += ["#", "# %-70s %7s %12s %7s" % ("kernel", "calls", "avg us", "% time")]
-        for r in rows[:12]:
-            lines.append("# %-70s %7s %12.2f %7.2f" % (
-                r["Name"].replace("void sdpa::(anonymous namespace)::", "")[:70], r["Calls"],
+        lines += ["#", "# %-96s %7s %12s %7s" % ("kernel", "calls", "avg us", "% time")]
+        for r in rows[:40]:
+            lines.append("# %-96s %7s %12.2f %7.2f" % (
+                r["Name"].replace("void sdpa::(anonymous namespace)::", "")[:96], r["Calls"],
                 float(r["AverageNs"]) / 1e3, float(r["Percentage"])))
         hit = [r for r in rows if args.kernel in r["Name"]]
         if not hit:
@@ -623,7 +625,7 @@ def main():
     g.add_argument("--calib-bytes", type=int, default=1 << 28)
     g.add_argument("--algorithmic-bytes", type=float, default=0.0)
     g.add_argument("--algorithmic-flops", type=float, default=0.0)
-    g.add_argument("--sources", choices=["prefill", "decode", "none"], default="prefill")
+    g.add_argument("--sources", choices=["prefill", "decode", "all", "none"], default="prefill")
     g.add_argument("--title", action="append", default=[])
     g.add_argument("--command", action="append", default=[])
     g.add_argument("--note", action="append", default=[])
