@@ -223,6 +223,7 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(Params p, int n_hgr
 
     const int lane = threadIdx.x;
     const int wave = blockIdx.x;
+    const int Dt = p.D;              // true head dim (<= D, the padded one)
     const int per_b = p.Hkv * n_hgrp;            // units per batch entry
     const int64_t S = steps_before(p, p.B, per_b);
     const int64_t W = share_waves(S);
@@ -296,9 +297,14 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(Params p, int n_hgr
         const uint16_t* src = static_cast<const uint16_t*>(p.q) + b * p.qs.sb + h * p.qs.sh + 8 * q4;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            i16x8 v = *reinterpret_cast<const i16x8*>(src + 32 * t);
-            if (k_chan) {   // q_d * k_scale[g, d], rounded to the element type
-                const float* ks = p.k_scale + g * D + 32 * t + 8 * q4;
+            // Columns past the true head dim (a multiple of 8) are zero: the
+            // load is unconditional (from the row's first chunk there) and
+            // its value replaced, so no load waits behind a branch.
+            const bool cin = 32 * t + 8 * q4 < Dt;
+            const i16x8 raw = *reinterpret_cast<const i16x8*>(src + (cin ? 32 * t : -8 * q4));
+            i16x8 v = cin ? raw : i16x8{};
+            if (k_chan && cin) {   // q_d * k_scale[g, d], rounded to the element type
+                const float* ks = p.k_scale + g * Dt + 32 * t + 8 * q4;
                 const uint4 u = __builtin_bit_cast(uint4, v);
                 const uint32_t in[4] = {u.x, u.y, u.z, u.w};
                 uint32_t w[4];
@@ -359,11 +365,15 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(Params p, int n_hgr
         const __amdgpu_buffer_rsrc_t krs = make_rsrc(kg, lr.n * p.ks.sr * kEs);
         const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vg, lr.n * p.vs.sr * kEs);
         const int j0 = static_cast<int>(fls) * kStep + ld_row;
+        // Padded columns load as zeros: their lanes' offsets start 2^31 bytes
+        // past any row (one select per step, so every load stays one
+        // unconditional instruction).
+        const uint32_t col_off = ld_col < Dt ? static_cast<uint32_t>(ld_col * kEs) : 0x80000000u;
 #pragma unroll
         for (int n = 0; n < kLd; ++n) {
             const int key = j0 + n * kRpl;
-            kst[n] = load16_stream(krs, (key * static_cast<int>(p.ks.sr) + ld_col) * kEs);
-            vst[n] = load16_stream(vrs, (key * static_cast<int>(p.vs.sr) + ld_col) * kEs);
+            kst[n] = load16_stream(krs, static_cast<int>(static_cast<uint32_t>(key * static_cast<int>(p.ks.sr) * kEs) + col_off));
+            vst[n] = load16_stream(vrs, static_cast<int>(static_cast<uint32_t>(key * static_cast<int>(p.vs.sr) * kEs) + col_off));
         }
     };
 
@@ -628,9 +638,9 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(Params p, int n_hgr
 #pragma unroll
     for (int cc = 0; cc < NPL; ++cc) {
         const int d = lane + 64 * cc;
-        if (d < D) {
+        if (d < p.D) {   // columns past the true head dim are padding
             // An int8 V scale factors out of the sum over keys.
-            const float vsc = !p.kv_int8 ? 1.f : (p.v_quant == 1 ? p.v_scale[0] : p.v_scale[g * D + d]);
+            const float vsc = !p.kv_int8 ? 1.f : (p.v_quant == 1 ? p.v_scale[0] : p.v_scale[g * p.D + d]);
             const float o = empty ? (p.masked_zero ? 0.f : __builtin_nanf("")) : A[cc] * vsc * inv;
             Elem<T>::store(p.o, orow + d, o);
         }
@@ -668,17 +678,23 @@ hipError_t launch_one(const Params& p, hipStream_t s) {
 
 }  // namespace
 
+// The kernel's head dim for a true head dim D: 64 or 128, columns past D
+// padded with zeros (loaded as zeros, never stored).
+int decode_padded_dim(int D) { return D <= 64 ? 64 : 128; }
+
 // U + W - 1 record slots of min(G, 16) heads each (U = units, W = waves).
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int D) {
     const int group = Hq / Hkv;
     const int64_t units = static_cast<int64_t>(B) * Hkv * slice_count(group);
-    return static_cast<size_t>(units + kWavesTotal) * heads_per_slot(group) * rec_stride(D) *
-           sizeof(float);
+    return static_cast<size_t>(units + kWavesTotal) * heads_per_slot(group) *
+           rec_stride(decode_padded_dim(D)) * sizeof(float);
 }
 
 bool decode_split_supported(const Params& p, DType dt) {
     if (dt != DType::BF16 && dt != DType::F16) return false;
-    if (p.D != 64 && p.D != 128) return false;
+    // Head dims that are whole 16-byte chunks (whole 16-value chunks for an
+    // int8 cache) up to 128, run at 64 or 128.
+    if (p.D < 8 || p.D > 128 || p.D % (p.kv_int8 ? 16 : 8) != 0) return false;
     if (p.Lq != 1 || p.Lk == 0) return false;
     // Buffer offsets of one (b, kv head) slice are 32-bit, including the
     // up-to-one-step overrun past the live length.
@@ -701,8 +717,9 @@ bool decode_split_supported(const Params& p, DType dt) {
 }
 
 hipError_t launch_decode_split(const Params& p, DType dt, hipStream_t s) {
-    if (dt == DType::BF16) return p.D == 128 ? launch_one<true, 128>(p, s) : launch_one<true, 64>(p, s);
-    return p.D == 128 ? launch_one<false, 128>(p, s) : launch_one<false, 64>(p, s);
+    const bool d128 = decode_padded_dim(p.D) == 128;
+    if (dt == DType::BF16) return d128 ? launch_one<true, 128>(p, s) : launch_one<true, 64>(p, s);
+    return d128 ? launch_one<false, 128>(p, s) : launch_one<false, 64>(p, s);
 }
 
 }  // namespace sdpa

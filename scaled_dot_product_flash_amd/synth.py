@@ -143,6 +143,9 @@ D100_BF16 = CAUSAL_GQA_BF16.replace(
     name="bf16 causal GQA prefill B4 H32/8 L4096 D100", head_dim=100, seed=15)
 D96_F32 = CAUSAL_GQA_BF16.replace(
     name="fp32 causal GQA prefill B4 H32/8 L4096 D96", dtype="f32", head_dim=96, seed=16)
+# Decode at a head dim below 128 (run padded to 128 by the split decode path).
+DECODE_D96_F16 = DECODE_F16.replace(name="fp16 decode B64 H32/8 cache8192 D96", head_dim=96,
+                                    seed=17)
 
 # Workloads of the extensions beyond the five (measured and tested the same way).
 EXTRA_WORKLOADS = {
@@ -157,6 +160,7 @@ EXTRA_WORKLOADS = {
     "d96_bf16": D96_BF16,
     "d100_bf16": D100_BF16,
     "d96_f32": D96_F32,
+    "decode_d96_f16": DECODE_D96_F16,
 }
 
 # The model shapes the OneGPU "Attention" page times (its "Performance"

@@ -279,3 +279,33 @@ def test_int8_cache_is_decode_only_and_checked():
         p = _problem(**bad)
         assert lib.attn_forward(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, None, None, None,
                                 0, None) == sdpa.ERR_INVALID
+
+
+@pytest.mark.parametrize("D,int8,split", [(96, 0, True), (40, 0, True), (8, 0, True),
+                                         (112, 1, True), (48, 1, True), (24, 1, False),
+                                         (100, 0, False), (136, 0, False)])
+def test_decode_split_head_dims(D, int8, split):
+    """Head dims that are whole 16-byte chunks (16-value chunks for an int8
+    cache) up to 128 take the split decode path, padded to 64 or 128: its
+    workspace holds padded records.  Others fall back to the forward path,
+    or are unsupported with an int8 cache."""
+    lib = sdpa.load_library()
+    B, Hq, Hkv, Lk = 3, 8, 2, 1000
+    kw = dict(batch=B, q_heads=Hq, kv_heads=Hkv, q_len=1, k_len=Lk, head_dim=D,
+              dtype=sdpa.DTYPE_F16)
+    if int8:
+        kw.update(kv_int8=1, k_quant=1, v_quant=1, k_scale=0x1000, v_scale=0x1000)
+    p = _problem(**kw)
+    for lay, H, L in (("q", Hq, 1), ("k", Hkv, Lk), ("v", Hkv, Lk), ("o", Hq, 1)):
+        setattr(p, lay, sdpa.Layout(0, L * H * D, D, H * D))
+    need = sdpa.workspace_size(p, sdpa.OP_DECODE)
+    dp = 64 if D <= 64 else 128
+    split_bytes = (B * Hkv + 2048) * (Hq // Hkv) * (dp + 4) * 4
+    if split:
+        assert need >= split_bytes
+    elif int8:
+        rc = lib.attn_decode(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, None, None, FAKE,
+                             1 << 30, None)
+        assert rc == sdpa.ERR_UNSUPPORTED and b"multiple of 16" in lib.attn_last_error()
+    else:
+        assert need != split_bytes

@@ -376,6 +376,11 @@ DECODE = [
     ("bf16", 5, 8, 8, 700, 64, [700, 1, 128, 129, 0]),
     ("f16", 3, 32, 1, 513, 128, [513, 256, 255]),
     ("bf16", 2, 6, 2, 9000, 128, [9000, 4097]),
+    # head dims below 128 that are whole 16-byte chunks run padded to 64/128
+    ("f16", 4, 16, 4, 600, 96, [600, 1, 300, 0]),
+    ("bf16", 3, 8, 2, 500, 40, [500, 17, 250]),
+    ("f16", 2, 4, 4, 300, 8, [300, 33]),
+    ("bf16", 2, 32, 8, 1000, 112, [1000, 999]),
 ]
 
 
@@ -621,6 +626,12 @@ INT8 = {
     "i8_channel_lens0_mask": synth.DECODE_F16.replace(
         batch=8, k_len=600, kv_quant="channel", lens="cross", lens_zero_at=2, lens_full_at=3,
         mask="keys", mask_all_at=5, seed=34),
+    # padded head dims (multiples of 16 below 128): per-channel scales indexed by the true dim
+    "i8_channel_D96": synth.DECODE_F16.replace(batch=6, k_len=800, head_dim=96,
+                                               kv_quant="channel", seed=35),
+    "i8_tensor_bf16_D48": synth.DECODE_F16.replace(dtype="bf16", batch=5, k_len=500, head_dim=48,
+                                                   kv_quant="mixed", lens="cross", lens_zero_at=1,
+                                                   lens_full_at=0, seed=36),
 }
 
 
@@ -633,6 +644,16 @@ def test_int8_cache_decode(name, policy):
     assert sdpa.last_kernel() == "decode_splitk_int8"
     ro, rl = pu.run_oracle(case, policy)
     pu.compare(o, ro, lse, rl, spec.dtype, policy, what=name)
+
+
+def test_decode_d96_full_size_every_row():
+    """Decode at head dim 96 (padded to 128 on the split path) at full size."""
+    spec = synth.EXTRA_WORKLOADS["decode_d96_f16"]
+    case = synth.generate(spec)
+    o, lse, _ = pu.run_hip(case, "nan", return_lse=True)
+    assert sdpa.last_kernel() == "decode_splitk"
+    ro, rl = pu.run_oracle(case, "nan")
+    pu.compare(o, ro, lse, rl, spec.dtype, "nan", what=spec.name)
 
 
 def test_int8_cache_decode_full_size_every_row():
