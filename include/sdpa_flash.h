@@ -155,7 +155,7 @@ typedef struct attn_problem {
      * ATTN_QUANT_PER_TENSOR uses scale[0], ATTN_QUANT_PER_CHANNEL uses
      * scale[g * head_dim + d] for kv head g.  k_scale / v_scale are device
      * pointers.  Only attn_decode runs int8 caches (fp16 or bf16 Q/O,
-     * head_dim a multiple of 16 up to 128; K/V rows and strides 16-byte
+     * head_dim a multiple of 16 up to 256; K/V rows and strides 16-byte
      * aligned); other problems return ATTN_ERR_UNSUPPORTED.                   */
     int32_t kv_int8;
     int32_t k_quant;

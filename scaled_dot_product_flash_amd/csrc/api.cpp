@@ -200,7 +200,7 @@ const char* attn_version(void) { return "sdpa_flash 0.1 (gfx950)"; }
 // Workspace of the split decode path; depends on the shape only.
 size_t decode_split_ws(const attn_problem* p) {
     const bool shape_ok = (p->dtype == ATTN_DTYPE_BF16 || p->dtype == ATTN_DTYPE_F16) &&
-                          p->head_dim >= 8 && p->head_dim <= 128 &&
+                          p->head_dim >= 8 && p->head_dim <= 256 &&
                           p->head_dim % (p->kv_int8 ? 16 : 8) == 0 && p->q_len == 1 &&
                           p->k_len > 0;
     return shape_ok ? sdpa::decode_workspace_bytes(p->batch, p->q_heads, p->kv_heads, p->head_dim)
@@ -324,7 +324,7 @@ attn_status attn_decode(const attn_problem* p, const void* q, const void* k, con
     }
     if (p->kv_int8)
         return fail(ATTN_ERR_UNSUPPORTED, "int8 cache decode needs fp16/bf16, a head_dim that is "
-                                          "a multiple of 16 up to 128 and 16-byte aligned K/V rows");
+                                          "a multiple of 16 up to 256 and 16-byte aligned K/V rows");
     return attn_forward(p, q, k, v, o, mask, key_lens, lse, workspace, workspace_bytes, stream);
 }
 

@@ -61,7 +61,10 @@ using namespace mfma;
 
 constexpr int kStep = 32;          // keys per wave step (two 16-key MFMA blocks)
 
-constexpr int kWavesTotal = 2048;  // persistent waves: 8 per CU on 256 CUs
+// Persistent waves for padded head dim DP: eight per CU on 256 CUs up to
+// 128; four at 256, whose LDS rows are twice as long (the bytes in flight
+// per CU stay the same).
+__host__ __device__ constexpr int waves_total(int DP) { return DP > 128 ? 1024 : 2048; }
 constexpr float kSlack = 8.f;      // lazy-rescale threshold, base-2 units
 
 // Wave-private LDS rows.  K rows are read 16 lanes x 16 bytes down one column
@@ -197,8 +200,8 @@ __device__ int64_t steps_before(const Params& p, int b, int per_b_units) {
 }
 
 // Waves that share S steps: every wave gets at least one.
-__device__ __forceinline__ int64_t share_waves(int64_t S) {
-    return S < kWavesTotal ? S : kWavesTotal;
+__device__ __forceinline__ int64_t share_waves(int64_t S, int DP) {
+    return S < waves_total(DP) ? S : waves_total(DP);
 }
 
 // Wave that owns flattened step x when S steps are cut into W equal shares
@@ -226,7 +229,7 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(Params p, int n_hgr
     const int Dt = p.D;              // true head dim (<= D, the padded one)
     const int per_b = p.Hkv * n_hgrp;            // units per batch entry
     const int64_t S = steps_before(p, p.B, per_b);
-    const int64_t W = share_waves(S);
+    const int64_t W = share_waves(S, D);
     if (wave >= W) return;
     const int64_t a = S * wave / W, e = S * (wave + 1) / W;
     if (a >= e) return;
@@ -550,7 +553,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(Params p, int n_hgr
 #pragma unroll
     for (int cc = 0; cc < NPL; ++cc) A[cc] = 0.f;
     if (sb > 0) {
-        const int64_t W = share_waves(S);
+        const int64_t W = share_waves(S, D);
         const int w_lo = owner_wave(first, S, W), w_hi = owner_wave(first + sb - 1, S, W);
         const int n = w_hi - w_lo + 1;
         const int rs = rec_stride(D);
@@ -655,7 +658,7 @@ int heads_per_slot(int group) { return group < 16 ? group : 16; }
 template <bool kBf16, int D>
 hipError_t launch_one(const Params& p, hipStream_t s) {
     const int n_hgrp = slice_count(p.group), hs = heads_per_slot(p.group);
-    const dim3 g(kWavesTotal), blk(64);
+    const dim3 g(waves_total(D)), blk(64);
     const bool cap = p.softcap > 0.f;
     if (p.kv_int8 && cap)
         hipLaunchKernelGGL((decode_split_kernel<kBf16, D, true, true>), g, blk, 0, s, p, n_hgrp, hs);
@@ -678,23 +681,24 @@ hipError_t launch_one(const Params& p, hipStream_t s) {
 
 }  // namespace
 
-// The kernel's head dim for a true head dim D: 64 or 128, columns past D
-// padded with zeros (loaded as zeros, never stored).
-int decode_padded_dim(int D) { return D <= 64 ? 64 : 128; }
+// The kernel's head dim for a true head dim D: 64, 128 or 256, columns past
+// D padded with zeros (loaded as zeros, never stored).
+int decode_padded_dim(int D) { return D <= 64 ? 64 : (D <= 128 ? 128 : 256); }
 
 // U + W - 1 record slots of min(G, 16) heads each (U = units, W = waves).
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int D) {
     const int group = Hq / Hkv;
     const int64_t units = static_cast<int64_t>(B) * Hkv * slice_count(group);
-    return static_cast<size_t>(units + kWavesTotal) * heads_per_slot(group) *
-           rec_stride(decode_padded_dim(D)) * sizeof(float);
+    const int DP = decode_padded_dim(D);
+    return static_cast<size_t>(units + waves_total(DP)) * heads_per_slot(group) * rec_stride(DP) *
+           sizeof(float);
 }
 
 bool decode_split_supported(const Params& p, DType dt) {
     if (dt != DType::BF16 && dt != DType::F16) return false;
     // Head dims that are whole 16-byte chunks (whole 16-value chunks for an
-    // int8 cache) up to 128, run at 64 or 128.
-    if (p.D < 8 || p.D > 128 || p.D % (p.kv_int8 ? 16 : 8) != 0) return false;
+    // int8 cache) up to 256, run at 64, 128 or 256.
+    if (p.D < 8 || p.D > 256 || p.D % (p.kv_int8 ? 16 : 8) != 0) return false;
     if (p.Lq != 1 || p.Lk == 0) return false;
     // Buffer offsets of one (b, kv head) slice are 32-bit, including the
     // up-to-one-step overrun past the live length.
@@ -717,9 +721,12 @@ bool decode_split_supported(const Params& p, DType dt) {
 }
 
 hipError_t launch_decode_split(const Params& p, DType dt, hipStream_t s) {
-    const bool d128 = decode_padded_dim(p.D) == 128;
-    if (dt == DType::BF16) return d128 ? launch_one<true, 128>(p, s) : launch_one<true, 64>(p, s);
-    return d128 ? launch_one<false, 128>(p, s) : launch_one<false, 64>(p, s);
+    const int DP = decode_padded_dim(p.D);
+    if (dt == DType::BF16)
+        return DP == 64 ? launch_one<true, 64>(p, s)
+                        : (DP == 128 ? launch_one<true, 128>(p, s) : launch_one<true, 256>(p, s));
+    return DP == 64 ? launch_one<false, 64>(p, s)
+                    : (DP == 128 ? launch_one<false, 128>(p, s) : launch_one<false, 256>(p, s));
 }
 
 }  // namespace sdpa

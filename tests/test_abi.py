@@ -196,14 +196,14 @@ def test_decode_workspace_is_checked_before_launch():
 
 
 def test_decode_workspace_covers_the_forward_fallback():
-    """A decode shape the split decode path does not take (head dim 256) runs
-    as a forward call, whose few query blocks split the keys: the decode
-    workspace size covers that call."""
+    """A decode shape the split decode path does not take (head dim 250, not
+    whole 16-byte chunks) runs as a forward call, whose few query blocks split
+    the keys and whose K/V are staged: the decode workspace covers that call."""
     lib = sdpa.load_library()
-    p = _problem(batch=2, q_heads=12, kv_heads=3, q_len=1, k_len=681, head_dim=256,
+    p = _problem(batch=2, q_heads=12, kv_heads=3, q_len=1, k_len=681, head_dim=250,
                  dtype=sdpa.DTYPE_BF16, causal=1)
     for lay, H, L in (("q", 12, 1), ("k", 3, 681), ("v", 3, 681), ("o", 12, 1)):
-        setattr(p, lay, sdpa.Layout(0, L * H * 256, 256, H * 256))
+        setattr(p, lay, sdpa.Layout(0, L * H * 250, 250, H * 250))
     fwd = sdpa.workspace_size(p, sdpa.OP_FORWARD)
     assert fwd > 0
     assert sdpa.workspace_size(p, sdpa.OP_DECODE) >= fwd
@@ -282,13 +282,15 @@ def test_int8_cache_is_decode_only_and_checked():
 
 
 @pytest.mark.parametrize("D,int8,split", [(96, 0, True), (40, 0, True), (8, 0, True),
-                                         (112, 1, True), (48, 1, True), (24, 1, False),
-                                         (100, 0, False), (136, 0, False)])
+                                         (136, 0, True), (256, 0, True), (112, 1, True),
+                                         (48, 1, True), (208, 1, True), (24, 1, False),
+                                         (100, 0, False), (250, 0, False)])
 def test_decode_split_head_dims(D, int8, split):
     """Head dims that are whole 16-byte chunks (16-value chunks for an int8
-    cache) up to 128 take the split decode path, padded to 64 or 128: its
-    workspace holds padded records.  Others fall back to the forward path,
-    or are unsupported with an int8 cache."""
+    cache) up to 256 take the split decode path, padded to 64, 128 or 256
+    (1024 waves instead of 2048 at 256): its workspace holds padded records.
+    Others fall back to the forward path, or are unsupported with an int8
+    cache."""
     lib = sdpa.load_library()
     B, Hq, Hkv, Lk = 3, 8, 2, 1000
     kw = dict(batch=B, q_heads=Hq, kv_heads=Hkv, q_len=1, k_len=Lk, head_dim=D,
@@ -299,8 +301,8 @@ def test_decode_split_head_dims(D, int8, split):
     for lay, H, L in (("q", Hq, 1), ("k", Hkv, Lk), ("v", Hkv, Lk), ("o", Hq, 1)):
         setattr(p, lay, sdpa.Layout(0, L * H * D, D, H * D))
     need = sdpa.workspace_size(p, sdpa.OP_DECODE)
-    dp = 64 if D <= 64 else 128
-    split_bytes = (B * Hkv + 2048) * (Hq // Hkv) * (dp + 4) * 4
+    dp = 64 if D <= 64 else (128 if D <= 128 else 256)
+    split_bytes = (B * Hkv + (1024 if dp == 256 else 2048)) * (Hq // Hkv) * (dp + 4) * 4
     if split:
         assert need >= split_bytes
     elif int8:

@@ -381,6 +381,8 @@ DECODE = [
     ("bf16", 3, 8, 2, 500, 40, [500, 17, 250]),
     ("f16", 2, 4, 4, 300, 8, [300, 33]),
     ("bf16", 2, 32, 8, 1000, 112, [1000, 999]),
+    ("f16", 3, 8, 4, 700, 256, [700, 64, 333]),
+    ("bf16", 2, 16, 2, 400, 200, [400, 1]),
 ]
 
 
@@ -632,6 +634,9 @@ INT8 = {
     "i8_tensor_bf16_D48": synth.DECODE_F16.replace(dtype="bf16", batch=5, k_len=500, head_dim=48,
                                                    kv_quant="mixed", lens="cross", lens_zero_at=1,
                                                    lens_full_at=0, seed=36),
+    "i8_channel_D256_window": synth.DECODE_F16.replace(batch=4, k_len=900, head_dim=256,
+                                                       kv_quant="channel", local_window=500,
+                                                       seed=37),
 }
 
 
