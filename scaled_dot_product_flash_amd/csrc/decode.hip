@@ -61,10 +61,14 @@ using namespace mfma;
 
 constexpr int kStep = 32;          // keys per wave step (two 16-key MFMA blocks)
 
-// Persistent waves for padded head dim DP: eight per CU on 256 CUs up to
-// 128; four at 256, whose LDS rows are twice as long (the bytes in flight
-// per CU stay the same).
-__host__ __device__ constexpr int waves_total(int DP) { return DP > 128 ? 1024 : 2048; }
+// Persistent waves (256 CUs) for padded head dim DP and cache type, the
+// fastest of 1024 / 1536 / 2048 measured on each: four per CU for 16-bit
+// caches at 128 and 256 (at 256 the LDS rows are twice as long), eight for
+// 64 and for int8 caches, whose steps carry fewer bytes.
+__host__ __device__ constexpr int waves_total(int DP, bool i8) {
+    return DP > 128 || (DP == 128 && !i8) ? 1024 : 2048;
+}
+constexpr int kWavesMax = 2048;
 constexpr float kSlack = 8.f;      // lazy-rescale threshold, base-2 units
 
 // Wave-private LDS rows.  K rows are read 16 lanes x 16 bytes down one column
@@ -200,8 +204,8 @@ __device__ int64_t steps_before(const Params& p, int b, int per_b_units) {
 }
 
 // Waves that share S steps: every wave gets at least one.
-__device__ __forceinline__ int64_t share_waves(int64_t S, int DP) {
-    return S < waves_total(DP) ? S : waves_total(DP);
+__device__ __forceinline__ int64_t share_waves(int64_t S, int DP, bool i8) {
+    return S < waves_total(DP, i8) ? S : waves_total(DP, i8);
 }
 
 // Wave that owns flattened step x when S steps are cut into W equal shares
@@ -229,7 +233,7 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(Params p, int n_hgr
     const int Dt = p.D;              // true head dim (<= D, the padded one)
     const int per_b = p.Hkv * n_hgrp;            // units per batch entry
     const int64_t S = steps_before(p, p.B, per_b);
-    const int64_t W = share_waves(S, D);
+    const int64_t W = share_waves(S, D, kI8);
     if (wave >= W) return;
     const int64_t a = S * wave / W, e = S * (wave + 1) / W;
     if (a >= e) return;
@@ -553,7 +557,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(Params p, int n_hgr
 #pragma unroll
     for (int cc = 0; cc < NPL; ++cc) A[cc] = 0.f;
     if (sb > 0) {
-        const int64_t W = share_waves(S, D);
+        const int64_t W = share_waves(S, D, p.kv_int8 != 0);
         const int w_lo = owner_wave(first, S, W), w_hi = owner_wave(first + sb - 1, S, W);
         const int n = w_hi - w_lo + 1;
         const int rs = rec_stride(D);
@@ -658,7 +662,7 @@ int heads_per_slot(int group) { return group < 16 ? group : 16; }
 template <bool kBf16, int D>
 hipError_t launch_one(const Params& p, hipStream_t s) {
     const int n_hgrp = slice_count(p.group), hs = heads_per_slot(p.group);
-    const dim3 g(waves_total(D)), blk(64);
+    const dim3 g(waves_total(D, p.kv_int8 != 0)), blk(64);
     const bool cap = p.softcap > 0.f;
     if (p.kv_int8 && cap)
         hipLaunchKernelGGL((decode_split_kernel<kBf16, D, true, true>), g, blk, 0, s, p, n_hgrp, hs);
@@ -689,8 +693,9 @@ int decode_padded_dim(int D) { return D <= 64 ? 64 : (D <= 128 ? 128 : 256); }
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int D) {
     const int group = Hq / Hkv;
     const int64_t units = static_cast<int64_t>(B) * Hkv * slice_count(group);
+    // Slots for the most waves any cache type uses at this shape.
     const int DP = decode_padded_dim(D);
-    return static_cast<size_t>(units + waves_total(DP)) * heads_per_slot(group) * rec_stride(DP) *
+    return static_cast<size_t>(units + kWavesMax) * heads_per_slot(group) * rec_stride(DP) *
            sizeof(float);
 }
 

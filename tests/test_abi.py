@@ -287,10 +287,9 @@ def test_int8_cache_is_decode_only_and_checked():
                                          (100, 0, False), (250, 0, False)])
 def test_decode_split_head_dims(D, int8, split):
     """Head dims that are whole 16-byte chunks (16-value chunks for an int8
-    cache) up to 256 take the split decode path, padded to 64, 128 or 256
-    (1024 waves instead of 2048 at 256): its workspace holds padded records.
-    Others fall back to the forward path, or are unsupported with an int8
-    cache."""
+    cache) up to 256 take the split decode path, padded to 64, 128 or 256:
+    its workspace holds padded records for up to 2048 waves.  Others fall
+    back to the forward path, or are unsupported with an int8 cache."""
     lib = sdpa.load_library()
     B, Hq, Hkv, Lk = 3, 8, 2, 1000
     kw = dict(batch=B, q_heads=Hq, kv_heads=Hkv, q_len=1, k_len=Lk, head_dim=D,
@@ -302,7 +301,7 @@ def test_decode_split_head_dims(D, int8, split):
         setattr(p, lay, sdpa.Layout(0, L * H * D, D, H * D))
     need = sdpa.workspace_size(p, sdpa.OP_DECODE)
     dp = 64 if D <= 64 else (128 if D <= 128 else 256)
-    split_bytes = (B * Hkv + (1024 if dp == 256 else 2048)) * (Hq // Hkv) * (dp + 4) * 4
+    split_bytes = (B * Hkv + 2048) * (Hq // Hkv) * (dp + 4) * 4
     if split:
         assert need >= split_bytes
     elif int8:
