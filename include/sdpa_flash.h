@@ -208,13 +208,17 @@ attn_status attn_forward(const attn_problem* p, const void* q, const void* k, co
  * GroupQueryAttention README, split-K decode variants and BNSH caches).
  * Same arguments and semantics as attn_forward, with p->q_len == 1 and
  * p->k_len the cache capacity; key_lens gives the live length of each batch
- * entry.  The live keys of all (batch entry, kv head) pairs are cut, on the
- * device from key_lens, into equal contiguous shares over a fixed set of
- * waves; each share's partial (max, sum, accumulator) goes to the workspace
- * (whose size depends on the shape only) and a second kernel merges a row's
- * partials in key order.  Shapes or buffers that path does not take (head
- * dims other than 64 and 128, fp32, unaligned rows) run as attn_forward
- * would; attn_workspace_size(p, ATTN_OP_DECODE) covers both.
+ * entry.  Two modes, chosen from the shape: for large calls the live keys of
+ * all (batch entry, kv head) pairs are cut, on the device from key_lens, into
+ * equal contiguous shares over a fixed set of waves; each share's partial
+ * (max, sum, accumulator) goes to the workspace (whose size depends on the
+ * shape only) and a second kernel merges a row's partials in key order.  For
+ * small calls (a few 32-key steps per wave) one workgroup takes each (batch
+ * entry, kv head) pair, folds its waves' partials in key order on chip and
+ * writes the outputs; the workspace is then unused.  Shapes or buffers that
+ * neither mode takes (fp32, head dims that are not whole 16-byte chunks up to
+ * 256, unaligned rows) run as attn_forward would;
+ * attn_workspace_size(p, ATTN_OP_DECODE) covers every case.
  */
 attn_status attn_decode(const attn_problem* p, const void* q, const void* k, const void* v,
                         void* o, const float* mask, const int32_t* key_lens, float* lse,
@@ -249,8 +253,11 @@ attn_status attn_workspace_size(const attn_problem* p, int32_t op, size_t* bytes
 const char* attn_last_error(void);
 
 /* Name of the kernel family the last successful call on this thread launched
- * ("prefill_mfma", "prefill_f32", "decode_splitk", "generic", or "" when the
- * call had no work).  For tests and profiling; the string is static.        */
+ * ("prefill_mfma", "prefill_f32", "decode_splitk", "decode_unit" (each with
+ * "_int8" for an int8 cache), "generic", or "" when the call had no work).
+ * For tests and profiling; the string is static.  The environment variable
+ * SDPA_FLASH_KERNEL=generic sends every call to the any-shape kernel, and
+ * =decode_splitk or =decode_unit fixes the decode mode.                    */
 const char* attn_last_kernel(void);
 
 /* Library version string. */

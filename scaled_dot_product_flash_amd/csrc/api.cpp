@@ -319,8 +319,17 @@ attn_status attn_decode(const attn_problem* p, const void* q, const void* k, con
         if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
             return fail(ATTN_ERR_INVALID, "workspace must be 16-byte aligned");
         prm.ws = workspace;
-        g_kernel = p->kv_int8 ? "decode_splitk_int8" : "decode_splitk";
-        return launched(sdpa::launch_decode_split(prm, dt, s));
+        // SDPA_FLASH_KERNEL=decode_unit / decode_splitk picks the mode (tests
+        // run every case through both); by default the shape decides.
+        const char* km = std::getenv("SDPA_FLASH_KERNEL");
+        const bool unit = (km && std::strcmp(km, "decode_unit") == 0)     ? true
+                          : (km && std::strcmp(km, "decode_splitk") == 0) ? false
+                                                                           : sdpa::decode_unit_preferred(prm);
+        if (unit)
+            g_kernel = p->kv_int8 ? "decode_unit_int8" : "decode_unit";
+        else
+            g_kernel = p->kv_int8 ? "decode_splitk_int8" : "decode_splitk";
+        return launched(sdpa::launch_decode_split(prm, dt, s, unit));
     }
     if (p->kv_int8)
         return fail(ATTN_ERR_UNSUPPORTED, "int8 cache decode needs fp16/bf16, a head_dim that is "

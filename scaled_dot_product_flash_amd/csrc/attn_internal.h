@@ -67,7 +67,10 @@ size_t prefill_mfma_stage_bytes(int B, int Hkv, int Lk, int D);
 bool prefill_mfma_supported(const Params& p, DType dt);
 bool decode_split_supported(const Params& p, DType dt);
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int D);
-hipError_t launch_decode_split(const Params& p, DType dt, hipStream_t s);
+// unit: one workgroup per (entry, kv head, head slice), no workspace and no
+// merge; otherwise the split over equal shares of all steps plus the merge.
+bool decode_unit_preferred(const Params& p);
+hipError_t launch_decode_split(const Params& p, DType dt, hipStream_t s, bool unit);
 
 void prefill_f32_plan(int B, int Hq, int Hkv, int Lq, int Lk, int D, int* split_len,
                       int* n_split);

@@ -24,6 +24,12 @@
 // README, split-K decode variants).  The query row against the cache follows
 // llm.istanbul "05_attention", "attention_decode Farki".
 //
+// Unit mode, for calls too small to need that balance (a few steps per
+// wave): one workgroup per unit, its waves taking equal contiguous shares of
+// the unit's steps; the workgroup folds its waves' partials in LDS in wave
+// order (key order) and writes the outputs, with no workspace records and no
+// merge kernel.  The host picks the mode from the shape.
+//
 // A step: K/V rows are loaded with coalesced 16-byte raw-buffer loads bounded
 // at the unit's live length (zeros past it; rows past the length are never
 // read), marked non-temporal since each byte is read once, and prefetched
@@ -69,6 +75,12 @@ __host__ __device__ constexpr int waves_total(int DP, bool i8) {
     return DP > 128 || (DP == 128 && !i8) ? 1024 : 2048;
 }
 constexpr int kWavesMax = 2048;
+// Unit mode: waves per workgroup at most, for padded head dim DP and cache
+// type (the register budget of a workgroup that size: at 64, four waves per
+// SIMD; at 128 and for int8 rows at 256, two; 16-bit rows at 256, one).
+__host__ __device__ constexpr int unit_waves_max(int DP, bool i8) {
+    return DP == 64 ? 16 : (DP == 128 || i8 ? 8 : 4);
+}
 constexpr float kSlack = 8.f;      // lazy-rescale threshold, base-2 units
 
 // Wave-private LDS rows.  K rows are read 16 lanes x 16 bytes down one column
@@ -214,60 +226,92 @@ __device__ __forceinline__ int owner_wave(int64_t x, int64_t S, int64_t W) {
     return static_cast<int>(((x + 1) * W - 1) / S);
 }
 
-template <bool kBf16, int D, bool kCap, bool kI8>
-__global__ __launch_bounds__(64, 2) void decode_split_kernel(Params p, int n_hgrp, int slot_heads) {
+// LDS bytes per wave of the unit mode: its staging rows, later its records
+// (16 heads x rec_stride floats).
+template <int D, bool kI8>
+__host__ __device__ constexpr int unit_wave_bytes() {
+    constexpr int stage = kI8 ? I8Lay<D>::kWaveBytes : DLay<D>::kWaveBytes;
+    constexpr int recs = 16 * rec_stride(D) * 4;
+    return stage > recs ? stage : recs;
+}
+
+// The decode step loop of one wave.  Split mode (kUnit false): the wave is a
+// workgroup of its own and takes an equal share of all units' steps, writing
+// one record per unit it touches to the workspace.  Unit mode: a workgroup
+// takes one whole unit, its waves equal contiguous shares of that unit's
+// steps, and the workgroup folds its waves' records in LDS (wave order = key
+// order) and writes the outputs itself, with no workspace and no merge
+// kernel.  smem: this workgroup's LDS (one wave's rows in split mode, one
+// unit_wave_bytes() slice per wave in unit mode).
+template <bool kBf16, int D, bool kCap, bool kI8, bool kUnit>
+__device__ __forceinline__ void decode_body(const Params& p, int n_hgrp, int slot_heads,
+                                            uint8_t* smem_base) {
     using M = Mma<kBf16>;
     using LY = DLay<D>;
     constexpr int KS = LY::KS, VS = LY::VS;
     constexpr int NT = D / 32;       // 32-wide d-steps of the score product
     constexpr int ND = D / 16;       // 16-row d-tiles of the output
     using L8 = I8Lay<D>;
-    __shared__ __attribute__((aligned(16))) uint8_t smem[kI8 ? L8::kWaveBytes : LY::kWaveBytes];
+
+    const int lane = kUnit ? static_cast<int>(threadIdx.x & 63) : static_cast<int>(threadIdx.x);
+    const int wave = kUnit ? uniform32(threadIdx.x >> 6) : blockIdx.x;
+    uint8_t* const smem = smem_base + (kUnit ? wave * unit_wave_bytes<D, kI8>() : 0);
     uint16_t* const k_sh = reinterpret_cast<uint16_t*>(smem);
     uint16_t* const v_sh = k_sh + kStep * KS;
     uint8_t* const k8 = smem;                         // int8 cache: rows of L8::RS bytes
     uint8_t* const v8 = smem + kStep * L8::RS;
-
-    const int lane = threadIdx.x;
-    const int wave = blockIdx.x;
     const int Dt = p.D;              // true head dim (<= D, the padded one)
     const int per_b = p.Hkv * n_hgrp;            // units per batch entry
-    const int64_t S = steps_before(p, p.B, per_b);
-    const int64_t W = share_waves(S, D, kI8);
-    if (wave >= W) return;
-    const int64_t a = S * wave / W, e = S * (wave + 1) / W;
-    if (a >= e) return;
 
-    // Locate the unit holding step a: 64 entries per round, one per lane;
-    // an inclusive prefix sum over the lanes finds the first entry whose
-    // steps end past a (a < S, so some round finds it).
     int b = 0;
-    int64_t base_b = 0;                          // first step of entry b
     int64_t sb = 0;                              // steps of each unit of entry b
-    for (int b0 = 0; b0 < p.B; b0 += 64) {
-        const int bb = b0 + lane;
-        const int64_t st = bb < p.B ? steps_of_lane(p, bb) : 0;
-        int64_t incl = st * per_b;
+    int uu = 0;                                  // unit within the entry
+    int64_t ls = 0;                              // step within the unit
+    int64_t a = 0, e = 0;                        // this wave's steps, flattened
+    if constexpr (kUnit) {
+        const int nw = uniform32(blockDim.x >> 6);
+        b = static_cast<int>(blockIdx.x / per_b);
+        uu = static_cast<int>(blockIdx.x % per_b);
+        sb = steps_of(p, b);
+        ls = sb * wave / nw;
+        e = sb * (wave + 1) / nw - ls;           // may be 0: the wave still joins the fold
+    } else {
+        const int64_t S = steps_before(p, p.B, per_b);
+        const int64_t W = share_waves(S, D, kI8);
+        if (wave >= W) return;
+        a = S * wave / W;
+        e = S * (wave + 1) / W;
+        if (a >= e) return;
+
+        // Locate the unit holding step a: 64 entries per round, one per lane;
+        // an inclusive prefix sum over the lanes finds the first entry whose
+        // steps end past a (a < S, so some round finds it).
+        int64_t base_b = 0;                      // first step of entry b
+        for (int b0 = 0; b0 < p.B; b0 += 64) {
+            const int bb = b0 + lane;
+            const int64_t st = bb < p.B ? steps_of_lane(p, bb) : 0;
+            int64_t incl = st * per_b;
 #pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const int64_t y = __shfl_up(incl, off, 64);
-            if (lane >= off) incl += y;
+            for (int off = 1; off < 64; off <<= 1) {
+                const int64_t y = __shfl_up(incl, off, 64);
+                if (lane >= off) incl += y;
+            }
+            const uint64_t hit = __builtin_amdgcn_ballot_w64(base_b + incl > a);
+            if (hit) {
+                const int l = __builtin_ctzll(hit);
+                b = b0 + l;
+                sb = uniform64(__shfl(st, l, 64));
+                base_b = uniform64(base_b + __shfl(incl, l, 64) - sb * per_b);
+                break;
+            }
+            base_b = uniform64(base_b + __shfl(incl, 63, 64));
         }
-        const uint64_t hit = __builtin_amdgcn_ballot_w64(base_b + incl > a);
-        if (hit) {
-            const int l = __builtin_ctzll(hit);
-            b = b0 + l;
-            sb = uniform64(__shfl(st, l, 64));
-            base_b = uniform64(base_b + __shfl(incl, l, 64) - sb * per_b);
-            break;
-        }
-        base_b = uniform64(base_b + __shfl(incl, 63, 64));
+        // The scan and steps_before count the same steps, so an entry is always
+        // found; a wave that found none (sb == 0) has nothing to do.
+        if (sb <= 0) return;
+        uu = static_cast<int>((a - base_b) / sb);
+        ls = (a - base_b) % sb;
     }
-    // The scan and steps_before count the same steps, so an entry is always
-    // found; a wave that found none (sb == 0) has nothing to do.
-    if (sb <= 0) return;
-    int uu = static_cast<int>((a - base_b) / sb);   // unit within the entry
-    int64_t ls = (a - base_b) % sb;                 // step within the unit
 
     const int col = lane & 15, q4 = lane >> 4;
     const int ld_row = kI8 ? lane / L8::kRowChunks : lane / LY::kRowChunks;
@@ -385,12 +429,12 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(Params p, int n_hgr
     };
 
     begin_unit();
-    fetch(b, uu, ls);
+    if (!kUnit || a < e) fetch(b, uu, ls);
     for (int64_t x = a; x < e; ++x) {
         // Cursor of step x + 1 (next unit, skipping entries with no live key).
         int nb = b, nuu = uu;
         int64_t nls = ls + 1;
-        if (nls == sb) {
+        if (!kUnit && nls == sb) {
             nls = 0;
             if (++nuu == per_b) {
                 nuu = 0;
@@ -519,7 +563,7 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(Params p, int n_hgr
             }
         }
 
-        if (nb != b || nuu != uu || x + 1 == e) {
+        if (!kUnit && (nb != b || nuu != uu || x + 1 == e)) {
             end_unit();
             if (x + 1 < e) {
                 b = nb;
@@ -530,6 +574,68 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(Params p, int n_hgr
         }
         ls = nls;
     }
+    if constexpr (kUnit) {
+        // Column totals of the running sums, as end_unit.
+        float lt = l_sum + __shfl_xor(l_sum, 16, 64);
+        lt = lt + __shfl_xor(lt, 32, 64);
+        __syncthreads();             // every wave is done with its staging rows
+        constexpr int RS = rec_stride(D);
+        float* const recs = reinterpret_cast<float*>(smem_base);   // [wave][16 heads][RS]
+        float* const rec = recs + (wave * 16 + col) * RS;
+#pragma unroll
+        for (int d = 0; d < ND; ++d) *reinterpret_cast<f32x4*>(rec + 4 + 16 * d + 4 * q4) = acc[d];
+        if (q4 == 0) {
+            rec[0] = m_ref;
+            rec[1] = lt;
+        }
+        __syncthreads();
+        // Fold the waves' records in wave order (= key order), then the sink,
+        // the empty-row policy and the LSE, as the merge kernel does; items
+        // (head, d) with d fastest, so the stores are contiguous.
+        using T = std::conditional_t<kBf16, bf16_t, _Float16>;
+        const int nw = uniform32(blockDim.x >> 6);
+        const int g = uu / n_hgrp, hbase = (uu % n_hgrp) * 16;
+        const int nh = p.group - hbase < 16 ? p.group - hbase : 16;
+        const float ksc = (kI8 && p.k_quant == 1) ? p.k_scale[0] : 1.f;
+        const float cr = p.mask ? kLog2e : p.scale_log2 * ksc;
+        const float to_nat = p.mask ? 1.f : p.scale * ksc;
+        for (int it = threadIdx.x; it < nh * Dt; it += blockDim.x) {
+            const int hc = it / Dt, d = it - hc * Dt;
+            float Mx = kNegInf;
+            for (int w = 0; w < nw; ++w) Mx = fmaxf(Mx, recs[(w * 16 + hc) * RS]);
+            float L = 0.f, A = 0.f;
+            for (int w = 0; w < nw; ++w) {
+                const float* r = recs + (w * 16 + hc) * RS;
+                const float f = (r[0] == kNegInf) ? 0.f : fast_exp2((r[0] - Mx) * cr);
+                L = fmaf(r[1], f, L);
+                A = fmaf(r[4 + d], f, A);
+            }
+            const int h = g * p.group + hbase + hc;
+            float m_nat = Mx * to_nat;
+            const float fs = fold_sink(p, h, m_nat, L);
+            const bool empty = (L == 0.f);
+            const float inv = fs / L;
+            const float vsc = !kI8 ? 1.f : (p.v_quant == 1 ? p.v_scale[0] : p.v_scale[g * Dt + d]);
+            const float o = empty ? (p.masked_zero ? 0.f : __builtin_nanf("")) : A * vsc * inv;
+            Elem<T>::store(p.o, b * p.os.sb + h * p.os.sh + d, o);
+            if (p.lse && d == 0)
+                p.lse[b * p.ls.sb + h * p.ls.sh] = empty ? kNegInf : row_lse(m_nat, L);
+        }
+    }
+}
+
+template <bool kBf16, int D, bool kCap, bool kI8>
+__global__ __launch_bounds__(64, 2) void decode_split_kernel(Params p, int n_hgrp, int slot_heads) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kI8 ? I8Lay<D>::kWaveBytes : DLay<D>::kWaveBytes];
+    decode_body<kBf16, D, kCap, kI8, false>(p, n_hgrp, slot_heads, smem);
+}
+
+// One workgroup per unit; nw = blockDim.x / 64 waves, nw * unit_wave_bytes()
+// bytes of dynamic LDS.
+template <bool kBf16, int D, bool kCap, bool kI8>
+__global__ __launch_bounds__(64 * unit_waves_max(D, kI8)) void decode_unit_kernel(Params p, int n_hgrp) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t dsmem[];
+    decode_body<kBf16, D, kCap, kI8, true>(p, n_hgrp, 0, dsmem);
 }
 
 // One wave per (b, h): merge the records of the waves that covered its unit,
@@ -659,8 +765,39 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(Params p, int n_hgr
 int slice_count(int group) { return (group + 15) / 16; }
 int heads_per_slot(int group) { return group < 16 ? group : 16; }
 
+// Waves per workgroup of the unit mode: one per step of the longest
+// possible unit, at most unit_waves_max.
+int unit_waves(const Params& p, int DP) {
+    const int64_t smax = (static_cast<int64_t>(p.Lk) + kStep - 1) / kStep;
+    const int cap = unit_waves_max(DP, p.kv_int8 != 0);
+    return smax < cap ? static_cast<int>(smax < 1 ? 1 : smax) : cap;
+}
+
 template <bool kBf16, int D>
-hipError_t launch_one(const Params& p, hipStream_t s) {
+hipError_t launch_unit(const Params& p, hipStream_t s) {
+    const int n_hgrp = slice_count(p.group);
+    const int nw = unit_waves(p, D);
+    const dim3 g(static_cast<uint32_t>(static_cast<int64_t>(p.B) * p.Hkv * n_hgrp)), blk(64 * nw);
+    const bool cap = p.softcap > 0.f;
+    if (p.kv_int8) {
+        const size_t lds = static_cast<size_t>(nw) * unit_wave_bytes<D, true>();
+        if (cap)
+            hipLaunchKernelGGL((decode_unit_kernel<kBf16, D, true, true>), g, blk, lds, s, p, n_hgrp);
+        else
+            hipLaunchKernelGGL((decode_unit_kernel<kBf16, D, false, true>), g, blk, lds, s, p, n_hgrp);
+    } else {
+        const size_t lds = static_cast<size_t>(nw) * unit_wave_bytes<D, false>();
+        if (cap)
+            hipLaunchKernelGGL((decode_unit_kernel<kBf16, D, true, false>), g, blk, lds, s, p, n_hgrp);
+        else
+            hipLaunchKernelGGL((decode_unit_kernel<kBf16, D, false, false>), g, blk, lds, s, p, n_hgrp);
+    }
+    return hipGetLastError();
+}
+
+template <bool kBf16, int D>
+hipError_t launch_one(const Params& p, hipStream_t s, bool unit) {
+    if (unit) return launch_unit<kBf16, D>(p, s);
     const int n_hgrp = slice_count(p.group), hs = heads_per_slot(p.group);
     const dim3 g(waves_total(D, p.kv_int8 != 0)), blk(64);
     const bool cap = p.softcap > 0.f;
@@ -725,13 +862,33 @@ bool decode_split_supported(const Params& p, DType dt) {
     return al(p.q, p.qs, 8) && al(p.k, p.ks, 8) && al(p.v, p.vs, 8);
 }
 
-hipError_t launch_decode_split(const Params& p, DType dt, hipStream_t s) {
+// The unit mode saves the merge kernel and the records (about 10 us on small
+// calls) but runs each unit on one workgroup, whose waves walk their steps
+// one HBM round trip after another; the split mode spreads every unit over
+// the whole GPU.  Measured crossovers (one MI355X, full-length caches): the
+// unit mode wins up to 8 steps per wave at head dims 64/128 (16 when at most
+// 256 waves run in all), 4 at 256 with 16-bit rows, 16 with int8 rows, while
+// its workgroups fit in about two rounds on the GPU.
+bool decode_unit_preferred(const Params& p) {
+    const int DP = decode_padded_dim(p.D);
+    const bool i8 = p.kv_int8 != 0;
+    const int64_t smax = (static_cast<int64_t>(p.Lk) + kStep - 1) / kStep;
+    const int nw = unit_waves(p, DP);
+    const int64_t waves = static_cast<int64_t>(p.B) * p.Hkv * slice_count(p.group) * nw;
+    const int64_t per_wave = (smax + nw - 1) / nw;
+    const int64_t limit = i8 ? 16 : (DP == 256 ? 4 : (waves <= 256 ? 16 : 8));
+    return per_wave <= limit && waves <= 4096;
+}
+
+hipError_t launch_decode_split(const Params& p, DType dt, hipStream_t s, bool unit) {
     const int DP = decode_padded_dim(p.D);
     if (dt == DType::BF16)
-        return DP == 64 ? launch_one<true, 64>(p, s)
-                        : (DP == 128 ? launch_one<true, 128>(p, s) : launch_one<true, 256>(p, s));
-    return DP == 64 ? launch_one<false, 64>(p, s)
-                    : (DP == 128 ? launch_one<false, 128>(p, s) : launch_one<false, 256>(p, s));
+        return DP == 64 ? launch_one<true, 64>(p, s, unit)
+                        : (DP == 128 ? launch_one<true, 128>(p, s, unit)
+                                     : launch_one<true, 256>(p, s, unit));
+    return DP == 64 ? launch_one<false, 64>(p, s, unit)
+                    : (DP == 128 ? launch_one<false, 128>(p, s, unit)
+                                 : launch_one<false, 256>(p, s, unit));
 }
 
 }  // namespace sdpa

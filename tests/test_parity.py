@@ -386,18 +386,25 @@ DECODE = [
 ]
 
 
+# The two decode modes: the split over equal shares of all steps with its
+# ordered merge, and one workgroup per unit folding in LDS.
+DECODE_MODES = ["decode_splitk", "decode_unit"]
+
+
 @pytest.mark.parametrize("cfg", DECODE, ids=lambda c: "x".join(map(str, c[:6])))
 @pytest.mark.parametrize("policy", ["nan", "zero"])
-def test_decode_split_path(cfg, policy, monkeypatch):
-    """Split-K decode + ordered combine against the oracle and the any-shape kernel."""
+@pytest.mark.parametrize("mode", DECODE_MODES)
+def test_decode_split_path(cfg, policy, mode, monkeypatch):
+    """Decode in each mode against the oracle and the any-shape kernel."""
     import scaled_dot_product_flash_amd as sdpa
     dtype, B, Hq, Hkv, cap, D, lens = cfg
     spec = synth.Spec("decode", B, Hq, Hkv, 1, cap, D, dtype, seed=cap + B, kv_layout="bhsd",
                       causal=True, decode=True, lens="uniform", lse=True)
     case = synth.generate(spec)
     case.key_lens[:] = lens
+    monkeypatch.setenv("SDPA_FLASH_KERNEL", mode)
     o1, l1, (_, _, tens) = pu.run_hip(case, policy)
-    assert sdpa.last_kernel() == "decode_splitk"
+    assert sdpa.last_kernel() == mode
     ro, rl = pu.run_oracle(case, policy)
     pu.compare(o1, ro, l1, rl, dtype, policy, what="decode %s" % (cfg,))
     monkeypatch.setenv("SDPA_FLASH_KERNEL", "generic")
@@ -559,24 +566,33 @@ VARIANTS = {
         softcap=4.0, lens_zero_at=1, lens_full_at=0, mask_all_at=2, seed=31), "prefill_f32"),
     "decode_window_cap_sink": (synth.DECODE_F16.replace(
         batch=8, k_len=1000, local_window=100, softcap=30.0, sink="heads", seed=27),
-        "decode_splitk"),
+        "decode"),
     "decode_window0_bf16": (synth.DECODE_F16.replace(
-        dtype="bf16", batch=8, k_len=700, head_dim=64, local_window=0, seed=28), "decode_splitk"),
+        dtype="bf16", batch=8, k_len=700, head_dim=64, local_window=0, seed=28), "decode"),
     "decode_sink_zero_lens0": (synth.DECODE_F16.replace(
         batch=8, k_len=500, lens="cross", lens_zero_at=3, lens_full_at=4, sink="zero",
-        local_window=3000, seed=29), "decode_splitk"),
+        local_window=3000, seed=29), "decode"),
 }
+
+
+def _run_and_compare(spec, kernel, policy, name, monkeypatch):
+    """Runs a case on its expected kernel ("decode": in both decode modes)
+    and compares it with the oracle."""
+    case = synth.generate(spec)
+    ro, rl = pu.run_oracle(case, policy)
+    for want in (DECODE_MODES if kernel == "decode" else [kernel]):
+        if kernel == "decode":
+            monkeypatch.setenv("SDPA_FLASH_KERNEL", want)
+        o, lse, _ = pu.run_hip(case, policy, return_lse=True)
+        assert sdpa.last_kernel() == want
+        pu.compare(o, ro, lse, rl, spec.dtype, policy, what="%s %s" % (name, want))
 
 
 @pytest.mark.parametrize("name", sorted(VARIANTS))
 @pytest.mark.parametrize("policy", ["nan", "zero"])
-def test_score_variants_full_compare(name, policy):
+def test_score_variants_full_compare(name, policy, monkeypatch):
     spec, kernel = VARIANTS[name]
-    case = synth.generate(spec)
-    o, lse, _ = pu.run_hip(case, policy, return_lse=True)
-    assert sdpa.last_kernel() == kernel
-    ro, rl = pu.run_oracle(case, policy)
-    pu.compare(o, ro, lse, rl, spec.dtype, policy, what=name)
+    _run_and_compare(spec, kernel, policy, name, monkeypatch)
 
 
 def test_sink_rows_without_keys_are_zero():
@@ -642,11 +658,13 @@ INT8 = {
 
 @pytest.mark.parametrize("name", sorted(INT8))
 @pytest.mark.parametrize("policy", ["nan", "zero"])
-def test_int8_cache_decode(name, policy):
+@pytest.mark.parametrize("mode", DECODE_MODES)
+def test_int8_cache_decode(name, policy, mode, monkeypatch):
     spec = INT8[name]
     case = synth.generate(spec)
+    monkeypatch.setenv("SDPA_FLASH_KERNEL", mode)
     o, lse, _ = pu.run_hip(case, policy, return_lse=True)
-    assert sdpa.last_kernel() == "decode_splitk_int8"
+    assert sdpa.last_kernel() == mode + "_int8"
     ro, rl = pu.run_oracle(case, policy)
     pu.compare(o, ro, lse, rl, spec.dtype, policy, what=name)
 
@@ -691,19 +709,15 @@ DOCS = {
         batch=1, q_heads=2, kv_heads=1, q_len=40, k_len=800, head_dim=33, docs="random",
         causal_offset=None, sink="heads", seed=47), "prefill_f32"),
     "docs_decode": (synth.DECODE_F16.replace(
-        batch=8, k_len=700, docs="random", seed=46), "decode_splitk"),
+        batch=8, k_len=700, docs="random", seed=46), "decode"),
 }
 
 
 @pytest.mark.parametrize("name", sorted(DOCS))
 @pytest.mark.parametrize("policy", ["nan", "zero"])
-def test_doc_masks_full_compare(name, policy):
+def test_doc_masks_full_compare(name, policy, monkeypatch):
     spec, kernel = DOCS[name]
-    case = synth.generate(spec)
-    o, lse, _ = pu.run_hip(case, policy, return_lse=True)
-    assert sdpa.last_kernel() == kernel
-    ro, rl = pu.run_oracle(case, policy)
-    pu.compare(o, ro, lse, rl, spec.dtype, policy, what=name)
+    _run_and_compare(spec, kernel, policy, name, monkeypatch)
 
 
 def test_docs_bf16_full_size_sampled():
@@ -890,7 +904,8 @@ def test_large_finite_mask(cfg, monkeypatch):
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-def test_large_finite_mask_decode(dtype):
+@pytest.mark.parametrize("mode", DECODE_MODES)
+def test_large_finite_mask_decode(dtype, mode, monkeypatch):
     import scaled_dot_product_flash_amd as sdpa
     spec = synth.DECODE_F16.replace(dtype=dtype, batch=6, k_len=300, seed=61)
     case = synth.generate(spec)
@@ -898,9 +913,10 @@ def test_large_finite_mask_decode(dtype):
     rng = np.random.default_rng(78)
     mask = _large_mask_rows(rng, 6, 300)[:, None, None, :]
     case = synth.Case(spec, case.q, case.k, case.v, case.key_lens, np.ascontiguousarray(mask))
+    monkeypatch.setenv("SDPA_FLASH_KERNEL", mode)
     for policy in ("nan", "zero"):
         o, lse, _ = pu.run_hip(case, policy, return_lse=True)
-        assert sdpa.last_kernel() == "decode_splitk"
+        assert sdpa.last_kernel() == mode
         ro, rl = pu.run_oracle(case, policy)
         _compare_large(o, lse, ro, rl, dtype, policy, what="decode %s %s" % (dtype, policy))
 
@@ -940,3 +956,16 @@ def test_page_model_shapes(name):
     assert sdpa.last_kernel() != "generic"
     ro, rl = pu.run_oracle(case, "nan")
     pu.compare(o, ro, lse, rl, spec.dtype, "nan", what=name)
+
+
+def test_decode_mode_chosen_by_shape():
+    """Small decodes (each wave a few steps) run one workgroup per unit with
+    no merge; long caches run the split over equal shares plus the merge."""
+    small = synth.PAGE_SHAPES["Whisper-small decoder step B1 H12 cache448 D64 fp16"]
+    long = synth.DECODE_F16.replace(batch=2, q_heads=8, kv_heads=2, k_len=8192, seed=62)
+    for spec, want in ((small, "decode_unit"), (long, "decode_splitk")):
+        case = synth.generate(spec)
+        o, lse, _ = pu.run_hip(case, "nan", return_lse=True)
+        assert sdpa.last_kernel() == want, spec.name
+        ro, rl = pu.run_oracle(case, "nan")
+        pu.compare(o, ro, lse, rl, spec.dtype, "nan", what=spec.name)

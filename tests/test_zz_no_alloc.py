@@ -12,20 +12,25 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-def test_noalloc_decode_matches_decode(dtype):
+@pytest.mark.parametrize("small_mode", ["decode_splitk", "decode_unit"])
+def test_noalloc_decode_matches_decode(dtype, small_mode, monkeypatch):
+    """The large call runs the split mode (records in the fixed array); the
+    smaller one runs the split mode too, or the unit mode, which needs no
+    scratch at all."""
     torch = pu.torch_mod()
-    shapes = [(64, 8192, 4), (5, 300, 41)]          # second call smaller
-    for B, Lk, seed in shapes:
+    shapes = [(64, 8192, 4, "decode_splitk"), (5, 300, 41, small_mode)]   # second call smaller
+    for B, Lk, seed, mode in shapes:
+        monkeypatch.setenv("SDPA_FLASH_KERNEL", mode)
         spec = synth.DECODE_F16.replace(dtype=dtype, batch=B, k_len=Lk, seed=seed)
         case = synth.generate(spec)
         q, k, v = (pu.to_dev(x, dtype) for x in (case.q, case.k, case.v))
         lens = torch.from_numpy(case.key_lens).cuda()
         want, want_lse = sdpa.decode(q, k, v, lens, kv_layout="bhsd", return_lse=True)
-        assert sdpa.last_kernel() == "decode_splitk"
+        assert sdpa.last_kernel() == mode
         out = torch.full_like(q, float("nan"))
         got, got_lse = sdpa.decode_noalloc(q, k, v, lens, kv_layout="bhsd", return_lse=True,
                                            out=out)
-        assert sdpa.last_kernel() == "decode_splitk"
+        assert sdpa.last_kernel() == mode
         torch.cuda.synchronize()
         assert torch.equal(got.view(torch.int16), want.view(torch.int16)), (B, Lk)
         assert torch.equal(got_lse.view(torch.int32), want_lse.view(torch.int32)), (B, Lk)
