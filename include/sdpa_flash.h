@@ -192,8 +192,11 @@ typedef struct attn_problem {
  *              lengths", last paragraph).  bf16/fp16 head dims that are not
  *              a multiple of 8 also keep copies of K and V there, padded to
  *              one (OneGPU "Attention", "What it covers": other head dims
- *              are padded up).  The size depends on the shape only; the
- *              contents need no initialisation and are scratch.
+ *              are padded up).  A bf16/fp16 problem with q_len == 1 runs
+ *              on attn_decode's kernels (for instance a cross-attention
+ *              step) and needs their workspace.  The size depends on the
+ *              shape only; the contents need no initialisation and are
+ *              scratch.
  *   stream     hipStream_t to enqueue on.
  * Returns ATTN_OK, or an error with nothing enqueued (ATTN_ERR_WORKSPACE
  * when a needed workspace is missing or too small).

@@ -208,17 +208,21 @@ size_t decode_split_ws(const attn_problem* p) {
 }
 
 // Workspace of the prefill paths' key-range splits (fp32 kernel; bf16/fp16
-// matrix-core kernel on small grids); shape only.
+// matrix-core kernel on small grids), and with one query row of the decode
+// kernels that such a call runs on; shape only.
 size_t forward_ws(const attn_problem* p) {
+    const size_t dec = decode_split_ws(p);
     if (p->dtype == ATTN_DTYPE_F32)
         return sdpa::prefill_f32_workspace_bytes(p->batch, p->q_heads, p->kv_heads, p->q_len,
                                                  p->k_len, p->head_dim);
     // Staged K/V copies (head dims not a multiple of 8) first, then the
     // key-range split's records.
-    return sdpa::prefill_mfma_stage_bytes(p->batch, p->kv_heads, p->k_len, p->head_dim) +
-           sdpa::prefill_mfma_workspace_bytes(p->batch, p->q_heads, p->kv_heads, p->q_len,
-                                              p->k_len, p->head_dim,
-                                              p->causal && p->window > 0, p->doc_start != nullptr);
+    const size_t pre =
+        sdpa::prefill_mfma_stage_bytes(p->batch, p->kv_heads, p->k_len, p->head_dim) +
+        sdpa::prefill_mfma_workspace_bytes(p->batch, p->q_heads, p->kv_heads, p->q_len, p->k_len,
+                                           p->head_dim, p->causal && p->window > 0,
+                                           p->doc_start != nullptr);
+    return pre > dec ? pre : dec;
 }
 
 // attn_decode runs the split decode path when the shape and the buffers allow
@@ -227,6 +231,32 @@ size_t decode_ws(const attn_problem* p) {
     const size_t a = decode_split_ws(p);
     const size_t b = p->kv_int8 ? 0 : forward_ws(p);
     return a > b ? a : b;
+}
+
+// One query row per (batch entry, head) on the decode kernels (the caller has
+// checked sdpa::decode_split_supported): the split mode with its merge, or
+// one workgroup per unit.  The workspace is checked in both modes, so that
+// whether a call needs one never depends on the mode the shape picks.
+attn_status run_decode(const attn_problem* p, sdpa::Params& prm, sdpa::DType dt, hipStream_t s,
+                       void* workspace, size_t workspace_bytes) {
+    const size_t need = decode_split_ws(p);
+    if (!workspace || workspace_bytes < need)
+        return fail(ATTN_ERR_WORKSPACE, "decode needs %zu workspace bytes, got %zu", need,
+                    workspace ? workspace_bytes : size_t(0));
+    if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+        return fail(ATTN_ERR_INVALID, "workspace must be 16-byte aligned");
+    prm.ws = workspace;
+    // SDPA_FLASH_KERNEL=decode_unit / decode_splitk picks the mode (tests
+    // run every case through both); by default the shape decides.
+    const char* km = std::getenv("SDPA_FLASH_KERNEL");
+    const bool unit = (km && std::strcmp(km, "decode_unit") == 0)     ? true
+                      : (km && std::strcmp(km, "decode_splitk") == 0) ? false
+                                                                       : sdpa::decode_unit_preferred(prm);
+    if (unit)
+        g_kernel = p->kv_int8 ? "decode_unit_int8" : "decode_unit";
+    else
+        g_kernel = p->kv_int8 ? "decode_splitk_int8" : "decode_splitk";
+    return launched(sdpa::launch_decode_split(prm, dt, s, unit));
 }
 
 attn_status attn_workspace_size(const attn_problem* p, int32_t op, size_t* bytes) {
@@ -255,6 +285,11 @@ attn_status attn_forward(const attn_problem* p, const void* q, const void* k, co
     sdpa::Params prm = make_params(p, q, k, v, o, mask, key_lens, lse);
     const auto dt = static_cast<sdpa::DType>(p->dtype);
     const hipStream_t s = static_cast<hipStream_t>(stream);
+    // One query row (a cross-attention step, or decode called as a forward):
+    // the decode kernels read each live K/V row once for a whole head group,
+    // where a prefill tile would fill one of its rows.
+    if (!force_generic() && p->q_len == 1 && sdpa::decode_split_supported(prm, dt))
+        return run_decode(p, prm, dt, s, workspace, workspace_bytes);
     if (!force_generic() && (dt == sdpa::DType::BF16 || dt == sdpa::DType::F16)) {
         sdpa::prefill_mfma_plan(p->batch, p->q_heads, p->kv_heads, p->q_len, p->k_len,
                                 p->head_dim, p->causal && p->window > 0, p->doc_start != nullptr,
@@ -311,26 +346,8 @@ attn_status attn_decode(const attn_problem* p, const void* q, const void* k, con
     sdpa::Params prm = make_params(p, q, k, v, o, mask, key_lens, lse);
     const auto dt = static_cast<sdpa::DType>(p->dtype);
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    if (!force_generic() && sdpa::decode_split_supported(prm, dt)) {
-        const size_t need = decode_split_ws(p);
-        if (!workspace || workspace_bytes < need)
-            return fail(ATTN_ERR_WORKSPACE, "decode needs %zu workspace bytes, got %zu", need,
-                        workspace ? workspace_bytes : size_t(0));
-        if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
-            return fail(ATTN_ERR_INVALID, "workspace must be 16-byte aligned");
-        prm.ws = workspace;
-        // SDPA_FLASH_KERNEL=decode_unit / decode_splitk picks the mode (tests
-        // run every case through both); by default the shape decides.
-        const char* km = std::getenv("SDPA_FLASH_KERNEL");
-        const bool unit = (km && std::strcmp(km, "decode_unit") == 0)     ? true
-                          : (km && std::strcmp(km, "decode_splitk") == 0) ? false
-                                                                           : sdpa::decode_unit_preferred(prm);
-        if (unit)
-            g_kernel = p->kv_int8 ? "decode_unit_int8" : "decode_unit";
-        else
-            g_kernel = p->kv_int8 ? "decode_splitk_int8" : "decode_splitk";
-        return launched(sdpa::launch_decode_split(prm, dt, s, unit));
-    }
+    if (!force_generic() && sdpa::decode_split_supported(prm, dt))
+        return run_decode(p, prm, dt, s, workspace, workspace_bytes);
     if (p->kv_int8)
         return fail(ATTN_ERR_UNSUPPORTED, "int8 cache decode needs fp16/bf16, a head_dim that is "
                                           "a multiple of 16 up to 256 and 16-byte aligned K/V rows");

@@ -195,6 +195,20 @@ def test_decode_workspace_is_checked_before_launch():
     assert rc == sdpa.ERR_INVALID and b"aligned" in lib.attn_last_error()
 
 
+def test_forward_one_row_runs_decode_kernels_with_their_workspace():
+    """A forward call with one query row runs on the decode kernels, so its
+    workspace covers theirs, and it is checked before anything runs."""
+    lib = sdpa.load_library()
+    p = _problem(q_len=1, k_len=4096, dtype=sdpa.DTYPE_F16, head_dim=128)
+    for lay, H, L in (("q", 4, 1), ("k", 2, 4096), ("v", 2, 4096), ("o", 4, 1)):
+        setattr(p, lay, sdpa.Layout(0, L * H * 128, 128, H * 128))
+    fwd = sdpa.workspace_size(p, sdpa.OP_FORWARD)
+    assert fwd == sdpa.workspace_size(p, sdpa.OP_DECODE) > 0
+    rc = lib.attn_forward(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, None, None, None, 0,
+                          None)
+    assert rc == sdpa.ERR_WORKSPACE and b"decode needs" in lib.attn_last_error()
+
+
 def test_decode_workspace_covers_the_forward_fallback():
     """A decode shape the split decode path does not take (head dim 250, not
     whole 16-byte chunks) runs as a forward call, whose few query blocks split

@@ -324,7 +324,7 @@ SPLIT = {
                                                    k_len=1500, head_dim=96, docs="packed",
                                                    doc_mean=300, seed=44),
     "f16_D128_softcap_sink_zero": synth.CHUNK_F16.replace(batch=3, q_heads=4, kv_heads=1,
-                                                          q_len=1, k_len=5000, softcap=10.0,
+                                                          q_len=2, k_len=5000, softcap=10.0,
                                                           sink="zero", lens="cross",
                                                           lens_zero_at=0, seed=45),
 }
@@ -969,3 +969,34 @@ def test_decode_mode_chosen_by_shape():
         assert sdpa.last_kernel() == want, spec.name
         ro, rl = pu.run_oracle(case, "nan")
         pu.compare(o, ro, lse, rl, spec.dtype, "nan", what=spec.name)
+
+
+# Forward calls with one query row run on the decode kernels (both modes):
+# non-causal cross-attention, a global causal offset with a window and
+# document starts, the per-entry end-aligned rule with softcap and sinks,
+# and a broadcast key mask with lengths.
+FORWARD_ONE_ROW = {
+    "whisper_cross_f16": synth.PAGE_SHAPES["Whisper-small cross-attention B1 H12 Lq1 Lk1500 D64 fp16"],
+    "offset_window_docs_bf16": synth.CAUSAL_GQA_BF16.replace(
+        batch=3, q_heads=8, kv_heads=2, q_len=1, k_len=500, causal_offset=300, local_window=60,
+        docs="random", seed=63),
+    "end_softcap_sink_f16": synth.CHUNK_F16.replace(
+        batch=6, q_heads=8, kv_heads=2, q_len=1, k_len=900, lens="cross", lens_zero_at=2,
+        lens_full_at=3, softcap=10.0, sink="heads", seed=64),
+    "mask_lens_bf16_D128": synth.CROSS_MASK_F16.replace(
+        dtype="bf16", batch=8, q_heads=8, kv_heads=8, q_len=1, k_len=777, head_dim=128, seed=65),
+}
+
+
+@pytest.mark.parametrize("name", sorted(FORWARD_ONE_ROW))
+@pytest.mark.parametrize("policy", ["nan", "zero"])
+@pytest.mark.parametrize("mode", DECODE_MODES)
+def test_forward_one_query_row_on_decode_kernels(name, policy, mode, monkeypatch):
+    spec = FORWARD_ONE_ROW[name]
+    assert spec.q_len == 1 and not spec.decode
+    case = synth.generate(spec)
+    monkeypatch.setenv("SDPA_FLASH_KERNEL", mode)
+    o, lse, _ = pu.run_hip(case, policy, return_lse=True)
+    assert sdpa.last_kernel() == mode
+    ro, rl = pu.run_oracle(case, policy)
+    pu.compare(o, ro, lse, rl, spec.dtype, policy, what="%s %s" % (name, mode))
