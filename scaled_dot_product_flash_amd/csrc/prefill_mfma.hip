@@ -1032,11 +1032,20 @@ hipError_t launch_one(const Params& p, hipStream_t s) {
 
 // Key ranges for small grids (shape only): when the query blocks would leave
 // at least half of the GPU's resident workgroup slots empty (256 CUs of an
-// MI355X; three slots per CU at head dim 64), each block's keys are cut into
-// ranges of a whole number of tiles, at least 4 tiles each and at most 32
-// ranges, aiming at two workgroups per slot.  Each range writes its rows'
-// (m, l, acc) records, which costs about as much HBM traffic as the output
-// per range, so grids that already fill the GPU are not split.
+// MI355X; three slots per CU at head dim 64), each block's keys may be cut
+// into ranges of a whole number of tiles, at most 32 ranges, aiming at two
+// workgroups per slot.  Each range writes its rows' (m, l, acc) records in
+// fp32 (about twice the output's bytes per range, read back by the merge
+// kernel), so a range must carry enough tiles to pay for them; the fewer the
+// blocks, the more an idle CU costs and the shorter a range may be:
+//   blocks <= 32: ranges of at least 4 tiles;
+//   blocks <= 128: at least 8 tiles, keys of at least 32 tiles;
+//   blocks <= 256: at least 16 tiles, keys of at least 128 tiles;
+//   more blocks: no split.
+// (Measured on one MI355X over 16 shapes, head dims 64 and 128; e.g. BERT-
+// base B8 S512 (384 blocks of 8 tiles) 44 us split into two ranges against
+// 16 us whole, B1 H8 L1024 D128 (32 blocks of 16 tiles) 29 us in four
+// ranges against 33 us whole.)
 void prefill_mfma_plan(int B, int Hq, int Hkv, int Lq, int Lk, int D, bool window, bool docs,
                        int* split_len, int* n_split) {
     *split_len = 0;
@@ -1050,8 +1059,17 @@ void prefill_mfma_plan(int B, int Hq, int Hkv, int Lq, int Lk, int D, bool windo
     const int64_t slots = 256 * blocks_per_cu(DP, shrt);
     const int64_t tiles = (static_cast<int64_t>(Lk) + kBN - 1) / kBN;
     if (2 * blocks > slots || tiles < 8) return;
+    int64_t per_min;                                  // tiles per range at least
+    if (blocks <= 32)
+        per_min = 4;
+    else if (blocks <= 128 && tiles >= 32)
+        per_min = 8;
+    else if (blocks <= 256 && tiles >= 128)
+        per_min = 16;
+    else
+        return;
     int64_t n = (2 * slots + blocks - 1) / blocks;
-    if (n > tiles / 4) n = tiles / 4;
+    if (n > tiles / per_min) n = tiles / per_min;
     if (n > 32) n = 32;
     if (n < 2) return;
     const int64_t per = (tiles + n - 1) / n;          // tiles per range

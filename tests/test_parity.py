@@ -320,8 +320,8 @@ SPLIT = {
                                                      kv_heads=1, q_len=64, k_len=2048,
                                                      head_dim=256, lens=None, local_window=700,
                                                      sink="heads", seed=43),
-    "bf16_D96_docs": synth.CAUSAL_GQA_BF16.replace(batch=1, q_heads=4, kv_heads=1, q_len=1500,
-                                                   k_len=1500, head_dim=96, docs="packed",
+    "bf16_D96_docs": synth.CAUSAL_GQA_BF16.replace(batch=1, q_heads=4, kv_heads=1, q_len=2100,
+                                                   k_len=2100, head_dim=96, docs="packed",
                                                    doc_mean=300, seed=44),
     "f16_D128_softcap_sink_zero": synth.CHUNK_F16.replace(batch=3, q_heads=4, kv_heads=1,
                                                           q_len=2, k_len=5000, softcap=10.0,
