@@ -765,10 +765,18 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(Params p, int n_hgr
 int slice_count(int group) { return (group + 15) / 16; }
 int heads_per_slot(int group) { return group < 16 ? group : 16; }
 
+// Steps of the longest possible unit: the cache capacity bounds the live
+// keys, and so does a causal local window (the one row sees at most W keys).
+int64_t max_unit_steps(const Params& p) {
+    int64_t keys = p.Lk;
+    if (p.causal && p.window > 0 && p.window < keys) keys = p.window;
+    return (keys + kStep - 1) / kStep;
+}
+
 // Waves per workgroup of the unit mode: one per step of the longest
 // possible unit, at most unit_waves_max.
 int unit_waves(const Params& p, int DP) {
-    const int64_t smax = (static_cast<int64_t>(p.Lk) + kStep - 1) / kStep;
+    const int64_t smax = max_unit_steps(p);
     const int cap = unit_waves_max(DP, p.kv_int8 != 0);
     return smax < cap ? static_cast<int>(smax < 1 ? 1 : smax) : cap;
 }
@@ -868,11 +876,12 @@ bool decode_split_supported(const Params& p, DType dt) {
 // the whole GPU.  Measured crossovers (one MI355X, full-length caches): the
 // unit mode wins up to 8 steps per wave at head dims 64/128 (16 when at most
 // 256 waves run in all), 4 at 256 with 16-bit rows, 16 with int8 rows, while
-// its workgroups fit in about two rounds on the GPU.
+// its workgroups fit in about two rounds on the GPU (e.g. 64 entries of 2048
+// keys, or of a 2047-key window over 8192: 79 us against 88 split).
 bool decode_unit_preferred(const Params& p) {
     const int DP = decode_padded_dim(p.D);
     const bool i8 = p.kv_int8 != 0;
-    const int64_t smax = (static_cast<int64_t>(p.Lk) + kStep - 1) / kStep;
+    const int64_t smax = max_unit_steps(p);
     const int nw = unit_waves(p, DP);
     const int64_t waves = static_cast<int64_t>(p.B) * p.Hkv * slice_count(p.group) * nw;
     const int64_t per_wave = (smax + nw - 1) / nw;

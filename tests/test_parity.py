@@ -622,11 +622,17 @@ def test_variant_prefill_full_size_sampled(name):
     pu.compare(go, ro, gl, rl, spec.dtype, "nan", what=spec.name)
 
 
-def test_variant_decode_full_size_every_row():
+@pytest.mark.parametrize("mode", [None] + DECODE_MODES)
+def test_variant_decode_full_size_every_row(mode, monkeypatch):
+    """The window + sink decode workload at full size, in the mode its shape
+    picks (the window bounds every unit to 64 steps: one workgroup per unit)
+    and in each mode forced."""
     spec = synth.EXTRA_WORKLOADS["decode_window_f16"]
     case = synth.generate(spec)
+    if mode:
+        monkeypatch.setenv("SDPA_FLASH_KERNEL", mode)
     o, lse, _ = pu.run_hip(case, "nan", return_lse=True)
-    assert sdpa.last_kernel() == "decode_splitk"
+    assert sdpa.last_kernel() == (mode or "decode_unit")
     ro, rl = pu.run_oracle(case, "nan")
     pu.compare(o, ro, lse, rl, spec.dtype, "nan", what=spec.name)
 

@@ -13,13 +13,17 @@ import parity_util as pu
 pytestmark = pytest.mark.gpu
 
 # A prefill whose query blocks are too few for the GPU (the keys are cut into
-# ranges: workspace + merge kernel) and a split decode (workspace + merge).
+# ranges: workspace + merge kernel), a split decode (workspace + merge) and a
+# small decode (one workgroup per unit, folding in LDS).
 CASES = {
     "chunk_split_f16": synth.CHUNK_F16.replace(batch=2, q_heads=8, kv_heads=2, q_len=64,
                                                k_len=2048, lens="cross", lens_zero_at=9,
                                                lens_full_at=1, seed=21),
-    "decode_f16": synth.DECODE_F16.replace(batch=8, k_len=1000, seed=22),
+    "decode_split_f16": synth.DECODE_F16.replace(batch=8, k_len=8192, seed=23),
+    "decode_unit_f16": synth.DECODE_F16.replace(batch=8, k_len=1000, seed=22),
 }
+KERNEL = {"chunk_split_f16": "prefill_mfma", "decode_split_f16": "decode_splitk",
+          "decode_unit_f16": "decode_unit"}
 
 
 def _call(case, t, **kw):
@@ -45,6 +49,7 @@ def test_caller_stream_matches_current_stream(name):
     case = synth.generate(CASES[name])
     t = _tensors(case)
     o_ref, l_ref = _call(case, t)
+    assert sdpa.last_kernel() == KERNEL[name]
     assert sdpa.last_workspace_bytes() > 0
     torch.cuda.synchronize()
     side = torch.cuda.Stream()
@@ -65,6 +70,7 @@ def test_graph_replays_match_eager(name):
     case = synth.generate(CASES[name])
     t = _tensors(case)
     _call(case, t)                       # library loaded, first launch done
+    assert sdpa.last_kernel() == KERNEL[name]
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
