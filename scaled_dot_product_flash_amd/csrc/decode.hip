@@ -874,10 +874,12 @@ bool decode_split_supported(const Params& p, DType dt) {
 // calls) but runs each unit on one workgroup, whose waves walk their steps
 // one HBM round trip after another; the split mode spreads every unit over
 // the whole GPU.  Measured crossovers (one MI355X, full-length caches): the
-// unit mode wins up to 8 steps per wave at head dims 64/128 (16 when at most
-// 256 waves run in all), 4 at 256 with 16-bit rows, 16 with int8 rows, while
-// its workgroups fit in about two rounds on the GPU (e.g. 64 entries of 2048
-// keys, or of a 2047-key window over 8192: 79 us against 88 split).
+// unit mode wins up to 16 steps per wave at head dim 64 (64 entries of 8192
+// keys, 8192 waves in two rounds: 103 us against 110 split), up to 8 at 128
+// (16 when at most 256 waves run in all), 4 at 256 with 16-bit rows and 16
+// with int8 rows, while its workgroups fit in about two rounds on the GPU
+// (e.g. 64 entries of 2048 keys, or of a 2047-key window over 8192: 79 us
+// against 88 split; 64 entries of 8192 keys at 128: 190 against 173).
 bool decode_unit_preferred(const Params& p) {
     const int DP = decode_padded_dim(p.D);
     const bool i8 = p.kv_int8 != 0;
@@ -885,6 +887,7 @@ bool decode_unit_preferred(const Params& p) {
     const int nw = unit_waves(p, DP);
     const int64_t waves = static_cast<int64_t>(p.B) * p.Hkv * slice_count(p.group) * nw;
     const int64_t per_wave = (smax + nw - 1) / nw;
+    if (DP == 64 && !i8) return per_wave <= 16 && waves <= 8192;
     const int64_t limit = i8 ? 16 : (DP == 256 ? 4 : (waves <= 256 ? 16 : 8));
     return per_wave <= limit && waves <= 4096;
 }
