@@ -9,12 +9,12 @@
 // causal bound of the one query row) form ceil(len/32) steps of 32 keys.
 //
 // Load balance.  Per-batch lengths differ widely, so cutting each unit into
-// fixed ranges leaves the GPU half idle at the end.  Instead W waves (2048:
-// eight per CU of an MI355X; as many as there are steps when there are
-// fewer) each take an equal contiguous share of the concatenated steps of
-// all units, in unit order; every wave
-// computes the same per-batch prefix sums from the lengths, so the cut needs
-// no host round trip.  A wave writes one partial record (reference max, sum,
+// fixed ranges leaves the GPU half idle at the end.  Instead W waves (1024
+// or 2048 by head dim and cache type: four or eight per CU of an MI355X; as
+// many as there are steps when there are fewer) each take an equal
+// contiguous share of the concatenated steps of all units, in unit order;
+// every wave computes the same per-batch prefix sums from the lengths, so the
+// cut needs no host round trip.  A wave writes one partial record (reference max, sum,
 // unnormalised accumulator) for each unit it touches, at slot (unit + wave):
 // waves and units advance together, so no two (unit, wave) pairs share a slot,
 // and U + W - 1 slots suffice.  The merge kernel recomputes which waves cover
