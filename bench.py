@@ -371,22 +371,27 @@ def live_kv_bytes(case) -> float:
     return float(lens.sum()) * s.kv_heads * s.head_dim * 2 * elem
 
 
-def other_workloads(sdpa, synth, steps: int, warmup: int):
+def other_workloads(sdpa, synth, steps: int, warmup: int, only=None):
     """The other workloads (report only): the smaller named workloads, the
     extensions' workloads and the pages' model shapes.  Calls under 100 us are
     re-timed back to back behind a short spin kernel, so us_per_call is GPU
     time even where the host's launch cost (host_us_per_call) is the longer;
     tflops counts visible (row, key) pairs only; decode lines add the GB/s of
-    live K/V read."""
+    live K/V read.  only: workload keys (synth names) to run, else all."""
     import torch
     out = []
-    specs = [synth.WORKLOADS[n] for n in ("tiny_f32", "causal_gqa_f32", "cross_mask_f16")]
-    specs += [synth.EXTRA_WORKLOADS[n]
+    specs = [(n, synth.WORKLOADS[n]) for n in ("tiny_f32", "causal_gqa_f32", "cross_mask_f16")]
+    specs += [(n, synth.EXTRA_WORKLOADS[n])
               for n in ("chunk_f16", "long_chunk_bf16", "window_bf16", "softcap_sink_bf16",
                         "docs_bf16", "d96_bf16", "d256_bf16", "d100_bf16", "d96_f32",
                         "decode_window_f16", "decode_int8_f16", "decode_d96_f16")]
-    specs += list(synth.PAGE_SHAPES.values())
-    for spec in specs:
+    specs += list(synth.PAGE_SHAPES.items())
+    if only:
+        unknown = set(only) - {n for n, _ in specs}
+        if unknown:
+            raise SystemExit("unknown workload(s): %s" % ", ".join(sorted(unknown)))
+        specs = [(n, s) for n, s in specs if n in only]
+    for _, spec in specs:
         case = synth.generate(spec)
         t = workload_tensors(case)
         o = torch.empty_like(t["q"])
@@ -612,6 +617,8 @@ def main():
                     help="skip the MFMA-loop / streaming ceilings")
     ap.add_argument("--settle", type=float, default=1.0,
                     help="seconds of untimed calls before each workload's warmup (clock ramp)")
+    ap.add_argument("--workload", action="append", default=[],
+                    help="with --only others: run just this workload (repeatable)")
     ap.add_argument("--only", choices=["prefill", "decode", "ceilings", "others",
                                        "calibrate-copy"],
                     help="run one part only (for profiling runs)")
@@ -666,7 +673,8 @@ def main():
         return
     if args.only == "others":
         print(json.dumps({"other_workloads": other_workloads(sdpa, synth, args.steps,
-                                                             args.warmup)}), flush=True)
+                                                             args.warmup, args.workload)}),
+              flush=True)
         return
     result = {}
     case = None

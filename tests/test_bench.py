@@ -110,3 +110,12 @@ def test_source_hash_ignores_comments_only():
     assert bench.code_text(a) == bench.code_text(b)
     assert bench.code_text(a) != bench.code_text(a.replace("x + 1", "x + 2"))
     assert bench.code_text(a) != bench.code_text(a.replace('"a // b"', '"a / b"'))
+
+
+def test_other_workload_filter_rejects_unknown_names():
+    """--only others --workload NAME runs just that workload (for counter
+    passes over one of them); a name that is not one of them is refused
+    before anything runs."""
+    import pytest
+    with pytest.raises(SystemExit, match="unknown workload"):
+        bench.other_workloads(None, synth, 1, 0, only=["no_such_workload"])
