@@ -192,8 +192,8 @@ typedef struct attn_problem {
  *              lengths", last paragraph).  bf16/fp16 head dims that are not
  *              a multiple of 8 also keep copies of K and V there, padded to
  *              one (OneGPU "Attention", "What it covers": other head dims
- *              are padded up).  A bf16/fp16 problem with q_len == 1 runs
- *              on attn_decode's kernels (for instance a cross-attention
+ *              are padded up).  A problem with q_len == 1 that attn_decode's
+ *              kernels take runs on them (for instance a cross-attention
  *              step) and needs their workspace.  The size depends on the
  *              shape only; the contents need no initialisation and are
  *              scratch.
@@ -218,9 +218,11 @@ attn_status attn_forward(const attn_problem* p, const void* q, const void* k, co
  * shape only) and a second kernel merges a row's partials in key order.  For
  * small calls (a few 32-key steps per wave) one workgroup takes each (batch
  * entry, kv head) pair, folds its waves' partials in key order on chip and
- * writes the outputs; the workspace is then unused.  Shapes or buffers that
- * neither mode takes (fp32, head dims that are not whole 16-byte chunks up to
- * 256, unaligned rows) run as attn_forward would;
+ * writes the outputs; the workspace is then unused.  Both modes take
+ * bf16/fp16 Q/K/V (or an int8 cache) with head dims that are whole 16-byte
+ * chunks up to 256, and fp32 Q/K/V with head dims that are multiples of 4 up
+ * to 128.  Shapes or buffers that neither mode takes (other head dims,
+ * unaligned rows) run as attn_forward would;
  * attn_workspace_size(p, ATTN_OP_DECODE) covers every case.
  */
 attn_status attn_decode(const attn_problem* p, const void* q, const void* k, const void* v,

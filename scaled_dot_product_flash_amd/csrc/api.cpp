@@ -199,10 +199,12 @@ const char* attn_version(void) { return "sdpa_flash 0.1 (gfx950)"; }
 
 // Workspace of the split decode path; depends on the shape only.
 size_t decode_split_ws(const attn_problem* p) {
-    const bool shape_ok = (p->dtype == ATTN_DTYPE_BF16 || p->dtype == ATTN_DTYPE_F16) &&
-                          p->head_dim >= 8 && p->head_dim <= 256 &&
-                          p->head_dim % (p->kv_int8 ? 16 : 8) == 0 && p->q_len == 1 &&
-                          p->k_len > 0;
+    const bool half = (p->dtype == ATTN_DTYPE_BF16 || p->dtype == ATTN_DTYPE_F16) &&
+                      p->head_dim >= 8 && p->head_dim <= 256 &&
+                      p->head_dim % (p->kv_int8 ? 16 : 8) == 0;
+    const bool f32 = p->dtype == ATTN_DTYPE_F32 && !p->kv_int8 && p->head_dim >= 4 &&
+                     p->head_dim <= 128 && p->head_dim % 4 == 0;
+    const bool shape_ok = (half || f32) && p->q_len == 1 && p->k_len > 0;
     return shape_ok ? sdpa::decode_workspace_bytes(p->batch, p->q_heads, p->kv_heads, p->head_dim)
                     : 0;
 }
@@ -212,9 +214,11 @@ size_t decode_split_ws(const attn_problem* p) {
 // kernels that such a call runs on; shape only.
 size_t forward_ws(const attn_problem* p) {
     const size_t dec = decode_split_ws(p);
-    if (p->dtype == ATTN_DTYPE_F32)
-        return sdpa::prefill_f32_workspace_bytes(p->batch, p->q_heads, p->kv_heads, p->q_len,
-                                                 p->k_len, p->head_dim);
+    if (p->dtype == ATTN_DTYPE_F32) {
+        const size_t pre = sdpa::prefill_f32_workspace_bytes(p->batch, p->q_heads, p->kv_heads,
+                                                             p->q_len, p->k_len, p->head_dim);
+        return pre > dec ? pre : dec;
+    }
     // Staged K/V copies (head dims not a multiple of 8) first, then the
     // key-range split's records.
     const size_t pre =
@@ -251,7 +255,7 @@ attn_status run_decode(const attn_problem* p, sdpa::Params& prm, sdpa::DType dt,
     const char* km = std::getenv("SDPA_FLASH_KERNEL");
     const bool unit = (km && std::strcmp(km, "decode_unit") == 0)     ? true
                       : (km && std::strcmp(km, "decode_splitk") == 0) ? false
-                                                                       : sdpa::decode_unit_preferred(prm);
+                                                                       : sdpa::decode_unit_preferred(prm, dt);
     if (unit)
         g_kernel = p->kv_int8 ? "decode_unit_int8" : "decode_unit";
     else

@@ -69,7 +69,7 @@ bool decode_split_supported(const Params& p, DType dt);
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int D);
 // unit: one workgroup per (entry, kv head, head slice), no workspace and no
 // merge; otherwise the split over equal shares of all steps plus the merge.
-bool decode_unit_preferred(const Params& p);
+bool decode_unit_preferred(const Params& p, DType dt);
 hipError_t launch_decode_split(const Params& p, DType dt, hipStream_t s, bool unit);
 
 void prefill_f32_plan(int B, int Hq, int Hkv, int Lq, int Lk, int D, int* split_len,

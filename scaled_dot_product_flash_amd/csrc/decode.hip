@@ -46,6 +46,9 @@
 // is [lo, hi) and steps count from lo); the softcap maps raw scores before
 // the mask; the sink joins the denominator in the merge.
 //
+// fp32 Q/K/V (head dims up to 128): the same steps on 16x16x4 fp32 matrix
+// operations, P not rounded; rows staged as fp32 in LDS.
+//
 // Int8 cache (GroupQueryAttention README, "Inputs": k_scale / v_scale): rows
 // are read as 16-byte loads of 16 int8 values -- half the bytes of fp16 --
 // stored in LDS as they are, and widened to the element type as the MFMA
@@ -77,9 +80,10 @@ __host__ __device__ constexpr int waves_total(int DP, bool i8) {
 constexpr int kWavesMax = 2048;
 // Unit mode: waves per workgroup at most, for padded head dim DP and cache
 // type (the register budget of a workgroup that size: at 64, four waves per
-// SIMD; at 128 and for int8 rows at 256, two; 16-bit rows at 256, one).
-__host__ __device__ constexpr int unit_waves_max(int DP, bool i8) {
-    return DP == 64 ? 16 : (DP == 128 || i8 ? 8 : 4);
+// SIMD; at 128 and for int8 rows at 256, two; 16-bit rows at 256, one; fp32
+// rows: what fits the LDS, 8 at 64 and 4 at 128).
+__host__ __device__ constexpr int unit_waves_max(int DP, bool i8, bool f32 = false) {
+    return f32 ? (DP == 64 ? 8 : 4) : (DP == 64 ? 16 : (DP == 128 || i8 ? 8 : 4));
 }
 constexpr float kSlack = 8.f;      // lazy-rescale threshold, base-2 units
 
@@ -104,6 +108,17 @@ template <int D> struct I8Lay {
     static constexpr int kLoads = kStep / kRowsPerLoad;
     static constexpr int RS = D + 16;
     static constexpr int kWaveBytes = kStep * 2 * RS;
+};
+
+// fp32 rows (fp32 Q/K/V, head dims up to 128): 4 floats per 16-byte load,
+// rows of RS floats (16 bytes of padding) for K and V alike.  The K reads
+// (16 bytes per lane, 16 rows) land 16 bytes mod 256 apart on the banks.
+template <int D> struct F32Lay {
+    static constexpr int kRowChunks = D / 4;
+    static constexpr int kRowsPerLoad = 64 / kRowChunks;
+    static constexpr int kLoads = kStep / kRowsPerLoad;
+    static constexpr int RS = D + 4;
+    static constexpr int kWaveBytes = kStep * 2 * RS * 4;
 };
 
 // 16 signed bytes -> 16 elements of the MFMA type, exactly.
@@ -228,9 +243,10 @@ __device__ __forceinline__ int owner_wave(int64_t x, int64_t S, int64_t W) {
 
 // LDS bytes per wave of the unit mode: its staging rows, later its records
 // (16 heads x rec_stride floats).
-template <int D, bool kI8>
+template <int D, bool kI8, bool kF32 = false>
 __host__ __device__ constexpr int unit_wave_bytes() {
-    constexpr int stage = kI8 ? I8Lay<D>::kWaveBytes : DLay<D>::kWaveBytes;
+    constexpr int stage =
+        kF32 ? F32Lay<D>::kWaveBytes : (kI8 ? I8Lay<D>::kWaveBytes : DLay<D>::kWaveBytes);
     constexpr int recs = 16 * rec_stride(D) * 4;
     return stage > recs ? stage : recs;
 }
@@ -243,7 +259,11 @@ __host__ __device__ constexpr int unit_wave_bytes() {
 // order) and writes the outputs itself, with no workspace and no merge
 // kernel.  smem: this workgroup's LDS (one wave's rows in split mode, one
 // unit_wave_bytes() slice per wave in unit mode).
-template <bool kBf16, int D, bool kCap, bool kI8, bool kUnit>
+// kF32: fp32 Q/K/V (kBf16 unused), on 16x16x4 fp32 matrix operations: the
+// scores' d-sum runs lane group q4 over columns (D/4) q4 .. + D/4 - 1 (each
+// lane's K and Q pieces contiguous), and output row i of d-tile dt is column
+// (D/16) i + dt (each lane's V piece contiguous); P is not rounded.
+template <bool kBf16, int D, bool kCap, bool kI8, bool kUnit, bool kF32 = false>
 __device__ __forceinline__ void decode_body(const Params& p, int n_hgrp, int slot_heads,
                                             uint8_t* smem_base) {
     using M = Mma<kBf16>;
@@ -252,14 +272,18 @@ __device__ __forceinline__ void decode_body(const Params& p, int n_hgrp, int slo
     constexpr int NT = D / 32;       // 32-wide d-steps of the score product
     constexpr int ND = D / 16;       // 16-row d-tiles of the output
     using L8 = I8Lay<D>;
+    using FL = F32Lay<D>;
+    static_assert(!kF32 || (!kI8 && D <= 128), "fp32 rows: no int8, head dims up to 128");
 
     const int lane = kUnit ? static_cast<int>(threadIdx.x & 63) : static_cast<int>(threadIdx.x);
     const int wave = kUnit ? uniform32(threadIdx.x >> 6) : blockIdx.x;
-    uint8_t* const smem = smem_base + (kUnit ? wave * unit_wave_bytes<D, kI8>() : 0);
+    uint8_t* const smem = smem_base + (kUnit ? wave * unit_wave_bytes<D, kI8, kF32>() : 0);
     uint16_t* const k_sh = reinterpret_cast<uint16_t*>(smem);
     uint16_t* const v_sh = k_sh + kStep * KS;
     uint8_t* const k8 = smem;                         // int8 cache: rows of L8::RS bytes
     uint8_t* const v8 = smem + kStep * L8::RS;
+    float* const kf = reinterpret_cast<float*>(smem);     // fp32 rows of FL::RS floats
+    float* const vf = kf + kStep * FL::RS;
     const int Dt = p.D;              // true head dim (<= D, the padded one)
     const int per_b = p.Hkv * n_hgrp;            // units per batch entry
 
@@ -314,8 +338,9 @@ __device__ __forceinline__ void decode_body(const Params& p, int n_hgrp, int slo
     }
 
     const int col = lane & 15, q4 = lane >> 4;
-    const int ld_row = kI8 ? lane / L8::kRowChunks : lane / LY::kRowChunks;
-    const int ld_col = kI8 ? (lane % L8::kRowChunks) * 16 : (lane % LY::kRowChunks) * 8;
+    const int ld_row = kF32 ? lane / FL::kRowChunks : (kI8 ? lane / L8::kRowChunks : lane / LY::kRowChunks);
+    const int ld_col = kF32 ? (lane % FL::kRowChunks) * 4
+                            : (kI8 ? (lane % L8::kRowChunks) * 16 : (lane % LY::kRowChunks) * 8);
     // Raw scores are q.k with the K integers; a per-tensor K scale joins c.
     // With a mask the scores are natural: sc = scale (times that K scale)
     // maps raw to natural, and c = log2(e).
@@ -333,6 +358,7 @@ __device__ __forceinline__ void decode_body(const Params& p, int n_hgrp, int slo
     bool live_col = false;
     int64_t kv_lo = 0, kv_hi = 0;   // kv_hi: live keys counted from kv_lo
     i16x8 qop[NT];
+    float qf[kF32 ? D / 4 : 1];      // fp32: Q columns (D/4) q4 .. + D/4 - 1 of head col
     const float* mrow = nullptr;
     float m_ref = kNegInf, l_sum = 0.f;
     f32x4 acc[ND];
@@ -345,9 +371,23 @@ __device__ __forceinline__ void decode_body(const Params& p, int n_hgrp, int slo
         const LiveRange lr = live_range(p, b);
         kv_lo = lr.lo;
         kv_hi = lr.n;
+        if constexpr (kF32) {
+            // Whole 16-byte chunks (the true head dim is a multiple of 4):
+            // columns past it are zero, loaded unconditionally from the row's
+            // first chunk and replaced.
+            const float* srcf = static_cast<const float*>(p.q) + b * p.qs.sb + h * p.qs.sh;
+#pragma unroll
+            for (int m = 0; m < D / 16; ++m) {
+                const int c0 = (D / 4) * q4 + 4 * m;
+                const bool cin = live_col && c0 < Dt;
+                const f32x4 raw = *reinterpret_cast<const f32x4*>(srcf + (c0 < Dt ? c0 : 0));
+#pragma unroll
+                for (int e2 = 0; e2 < 4; ++e2) qf[4 * m + e2] = cin ? raw[e2] : 0.f;
+            }
+        }
         const uint16_t* src = static_cast<const uint16_t*>(p.q) + b * p.qs.sb + h * p.qs.sh + 8 * q4;
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
+        for (int t = 0; t < (kF32 ? 0 : NT); ++t) {
             // Columns past the true head dim (a multiple of 8) are zero: the
             // load is unconditional (from the row's first chunk there) and
             // its value replaced, so no load waits behind a branch.
@@ -384,6 +424,22 @@ __device__ __forceinline__ void decode_body(const Params& p, int n_hgrp, int slo
 #pragma unroll
         for (int d = 0; d < ND; ++d) acc[d] = f32x4{};
     };
+    // This lane's accumulators into record rec (acc[0..D) at rec + 4).
+    auto store_acc = [&](float* rec) {
+        if constexpr (kF32) {
+            // acc[dt][r] holds column (D/16) (4 q4 + r) + dt.
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int m = 0; m < D / 64; ++m)
+                    *reinterpret_cast<f32x4*>(rec + 4 + (D / 16) * (4 * q4 + r) + 4 * m) =
+                        f32x4{acc[4 * m][r], acc[4 * m + 1][r], acc[4 * m + 2][r], acc[4 * m + 3][r]};
+        } else {
+#pragma unroll
+            for (int d = 0; d < ND; ++d)
+                *reinterpret_cast<f32x4*>(rec + 4 + 16 * d + 4 * q4) = acc[d];
+        }
+    };
     auto end_unit = [&]() {
         // Column total of the running sum: the 4 lanes of column col, fixed order.
         float lt = l_sum + __shfl_xor(l_sum, 16, 64);
@@ -391,9 +447,7 @@ __device__ __forceinline__ void decode_body(const Params& p, int n_hgrp, int slo
         if (live_col) {
             const int64_t unit = static_cast<int64_t>(b) * per_b + uu;
             float* rec = static_cast<float*>(p.ws) + ((unit + wave) * slot_heads + col) * rec_stride(D);
-#pragma unroll
-            for (int d = 0; d < ND; ++d)
-                *reinterpret_cast<f32x4*>(rec + 4 + 16 * d + 4 * q4) = acc[d];
+            store_acc(rec);
             if (q4 == 0) {
                 rec[0] = m_ref;
                 rec[1] = lt;
@@ -402,9 +456,9 @@ __device__ __forceinline__ void decode_body(const Params& p, int n_hgrp, int slo
     };
 
     // Prefetch of one step, given the (entry, unit, step-in-unit) of that step.
-    constexpr int kEs = kI8 ? 1 : 2;                          // cache bytes per element
-    constexpr int kLd = kI8 ? L8::kLoads : LY::kLoads;
-    constexpr int kRpl = kI8 ? L8::kRowsPerLoad : LY::kRowsPerLoad;
+    constexpr int kEs = kF32 ? 4 : (kI8 ? 1 : 2);             // cache bytes per element
+    constexpr int kLd = kF32 ? FL::kLoads : (kI8 ? L8::kLoads : LY::kLoads);
+    constexpr int kRpl = kF32 ? FL::kRowsPerLoad : (kI8 ? L8::kRowsPerLoad : LY::kRowsPerLoad);
     i16x8 kst[kLd], vst[kLd];
     auto fetch = [&](int fb, int fuu, int64_t fls) {
         const int fg = fuu / n_hgrp;
@@ -448,7 +502,10 @@ __device__ __forceinline__ void decode_body(const Params& p, int n_hgrp, int slo
 #pragma unroll
         for (int n = 0; n < kLd; ++n) {
             const int row = n * kRpl + ld_row;
-            if (kI8) {
+            if (kF32) {
+                *reinterpret_cast<i16x8*>(&kf[row * FL::RS + ld_col]) = kst[n];
+                *reinterpret_cast<i16x8*>(&vf[row * FL::RS + ld_col]) = vst[n];
+            } else if (kI8) {
                 *reinterpret_cast<i16x8*>(&k8[row * L8::RS + ld_col]) = kst[n];
                 *reinterpret_cast<i16x8*>(&v8[row * L8::RS + ld_col]) = vst[n];
             } else {
@@ -469,7 +526,18 @@ __device__ __forceinline__ void decode_body(const Params& p, int n_hgrp, int slo
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             s[kb] = f32x4{};
-            if constexpr (kI8) {
+            if constexpr (kF32) {
+                // Operation t: A[col][q4] = K[16 kb + col][(D/4) q4 + t],
+                // B[q4][col] = Q[head col][(D/4) q4 + t].
+                const float* krow = &kf[(kb * 16 + col) * FL::RS + (D / 4) * q4];
+#pragma unroll
+                for (int m = 0; m < D / 16; ++m) {
+                    const f32x4 kv = *reinterpret_cast<const f32x4*>(krow + 4 * m);
+#pragma unroll
+                    for (int e2 = 0; e2 < 4; ++e2)
+                        s[kb] = __builtin_amdgcn_mfma_f32_16x16x4f32(kv[e2], qf[4 * m + e2], s[kb], 0, 0, 0);
+                }
+            } else if constexpr (kI8) {
                 const uint8_t* krow = &k8[(8 * (col >> 2) + 4 * kb + (col & 3)) * L8::RS + 8 * q4];
 #pragma unroll
                 for (int t = 0; t < NT; ++t)
@@ -528,14 +596,25 @@ __device__ __forceinline__ void decode_body(const Params& p, int n_hgrp, int slo
         const float sub = (m_ref == kNegInf || !nat) ? 0.f : m_ref;
         // P^T operand (16x16x32 B layout): k = 8*q4 + e <-> key key_at(e / 4, e % 4)
         // (fp16/bf16 rows: e < 4 ? 4*q4 + e : 16 + 4*q4 + e - 4; int8 rows: 8*q4 + e).
-        uint32_t w4[4];
+        uint32_t w4[4] = {0u, 0u, 0u, 0u};
+        float pf[2][4];                  // fp32 rows: p of key key_at(kb, r), not rounded
+        if constexpr (kF32) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int e2 = 0; e2 < 2; ++e2) {
-                w4[2 * kb + e2] = M::pack_out(fast_exp2(fmaf(s[kb][2 * e2] - sub, c, neg_mc)),
-                                              fast_exp2(fmaf(s[kb][2 * e2 + 1] - sub, c, neg_mc)));
-                l_sum = M::sum2(w4[2 * kb + e2], l_sum);
+                for (int r = 0; r < 4; ++r) {
+                    pf[kb][r] = fast_exp2(fmaf(s[kb][r] - sub, c, neg_mc));
+                    l_sum += pf[kb][r];
+                }
+        } else {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+                for (int e2 = 0; e2 < 2; ++e2) {
+                    w4[2 * kb + e2] = M::pack_out(fast_exp2(fmaf(s[kb][2 * e2] - sub, c, neg_mc)),
+                                                  fast_exp2(fmaf(s[kb][2 * e2 + 1] - sub, c, neg_mc)));
+                    l_sum = M::sum2(w4[2 * kb + e2], l_sum);
+                }
             }
         }
         const i16x8 pop = __builtin_bit_cast(i16x8, (uint4){w4[0], w4[1], w4[2], w4[3]});
@@ -546,7 +625,24 @@ __device__ __forceinline__ void decode_body(const Params& p, int n_hgrp, int slo
         // byte i of those eight rows, i.e. column 16*dt + (lane % 16) of keys
         // 8*q4 .. 8*q4 + 7, the P^T operand's keys.
         const int gi = lane & 15;
-        if constexpr (kI8) {
+        if constexpr (kF32) {
+            // Operation (kb, u): A[col][q4] = V[16 kb + 4 q4 + u][(D/16) col + dt],
+            // B[q4][col] = p of key 16 kb + 4 q4 + u (this lane's score r = u).
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const float* vrow = &vf[(16 * kb + 4 * q4 + u) * FL::RS + (D / 16) * col];
+#pragma unroll
+                    for (int m = 0; m < D / 64; ++m) {
+                        const f32x4 vv = *reinterpret_cast<const f32x4*>(vrow + 4 * m);
+#pragma unroll
+                        for (int e2 = 0; e2 < 4; ++e2)
+                            acc[4 * m + e2] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                                vv[e2], pf[kb][u], acc[4 * m + e2], 0, 0, 0);
+                    }
+                }
+        } else if constexpr (kI8) {
             const uint8_t* vr = &v8[(8 * q4 + (gi >> 1)) * L8::RS + 8 * (gi & 1)];
 #pragma unroll
             for (int d = 0; d < ND; ++d)
@@ -582,8 +678,7 @@ __device__ __forceinline__ void decode_body(const Params& p, int n_hgrp, int slo
         constexpr int RS = rec_stride(D);
         float* const recs = reinterpret_cast<float*>(smem_base);   // [wave][16 heads][RS]
         float* const rec = recs + (wave * 16 + col) * RS;
-#pragma unroll
-        for (int d = 0; d < ND; ++d) *reinterpret_cast<f32x4*>(rec + 4 + 16 * d + 4 * q4) = acc[d];
+        store_acc(rec);
         if (q4 == 0) {
             rec[0] = m_ref;
             rec[1] = lt;
@@ -592,7 +687,7 @@ __device__ __forceinline__ void decode_body(const Params& p, int n_hgrp, int slo
         // Fold the waves' records in wave order (= key order), then the sink,
         // the empty-row policy and the LSE, as the merge kernel does; items
         // (head, d) with d fastest, so the stores are contiguous.
-        using T = std::conditional_t<kBf16, bf16_t, _Float16>;
+        using T = std::conditional_t<kF32, float, std::conditional_t<kBf16, bf16_t, _Float16>>;
         const int nw = uniform32(blockDim.x >> 6);
         const int g = uu / n_hgrp, hbase = (uu % n_hgrp) * 16;
         const int nh = p.group - hbase < 16 ? p.group - hbase : 16;
@@ -624,18 +719,19 @@ __device__ __forceinline__ void decode_body(const Params& p, int n_hgrp, int slo
     }
 }
 
-template <bool kBf16, int D, bool kCap, bool kI8>
+template <bool kBf16, int D, bool kCap, bool kI8, bool kF32 = false>
 __global__ __launch_bounds__(64, 2) void decode_split_kernel(Params p, int n_hgrp, int slot_heads) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[kI8 ? I8Lay<D>::kWaveBytes : DLay<D>::kWaveBytes];
-    decode_body<kBf16, D, kCap, kI8, false>(p, n_hgrp, slot_heads, smem);
+    __shared__ __attribute__((aligned(16))) uint8_t
+        smem[kF32 ? F32Lay<D>::kWaveBytes : (kI8 ? I8Lay<D>::kWaveBytes : DLay<D>::kWaveBytes)];
+    decode_body<kBf16, D, kCap, kI8, false, kF32>(p, n_hgrp, slot_heads, smem);
 }
 
 // One workgroup per unit; nw = blockDim.x / 64 waves, nw * unit_wave_bytes()
 // bytes of dynamic LDS.
-template <bool kBf16, int D, bool kCap, bool kI8>
-__global__ __launch_bounds__(64 * unit_waves_max(D, kI8)) void decode_unit_kernel(Params p, int n_hgrp) {
+template <bool kBf16, int D, bool kCap, bool kI8, bool kF32 = false>
+__global__ __launch_bounds__(64 * unit_waves_max(D, kI8, kF32)) void decode_unit_kernel(Params p, int n_hgrp) {
     extern __shared__ __attribute__((aligned(16))) uint8_t dsmem[];
-    decode_body<kBf16, D, kCap, kI8, true>(p, n_hgrp, 0, dsmem);
+    decode_body<kBf16, D, kCap, kI8, true, kF32>(p, n_hgrp, 0, dsmem);
 }
 
 // One wave per (b, h): merge the records of the waves that covered its unit,
@@ -775,16 +871,16 @@ int64_t max_unit_steps(const Params& p) {
 
 // Waves per workgroup of the unit mode: one per step of the longest
 // possible unit, at most unit_waves_max.
-int unit_waves(const Params& p, int DP) {
+int unit_waves(const Params& p, int DP, bool f32) {
     const int64_t smax = max_unit_steps(p);
-    const int cap = unit_waves_max(DP, p.kv_int8 != 0);
+    const int cap = unit_waves_max(DP, p.kv_int8 != 0, f32);
     return smax < cap ? static_cast<int>(smax < 1 ? 1 : smax) : cap;
 }
 
 template <bool kBf16, int D>
 hipError_t launch_unit(const Params& p, hipStream_t s) {
     const int n_hgrp = slice_count(p.group);
-    const int nw = unit_waves(p, D);
+    const int nw = unit_waves(p, D, false);
     const dim3 g(static_cast<uint32_t>(static_cast<int64_t>(p.B) * p.Hkv * n_hgrp)), blk(64 * nw);
     const bool cap = p.softcap > 0.f;
     if (p.kv_int8) {
@@ -828,6 +924,34 @@ hipError_t launch_one(const Params& p, hipStream_t s, bool unit) {
     return hipGetLastError();
 }
 
+// fp32 Q/K/V (head dims up to 128): the same two modes.
+template <int D>
+hipError_t launch_one_f32(const Params& p, hipStream_t s, bool unit) {
+    const int n_hgrp = slice_count(p.group), hs = heads_per_slot(p.group);
+    const bool cap = p.softcap > 0.f;
+    if (unit) {
+        const int nw = unit_waves(p, D, true);
+        const dim3 g(static_cast<uint32_t>(static_cast<int64_t>(p.B) * p.Hkv * n_hgrp)), blk(64 * nw);
+        const size_t lds = static_cast<size_t>(nw) * unit_wave_bytes<D, false, true>();
+        if (cap)
+            hipLaunchKernelGGL((decode_unit_kernel<false, D, true, false, true>), g, blk, lds, s, p, n_hgrp);
+        else
+            hipLaunchKernelGGL((decode_unit_kernel<false, D, false, false, true>), g, blk, lds, s, p, n_hgrp);
+        return hipGetLastError();
+    }
+    const dim3 g(waves_total(D, false)), blk(64);
+    if (cap)
+        hipLaunchKernelGGL((decode_split_kernel<false, D, true, false, true>), g, blk, 0, s, p, n_hgrp, hs);
+    else
+        hipLaunchKernelGGL((decode_split_kernel<false, D, false, false, true>), g, blk, 0, s, p, n_hgrp, hs);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t rows = static_cast<int64_t>(p.B) * p.Hq;
+    const dim3 cgrid(static_cast<uint32_t>((rows + 3) / 4));
+    hipLaunchKernelGGL((decode_combine_kernel<float, D>), cgrid, dim3(256), 0, s, p, n_hgrp, hs);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 // The kernel's head dim for a true head dim D: 64, 128 or 256, columns past
@@ -845,17 +969,32 @@ size_t decode_workspace_bytes(int B, int Hq, int Hkv, int D) {
 }
 
 bool decode_split_supported(const Params& p, DType dt) {
-    if (dt != DType::BF16 && dt != DType::F16) return false;
-    // Head dims that are whole 16-byte chunks (whole 16-value chunks for an
-    // int8 cache) up to 256, run at 64, 128 or 256.
-    if (p.D < 8 || p.D > 256 || p.D % (p.kv_int8 ? 16 : 8) != 0) return false;
+    const bool f32 = dt == DType::F32;
+    if (f32) {
+        // fp32: head dims that are whole 16-byte chunks up to 128, run at 64
+        // or 128.
+        if (p.kv_int8 || p.D < 4 || p.D > 128 || p.D % 4 != 0) return false;
+    } else {
+        if (dt != DType::BF16 && dt != DType::F16) return false;
+        // Head dims that are whole 16-byte chunks (whole 16-value chunks for
+        // an int8 cache) up to 256, run at 64, 128 or 256.
+        if (p.D < 8 || p.D > 256 || p.D % (p.kv_int8 ? 16 : 8) != 0) return false;
+    }
     if (p.Lq != 1 || p.Lk == 0) return false;
     // Buffer offsets of one (b, kv head) slice are 32-bit, including the
     // up-to-one-step overrun past the live length.
+    const int64_t es = f32 ? 4 : 2;                  // bytes per element (int8: at most)
     if (p.ks.sr >= (1 << 24) || p.vs.sr >= (1 << 24)) return false;
-    if ((static_cast<int64_t>(p.Lk) + kStep) * p.ks.sr * 2 >= (int64_t(1) << 31) ||
-        (static_cast<int64_t>(p.Lk) + kStep) * p.vs.sr * 2 >= (int64_t(1) << 31))
+    if ((static_cast<int64_t>(p.Lk) + kStep) * p.ks.sr * es >= (int64_t(1) << 31) ||
+        (static_cast<int64_t>(p.Lk) + kStep) * p.vs.sr * es >= (int64_t(1) << 31))
         return false;
+    if (f32) {   // 16-byte loads of 4 floats
+        auto al4 = [](const void* ptr, const Strides& st) {
+            return reinterpret_cast<uintptr_t>(ptr) % 16 == 0 && st.sb % 4 == 0 &&
+                   st.sh % 4 == 0 && st.sr % 4 == 0;
+        };
+        return al4(p.q, p.qs) && al4(p.k, p.ks) && al4(p.v, p.vs);
+    }
     auto al = [](const void* ptr, const Strides& st, int a) {
         return reinterpret_cast<uintptr_t>(ptr) % (2 * a) == 0 && st.sb % a == 0 &&
                st.sh % a == 0 && st.sr % a == 0;
@@ -879,21 +1018,27 @@ bool decode_split_supported(const Params& p, DType dt) {
 // (16 when at most 256 waves run in all), 4 at 256 with 16-bit rows and 16
 // with int8 rows, while its workgroups fit in about two rounds on the GPU
 // (e.g. 64 entries of 2048 keys, or of a 2047-key window over 8192: 79 us
-// against 88 split; 64 entries of 8192 keys at 128: 190 against 173).
-bool decode_unit_preferred(const Params& p) {
+// against 88 split; 64 entries of 8192 keys at 128: 190 against 173).  fp32
+// rows: up to 8 steps per wave at 64 (16 entries of 2048 keys: 29 against 32
+// split), 4 at 128 (4 entries of 1024 keys: 36 against 26 split).
+bool decode_unit_preferred(const Params& p, DType dt) {
     const int DP = decode_padded_dim(p.D);
-    const bool i8 = p.kv_int8 != 0;
+    const bool i8 = p.kv_int8 != 0, f32 = dt == DType::F32;
     const int64_t smax = max_unit_steps(p);
-    const int nw = unit_waves(p, DP);
+    const int nw = unit_waves(p, DP, f32);
     const int64_t waves = static_cast<int64_t>(p.B) * p.Hkv * slice_count(p.group) * nw;
     const int64_t per_wave = (smax + nw - 1) / nw;
-    if (DP == 64 && !i8) return per_wave <= 16 && waves <= 8192;
+    if (DP == 64 && !i8 && !f32) return per_wave <= 16 && waves <= 8192;
+    // fp32 rows: four waves per workgroup at 128, eight at 64.
+    if (f32) return per_wave <= (DP == 128 ? 4 : 8) && waves <= 4096;
     const int64_t limit = i8 ? 16 : (DP == 256 ? 4 : (waves <= 256 ? 16 : 8));
     return per_wave <= limit && waves <= 4096;
 }
 
 hipError_t launch_decode_split(const Params& p, DType dt, hipStream_t s, bool unit) {
     const int DP = decode_padded_dim(p.D);
+    if (dt == DType::F32)
+        return DP == 64 ? launch_one_f32<64>(p, s, unit) : launch_one_f32<128>(p, s, unit);
     if (dt == DType::BF16)
         return DP == 64 ? launch_one<true, 64>(p, s, unit)
                         : (DP == 128 ? launch_one<true, 128>(p, s, unit)

@@ -295,6 +295,28 @@ def test_int8_cache_is_decode_only_and_checked():
                                 0, None) == sdpa.ERR_INVALID
 
 
+@pytest.mark.parametrize("D,split", [(128, True), (64, True), (100, True), (4, True),
+                                     (96, True), (130, False), (256, False), (50, False)])
+def test_decode_f32_head_dims(D, split):
+    """fp32 decode on the decode kernels: head dims that are whole 16-byte
+    chunks (multiples of 4) up to 128, padded to 64 or 128, with the same
+    records; others run as a forward call.  A forward call with one query row
+    needs the same workspace."""
+    B, Hq, Hkv, Lk = 3, 8, 2, 1000
+    p = _problem(batch=B, q_heads=Hq, kv_heads=Hkv, q_len=1, k_len=Lk, head_dim=D,
+                 dtype=sdpa.DTYPE_F32)
+    for lay, H, L in (("q", Hq, 1), ("k", Hkv, Lk), ("v", Hkv, Lk), ("o", Hq, 1)):
+        setattr(p, lay, sdpa.Layout(0, L * H * D, D, H * D))
+    need = sdpa.workspace_size(p, sdpa.OP_DECODE)
+    dp = 64 if D <= 64 else 128
+    split_bytes = (B * Hkv + 2048) * (Hq // Hkv) * (dp + 4) * 4
+    if split:
+        assert need >= split_bytes
+        assert sdpa.workspace_size(p, sdpa.OP_FORWARD) == need
+    else:
+        assert need != split_bytes
+
+
 @pytest.mark.parametrize("D,int8,split", [(96, 0, True), (40, 0, True), (8, 0, True),
                                          (136, 0, True), (256, 0, True), (112, 1, True),
                                          (48, 1, True), (208, 1, True), (24, 1, False),

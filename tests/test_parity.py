@@ -383,6 +383,12 @@ DECODE = [
     ("bf16", 2, 32, 8, 1000, 112, [1000, 999]),
     ("f16", 3, 8, 4, 700, 256, [700, 64, 333]),
     ("bf16", 2, 16, 2, 400, 200, [400, 1]),
+    # fp32 Q/K/V: head dims that are whole 16-byte chunks up to 128 (padded to 64/128)
+    ("f32", 4, 16, 4, 900, 128, [900, 1, 450, 0]),
+    ("f32", 3, 8, 8, 700, 64, [700, 65, 0]),
+    ("f32", 2, 32, 1, 513, 100, [513, 300]),
+    ("f32", 2, 4, 2, 300, 4, [300, 33]),
+    ("f32", 2, 48, 2, 2100, 96, [2100, 1000]),
 ]
 
 
@@ -569,6 +575,9 @@ VARIANTS = {
         "decode"),
     "decode_window0_bf16": (synth.DECODE_F16.replace(
         dtype="bf16", batch=8, k_len=700, head_dim=64, local_window=0, seed=28), "decode"),
+    "decode_f32_window_cap_sink": (synth.DECODE_F16.replace(
+        dtype="f32", batch=4, k_len=900, local_window=100, softcap=30.0, sink="heads", seed=39),
+        "decode"),
     "decode_sink_zero_lens0": (synth.DECODE_F16.replace(
         batch=8, k_len=500, lens="cross", lens_zero_at=3, lens_full_at=4, sink="zero",
         local_window=3000, seed=29), "decode"),
@@ -968,8 +977,11 @@ def test_decode_mode_chosen_by_shape():
     """Small decodes (each wave a few steps) run one workgroup per unit with
     no merge; long caches run the split over equal shares plus the merge."""
     small = synth.PAGE_SHAPES["Whisper-small decoder step B1 H12 cache448 D64 fp16"]
+    small32 = synth.PAGE_SHAPES["Whisper-small decoder step B1 H12 cache448 D64"]
     long = synth.DECODE_F16.replace(batch=2, q_heads=8, kv_heads=2, k_len=8192, seed=62)
-    for spec, want in ((small, "decode_unit"), (long, "decode_splitk")):
+    long32 = long.replace(dtype="f32", seed=63)
+    for spec, want in ((small, "decode_unit"), (small32, "decode_unit"), (long, "decode_splitk"),
+                       (long32, "decode_splitk")):
         case = synth.generate(spec)
         o, lse, _ = pu.run_hip(case, "nan", return_lse=True)
         assert sdpa.last_kernel() == want, spec.name
@@ -991,6 +1003,12 @@ FORWARD_ONE_ROW = {
         lens_full_at=3, softcap=10.0, sink="heads", seed=64),
     "mask_lens_bf16_D128": synth.CROSS_MASK_F16.replace(
         dtype="bf16", batch=8, q_heads=8, kv_heads=8, q_len=1, k_len=777, head_dim=128, seed=65),
+    "whisper_cross_f32": synth.PAGE_SHAPES["Whisper-small cross-attention B1 H12 Lq1 Lk1500 D64"],
+    "mask_lens_f32_D64": synth.CROSS_MASK_F16.replace(
+        dtype="f32", batch=6, q_heads=8, kv_heads=8, q_len=1, k_len=555, head_dim=64, seed=66),
+    "offset_window_docs_f32": synth.CAUSAL_GQA_F32.replace(
+        batch=3, q_heads=8, kv_heads=2, q_len=1, k_len=500, head_dim=128, causal_offset=300,
+        local_window=60, docs="random", seed=67),
 }
 
 
