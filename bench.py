@@ -384,7 +384,8 @@ def other_workloads(sdpa, synth, steps: int, warmup: int, only=None):
     specs += [(n, synth.EXTRA_WORKLOADS[n])
               for n in ("chunk_f16", "long_chunk_bf16", "window_bf16", "softcap_sink_bf16",
                         "docs_bf16", "d96_bf16", "d256_bf16", "d100_bf16", "d96_f32",
-                        "decode_window_f16", "decode_int8_f16", "decode_d96_f16")]
+                        "decode_window_f16", "decode_int8_f16", "decode_d96_f16",
+                        "decode_f32")]
     specs += list(synth.PAGE_SHAPES.items())
     if only:
         unknown = set(only) - {n for n, _ in specs}

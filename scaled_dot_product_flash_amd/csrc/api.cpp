@@ -291,8 +291,16 @@ attn_status attn_forward(const attn_problem* p, const void* q, const void* k, co
     const hipStream_t s = static_cast<hipStream_t>(stream);
     // One query row (a cross-attention step, or decode called as a forward):
     // the decode kernels read each live K/V row once for a whole head group,
-    // where a prefill tile would fill one of its rows.
-    if (!force_generic() && p->q_len == 1 && sdpa::decode_split_supported(prm, dt))
+    // where a prefill tile would fill one of its rows.  Except small fp32
+    // problems without head groups (fewer than 64 kv heads in all): there
+    // the fp32 prefill kernel's key ranges spread the few heads wider than
+    // the decode kernels, whose fp32 steps cost 16 columns of matrix work
+    // for the one head (the Whisper cross-attention step, 12 heads of 1500
+    // keys: 18.9 us against 21.3).
+    const bool small_mha_f32 = dt == sdpa::DType::F32 && p->q_heads == p->kv_heads &&
+                               static_cast<int64_t>(p->batch) * p->kv_heads < 64;
+    if (!force_generic() && p->q_len == 1 && !small_mha_f32 &&
+        sdpa::decode_split_supported(prm, dt))
         return run_decode(p, prm, dt, s, workspace, workspace_bytes);
     if (!force_generic() && (dt == sdpa::DType::BF16 || dt == sdpa::DType::F16)) {
         sdpa::prefill_mfma_plan(p->batch, p->q_heads, p->kv_heads, p->q_len, p->k_len,

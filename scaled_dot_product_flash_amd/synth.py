@@ -146,6 +146,8 @@ D96_F32 = CAUSAL_GQA_BF16.replace(
 # Decode at a head dim below 128 (run padded to 128 by the split decode path).
 DECODE_D96_F16 = DECODE_F16.replace(name="fp16 decode B64 H32/8 cache8192 D96", head_dim=96,
                                     seed=17)
+# The decode shape with fp32 Q/K/V.
+DECODE_F32 = DECODE_F16.replace(name="fp32 decode B64 H32/8 cache8192 D128", dtype="f32", seed=18)
 
 # Workloads of the extensions beyond the five (measured and tested the same way).
 EXTRA_WORKLOADS = {
@@ -161,6 +163,7 @@ EXTRA_WORKLOADS = {
     "d100_bf16": D100_BF16,
     "d96_f32": D96_F32,
     "decode_d96_f16": DECODE_D96_F16,
+    "decode_f32": DECODE_F32,
 }
 
 # The model shapes the OneGPU "Attention" page times (its "Performance"

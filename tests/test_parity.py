@@ -480,6 +480,8 @@ def test_fp32_vector_path(cfg, monkeypatch):
         case = synth.Case(spec, case.q, case.k, case.v, case.key_lens, m)
     for policy in ("nan", "zero"):
         o1, l1, (_, _, tens) = pu.run_hip(case, policy)
+        # (The one-row case is a small problem without head groups, which
+        # stays on this kernel rather than the decode kernels.)
         assert sdpa.last_kernel() == "prefill_f32"
         ro, rl = pu.run_oracle(case, policy)
         pu.compare(o1, ro, l1, rl, "f32", policy, what="f32 %s" % (cfg,))
@@ -687,6 +689,16 @@ def test_int8_cache_decode(name, policy, mode, monkeypatch):
 def test_decode_d96_full_size_every_row():
     """Decode at head dim 96 (padded to 128 on the split path) at full size."""
     spec = synth.EXTRA_WORKLOADS["decode_d96_f16"]
+    case = synth.generate(spec)
+    o, lse, _ = pu.run_hip(case, "nan", return_lse=True)
+    assert sdpa.last_kernel() == "decode_splitk"
+    ro, rl = pu.run_oracle(case, "nan")
+    pu.compare(o, ro, lse, rl, spec.dtype, "nan", what=spec.name)
+
+
+def test_decode_f32_full_size_every_row():
+    """fp32 decode at the decode workload's shape (split mode) on every row."""
+    spec = synth.EXTRA_WORKLOADS["decode_f32"]
     case = synth.generate(spec)
     o, lse, _ = pu.run_hip(case, "nan", return_lse=True)
     assert sdpa.last_kernel() == "decode_splitk"
@@ -1003,13 +1015,27 @@ FORWARD_ONE_ROW = {
         lens_full_at=3, softcap=10.0, sink="heads", seed=64),
     "mask_lens_bf16_D128": synth.CROSS_MASK_F16.replace(
         dtype="bf16", batch=8, q_heads=8, kv_heads=8, q_len=1, k_len=777, head_dim=128, seed=65),
-    "whisper_cross_f32": synth.PAGE_SHAPES["Whisper-small cross-attention B1 H12 Lq1 Lk1500 D64"],
+    "gqa_cross_f32": synth.PAGE_SHAPES["Whisper-small cross-attention B1 H12 Lq1 Lk1500 D64"].replace(
+        batch=2, q_heads=16, kv_heads=4, seed=68),
     "mask_lens_f32_D64": synth.CROSS_MASK_F16.replace(
-        dtype="f32", batch=6, q_heads=8, kv_heads=8, q_len=1, k_len=555, head_dim=64, seed=66),
+        dtype="f32", batch=6, q_heads=16, kv_heads=4, q_len=1, k_len=555, head_dim=64, seed=66),
     "offset_window_docs_f32": synth.CAUSAL_GQA_F32.replace(
         batch=3, q_heads=8, kv_heads=2, q_len=1, k_len=500, head_dim=128, causal_offset=300,
         local_window=60, docs="random", seed=67),
 }
+
+
+def test_small_mha_f32_one_row_stays_on_the_f32_kernel():
+    """fp32 single-row forwards without head groups and with fewer than 64 kv
+    heads in all run on the fp32 prefill kernel (its key ranges spread the few
+    heads wider); with head groups they run on the decode kernels."""
+    cross = synth.PAGE_SHAPES["Whisper-small cross-attention B1 H12 Lq1 Lk1500 D64"]
+    for spec, want in ((cross, "prefill_f32"), (cross.replace(q_heads=48, seed=69), "decode_unit")):
+        case = synth.generate(spec)
+        o, lse, _ = pu.run_hip(case, "nan", return_lse=True)
+        assert sdpa.last_kernel() == want, spec
+        ro, rl = pu.run_oracle(case, "nan")
+        pu.compare(o, ro, lse, rl, spec.dtype, "nan", what="%s %s" % (spec.name, want))
 
 
 @pytest.mark.parametrize("name", sorted(FORWARD_ONE_ROW))
