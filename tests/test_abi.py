@@ -346,3 +346,19 @@ def test_decode_split_head_dims(D, int8, split):
         assert rc == sdpa.ERR_UNSUPPORTED and b"multiple of 16" in lib.attn_last_error()
     else:
         assert need != split_bytes
+
+
+def test_int8_cache_with_fp32_query_is_unsupported():
+    """An int8 cache is read with fp16/bf16 queries only; an fp32 problem with
+    kv_int8 = 1 is refused before anything runs (the fp32 decode kernels read
+    fp32 rows)."""
+    lib = sdpa.load_library()
+    B, Hq, Hkv, Lk, D = 2, 8, 2, 256, 64
+    p = _problem(batch=B, q_heads=Hq, kv_heads=Hkv, q_len=1, k_len=Lk, head_dim=D,
+                 dtype=sdpa.DTYPE_F32, kv_int8=1, k_quant=1, v_quant=1, k_scale=0x1000,
+                 v_scale=0x1000)
+    for lay, H, L in (("q", Hq, 1), ("k", Hkv, Lk), ("v", Hkv, Lk), ("o", Hq, 1)):
+        setattr(p, lay, sdpa.Layout(0, L * H * D, D, H * D))
+    rc = lib.attn_decode(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, None, None, FAKE,
+                         1 << 30, None)
+    assert rc == sdpa.ERR_UNSUPPORTED and b"fp16/bf16" in lib.attn_last_error()
